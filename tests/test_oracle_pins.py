@@ -1,0 +1,467 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+None of these retypes the oracle's own formula: each checks an identity, a
+worked example the pages print, a hand-worked value, a library routine that
+implements the same definition independently, or brute force on tiny
+inputs. A plausible slip in the oracle (a dropped term, a wrong sign or
+index, a transposed operand) fails at least one of them; the mutation tests
+at the end plant such slips in a copy of the oracle and check that.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- P1 cosine
+
+def test_p1_cosine_identities():
+    rng = np.random.default_rng(1)
+    a = rng.standard_normal((50, 33))
+    cos, *_ = O.route(a, a, None, 1e-6, None, None, -np.inf, -np.inf)
+    assert np.all(cos == 1.0)                       # cos(a, a) = 1 exactly
+    cos, *_ = O.route(a, -a, None, 1e-6, None, None, -np.inf, -np.inf)
+    assert np.all(cos == -1.0)                      # cos(a, -a) = -1
+    k = rng.uniform(0.1, 10.0, size=(50, 1))
+    cos, *_ = O.route(a, k * a, None, 1e-6, None, None, -np.inf, -np.inf)
+    assert np.allclose(cos, 1.0, atol=1e-15, rtol=0)
+    # orthogonal pair
+    x = np.zeros((2, 4)); y = np.zeros((2, 4))
+    x[0, 0] = 3.0; y[0, 1] = -2.0
+    x[1] = [1, 1, 0, 0]; y[1] = [1, -1, 5, 0]
+    cos, *_ = O.route(x, y, None, 1e-6, None, None, -np.inf, -np.inf)
+    assert np.all(cos == 0.0)
+    # zero vector: defined as 0; NaN input: NaN cosine, never exits
+    z = np.zeros((1, 4)); w = np.array([[1.0, 2.0, 3.0, np.nan]])
+    cos, _, mask, _ = O.route(z, z + 1, None, 1e-6, None, None, -np.inf, -np.inf)
+    assert cos[0] == 0.0
+    cos, _, mask, _ = O.route(w, w, None, 1e-6, None, None, -np.inf, -np.inf)
+    assert np.isnan(cos[0]) and mask[0] == 0
+
+
+def test_p1_cosine_matches_scipy_and_bounds():
+    from scipy.spatial.distance import cdist
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal((100_000, 8))
+    b = rng.standard_normal((100_000, 8)) * rng.uniform(0.01, 100, (100_000, 1))
+    cos, *_ = O.route(a, b, None, 1e-6, None, None, -np.inf, -np.inf)
+    assert np.all(cos <= 1.0) and np.all(cos >= -1.0)         # Cauchy-Schwarz
+    ref = 1.0 - np.array([cdist(a[i:i + 1], b[i:i + 1], "cosine")[0, 0] for i in range(200)])
+    assert np.allclose(cos[:200], ref, atol=1e-12, rtol=0)
+
+
+# ------------------------------------------------------- P2 the schedule
+
+def test_p2_tide_figure2_worked_example():
+    g = _gold("tide_fig2_schedule.json")
+    r = O.exit_schedule_ops(g["exit_layers"], g["n_layers"])
+    assert r["executed"] == g["executed"] == 56
+    assert r["baseline"] == g["baseline"] == 96
+    assert round(100 * r["reduction"]) == g["reduction_percent_rounded"]
+    # every skipped (token, layer) is filled: executed + filled = baseline
+    assert r["filled"] == 40 and r["executed"] + r["filled"] == r["baseline"]
+    with pytest.raises(ValueError):
+        O.exit_schedule_ops([0], 32)
+
+
+# ------------------------------------------------------------ P3 ridge
+
+def _ridge_obj(X, Y, W, lam):
+    # W in output-major layout [d_out][d_in]
+    R = X @ W.T - Y
+    return float(np.sum(R * R) + lam * np.sum(W * W))
+
+
+def test_p3_ridge_normal_equations_and_orientation():
+    rng = np.random.default_rng(3)
+    n, d_in, d_out, T = 40, 7, 5, 3
+    X = rng.standard_normal((n, d_in))
+    Y = rng.standard_normal((T, n, d_out))
+    lam = 0.3
+    W = O.ridge_fit(X, Y, lam)
+    assert W.shape == (T, d_out, d_in)
+    G = X.T @ X + lam * np.eye(d_in)
+    for t in range(T):
+        res = G @ W[t].T - X.T @ Y[t]
+        assert np.linalg.norm(res) <= 1e-10 * np.linalg.norm(X.T @ Y[t])
+
+
+def test_p3_ridge_matches_lstsq_and_sklearn():
+    from sklearn.linear_model import Ridge
+    rng = np.random.default_rng(4)
+    n, d = 64, 8
+    X = rng.standard_normal((n, d))
+    Y = rng.standard_normal((2, n, 3))
+    # lambda -> 0 on a full-rank system: ordinary least squares
+    W = O.ridge_fit(X, Y, 1e-12)
+    for t in range(2):
+        ls = np.linalg.lstsq(X, Y[t], rcond=None)[0]       # [d_in][d_out]
+        assert np.allclose(W[t], ls.T, atol=1e-9)
+    # an independent ridge implementation, no intercept
+    W = O.ridge_fit(X, Y, 2.5)
+    for t in range(2):
+        sk = Ridge(alpha=2.5, fit_intercept=False, solver="svd").fit(X, Y[t])
+        assert np.allclose(W[t], sk.coef_, atol=1e-10)
+
+
+def test_p3_ridge_closed_forms():
+    rng = np.random.default_rng(5)
+    n, d = 50, 6
+    X = rng.standard_normal((n, d))
+    Wstar = rng.standard_normal((4, d))                       # output-major
+    # exact linear targets, lambda = 0: the map is recovered
+    W = O.ridge_fit(X, (X @ Wstar.T)[None], 0.0)
+    assert np.allclose(W[0], Wstar, atol=1e-10)
+    # Y = X: W = I - lambda (X^T X + lambda I)^-1
+    lam = 0.7
+    W = O.ridge_fit(X, X[None], lam)
+    G = X.T @ X + lam * np.eye(d)
+    assert np.allclose(W[0], np.eye(d) - lam * np.linalg.inv(G), atol=1e-12)
+    # lambda -> infinity: W -> 0, bounded by |X^T Y| / lambda
+    Y = rng.standard_normal((1, n, 3))
+    W = O.ridge_fit(X, Y, 1e12)
+    assert np.linalg.norm(W) <= np.linalg.norm(X.T @ Y[0]) / 1e12 * 1.0001
+
+
+def test_p3_ridge_brute_force_minimum():
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((12, 3))
+    Y = rng.standard_normal((1, 12, 2))
+    lam = 0.5
+    W = O.ridge_fit(X, Y, lam)[0]
+    f0 = _ridge_obj(X, Y[0], W, lam)
+    for _ in range(2000):
+        P = rng.standard_normal(W.shape) * rng.choice([1e-1, 1e-3, 1e-5])
+        assert _ridge_obj(X, Y[0], W + P, lam) >= f0 - 1e-12
+
+
+# ---------------------------------------------------------- P4 compaction
+
+def _check_partition(mask, res, h):
+    n = len(mask)
+    cont, ext = list(res["cont_idx"]), list(res["exit_idx"])
+    assert set(cont).isdisjoint(ext)
+    assert sorted(cont + ext) == list(range(n))
+    assert cont == sorted(cont) and ext == sorted(ext)
+    assert all(mask[i] == 0 for i in cont) and all(mask[i] != 0 for i in ext)
+    assert list(res["counts"]) == [len(cont), len(ext)]
+    if h is not None:
+        for j, i in enumerate(cont):
+            assert np.array_equal(res["h_cont"][j], h[i])
+
+
+def test_p4_compaction_exhaustive_small():
+    for n in range(0, 13):
+        h = np.arange(n * 2, dtype=np.float64).reshape(n, 2)
+        for bits in range(1 << n):
+            mask = np.array([(bits >> i) & 1 for i in range(n)], dtype=np.uint8)
+            _check_partition(mask, O.compact(mask, h), h)
+
+
+@pytest.mark.parametrize("n", [0, 1, 63, 64, 65, 1023, 1024, 1025, 8192])
+def test_p4_compaction_edges(n):
+    rng = np.random.default_rng(n)
+    h = rng.standard_normal((n, 3))
+    rid = rng.permutation(4 * n + 1)[:n] if n else np.zeros(0, dtype=np.int64)
+    out = np.full((4 * n + 1, 3), np.nan)
+    for mask in (np.zeros(n, np.uint8), np.ones(n, np.uint8),
+                 (rng.random(n) < 0.3).astype(np.uint8)):
+        res = O.compact(mask, h, rid, out)
+        _check_partition(mask, res, h)
+        assert np.array_equal(res["row_ids_cont"], rid[res["cont_idx"]])
+        # exit scatter: exited rows land at their row id, nothing else moves
+        o = res["out"]
+        hit = set(int(rid[i]) for i in res["exit_idx"])
+        for i in res["exit_idx"]:
+            assert np.array_equal(o[rid[i]], h[i])
+        for r in range(o.shape[0]):
+            if r not in hit:
+                assert np.all(np.isnan(o[r]))
+
+
+# ------------------------------------------------------------- P5 kv fill
+
+def _hand_w4(n_layers, n_out, d, group, rng):
+    q = rng.integers(0, 256, size=(n_layers, n_out, d // 2), dtype=np.uint8)
+    s = rng.uniform(0.01, 0.1, size=(n_layers, n_out, d // group))
+    z = rng.uniform(0, 15, size=(n_layers, n_out, d // group))
+    return {"q": q, "scale": s, "zero": z, "group": group}
+
+
+def test_p5_identity_fill_is_direct_projection():
+    rng = np.random.default_rng(7)
+    d, Hkv, Dh, nl = 16, 2, 4, 3
+    wk = _hand_w4(nl, Hkv * Dh, d, 8, rng)
+    wv = _hand_w4(nl, Hkv * Dh, d, 8, rng)
+    # one-hot rows: the projection of e_k is column k of the dequantized weights
+    h = np.eye(d)[[3, 0, 11, 15]]
+    K, V = O.kv_fill_rows(h, None, 4, None, wk, wv)
+    Ke, Ve = O.kv_fill_rows(h, None, 4, np.stack([np.eye(d)] * nl), wk, wv)
+    assert np.array_equal(K, Ke) and np.array_equal(V, Ve)
+    for l in range(nl):
+        Wk = O.dequant_w4(wk["q"][l], wk["scale"][l], wk["zero"][l], 8)
+        for t, k in enumerate([3, 0, 11, 15]):
+            # hand unpack of element k of every output row
+            byte = wk["q"][l][:, k // 2]
+            nib = (byte & 15) if k % 2 == 0 else (byte >> 4)
+            want = (nib - wk["zero"][l][:, k // 8]) * wk["scale"][l][:, k // 8]
+            assert np.allclose(K[l, t], want, rtol=0, atol=1e-15)
+            assert np.allclose(Wk[:, k], want, rtol=0, atol=1e-15)
+
+
+def test_p5_map_orientation_and_slots():
+    rng = np.random.default_rng(8)
+    d, Hkv, Dh, nl = 8, 2, 2, 2
+    wk = _hand_w4(nl, Hkv * Dh, d, 4, rng)
+    wv = _hand_w4(nl, Hkv * Dh, d, 4, rng)
+    perm = [rng.permutation(d) for _ in range(nl)]
+    maps = np.zeros((nl, d, d))
+    for l in range(nl):
+        for j in range(d):
+            maps[l, j, perm[l][j]] = 1.0      # x_hat[j] = x[perm[j]]
+    h = rng.standard_normal((5, d))
+    row_idx = np.array([4, 1, 2])
+    slot = np.array([9, 3, 0, 7, 5])           # slot of each row of h
+    kc0 = np.full((nl, 10, Hkv, Dh), np.nan)
+    kc, vc = O.kv_fill(h, row_idx, 3, slot, maps, wk, wv, Hkv, Dh, kc0, kc0)
+    for l in range(nl):
+        Wk = O.dequant_w4(wk["q"][l], wk["scale"][l], wk["zero"][l], 4)
+        for t, r in enumerate(row_idx):
+            xh = h[r][perm[l]]
+            want = np.array([sum(Wk[o, j] * xh[j] for j in range(d)) for o in range(Hkv * Dh)])
+            assert np.allclose(kc[l, slot[r]].reshape(-1), want, atol=1e-12)
+            # head split: output o goes to head o // Dh, dim o % Dh
+            assert np.allclose(kc[l, slot[r], 1, 0], want[Dh], atol=1e-12)
+    untouched = [s for s in range(10) if s not in (5, 3, 0)]
+    assert np.all(np.isnan(kc[:, untouched]))
+
+
+# -------------------------------------------------------------- P6 router
+
+def test_p6_router_zero_weights_tie():
+    rng = np.random.default_rng(9)
+    h = rng.standard_normal((10, 16))
+    cos, prob, mask, all_exit = O.route(h, h, None, 1e-6, np.zeros((4, 16)), np.ones(4),
+                                         -np.inf, 0.5)
+    assert np.all(prob == 0.5)           # SiLU(0) = 0, sigmoid(0) = 1/2
+    assert np.all(mask == 0) and all_exit == 0   # strict: a tie continues
+
+
+def test_p6_router_param_count():
+    g = _gold("tide_router_params.json")
+    d, b = g["d"], g["b"]
+    n_params = np.zeros((b, d)).size + np.zeros((1, b)).size
+    assert n_params == 524_416
+    assert round(n_params / 1000) == g["approx_params_thousands"]
+
+
+def test_p6_router_matches_torch_functional():
+    import torch.nn.functional as F
+    rng = np.random.default_rng(10)
+    n, d, b = 37, 24, 6
+    hp = rng.standard_normal((n, d))
+    hc = rng.standard_normal((n, d)) * rng.uniform(0.1, 5, (n, 1))
+    gam = rng.uniform(0.5, 1.5, d)
+    wd = rng.standard_normal((b, d)) / math.sqrt(d)
+    wu = rng.standard_normal(b)
+    eps = 1e-5
+    _, prob, _, _ = O.route(hp, hc, gam, eps, wd, wu, -np.inf, -np.inf)
+    t = torch.from_numpy(hc)
+    x = F.rms_norm(t, (d,), weight=torch.from_numpy(gam), eps=eps)
+    z = F.linear(F.silu(F.linear(x, torch.from_numpy(wd))), torch.from_numpy(wu)[None])
+    ref = torch.sigmoid(z)[:, 0].numpy()
+    assert np.allclose(prob, ref, atol=1e-14, rtol=0)
+
+
+# ------------------------------------------------------------- P7 RMSNorm
+
+def test_p7_rmsnorm_scale_invariance():
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((20, 32))
+    wd = rng.standard_normal((8, 32))
+    wu = rng.standard_normal(8)
+    _, p1, _, _ = O.route(h, h, None, 0.0, wd, wu, -np.inf, -np.inf)
+    for c in (1e-3, 0.5, 7.0, 1e4):
+        _, pc, _, _ = O.route(h, c * h, None, 0.0, wd, wu, -np.inf, -np.inf)
+        assert np.allclose(p1, pc, atol=1e-13, rtol=0)
+    # eps matters only at small scale: p(c h) -> p(0) = sigmoid(W_up . SiLU(0))
+    _, p0, _, _ = O.route(h, 1e-9 * h, None, 1e-2, wd, wu, -np.inf, -np.inf)
+    assert np.allclose(p0, 0.5, atol=1e-6)
+
+
+# ------------------------------------------------------------- P8 dequant
+
+def test_p8_dequant_hand_example():
+    g = _gold("w4_dequant_hand.json")
+    got = O.dequant_w4(np.array(g["q_bytes"], np.uint8), np.array(g["scale"]),
+                       np.array(g["zero"]), g["group"])
+    assert np.array_equal(got, np.array(g["expected"]))
+
+
+@pytest.mark.parametrize("group,sz", [(32, "f32"), (64, "bf16"), (128, "bf16")])
+def test_p8_round_to_nearest_error_bound(group, sz):
+    from synth.generate import quantize_w4
+    g = torch.Generator().manual_seed(group)
+    w = torch.randn((16, 512), generator=g) / 20
+    q, s, z = quantize_w4(w, group, sz)
+    deq = O.dequant_w4(q.numpy(), s.float().numpy(), z.float().numpy(), group)
+    sf = np.repeat(s.float().numpy().astype(np.float64), group, axis=-1)
+    err = np.abs(deq - w.numpy().astype(np.float64))
+    assert np.all(err <= sf * (0.5 + 1e-5))
+
+
+# ------------------------------------------------------ P9 KV integrity
+
+def test_p9_kv_integrity_full_schedule():
+    """Every (token, layer > e) slot is written exactly once and nothing
+    else changes (River-LLM, 研究动机: Intrinsic KV Integrity)."""
+    rng = np.random.default_rng(12)
+    L, d, Hkv, Dh, n, n_slots = 8, 16, 2, 4, 24, 40
+    slot = rng.permutation(n_slots)[:n]
+    exits = rng.choice([2, 4, 6, 8], size=n)
+    wk = _hand_w4(L, Hkv * Dh, d, 8, rng)
+    wv = _hand_w4(L, Hkv * Dh, d, 8, rng)
+    h = rng.standard_normal((n, d))
+    kc = np.full((L, n_slots, Hkv, Dh), np.nan)
+    vc = kc.copy()
+    written = {}
+    for e in (2, 4, 6, 8):
+        rows = np.flatnonzero(exits == e)
+        if e == L or len(rows) == 0:
+            continue
+        sub = lambda w: {"q": w["q"][e:], "scale": w["scale"][e:], "zero": w["zero"][e:], "group": 8}
+        k2, v2 = O.kv_fill(h, rows, len(rows), slot, None, sub(wk), sub(wv), Hkv, Dh,
+                           kc[e:], vc[e:])
+        for l in range(L - e):
+            for r in rows:
+                key = (e + l, int(slot[r]))
+                written[key] = written.get(key, 0) + 1
+        kc[e:], vc[e:] = k2, v2
+    assert all(c == 1 for c in written.values())
+    expect = {(l, int(slot[r])) for r in range(n) for l in range(exits[r], L)}
+    assert set(written) == expect
+    for l in range(L):
+        for s in range(n_slots):
+            filled = not np.any(np.isnan(kc[l, s]))
+            assert filled == ((l, s) in expect)
+            assert filled == (not np.any(np.isnan(vc[l, s])))
+
+
+# ----------------------------------------------------------- P10 batch rule
+
+def test_p10_batch_rule_is_min_rule():
+    rng = np.random.default_rng(13)
+    d = 12
+    wd = rng.standard_normal((4, d)); wu = rng.standard_normal(4)
+    for trial in range(300):
+        n = int(rng.integers(1, 9))
+        hp = rng.standard_normal((n, d))
+        hc = hp + rng.uniform(0, 1.5) * rng.standard_normal((n, d))
+        tau = float(rng.uniform(-0.5, 1.0)); theta = float(rng.uniform(0, 1))
+        cos, prob, mtok, all_tok = O.route(hp, hc, None, 1e-6, wd, wu, tau, theta, O.RULE_TOKEN)
+        _, _, mb, all_b = O.route(hp, hc, None, 1e-6, wd, wu, tau, theta, O.RULE_BATCH_MIN)
+        want = int(cos.min() > tau and prob.min() > theta)
+        assert all_tok == all_b == want
+        assert np.all(mb == want)
+        assert all_tok == int(np.all(mtok == 1))
+    # adversarial: one token exactly at the threshold holds the batch back
+    hp = rng.standard_normal((4, d)); hc = hp.copy()
+    _, _, m, a = O.route(hp, hc, None, 1e-6, None, None, 1.0, -np.inf, O.RULE_BATCH_MIN)
+    assert a == 0 and np.all(m == 0)     # cos == 1 == tau is not > tau
+    _, _, m, a = O.route(hp, hc, None, 1e-6, wd, wu, 1.0, -np.inf, O.RULE_TOKEN)
+    assert a == 0 and np.all(m == 0)     # the same with the router on
+    _, _, m, a = O.route(hp, hc, None, 1e-6, 0 * wd, wu, -np.inf, 0.5, O.RULE_TOKEN)
+    assert a == 0 and np.all(m == 0)     # prob == 0.5 == theta is not > theta
+    _, _, m, a = O.route(hp[:0], hc[:0], None, 1e-6, None, None, 0.0, 0.0)
+    assert a == 0 and m.size == 0
+
+
+# --------------------------------------------------- P11 generator shape
+
+def test_p11_cosine_rises_with_depth():
+    from synth import get_config
+    from synth.generate import hidden_states
+    for idx in (0, 1):
+        cfg = get_config(idx)
+        hs = hidden_states(cfg, 256, range(0, cfg.L + 1))
+        means = []
+        for l in range(1, cfg.L + 1):
+            c, *_ = O.route(hs[l - 1].double().numpy(), hs[l].double().numpy(), None,
+                            1e-6, None, None, -np.inf, -np.inf)
+            means.append(c.mean())
+        assert all(b > a for a, b in zip(means, means[1:]))
+
+
+# --------------------------------------------------------- mutation checks
+
+def _mutant_oracle(old, new):
+    """A copy of the oracle module with one textual slip planted."""
+    import inspect
+    import types
+    import oracle.river_oracle as R
+    src = inspect.getsource(R)
+    assert src.count(old) >= 1, old
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+MUTANTS = [
+    # wrong operand in the cosine denominator
+    ("cos[ok] = dot[ok] / np.sqrt(na[ok] * nb[ok])",
+     "cos[ok] = dot[ok] / np.sqrt(na[ok] * na[ok])", "test_p1_cosine_matches_scipy_and_bounds"),
+    # RMSNorm without the mean over d
+    ("r = 1.0 / np.sqrt(nb / d + eps)", "r = 1.0 / np.sqrt(nb + eps)",
+     "test_p6_router_matches_torch_functional"),
+    # gamma dropped
+    ("x = b * g[None, :] * r[:, None]", "x = b * r[:, None]",
+     "test_p6_router_matches_torch_functional"),
+    # SiLU replaced by a sigmoid
+    ("act = u * _sigmoid(u)", "act = _sigmoid(u)", "test_p6_router_zero_weights_tie"),
+    # non-strict threshold
+    ("e = (cos > tau) & (prob > theta)", "e = (cos >= tau) & (prob > theta)",
+     "test_p10_batch_rule_is_min_rule"),
+    # inverted partition
+    ("if mask[i] != 0:", "if mask[i] == 0:", "test_p4_compaction_exhaustive_small"),
+    # nibble order swapped
+    ("lo = (q & 0x0F).astype(np.float64)", "lo = (q >> 4).astype(np.float64)",
+     "test_p8_dequant_hand_example"),
+    # zero point applied after the scale
+    ("return (vals - z) * s", "return vals * s - z", "test_p8_dequant_hand_example"),
+    # map applied transposed
+    ("xh = x if maps is None else x @ _f64(maps[l]).T",
+     "xh = x if maps is None else x @ _f64(maps[l])", "test_p5_map_orientation_and_slots"),
+    # projection weights applied transposed
+    ("K[l] = xh @ Wk.T", "K[l] = (xh @ Wk.T)[:, ::-1]", "test_p5_identity_fill_is_direct_projection"),
+    # ridge term dropped
+    ("G = X.T @ X + lam * np.eye(d_in)", "G = X.T @ X + np.eye(d_in)",
+     "test_p3_ridge_matches_lstsq_and_sklearn"),
+    # ridge result left input-major
+    ("out[t] = W.T", "out[t] = W.reshape(W.shape[::-1])", "test_p3_ridge_closed_forms"),
+    # off-by-one in the filled layers
+    ("filled = sum(n_layers - x for x in e)", "filled = sum(n_layers - x + 1 for x in e)",
+     "test_p2_tide_figure2_worked_example"),
+]
+
+
+@pytest.mark.parametrize("old,new,pin", MUTANTS, ids=[m[2] + ":" + m[1][:24] for m in MUTANTS])
+def test_mutation_is_caught(monkeypatch, old, new, pin):
+    mod = _mutant_oracle(old, new)
+    for name in O.__all__ if hasattr(O, "__all__") else dir(mod):
+        if hasattr(mod, name) and callable(getattr(mod, name)) and hasattr(O, name):
+            monkeypatch.setattr(O, name, getattr(mod, name))
+    with pytest.raises(AssertionError):
+        globals()[pin]()
