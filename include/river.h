@@ -1,0 +1,257 @@
+/*
+ * river.h -- C interface of the per-token exit-and-KV-fill library for
+ * AMD MI355X (gfx950).
+ *
+ * The step has three calls on the hot path and one off it:
+ *
+ *   river_route      which tokens exit at this layer
+ *   river_compact    stable split of the batch into continuing and exiting
+ *                    tokens, plus the exit scatter of hidden states
+ *   river_kv_fill    K/V of every skipped layer written into each exited
+ *                    token's own cache slot
+ *   river_ridge_fit  the closed-form ridge maps the fill applies
+ *
+ * Sources (web pages; cited by title and section):
+ *   River-LLM -- "River-LLM: Large Language Model Seamless Exit Based on
+ *     KV Share" (paper summary page): sections 前置知识, 核心方法,
+ *     方法步骤详情, 技术新颖性.
+ *   TIDE -- "TIDE: Token-Informed Depth Execution for Per-Token Early Exit
+ *     in LLM Inference" (reading notes): 系统架构, 模块3, 模块4, 关键公式.
+ *   RidgeFill -- news article "RidgeFill: 免训练后层缓存填充": method
+ *     paragraph under 思路源头 and the closed-form ridge regression box.
+ *
+ * Conventions for every call:
+ *   - Every pointer argument is a DEVICE pointer unless stated otherwise.
+ *     The caller owns all memory and keeps it alive until the stream has
+ *     run the enqueued work. The library allocates nothing; scratch memory
+ *     comes in through a caller-owned workspace (size from
+ *     river_workspace_size).
+ *   - Calls enqueue kernels on stream `s` and return without waiting,
+ *     except river_ridge_fit, which waits so that it can report a failed
+ *     factorization.
+ *   - Element types: RIVER_F32 (IEEE fp32) or RIVER_BF16 (bfloat16).
+ *     Arithmetic accumulates in fp32.
+ *   - Row-major matrices with a leading dimension `ld` in elements. Every
+ *     base pointer must be 16-byte aligned and ld * element size must be a
+ *     multiple of 16 bytes; d must be a multiple of 8.
+ *   - Argument errors are reported synchronously as a status code and a
+ *     message (river_last_error, thread-local); nothing is enqueued then.
+ *     No C++ exception crosses this interface. A failed kernel launch gives
+ *     RIVER_ERR_HIP.
+ *   - n = 0 (or m_max = 0) is a valid empty call.
+ *   - Calls are stateless and may run concurrently on different streams
+ *     when their outputs and workspaces do not overlap.
+ */
+#ifndef RIVER_H
+#define RIVER_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RIVER_OK = 0,
+  RIVER_ERR_ARG = 1,          /* a size, pointer or threshold is invalid     */
+  RIVER_ERR_DTYPE = 2,        /* an element type is not supported here       */
+  RIVER_ERR_ALIGN = 3,        /* a pointer or leading dimension is misaligned */
+  RIVER_ERR_UNSUPPORTED = 4,  /* a valid shape this build does not handle    */
+  RIVER_ERR_WORKSPACE = 5,    /* workspace missing or too small              */
+  RIVER_ERR_NOT_SPD = 6,      /* X^T X + lambda I is not positive definite   */
+  RIVER_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed  */
+} river_status;
+
+typedef enum { RIVER_F32 = 0, RIVER_BF16 = 1 } river_dtype;
+
+/* How per-token decisions become the mask (River-LLM 方法步骤详情 step 3
+ * takes the minimum over the batch; the same page's analysis and TIDE's
+ * per-token router motivate independent decisions). */
+typedef enum { RIVER_RULE_TOKEN = 0, RIVER_RULE_BATCH_MIN = 1 } river_rule;
+
+/* Operation ids for river_workspace_size. */
+typedef enum {
+  RIVER_OP_ROUTE = 0, RIVER_OP_COMPACT = 1, RIVER_OP_KV_FILL = 2, RIVER_OP_RIDGE_FIT = 3
+} river_op;
+
+/*
+ * Group-quantized int4 weights of one projection for n_layers consecutive
+ * layers (River-LLM 前置知识 PTQ: W4A16, 4-bit weights with 16-bit
+ * activations). For layer l, output row o and input channel k:
+ *
+ *   w[l][o][k] = (q_k - zero[l][o][k / group]) * scale[l][o][k / group]
+ *
+ * where q_k is the 4-bit value of byte q[l][o][k / 2], low nibble when k is
+ * even and high nibble when k is odd. Layers are contiguous:
+ *   q     : uint8 [n_layers][n_out][d / 2]
+ *   scale : sz_dtype [n_layers][n_out][d / group]
+ *   zero  : sz_dtype [n_layers][n_out][d / group]   (a real-valued zero point)
+ * n_out = n_kv_heads * head_dim; group must divide d.
+ */
+typedef struct {
+  const uint8_t* q;
+  const void* scale;
+  const void* zero;
+  river_dtype sz_dtype;
+  int group;
+} river_w4;
+
+/*
+ * river_route -- exit decision for n tokens at one layer.
+ *
+ * River-LLM 前置知识 and 方法步骤详情 step 3: the state-transition
+ * similarity cos_i = <h_prev_i, h_cur_i> / (|h_prev_i| |h_cur_i|) between a
+ * block's input and output. TIDE 关键公式 formula 3: the router
+ * prob_i = sigmoid(w_up . SiLU(W_down . RMSNorm(h_cur_i))), with
+ * RMSNorm(x) = gamma * x / sqrt(mean(x^2) + eps) over the d features and no
+ * biases. TIDE formula 4 and River-LLM step 3: strict thresholds.
+ *
+ *   e_i    = (cos_i > tau) AND (prob_i > theta)        (NaN compares false)
+ *   mask_i = e_i                          for RIVER_RULE_TOKEN
+ *   mask_i = AND_j e_j for every i        for RIVER_RULE_BATCH_MIN
+ *   *all_exit_out = AND_j e_j (0 when n = 0)
+ *
+ * h_prev, h_cur : dt [n][d] with leading dims ld_prev, ld_cur.
+ * gamma         : dt [d], or NULL for all ones.
+ * w_down        : dt [b][d], or NULL to switch the router off (prob = 1 and
+ *                 only the cosine test applies).
+ * w_up          : dt [b] (ignored when w_down is NULL).
+ * tau, theta    : thresholds; -INFINITY disables a test, +INFINITY forbids
+ *                 exit; NaN thresholds are rejected.
+ * cos_out, prob_out : fp32 [n], may be NULL.
+ * mask_out      : uint8 [n], required; 1 = exit.
+ * all_exit_out  : int32 [1], may be NULL.
+ * A zero-norm row has cos = 0. cos is clamped to [-1, 1].
+ * Requirements: n >= 0, d >= 8 and d % 8 == 0, b in [1, 512] when the
+ * router is on.
+ */
+river_status river_route(int n, int d, river_dtype dt,
+                         const void* h_prev, int64_t ld_prev,
+                         const void* h_cur, int64_t ld_cur,
+                         const void* gamma, float eps,
+                         const void* w_down, const void* w_up, int b,
+                         float tau, float theta, river_rule rule,
+                         float* cos_out, float* prob_out, uint8_t* mask_out,
+                         int32_t* all_exit_out, hipStream_t s);
+
+/*
+ * river_compact -- stable split by mask, row gather and exit scatter.
+ *
+ * TIDE 模块4: "Batch Compact" separates continuing from exiting tokens and
+ * "Exit Scatter" copies the exited tokens' hidden states back to their
+ * original positions in an output buffer.
+ *
+ *   cont_idx[0..n_cont)  = ascending i with mask[i] == 0
+ *   exit_idx[0..n_exit)  = ascending i with mask[i] != 0
+ *   counts[0] = n_cont, counts[1] = n_exit
+ *   h_cont[j]        = h[cont_idx[j]]            (if h_cont != NULL)
+ *   row_ids_cont[j]  = row_ids[cont_idx[j]]      (if row_ids_cont != NULL)
+ *   out[row_ids[i]]  = h[i] for every exiting i  (if out != NULL)
+ *
+ * mask    : uint8 [n].
+ * h       : dt [n][d], leading dim ld_h (may be NULL when h_cont and out
+ *           are both NULL).
+ * row_ids : int32 [n], or NULL for the identity 0..n-1.
+ * cont_idx, exit_idx : int32 [n] each; entries past the counts are left
+ *           untouched. counts : int32 [2].
+ * out     : dt [n_out_rows][d], leading dim ld_out. A row id outside
+ *           [0, n_out_rows) is skipped (not written).
+ * workspace : river_workspace_size(RIVER_OP_COMPACT, n, ...) bytes.
+ * The result is unique and deterministic.
+ */
+river_status river_compact(int n, int d, river_dtype dt, const uint8_t* mask,
+                           const void* h, int64_t ld_h, const int32_t* row_ids,
+                           int32_t* cont_idx, int32_t* exit_idx, int32_t* counts,
+                           void* h_cont, int64_t ld_cont, int32_t* row_ids_cont,
+                           void* out, int64_t ld_out, int64_t n_out_rows,
+                           void* workspace, size_t ws_bytes, hipStream_t s);
+
+/*
+ * river_kv_fill -- K/V of every skipped layer for each exited token.
+ *
+ * River-LLM 方法步骤详情 step 1 and 技术新颖性: the exit path writes the
+ * K/V of each skipped layer at the backbone's own address (same position
+ * index, head split and dimension layout), so the cache stays complete.
+ * RidgeFill 思路源头: the skipped layer's input is predicted from the exit
+ * state by a fitted linear map, then that layer's own projection writes the
+ * cache. With no map (identity) this is River-LLM's "State Propagation".
+ *
+ * For layer l = 0..n_layers-1 and t = 0..m-1, with r = row_idx[t] (or t):
+ *   x_hat = maps[l] . h[r]          (x_hat_j = sum_k maps[l][j][k] h[r][k];
+ *                                    x_hat = h[r] when maps is NULL)
+ *   K = Wk[l] . x_hat,  V = Wv[l] . x_hat      (n_out = n_kv_heads*head_dim)
+ *   k_cache[l][slot[r]][hh][dd] = K[hh*head_dim + dd], likewise V.
+ *
+ * m        : rows to fill = min(*m_dev, m_max) when m_dev is not NULL (a
+ *            device int32, e.g. counts+1 from river_compact, so no host
+ *            synchronisation is needed), else m_max.
+ * h        : dt [n_rows][d], leading dim ld_h.
+ * row_idx  : int32 [m_max] rows of h (e.g. exit_idx), or NULL for 0..m-1.
+ *            Entries outside [0, n_rows) are skipped.
+ * slot     : int32 [n_rows], the cache slot of each row of h. Slots of the
+ *            filled rows must be distinct; a slot outside [0, n_slots) is
+ *            skipped.
+ * maps     : dt [n_layers][d][d] (output-major), or NULL for the identity.
+ * wk, wv   : host pointers to int4 descriptors of n_layers layers.
+ * k_cache, v_cache : dt [n_layers][n_slots][n_kv_heads][head_dim]; the
+ *            first layer is the first skipped layer.
+ * workspace: with maps, at least river_workspace_size(RIVER_OP_KV_FILL,
+ *            m_max, d, 0, 0, 1) bytes; the layers are processed in as few
+ *            chunks as the given size allows. Without maps none is needed.
+ * Only the filled slots are written; every other byte is left unchanged.
+ * Requirements (bf16): d % 64 == 0, n_out % 32 == 0, group % 32 == 0.
+ */
+river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt,
+                           const void* h, int64_t ld_h, int n_rows,
+                           const int32_t* row_idx, const int32_t* slot,
+                           int n_layers, const void* maps,
+                           const river_w4* wk, const river_w4* wv,
+                           int n_kv_heads, int head_dim,
+                           void* k_cache, void* v_cache, int64_t n_slots,
+                           void* workspace, size_t ws_bytes, hipStream_t s);
+
+/*
+ * river_ridge_fit -- closed-form ridge maps (RidgeFill, ridge box):
+ *
+ *   W_t = (X^T X + lambda I)^-1 X^T Y_t     for t = 0..n_targets-1
+ *
+ * computed as an fp32 Cholesky factorization of G = X^T X + lambda I (Gram
+ * matrices accumulated in fp32), no intercept, lambda not scaled by n.
+ * X : xdt [n][d_in]; Y : ydt [n_targets][n][d_out]; xdt == ydt.
+ * W : wdt [n_targets][d_out][d_in], output-major, i.e. W[t] = W_t^T, the
+ *     layout river_kv_fill takes as maps.
+ * Waits for completion; returns RIVER_ERR_NOT_SPD when a pivot of the
+ * factorization is not positive (W is then unspecified).
+ * Requirements: d_in % 64 == 0 and d_out % 64 == 0 for bf16, n % 64 == 0
+ * for bf16; lambda >= 0.
+ */
+river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets,
+                             const void* X, river_dtype xdt,
+                             const void* Y, river_dtype ydt, float lambda,
+                             void* W, river_dtype wdt,
+                             void* workspace, size_t ws_bytes, hipStream_t s);
+
+/* Workspace bytes for an operation (arguments that do not apply are
+ * ignored): ROUTE -> 0; COMPACT (n); KV_FILL (n = m_max, d, n_layers; 0
+ * layers gives 0, the identity case); RIDGE_FIT (n, d = d_in, d_out,
+ * n_targets, and n_layers carries the dtype: RIVER_F32 or RIVER_BF16). */
+size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int n_layers);
+
+/* Message of the last failed call on this thread ("" when none). */
+const char* river_last_error(void);
+
+/* Library version string. */
+const char* river_version(void);
+
+/* Test hook: force the compaction index path (0 = automatic, 1 = single
+ * wave ballot, n <= 64; 2 = one workgroup scan; 3 = multi-workgroup scan).
+ * Process-wide; the paths give bitwise-identical results. */
+river_status river_debug_set_compact_path(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RIVER_H */

@@ -1,0 +1,98 @@
+"""The C-ABI library loads on a CPU-only host, exports every symbol the
+header declares, and rejects invalid arguments before touching a device."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import token_early_exit_amd as tee
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(river_[a-z_0-9]+)\s*\(", src))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    lib = tee.load()
+    declared = _declared_functions()
+    assert {"river_route", "river_compact", "river_kv_fill", "river_ridge_fit"} <= declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(tee.EXPORTS) == declared
+
+
+def test_version_and_error_string():
+    assert tee.version().startswith("river")
+    assert tee.load().river_last_error() is not None
+
+
+def test_workspace_sizes():
+    ws = tee.river_workspace_size
+    assert ws(tee.OP_ROUTE, 4096, 768) == 0
+    assert ws(tee.OP_KV_FILL, 4096, 768, 0, 0, 0) == 0           # identity: none
+    assert ws(tee.OP_KV_FILL, 4096, 768, 0, 0, 8) >= 8 * 4096 * 768 * 2
+    assert ws(tee.OP_COMPACT, 100000) >= 4 * 25
+    assert ws(tee.OP_RIDGE_FIT, 2048, 768, 768, 8, tee.RIVER_BF16) > 0
+
+
+def _route(**kw):
+    lib = tee.load()
+    a = dict(n=4, d=64, dt=tee.RIVER_F32, hp=16, ldp=64, hc=16, ldc=64, gamma=None, eps=1e-6,
+             wd=None, wu=None, b=0, tau=0.5, theta=0.5, rule=0, cos=None, prob=None, mask=16,
+             all=None, s=None)
+    a.update(kw)
+    return lib.river_route(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=7), 2),
+    (dict(n=-1), 1),
+    (dict(d=12), 1),
+    (dict(tau=math.nan), 1),
+    (dict(rule=5), 1),
+    (dict(eps=-1.0), 1),
+    (dict(wd=16, wu=16, b=0), 1),
+    (dict(wd=16, wu=None, b=32), 1),
+    (dict(hp=8), 3),
+    (dict(ldp=60), 1 + 2),       # ld below d -> alignment/ld error
+    (dict(mask=None), 1),
+])
+def test_route_argument_errors(kw, status):
+    assert _route(**kw) == status
+    assert len(tee.load().river_last_error()) > 0
+
+
+def test_kv_fill_and_ridge_argument_errors():
+    lib = tee.load()
+    w = tee.RiverW4(16, 16, 16, tee.RIVER_BF16, 64)
+    bad = tee.RiverW4(16, 16, 16, tee.RIVER_BF16, 48)
+    args = lambda **k: dict(dict(m=8, mdev=None, d=128, dt=tee.RIVER_BF16, h=16, ld=128, nrows=8,
+                                 ri=None, slot=16, nl=2, maps=None, wk=ctypes.byref(w),
+                                 wv=ctypes.byref(w), hk=2, hd=64, kc=16, vc=16, ns=8, ws=None,
+                                 wsn=0, s=None), **k).values()
+    assert lib.river_kv_fill(*args(m=0)) == 0                     # empty call
+    assert lib.river_kv_fill(*args(wk=ctypes.byref(bad))) == 1     # group does not divide d
+    assert lib.river_kv_fill(*args(maps=16)) == 5                  # maps need a workspace
+    assert lib.river_kv_fill(*args(m=9)) == 1                      # more rows than h has
+    assert lib.river_kv_fill(*args(kc=None)) == 1
+    r = lib.river_ridge_fit(64, 64, 64, 1, 16, tee.RIVER_BF16, 16, tee.RIVER_F32, 0.1, 16,
+                            tee.RIVER_F32, 16, 1 << 30, None)
+    assert r == 2                                                  # X, Y dtypes differ
+    r = lib.river_ridge_fit(64, 64, 64, 1, 16, tee.RIVER_BF16, 16, tee.RIVER_BF16, -1.0, 16,
+                            tee.RIVER_F32, 16, 1 << 30, None)
+    assert r == 1                                                  # negative lambda
+    r = lib.river_ridge_fit(64, 64, 64, 1, 16, tee.RIVER_BF16, 16, tee.RIVER_BF16, 0.1, 16,
+                            tee.RIVER_F32, 16, 10, None)
+    assert r == 5                                                  # workspace too small
+    assert lib.river_debug_set_compact_path(9) == 1

@@ -1,0 +1,181 @@
+"""Python binding of libriver (the per-token exit-and-KV-fill library).
+
+Argument marshalling only: every function forwards torch tensors' device
+pointers and the current HIP stream to the C interface declared in
+``include/river.h``; all arithmetic runs in the HIP kernels. There is no
+CPU fallback: if the library is not built, ``load()`` raises.
+
+The four calls keep the C names: ``river_route``, ``river_compact``,
+``river_kv_fill``, ``river_ridge_fit``; plus ``river_workspace_size``.
+"""
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libriver.so")
+
+RIVER_F32, RIVER_BF16 = 0, 1
+RULE_TOKEN, RULE_BATCH_MIN = 0, 1
+OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT = 0, 1, 2, 3
+STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_DTYPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED",
+          5: "ERR_WORKSPACE", 6: "ERR_NOT_SPD", 7: "ERR_HIP"}
+
+EXPORTS = ["river_route", "river_compact", "river_kv_fill", "river_ridge_fit",
+           "river_workspace_size", "river_last_error", "river_version",
+           "river_debug_set_compact_path"]
+
+
+class RiverError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+
+
+class RiverW4(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p),
+                ("sz_dtype", ctypes.c_int), ("group", ctypes.c_int)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_L = ctypes.c_int64
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+
+
+def load():
+    """Load libriver.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.river_route.argtypes = [_I, _I, _I, _P, _L, _P, _L, _P, _F, _P, _P, _I, _F, _F, _I,
+                                _P, _P, _P, _P, _P]
+    lib.river_compact.argtypes = [_I, _I, _I, _P, _P, _L, _P, _P, _P, _P, _P, _L, _P, _P, _L, _L,
+                                  _P, _S, _P]
+    lib.river_kv_fill.argtypes = [_I, _P, _I, _I, _P, _L, _I, _P, _P, _I, _P,
+                                  ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4), _I, _I,
+                                  _P, _P, _L, _P, _S, _P]
+    lib.river_ridge_fit.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _S, _P]
+    for f in ("river_route", "river_compact", "river_kv_fill", "river_ridge_fit",
+              "river_debug_set_compact_path"):
+        getattr(lib, f).restype = _I
+    lib.river_debug_set_compact_path.argtypes = [_I]
+    lib.river_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
+    lib.river_workspace_size.restype = _S
+    lib.river_last_error.restype = ctypes.c_char_p
+    lib.river_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ----------------------------------------------------------- marshalling
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dt(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return RIVER_BF16
+    if t.dtype == torch.float32:
+        return RIVER_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(st):
+    if st != 0:
+        raise RiverError(st, load().river_last_error().decode())
+
+
+def _ld(t):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("matrices must be 2-D with unit column stride")
+    return t.stride(0)
+
+
+def version():
+    return load().river_version().decode()
+
+
+def river_workspace_size(op, n=0, d=0, d_out=0, n_targets=0, n_layers=0):
+    return load().river_workspace_size(op, n, d, d_out, n_targets, n_layers)
+
+
+def river_debug_set_compact_path(path):
+    _check(load().river_debug_set_compact_path(path))
+
+
+def river_route(h_prev, h_cur, mask_out, *, gamma=None, eps=1e-6, w_down=None, w_up=None,
+                tau=-math.inf, theta=-math.inf, rule=RULE_TOKEN, cos_out=None, prob_out=None,
+                all_exit_out=None, stream=None):
+    n, d = h_cur.shape
+    b = 0 if w_down is None else w_down.shape[0]
+    _check(load().river_route(n, d, _dt(h_cur), _ptr(h_prev), _ld(h_prev), _ptr(h_cur), _ld(h_cur),
+                              _ptr(gamma), eps, _ptr(w_down), _ptr(w_up), b, tau, theta, rule,
+                              _ptr(cos_out), _ptr(prob_out), _ptr(mask_out), _ptr(all_exit_out),
+                              _stream(stream)))
+
+
+def river_compact(mask, h, cont_idx, exit_idx, counts, *, row_ids=None, h_cont=None,
+                  row_ids_cont=None, out=None, workspace=None, stream=None, d=None, dt=None):
+    n = mask.shape[0]
+    if h is not None:
+        d, dt = h.shape[1], _dt(h)
+        ld_h = _ld(h)
+    else:
+        ld_h = 0
+        d = d or 8
+        dt = RIVER_BF16 if dt is None else dt
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().river_compact(n, d, dt, _ptr(mask), _ptr(h), ld_h, _ptr(row_ids), _ptr(cont_idx),
+                                _ptr(exit_idx), _ptr(counts), _ptr(h_cont),
+                                _ld(h_cont) if h_cont is not None else 0, _ptr(row_ids_cont),
+                                _ptr(out), _ld(out) if out is not None else 0,
+                                out.shape[0] if out is not None else 0, _ptr(workspace), ws_n,
+                                _stream(stream)))
+
+
+def w4(q, scale, zero, group):
+    """int4 descriptor from (q, scale, zero) tensors; keeps no reference."""
+    return RiverW4(q.data_ptr(), scale.data_ptr(), zero.data_ptr(), _dt(scale), group)
+
+
+def river_kv_fill(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, *, m_max=None,
+                  m_dev=None, row_idx=None, maps=None, workspace=None, stream=None):
+    """wk, wv: (q, scale, zero, group) tuples of tensors."""
+    n_rows, d = h.shape
+    n_layers = wk[0].shape[0]
+    if m_max is None:
+        m_max = row_idx.shape[0] if row_idx is not None else n_rows
+    dk = w4(*wk)
+    dv = w4(*wv)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().river_kv_fill(m_max, _ptr(m_dev), d, _dt(h), _ptr(h), _ld(h), n_rows,
+                                _ptr(row_idx), _ptr(slot), n_layers, _ptr(maps),
+                                ctypes.byref(dk), ctypes.byref(dv), n_kv_heads, head_dim,
+                                _ptr(k_cache), _ptr(v_cache), k_cache.shape[1], _ptr(workspace),
+                                ws_n, _stream(stream)))
+
+
+def river_ridge_fit(X, Y, lam, W, *, workspace=None, stream=None):
+    n, d_in = X.shape
+    n_targets, _, d_out = Y.shape
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().river_ridge_fit(n, d_in, d_out, n_targets, _ptr(X), _dt(X), _ptr(Y), _dt(Y),
+                                  lam, _ptr(W), _dt(W), _ptr(workspace), ws_n, _stream(stream)))

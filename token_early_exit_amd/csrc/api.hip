@@ -1,0 +1,200 @@
+// C interface of the river library: argument validation, error reporting
+// and dispatch to the kernel launchers. Every function here is extern "C";
+// nothing throws across the interface.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "common.h"
+
+namespace river_host {
+
+static thread_local char g_err[512] = "";
+static int g_compact_path = 0;
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+river_status fail(river_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+river_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RIVER_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return RIVER_OK;
+}
+
+int compact_path_override() { return g_compact_path; }
+
+static bool dt_ok(river_dtype dt) { return dt == RIVER_F32 || dt == RIVER_BF16; }
+
+// leading dimension: >= d and a multiple of 16 bytes
+static bool ld_ok(int64_t ld, int d, river_dtype dt) {
+  return ld >= d && ((ld * (int64_t)esize(dt)) % 16) == 0;
+}
+
+}  // namespace river_host
+
+using namespace river_host;
+
+extern "C" {
+
+const char* river_last_error(void) { return g_err; }
+
+const char* river_version(void) { return "river 0.1.0 (gfx950)"; }
+
+river_status river_debug_set_compact_path(int path) {
+  if (path < 0 || path > 3) return fail(RIVER_ERR_ARG, "compact path must be 0..3, got %d", path);
+  g_compact_path = path;
+  return RIVER_OK;
+}
+
+size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int n_layers) {
+  (void)n_targets;
+  switch (op) {
+    case RIVER_OP_ROUTE: return 0;
+    case RIVER_OP_COMPACT: return n > 0 ? compact_workspace(n) : 0;
+    case RIVER_OP_KV_FILL:
+      if (n <= 0 || d <= 0 || n_layers <= 0) return 0;
+      return kv_fill_workspace(n, d, n_layers, RIVER_BF16);
+    case RIVER_OP_RIDGE_FIT:
+      if (n <= 0 || d <= 0 || d_out <= 0) return 0;
+      return ridge_workspace(n, d, d_out, n_layers == RIVER_F32 ? RIVER_F32 : RIVER_BF16);
+    default: return 0;
+  }
+}
+
+river_status river_route(int n, int d, river_dtype dt, const void* h_prev, int64_t ld_prev,
+                         const void* h_cur, int64_t ld_cur, const void* gamma, float eps,
+                         const void* w_down, const void* w_up, int b, float tau, float theta,
+                         river_rule rule, float* cos_out, float* prob_out, uint8_t* mask_out,
+                         int32_t* all_exit_out, hipStream_t s) {
+  g_err[0] = 0;
+  if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "route: dtype %d is not RIVER_F32 or RIVER_BF16", (int)dt);
+  if (n < 0) return fail(RIVER_ERR_ARG, "route: n = %d < 0", n);
+  if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "route: d = %d must be a positive multiple of 8", d);
+  if (rule != RIVER_RULE_TOKEN && rule != RIVER_RULE_BATCH_MIN)
+    return fail(RIVER_ERR_ARG, "route: unknown rule %d", (int)rule);
+  if (isnan(tau) || isnan(theta)) return fail(RIVER_ERR_ARG, "route: tau and theta must not be NaN");
+  if (!(eps >= 0.0f) || isinf(eps)) return fail(RIVER_ERR_ARG, "route: eps must be finite and >= 0");
+  if (w_down) {
+    if (b < 1 || b > 512) return fail(RIVER_ERR_ARG, "route: router width b = %d must be in [1, 512]", b);
+    if (!w_up) return fail(RIVER_ERR_ARG, "route: w_up is NULL while w_down is set");
+    if (!aligned16(w_down) || !aligned16(w_up)) return fail(RIVER_ERR_ALIGN, "route: router weights must be 16-byte aligned");
+  }
+  if (gamma && !aligned16(gamma)) return fail(RIVER_ERR_ALIGN, "route: gamma must be 16-byte aligned");
+  if (n == 0) {
+    if (all_exit_out) return launch_route(0, d, dt, nullptr, d, nullptr, d, nullptr, eps, nullptr,
+                                          nullptr, b, tau, theta, rule, nullptr, nullptr, nullptr,
+                                          all_exit_out, s);
+    return RIVER_OK;
+  }
+  if (!h_prev || !h_cur || !mask_out) return fail(RIVER_ERR_ARG, "route: h_prev, h_cur and mask_out are required");
+  if (!ld_ok(ld_prev, d, dt) || !ld_ok(ld_cur, d, dt))
+    return fail(RIVER_ERR_ALIGN, "route: leading dims must be >= d and a multiple of 16 bytes");
+  if (!aligned16(h_prev) || !aligned16(h_cur)) return fail(RIVER_ERR_ALIGN, "route: hidden states must be 16-byte aligned");
+  return launch_route(n, d, dt, h_prev, ld_prev, h_cur, ld_cur, gamma, eps, w_down, w_up, b, tau,
+                      theta, rule, cos_out, prob_out, mask_out, all_exit_out, s);
+}
+
+river_status river_compact(int n, int d, river_dtype dt, const uint8_t* mask, const void* h,
+                           int64_t ld_h, const int32_t* row_ids, int32_t* cont_idx,
+                           int32_t* exit_idx, int32_t* counts, void* h_cont, int64_t ld_cont,
+                           int32_t* row_ids_cont, void* out, int64_t ld_out, int64_t n_out_rows,
+                           void* workspace, size_t ws_bytes, hipStream_t s) {
+  g_err[0] = 0;
+  if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "compact: dtype %d is not RIVER_F32 or RIVER_BF16", (int)dt);
+  if (n < 0) return fail(RIVER_ERR_ARG, "compact: n = %d < 0", n);
+  if (!counts) return fail(RIVER_ERR_ARG, "compact: counts is required");
+  if (n > 0 && (!mask || !cont_idx || !exit_idx)) return fail(RIVER_ERR_ARG, "compact: mask, cont_idx and exit_idx are required");
+  bool rows = (h_cont || out);
+  if (rows) {
+    if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "compact: d = %d must be a positive multiple of 8", d);
+    if (n > 0 && !h) return fail(RIVER_ERR_ARG, "compact: h is required when h_cont or out is given");
+    if (n > 0 && (!ld_ok(ld_h, d, dt) || !aligned16(h))) return fail(RIVER_ERR_ALIGN, "compact: h misaligned or ld_h invalid");
+    if (h_cont && (!ld_ok(ld_cont, d, dt) || !aligned16(h_cont))) return fail(RIVER_ERR_ALIGN, "compact: h_cont misaligned or ld_cont invalid");
+    if (out && (!ld_ok(ld_out, d, dt) || !aligned16(out))) return fail(RIVER_ERR_ALIGN, "compact: out misaligned or ld_out invalid");
+    if (out && n_out_rows < 0) return fail(RIVER_ERR_ARG, "compact: n_out_rows < 0");
+  }
+  size_t need = n > 0 ? compact_workspace(n) : 0;
+  if (need && (!workspace || ws_bytes < need))
+    return fail(RIVER_ERR_WORKSPACE, "compact: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (workspace && !aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "compact: workspace must be 16-byte aligned");
+  int p = compact_path_override();
+  if (p == 1 && n > 64) return fail(RIVER_ERR_UNSUPPORTED, "compact: forced wave path needs n <= 64");
+  return launch_compact(n, d, dt, mask, h, ld_h, row_ids, cont_idx, exit_idx, counts, h_cont,
+                        ld_cont, row_ids_cont, out, ld_out, n_out_rows, workspace, ws_bytes, s);
+}
+
+river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
+                           int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
+                           int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
+                           int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
+                           int64_t n_slots, void* workspace, size_t ws_bytes, hipStream_t s) {
+  g_err[0] = 0;
+  if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "kv_fill: dtype %d is not RIVER_F32 or RIVER_BF16", (int)dt);
+  if (m_max < 0 || n_layers < 0 || n_rows < 0) return fail(RIVER_ERR_ARG, "kv_fill: negative size");
+  if (m_max == 0 || n_layers == 0) return RIVER_OK;
+  if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "kv_fill: d = %d must be a positive multiple of 8", d);
+  if (n_kv_heads < 1 || head_dim < 1) return fail(RIVER_ERR_ARG, "kv_fill: n_kv_heads and head_dim must be >= 1");
+  if (!h || !slot || !wk || !wv || !k_cache || !v_cache) return fail(RIVER_ERR_ARG, "kv_fill: a required pointer is NULL");
+  if (!row_idx && m_max > n_rows) return fail(RIVER_ERR_ARG, "kv_fill: m_max = %d > n_rows = %d without row_idx", m_max, n_rows);
+  if (n_slots < 1) return fail(RIVER_ERR_ARG, "kv_fill: n_slots must be >= 1");
+  if (!ld_ok(ld_h, d, dt) || !aligned16(h)) return fail(RIVER_ERR_ALIGN, "kv_fill: h misaligned or ld_h invalid");
+  for (const river_w4* w : {wk, wv}) {
+    if (!w->q || !w->scale || !w->zero) return fail(RIVER_ERR_ARG, "kv_fill: int4 descriptor has a NULL pointer");
+    if (!dt_ok(w->sz_dtype)) return fail(RIVER_ERR_DTYPE, "kv_fill: scale/zero dtype %d unsupported", (int)w->sz_dtype);
+    if (w->group < 2 || d % w->group || w->group % 2) return fail(RIVER_ERR_ARG, "kv_fill: group %d must be even and divide d", w->group);
+    if (!aligned16(w->q)) return fail(RIVER_ERR_ALIGN, "kv_fill: int4 weights must be 16-byte aligned");
+  }
+  int n_out = n_kv_heads * head_dim;
+  if (dt == RIVER_BF16) {
+    if (d % 64) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: bf16 path needs d %% 64 == 0 (d = %d)", d);
+    if (n_out % 32) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: bf16 path needs n_kv_heads*head_dim %% 32 == 0");
+    if (wk->group % 32 || wv->group % 32) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: bf16 path needs group %% 32 == 0");
+  }
+  if (!aligned16(k_cache) || !aligned16(v_cache) || (maps && !aligned16(maps)))
+    return fail(RIVER_ERR_ALIGN, "kv_fill: caches and maps must be 16-byte aligned");
+  if (maps) {
+    size_t need = kv_fill_workspace(m_max, d, 1, dt);
+    if (!workspace || ws_bytes < need)
+      return fail(RIVER_ERR_WORKSPACE, "kv_fill: at least %zu workspace bytes needed with maps, %zu given", need, ws_bytes);
+    if (!aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "kv_fill: workspace must be 16-byte aligned");
+  }
+  return launch_kv_fill(m_max, m_dev, d, dt, h, ld_h, n_rows, row_idx, slot, n_layers, maps, wk, wv,
+                        n_kv_heads, head_dim, k_cache, v_cache, n_slots, workspace, ws_bytes, s);
+}
+
+river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,
+                             river_dtype xdt, const void* Y, river_dtype ydt, float lambda,
+                             void* W, river_dtype wdt, void* workspace, size_t ws_bytes,
+                             hipStream_t s) {
+  g_err[0] = 0;
+  if (!dt_ok(xdt) || !dt_ok(ydt) || !dt_ok(wdt)) return fail(RIVER_ERR_DTYPE, "ridge_fit: unsupported dtype");
+  if (xdt != ydt) return fail(RIVER_ERR_DTYPE, "ridge_fit: X and Y must have the same dtype");
+  if (n < 1 || d_in < 1 || d_out < 1 || n_targets < 0) return fail(RIVER_ERR_ARG, "ridge_fit: invalid sizes");
+  if (!(lambda >= 0.0f) || isinf(lambda)) return fail(RIVER_ERR_ARG, "ridge_fit: lambda must be finite and >= 0");
+  if (n_targets == 0) return RIVER_OK;
+  if (!X || !Y || !W) return fail(RIVER_ERR_ARG, "ridge_fit: X, Y and W are required");
+  if (!aligned16(X) || !aligned16(Y) || !aligned16(W)) return fail(RIVER_ERR_ALIGN, "ridge_fit: X, Y, W must be 16-byte aligned");
+  if (xdt == RIVER_BF16 && (d_in % 64 || d_out % 64 || n % 64))
+    return fail(RIVER_ERR_UNSUPPORTED, "ridge_fit: bf16 path needs n, d_in, d_out multiples of 64");
+  if (xdt == RIVER_F32 && (d_in % 4 || d_out % 4)) return fail(RIVER_ERR_UNSUPPORTED, "ridge_fit: fp32 path needs d_in, d_out multiples of 4");
+  size_t need = ridge_workspace(n, d_in, d_out, xdt);
+  if (!workspace || ws_bytes < need)
+    return fail(RIVER_ERR_WORKSPACE, "ridge_fit: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "ridge_fit: workspace must be 16-byte aligned");
+  return launch_ridge_fit(n, d_in, d_out, n_targets, X, xdt, Y, lambda, W, wdt, workspace, ws_bytes, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Shared device helpers and host-side plumbing of the river library
+// (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "river.h"
+
+namespace river {
+
+// ------------------------------------------------------------ vector types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+// ------------------------------------------------------------ bf16 helpers
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// load element i of a dt array as fp32
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (BF16) return bf16_to_f32(((const uint16_t*)p)[i]);
+  else return ((const float*)p)[i];
+}
+
+// ----------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+// sum over aligned groups of G consecutive lanes (G a power of two <= 64)
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+}  // namespace river
+
+// ------------------------------------------------------------ host plumbing
+namespace river_host {
+
+void set_error(const char* fmt, ...);
+river_status fail(river_status st, const char* fmt, ...);
+river_status check_launch(const char* what);
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t esize(river_dtype dt) { return dt == RIVER_BF16 ? 2 : 4; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int compact_path_override();
+
+// launchers implemented by the kernel files; argument checks are done by
+// the caller (api.hip)
+river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int64_t ld_prev,
+                          const void* h_cur, int64_t ld_cur, const void* gamma, float eps,
+                          const void* w_down, const void* w_up, int b, float tau, float theta,
+                          river_rule rule, float* cos_out, float* prob_out, uint8_t* mask_out,
+                          int32_t* all_exit_out, hipStream_t s);
+
+size_t compact_workspace(int n);
+river_status launch_compact(int n, int d, river_dtype dt, const uint8_t* mask, const void* h,
+                            int64_t ld_h, const int32_t* row_ids, int32_t* cont_idx,
+                            int32_t* exit_idx, int32_t* counts, void* h_cont, int64_t ld_cont,
+                            int32_t* row_ids_cont, void* out, int64_t ld_out, int64_t n_out_rows,
+                            void* workspace, size_t ws_bytes, hipStream_t s);
+
+size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt);
+river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
+                            int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
+                            int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
+                            int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
+                            int64_t n_slots, void* workspace, size_t ws_bytes, hipStream_t s);
+
+size_t ridge_workspace(int n, int d_in, int d_out, river_dtype dt);
+river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,
+                              river_dtype xdt, const void* Y, float lambda, void* W,
+                              river_dtype wdt, void* workspace, size_t ws_bytes, hipStream_t s);
+
+}  // namespace river_host

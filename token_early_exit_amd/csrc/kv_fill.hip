@@ -1,0 +1,187 @@
+// kv_fill: K/V of every skipped layer, written into each exited token's
+// own cache slot.
+//
+// River-LLM, 方法步骤详情 step 1 / 技术新颖性: the exit path writes K/V at
+// the backbone's own addresses (position, head split, dimension layout).
+// RidgeFill, 思路源头: each skipped layer's input is predicted from the
+// exit state by a fitted linear map and the layer's own projection writes
+// the cache. With no map this is River-LLM's State Propagation.
+//
+// bf16 path, two grouped GEMM phases per chunk of layers:
+//   1. x_hat[l] = X . maps[l]^T       (bf16 MFMA, fp32 acc, rounded to bf16
+//                                      into the workspace); skipped when the
+//                                      map is the identity
+//   2. [K|V][l] = x_hat[l] . [Wk[l]; Wv[l]]^T   (int4 dequantized in
+//                                      registers, bf16 MFMA) with the cache
+//                                      scatter as the epilogue
+// Layers are the grid's z dimension, so one launch covers a whole chunk.
+//
+// Generic path (fp32, or shapes the MFMA tiles do not take): one workgroup
+// per (token, layer), fp32 throughout.
+#include "common.h"
+#include "gemm.h"
+
+namespace river {
+
+struct FillGeneric {
+  int m_max; const int32_t* m_dev; int d;
+  const void* h; int64_t ld_h; int n_rows;
+  const int32_t* row_idx; const int32_t* slot;
+  const void* maps;
+  const uint8_t* q[2]; const void* s[2]; const void* zp[2]; int group[2]; int sz_bf16[2];
+  int nh; int64_t n_slots;
+  void* kc; void* vc;
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void kv_fill_generic_kernel(FillGeneric a) {
+  extern __shared__ float sm[];   // x [d], x_hat [d]
+  float* x = sm;
+  float* xh = sm + a.d;
+  int m = a.m_max;
+  if (a.m_dev) {
+    const int md = *a.m_dev;
+    m = md < 0 ? 0 : (md < a.m_max ? md : a.m_max);
+  }
+  const int t = blockIdx.x, l = blockIdx.y;
+  if (t >= m) return;
+  const int r = a.row_idx ? a.row_idx[t] : t;
+  if (r < 0 || r >= a.n_rows) return;
+  const int sl = a.slot[r];
+  if (sl < 0 || sl >= a.n_slots) return;
+  const int d = a.d;
+  for (int k = threadIdx.x; k < d; k += blockDim.x) x[k] = load_elem<BF16>(a.h, (int64_t)r * a.ld_h + k);
+  __syncthreads();
+  if (a.maps) {
+    const int64_t mo = (int64_t)l * d * d;
+    for (int j = threadIdx.x; j < d; j += blockDim.x) {
+      float acc = 0.f;
+      for (int k = 0; k < d; ++k) acc = fmaf(load_elem<BF16>(a.maps, mo + (int64_t)j * d + k), x[k], acc);
+      xh[j] = acc;
+    }
+  } else {
+    for (int k = threadIdx.x; k < d; k += blockDim.x) xh[k] = x[k];
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < 2 * a.nh; o += blockDim.x) {
+    const int which = o >= a.nh ? 1 : 0;
+    const int row = o - which * a.nh;
+    const int grp = a.group[which];
+    const uint8_t* q = a.q[which] + ((int64_t)l * a.nh + row) * (d / 2);
+    const int64_t sz0 = ((int64_t)l * a.nh + row) * (d / grp);
+    float acc = 0.f;
+    for (int k = 0; k < d; k += 2) {
+      const uint8_t byte = q[k >> 1];
+      const int64_t gi = sz0 + k / grp;
+      const float sc = load_sz(a.s[which], gi, a.sz_bf16[which]);
+      const float ze = load_sz(a.zp[which], gi, a.sz_bf16[which]);
+      acc = fmaf(((float)(byte & 15) - ze) * sc, xh[k], acc);
+      acc = fmaf(((float)(byte >> 4) - ze) * sc, xh[k + 1], acc);
+    }
+    const int64_t off = ((int64_t)l * a.n_slots + sl) * a.nh + row;
+    if (BF16) ((uint16_t*)(which ? a.vc : a.kc))[off] = f32_to_bf16(acc);
+    else ((float*)(which ? a.vc : a.kc))[off] = acc;
+  }
+}
+
+}  // namespace river
+
+namespace river_host {
+using namespace river;
+
+static bool fill_mfma_ok(int d, river_dtype dt, int nh, const river_w4* wk, const river_w4* wv) {
+  return dt == RIVER_BF16 && d % 64 == 0 && nh % 32 == 0 && wk->group % 32 == 0 &&
+         wv->group % 32 == 0;
+}
+
+size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt) {
+  return align_up((size_t)n_layers * (size_t)m_max * (size_t)d * esize(dt), 256);
+}
+
+river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
+                            int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
+                            int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
+                            int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
+                            int64_t n_slots, void* workspace, size_t ws_bytes, hipStream_t s) {
+  const int nh = n_kv_heads * head_dim;
+  if (!fill_mfma_ok(d, dt, nh, wk, wv)) {
+    const size_t lds = 2 * (size_t)d * sizeof(float);
+    if (lds > 65536) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: d = %d too large for the generic path", d);
+    FillGeneric a{m_max, m_dev, d, h, ld_h, n_rows, row_idx, slot, maps,
+                  {wk->q, wv->q}, {wk->scale, wv->scale}, {wk->zero, wv->zero},
+                  {wk->group, wv->group},
+                  {wk->sz_dtype == RIVER_BF16, wv->sz_dtype == RIVER_BF16}, nh, n_slots,
+                  k_cache, v_cache};
+    dim3 grid(m_max, n_layers);
+    if (dt == RIVER_BF16) kv_fill_generic_kernel<true><<<grid, 256, lds, s>>>(a);
+    else kv_fill_generic_kernel<false><<<grid, 256, lds, s>>>(a);
+    return check_launch("kv_fill generic");
+  }
+
+  GemmArgs g{};
+  g.K = d;
+  g.M_max = m_max;
+  g.M_dev = m_dev;
+  g.q[0] = wk->q; g.q[1] = wv->q;
+  g.s[0] = wk->scale; g.s[1] = wv->scale;
+  g.zp[0] = wk->zero; g.zp[1] = wv->zero;
+  g.group[0] = wk->group; g.group[1] = wv->group;
+  g.sz_bf16[0] = wk->sz_dtype == RIVER_BF16; g.sz_bf16[1] = wv->sz_dtype == RIVER_BF16;
+  g.nh = nh;
+  g.q_bstride = (int64_t)nh * d / 2;
+  g.sz_bstride[0] = (int64_t)nh * (d / wk->group);
+  g.sz_bstride[1] = (int64_t)nh * (d / wv->group);
+  g.slot = slot;
+  g.n_slots = n_slots;
+  g.e_nrows = n_rows;
+  g.cache_bstride = n_slots * nh;
+
+  const bool small = m_max <= 64;
+  const int BM = small ? 64 : 128;
+  const int mt = (m_max + BM - 1) / BM;
+
+  auto stage2 = [&](int l0, int nl, const uint16_t* A, int64_t lda, int64_t a_bs,
+                    const int32_t* a_rows, int a_nrows) -> river_status {
+    GemmArgs q = g;
+    q.N = 2 * nh;
+    q.A = A; q.lda = lda; q.a_bstride = a_bs; q.a_rows = a_rows; q.a_nrows = a_nrows;
+    q.q[0] = wk->q + (int64_t)l0 * q.q_bstride;
+    q.q[1] = wv->q + (int64_t)l0 * q.q_bstride;
+    q.s[0] = (const char*)wk->scale + (int64_t)l0 * q.sz_bstride[0] * esize(wk->sz_dtype);
+    q.zp[0] = (const char*)wk->zero + (int64_t)l0 * q.sz_bstride[0] * esize(wk->sz_dtype);
+    q.s[1] = (const char*)wv->scale + (int64_t)l0 * q.sz_bstride[1] * esize(wv->sz_dtype);
+    q.zp[1] = (const char*)wv->zero + (int64_t)l0 * q.sz_bstride[1] * esize(wv->sz_dtype);
+    q.e_rows = row_idx;
+    q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
+    q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
+    dim3 grid((2 * nh) / 128 + ((2 * nh) % 128 ? 1 : 0), mt, nl);
+    if (small) gemm_nt_kernel<64, true, EPI_CACHE><<<grid, 256, 0, s>>>(q);
+    else gemm_nt_kernel<128, true, EPI_CACHE><<<grid, 256, 0, s>>>(q);
+    return check_launch("kv_fill projection");
+  };
+
+  if (!maps) return stage2(0, n_layers, (const uint16_t*)h, ld_h, 0, row_idx, n_rows);
+
+  const size_t per_layer = (size_t)m_max * d * 2;
+  int chunk = (int)(ws_bytes / per_layer);
+  if (chunk > n_layers) chunk = n_layers;
+  uint16_t* xh = (uint16_t*)workspace;
+  for (int l0 = 0; l0 < n_layers; l0 += chunk) {
+    const int nl = n_layers - l0 < chunk ? n_layers - l0 : chunk;
+    GemmArgs p = g;
+    p.N = d;
+    p.A = (const uint16_t*)h; p.lda = ld_h; p.a_bstride = 0; p.a_rows = row_idx; p.a_nrows = n_rows;
+    p.B = (const uint16_t*)maps + (int64_t)l0 * d * d; p.ldb = d; p.b_bstride = (int64_t)d * d;
+    p.C = xh; p.ldc = d; p.c_bstride = (int64_t)m_max * d;
+    dim3 grid(d / 128 + (d % 128 ? 1 : 0), mt, nl);
+    if (small) gemm_nt_kernel<64, false, EPI_BF16><<<grid, 256, 0, s>>>(p);
+    else gemm_nt_kernel<128, false, EPI_BF16><<<grid, 256, 0, s>>>(p);
+    river_status st = check_launch("kv_fill map");
+    if (st != RIVER_OK) return st;
+    st = stage2(l0, nl, xh, d, (int64_t)m_max * d, nullptr, m_max);
+    if (st != RIVER_OK) return st;
+  }
+  return RIVER_OK;
+}
+
+}  // namespace river_host

@@ -1,0 +1,310 @@
+// route: per-token exit decision.
+//
+// River-LLM, 前置知识 / 方法步骤详情 step 3: the cosine between a block's
+// input h_prev and output h_cur. TIDE, 关键公式 formula 3: the router
+// sigmoid(w_up . SiLU(W_down . RMSNorm(h_cur))); formula 4: strict
+// thresholds. TIDE 模块4 fuses RMSNorm and the router into one launch; here
+// the cosine is fused in as well, so h_prev and h_cur are each read once.
+//
+// bf16 path: one workgroup = 4 waves = 16*RT tokens. The four waves split
+// the feature dimension in 32-wide slabs; each wave keeps the 16xRT token
+// rows' partial norms in registers and runs the router down-projection on
+// bf16 MFMA (16x16x32) with the RMSNorm scale applied afterwards in fp32:
+//   u = r * (W_down . (gamma * h)),   r = 1 / sqrt(mean(h^2) + eps),
+// which never rounds the normalised vector to bf16. gamma != 1 is fed as
+// the exact fp32 product gamma*h split into two bf16 terms (hi + lo).
+// The partial results of the four waves are summed in LDS in a fixed order
+// (deterministic), then the SiLU / w_up / sigmoid epilogue runs per token.
+#include "common.h"
+
+namespace river {
+
+struct RouteArgs {
+  int n, d, b;
+  const void* hp; int64_t ldp;
+  const void* hc; int64_t ldc;
+  const void* gamma; float eps;
+  const void* wd; const void* wu;
+  float tau, theta;
+  float* cos_out; float* prob_out; uint8_t* mask_out;
+};
+
+__device__ __forceinline__ float cosine_from(float dot, float na, float nb) {
+  // NaN propagates (comparisons with NaN are false), zero norm gives 0
+  if (isnan(dot) || isnan(na) || isnan(nb)) return __builtin_nanf("");
+  if (!(na > 0.0f) || !(nb > 0.0f)) return 0.0f;
+  float c = dot / (sqrtf(na) * sqrtf(nb));
+  c = c > 1.0f ? 1.0f : c;
+  c = c < -1.0f ? -1.0f : c;
+  return c;
+}
+
+__device__ __forceinline__ void write_decision(const RouteArgs& a, int i, float c, float p,
+                                               bool router) {
+  bool e = router ? ((c > a.tau) && (p > a.theta)) : (c > a.tau);
+  if (a.cos_out) a.cos_out[i] = c;
+  if (a.prob_out) a.prob_out[i] = p;
+  a.mask_out[i] = e ? 1 : 0;
+}
+
+// --------------------------------------------------------- generic path
+// One wave per token row. Used for fp32 and for shapes the MFMA path does
+// not take. Dynamic LDS holds the normalised row (d floats) when the
+// router is on.
+template <bool BF16>
+__global__ __launch_bounds__(64) void route_generic_kernel(RouteArgs a) {
+  extern __shared__ float xs[];
+  const int i = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int d = a.d;
+  float dot = 0.f, na = 0.f, nb = 0.f;
+  const int64_t op = (int64_t)i * a.ldp, oc = (int64_t)i * a.ldc;
+  for (int k = lane; k < d; k += WAVE) {
+    float x = load_elem<BF16>(a.hp, op + k);
+    float y = load_elem<BF16>(a.hc, oc + k);
+    dot = fmaf(x, y, dot);
+    na = fmaf(x, x, na);
+    nb = fmaf(y, y, nb);
+  }
+  dot = wave_sum(dot);
+  na = wave_sum(na);
+  nb = wave_sum(nb);
+  const float c = cosine_from(dot, na, nb);
+  float p = 1.0f;
+  const bool router = a.wd != nullptr;
+  if (router) {
+    const float r = 1.0f / sqrtf(nb / (float)d + a.eps);
+    for (int k = lane; k < d; k += WAVE) {
+      float g = a.gamma ? load_elem<BF16>(a.gamma, k) : 1.0f;
+      xs[k] = load_elem<BF16>(a.hc, oc + k) * g;
+    }
+    __syncthreads();
+    float zp = 0.f;
+    for (int j = lane; j < a.b; j += WAVE) {
+      float u = 0.f;
+      const int64_t wo = (int64_t)j * d;
+      for (int k = 0; k < d; ++k) u = fmaf(load_elem<BF16>(a.wd, wo + k), xs[k], u);
+      u *= r;
+      const float act = u * sigmoidf_(u);
+      zp = fmaf(act, load_elem<BF16>(a.wu, j), zp);
+    }
+    p = sigmoidf_(wave_sum(zp));
+  }
+  if (lane == 0) write_decision(a, i, c, p, router);
+}
+
+// ------------------------------------------------------------ MFMA path
+template <int RT>
+struct SlabRegs {
+  u32x4 c[RT], p[RT];
+};
+
+template <int RT, int NT, bool HAS_GAMMA>
+__global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a) {
+  constexpr int T = 16 * RT;          // tokens per workgroup
+  constexpr int BW = NT * 16;         // router units held per wave
+  constexpr int TPR = 256 / T;        // epilogue threads per token
+  __shared__ float red[4][T][BW];     // per-wave partial U
+  __shared__ float nrm[4][T][3];      // per-wave partial dot, |a|^2, |b|^2
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row0 = blockIdx.x * T;
+  const int d = a.d, b = a.b, n = a.n;
+  const int fr = lane & 15;           // fragment row (token) / column (unit)
+  const int fk = (lane >> 4) * 8;     // fragment k offset inside a 32-slab
+
+  const uint16_t* hp = (const uint16_t*)a.hp;
+  const uint16_t* hc = (const uint16_t*)a.hc;
+  const uint16_t* wd = (const uint16_t*)a.wd;
+  const uint16_t* gm = (const uint16_t*)a.gamma;
+
+  const uint16_t* pc[RT];
+  const uint16_t* pp[RT];
+  bool rv[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = row0 + rt * 16 + fr;
+    rv[rt] = row < n;
+    const int rr = rv[rt] ? row : 0;
+    pc[rt] = hc + (int64_t)rr * a.ldc + fk;
+    pp[rt] = hp + (int64_t)rr * a.ldp + fk;
+  }
+  const uint16_t* pw[NT];
+  bool wv[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int j = nt * 16 + fr;
+    wv[nt] = j < b;
+    pw[nt] = wd + (int64_t)(wv[nt] ? j : 0) * d + fk;
+  }
+
+  f32x4 acc[RT][NT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[rt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dot[RT], na[RT], nb[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) dot[rt] = na[rt] = nb[rt] = 0.f;
+
+  const int KS = d / 32;
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  SlabRegs<RT> cur, nxt;
+  int ks = wave;
+  if (ks < KS) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      cur.c[rt] = rv[rt] ? *(const u32x4*)(pc[rt] + ks * 32) : zero4;
+      cur.p[rt] = rv[rt] ? *(const u32x4*)(pp[rt] + ks * 32) : zero4;
+    }
+  }
+  for (; ks < KS; ks += 4) {
+    const int k = ks * 32;
+    if (ks + 4 < KS) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        nxt.c[rt] = rv[rt] ? *(const u32x4*)(pc[rt] + k + 128) : zero4;
+        nxt.p[rt] = rv[rt] ? *(const u32x4*)(pp[rt] + k + 128) : zero4;
+      }
+    }
+    u32x4 wb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) wb[nt] = wv[nt] ? *(const u32x4*)(pw[nt] + k) : zero4;
+    u32x4 g4;
+    if constexpr (HAS_GAMMA) g4 = *(const u32x4*)(gm + k + fk);
+
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      // norms from the raw bf16 values
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float c0 = bf16_lo(cur.c[rt][w]), c1 = bf16_hi(cur.c[rt][w]);
+        const float p0 = bf16_lo(cur.p[rt][w]), p1 = bf16_hi(cur.p[rt][w]);
+        dot[rt] = fmaf(p0, c0, dot[rt]); dot[rt] = fmaf(p1, c1, dot[rt]);
+        na[rt] = fmaf(p0, p0, na[rt]);   na[rt] = fmaf(p1, p1, na[rt]);
+        nb[rt] = fmaf(c0, c0, nb[rt]);   nb[rt] = fmaf(c1, c1, nb[rt]);
+      }
+      if constexpr (HAS_GAMMA) {
+        u32x4 hi4, lo4;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float x0 = bf16_lo(cur.c[rt][w]) * bf16_lo(g4[w]);   // exact in fp32
+          const float x1 = bf16_hi(cur.c[rt][w]) * bf16_hi(g4[w]);
+          const uint32_t h = pack_bf16x2(x0, x1);
+          hi4[w] = h;
+          lo4[w] = pack_bf16x2(x0 - bf16_lo(h), x1 - bf16_hi(h));
+        }
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, hi4);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, lo4);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, wb[nt]);
+          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, acc[rt][nt], 0, 0, 0);
+          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, acc[rt][nt], 0, 0, 0);
+        }
+      } else {
+        const bf16x8 aa = __builtin_bit_cast(bf16x8, cur.c[rt]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, wb[nt]);
+          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, bb, acc[rt][nt], 0, 0, 0);
+        }
+      }
+    }
+    cur = nxt;
+  }
+
+  // lanes fr, fr+16, fr+32, fr+48 hold the same token row
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    dot[rt] += __shfl_xor(dot[rt], 16, WAVE); dot[rt] += __shfl_xor(dot[rt], 32, WAVE);
+    na[rt] += __shfl_xor(na[rt], 16, WAVE);   na[rt] += __shfl_xor(na[rt], 32, WAVE);
+    nb[rt] += __shfl_xor(nb[rt], 16, WAVE);   nb[rt] += __shfl_xor(nb[rt], 32, WAVE);
+    if (lane < 16) {
+      nrm[wave][rt * 16 + lane][0] = dot[rt];
+      nrm[wave][rt * 16 + lane][1] = na[rt];
+      nrm[wave][rt * 16 + lane][2] = nb[rt];
+    }
+    // 16x16 accumulator layout: column = lane % 16, row = 4 * (lane / 16) + i
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][rt * 16 + 4 * (lane >> 4) + i][nt * 16 + fr] = acc[rt][nt][i];
+  }
+  __syncthreads();
+
+  const int row = tid / TPR, part = tid % TPR;
+  const int gi = row0 + row;
+  const float sd = ((nrm[0][row][0] + nrm[1][row][0]) + nrm[2][row][0]) + nrm[3][row][0];
+  const float sa = ((nrm[0][row][1] + nrm[1][row][1]) + nrm[2][row][1]) + nrm[3][row][1];
+  const float sb = ((nrm[0][row][2] + nrm[1][row][2]) + nrm[2][row][2]) + nrm[3][row][2];
+  const float r = 1.0f / sqrtf(sb / (float)d + a.eps);
+  float zp = 0.f;
+  for (int u = part; u < b; u += TPR) {
+    const float s = ((red[0][row][u] + red[1][row][u]) + red[2][row][u]) + red[3][row][u];
+    const float x = s * r;
+    const float act = x * sigmoidf_(x);
+    zp = fmaf(act, load_elem<true>(a.wu, u), zp);
+  }
+  const float z = group_sum<TPR>(zp);
+  if (part == 0 && gi < n) write_decision(a, gi, cosine_from(sd, sa, sb), sigmoidf_(z), true);
+}
+
+// ------------------------------------------------------------ batch rule
+// AND of the per-token decisions; for the batch-min rule the AND is then
+// broadcast to every token's mask (River-LLM 方法步骤详情 step 3, TIDE
+// formula 4: exit only when every token of the batch passes).
+__global__ __launch_bounds__(1024) void route_finish_kernel(int n, uint8_t* mask, int32_t* all_out,
+                                                            int batch_min) {
+  int all = 1;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) all &= (mask[i] != 0);
+  all = __syncthreads_and(all);
+  if (n == 0) all = 0;
+  if (threadIdx.x == 0 && all_out) *all_out = all;
+  if (batch_min)
+    for (int i = threadIdx.x; i < n; i += blockDim.x) mask[i] = (uint8_t)all;
+}
+
+}  // namespace river
+
+namespace river_host {
+using namespace river;
+
+river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int64_t ld_prev,
+                          const void* h_cur, int64_t ld_cur, const void* gamma, float eps,
+                          const void* w_down, const void* w_up, int b, float tau, float theta,
+                          river_rule rule, float* cos_out, float* prob_out, uint8_t* mask_out,
+                          int32_t* all_exit_out, hipStream_t s) {
+  RouteArgs a{n, d, b, h_prev, ld_prev, h_cur, ld_cur, gamma, eps, w_down, w_up, tau, theta,
+              cos_out, prob_out, mask_out};
+  if (n > 0) {
+    const bool mfma = dt == RIVER_BF16 && w_down && d % 32 == 0 && b % 16 == 0 && b <= 128;
+    if (mfma) {
+      const bool two = n >= 8192;   // 32 tokens per workgroup once the grid is large
+      const bool g = gamma != nullptr;
+      if (two) {
+        dim3 grid((n + 31) / 32);
+        if (g) route_mfma_kernel<2, 8, true><<<grid, 256, 0, s>>>(a);
+        else route_mfma_kernel<2, 8, false><<<grid, 256, 0, s>>>(a);
+      } else {
+        dim3 grid((n + 15) / 16);
+        if (g) route_mfma_kernel<1, 8, true><<<grid, 256, 0, s>>>(a);
+        else route_mfma_kernel<1, 8, false><<<grid, 256, 0, s>>>(a);
+      }
+    } else {
+      const size_t lds = w_down ? (size_t)d * sizeof(float) : 0;
+      if (lds > 65536) return fail(RIVER_ERR_UNSUPPORTED, "route: router with d = %d needs the bf16 path (d %% 32 == 0, b %% 16 == 0, b <= 128)", d);
+      if (dt == RIVER_BF16) route_generic_kernel<true><<<n, 64, lds, s>>>(a);
+      else route_generic_kernel<false><<<n, 64, lds, s>>>(a);
+    }
+    river_status st = check_launch("route");
+    if (st != RIVER_OK) return st;
+  }
+  if (rule == RIVER_RULE_BATCH_MIN || all_exit_out) {
+    route_finish_kernel<<<1, 1024, 0, s>>>(n, mask_out, all_exit_out, rule == RIVER_RULE_BATCH_MIN);
+    return check_launch("route finish");
+  }
+  return RIVER_OK;
+}
+
+}  // namespace river_host
