@@ -1,0 +1,266 @@
+"""Benchmark of the per-token exit-and-KV-fill step on one MI355X.
+
+One step is one pass of the whole hot path over one batch: river_route at
+the exit layer, river_compact, then river_kv_fill of every skipped layer of
+the exited tokens (ridge maps + W4A16 K/V projection + cache write). The
+default workload is the GPT-2-small-shape prefill: 4096 tokens, d = 768,
+12 layers, exit check at layer 4, fill of layers 5..12. Inputs are seeded
+synthetic tensors; the ridge maps are fitted on the GPU (river_ridge_fit,
+outside the timed region) from synthetic calibration states.
+
+The timed region enqueues K steps back to back on one stream between two
+events, after W warm-up steps. Each step uses the next of R rotating input
+and output sets so that no set is still resident in the 256 MB MALL or the
+L2 when it comes round again (inputs sit in HBM when the region starts).
+
+Output: one JSON line with the metric, the roofline of the dominant kernel
+(measured live with events on the launch stream) and the oracle's CPU time
+on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import token_early_exit_amd as tee  # noqa: E402
+from synth import get_config  # noqa: E402
+from synth import generate as G  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=12, help="input/output sets cycled through")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
+    return ap.parse_args()
+
+
+class Workload:
+    """The GPT-2-shape prefill step, with R rotating sets of tensors."""
+
+    def __init__(self, R, dev="cuda"):
+        cfg = self.cfg = get_config(1)
+        e = self.e = cfg.route_layers[0]
+        self.layers = list(range(e + 1, cfg.L + 1))
+        self.nl = len(self.layers)
+        n, d = cfg.n_tokens, cfg.d
+        # drawn on the CPU (the same tensors the parity tests check), then moved
+        hs = G.hidden_states(cfg, n, [e - 1, e])
+        self.h_prev0, self.h_cur0 = hs[e - 1].to(dev), hs[e].to(dev)
+        self.wd, self.wu = (t.to(dev) for t in G.router_weights(cfg, e))
+        w = G.kv_weights(cfg, self.layers)
+        self.wk = tuple(t.to(dev) for t in w["wk"]) + (cfg.group,)
+        self.wv = tuple(t.to(dev) for t in w["wv"]) + (cfg.group,)
+        self.slot = G.slots(cfg, device=dev)
+        # ridge maps fitted on the GPU from the calibration pass
+        X, Y = (t.to(dev) for t in G.calibration(cfg, e))
+        self.maps = torch.empty((self.nl, d, d), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(tee.river_workspace_size(tee.OP_RIDGE_FIT, X.shape[0], d, d, self.nl,
+                                                  tee.RIVER_BF16), dtype=torch.uint8, device=dev)
+        t0 = time.perf_counter()
+        tee.river_ridge_fit(X, Y, cfg.ridge_lambda, self.maps, workspace=ws)
+        self.ridge_ms = (time.perf_counter() - t0) * 1e3
+        del X, Y, ws
+        # R rotating sets: states (perturbed copies), outputs, caches
+        self.sets = []
+        for r in range(R):
+            hp = self.h_prev0.clone()
+            hc = self.h_cur0.clone()
+            kc = torch.zeros((self.nl, cfg.n_slots, cfg.n_kv_heads, cfg.head_dim),
+                             dtype=torch.bfloat16, device=dev)
+            self.sets.append({
+                "hp": hp, "hc": hc, "kc": kc, "vc": torch.zeros_like(kc),
+                "mask": torch.empty(n, dtype=torch.uint8, device=dev),
+                "cont": torch.empty(n, dtype=torch.int32, device=dev),
+                "ext": torch.empty(n, dtype=torch.int32, device=dev),
+                "counts": torch.zeros(2, dtype=torch.int32, device=dev),
+                "out": torch.empty((n, d), dtype=torch.bfloat16, device=dev),
+            })
+        self.cws = torch.empty(max(256, tee.river_workspace_size(tee.OP_COMPACT, n)),
+                               dtype=torch.uint8, device=dev)
+        self.kws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, n, d, 0, 0, self.nl),
+                               dtype=torch.uint8, device=dev)
+
+    # the three calls of one step
+    def route(self, s):
+        cfg = self.cfg
+        tee.river_route(s["hp"], s["hc"], s["mask"], w_down=self.wd, w_up=self.wu,
+                        tau=cfg.tau, theta=cfg.theta)
+
+    def compact(self, s):
+        tee.river_compact(s["mask"], s["hc"], s["cont"], s["ext"], s["counts"], out=s["out"],
+                          workspace=self.cws)
+
+    def fill(self, s):
+        cfg = self.cfg
+        tee.river_kv_fill(s["hc"], self.slot, self.wk, self.wv, cfg.n_kv_heads, cfg.head_dim,
+                          s["kc"], s["vc"], m_max=cfg.n_tokens, m_dev=s["counts"][1:],
+                          row_idx=s["ext"], maps=self.maps, workspace=self.kws)
+
+    def step(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.route(s)
+        self.compact(s)
+        self.fill(s)
+
+    # algorithmic work of one step
+    def work(self, n_exit):
+        cfg = self.cfg
+        n, d, b, hd = cfg.n_tokens, cfg.d, cfg.b, cfg.hd
+        route_bytes = 2 * n * d * 2 + b * d * 2 + b * 2 + n * 1
+        compact_bytes = n * 1 + n * 4 + 2 * 4 + n * d * 2 + n_exit * d * 2
+        fill_flops = n_exit * self.nl * (2 * d * d + 2 * 2 * d * hd)
+        fill_bytes = (self.nl * d * d * 2 + self.nl * 2 * hd * (d // 2 + 2 * 2 * d // cfg.group)
+                      + n_exit * d * 2 + self.nl * n_exit * d * 2 * 2
+                      + self.nl * n_exit * 2 * hd * 2)
+        return route_bytes, compact_bytes, fill_flops, fill_bytes
+
+
+def time_region(fn, steps):
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def per_call_times(wl, steps):
+    """Average duration of each call, each bracketed by its own events on
+    the launch stream."""
+    names = ("route", "compact", "fill")
+    ev = {k: [] for k in names}
+    torch.cuda.synchronize()
+    for i in range(steps):
+        s = wl.sets[i % len(wl.sets)]
+        for k in names:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            getattr(wl, k)(s)
+            b.record()
+            ev[k].append((a, b))
+    torch.cuda.synchronize()
+    return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+
+
+def cpu_baseline(wl, target_s):
+    """The oracle (float64 NumPy, as it stands) on whole steps of the same
+    workload, repeated until about ``target_s`` seconds of CPU time."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    cfg = wl.cfg
+    hp = wl.h_prev0.double().cpu().numpy()
+    hc = wl.h_cur0.double().cpu().numpy()
+    wd = wl.wd.double().cpu().numpy()
+    wu = wl.wu.double().cpu().numpy()
+    maps = wl.maps.float().cpu().numpy()
+    wk = {"q": wl.wk[0].cpu().numpy(), "scale": wl.wk[1].double().cpu().numpy(),
+          "zero": wl.wk[2].double().cpu().numpy(), "group": cfg.group}
+    wv = {"q": wl.wv[0].cpu().numpy(), "scale": wl.wv[1].double().cpu().numpy(),
+          "zero": wl.wv[2].double().cpu().numpy(), "group": cfg.group}
+    slot = wl.slot.cpu().numpy()
+    kc = np.zeros((wl.nl, cfg.n_slots, cfg.n_kv_heads, cfg.head_dim))
+    steps, exited = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        _, _, mask, _ = O.route(hp, hc, None, 1e-6, wd, wu, cfg.tau, cfg.theta)
+        res = O.compact(mask, hc, None, np.zeros_like(hc))
+        ex = res["exit_idx"]
+        O.kv_fill(hc, ex, len(ex), slot, maps, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, kc)
+        steps += 1
+        exited += len(ex)
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    return {"value": exited / el, "unit": "exited tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{steps} whole steps of the same workload (route of {cfg.n_tokens} tokens, "
+                      f"compact, kv_fill of {len(ex)} exited tokens x {wl.nl} layers) in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    tee.load()
+    torch.cuda.set_device(0)
+    wl = Workload(args.rotate)
+
+    # warm-up, then the timed region
+    for i in range(args.warmup):
+        wl.step(i)
+    ms_total = time_region(wl.step, args.steps)
+    ms_step = ms_total / args.steps
+    n_exit = int(wl.sets[0]["counts"][1].item())
+    calls = per_call_times(wl, max(20, args.steps // 4))
+
+    route_b, compact_b, fill_f, fill_b = wl.work(n_exit)
+    value = n_exit / (ms_step * 1e-3)
+    # dominant kernel: the call with the largest share of the step
+    dom = max(calls, key=calls.get)
+    if dom == "fill":
+        ach = fill_f / (calls["fill"] * 1e-3) / 1e12
+        roof = {"kernel": "kv_fill (map + W4A16 projection GEMMs)", "bound": "mfma",
+                "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+    else:
+        by = route_b if dom == "route" else compact_b
+        ach = by / (calls[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+
+    line = {
+        "metric": "exited tokens/s (route+compact+kv_fill)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gpt2-small-shape prefill: 4096 tokens, d=768, L=12, exit check "
+                               "at layer 4 (tau=0.9, theta=0.5, router b=128), fill of layers "
+                               "5-12 through ridge maps and int4 (group 64) K/V, 12x64 KV heads",
+                   "exited_per_step": n_exit, "rotating_sets": args.rotate},
+        "breakdown_us": {k: v * 1e3 for k, v in calls.items()},
+        "fill_tflops": fill_f / (calls["fill"] * 1e-3) / 1e12,
+        "route_gbs": route_b / (calls["route"] * 1e-3) / 1e9,
+        "compact_gbs": compact_b / (calls["compact"] * 1e-3) / 1e9,
+        "ridge_fit_ms_once": wl.ridge_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

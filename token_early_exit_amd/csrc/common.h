@@ -27,8 +27,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 b = (__bf16)f;
   return __builtin_bit_cast(uint16_t, b);
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (lo in bits 0..15), one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// x & m, opaque to the compiler's known-bits analysis (so that a later
+// (float)((x >> 8 j) & 0xff) becomes a single v_cvt_f32_ubyte<j>)
+__device__ __forceinline__ uint32_t opaque_and(uint32_t x, uint32_t m) {
+  uint32_t r;
+  asm("v_and_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(m));
+  return r;
 }
 
 // load element i of a dt array as fp32

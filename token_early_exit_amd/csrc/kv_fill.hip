@@ -90,8 +90,11 @@ namespace river_host {
 using namespace river;
 
 static bool fill_mfma_ok(int d, river_dtype dt, int nh, const river_w4* wk, const river_w4* wv) {
-  return dt == RIVER_BF16 && d % 64 == 0 && nh % 32 == 0 && wk->group % 32 == 0 &&
-         wv->group % 32 == 0;
+  // group multiple of 64 (one group per K-slab); an even number of groups
+  // per row for bf16 scale/zero (read as aligned 4-byte words)
+  const bool even = wk->sz_dtype == RIVER_F32 || (d / wk->group) % 2 == 0;
+  return dt == RIVER_BF16 && d % 64 == 0 && nh % 32 == 0 && wk->group % 64 == 0 &&
+         wk->group == wv->group && wk->sz_dtype == wv->sz_dtype && even;
 }
 
 size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt) {
@@ -136,9 +139,6 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
   g.e_nrows = n_rows;
   g.cache_bstride = n_slots * nh;
 
-  const bool small = m_max <= 64;
-  const int BM = small ? 64 : 128;
-  const int mt = (m_max + BM - 1) / BM;
 
   auto stage2 = [&](int l0, int nl, const uint16_t* A, int64_t lda, int64_t a_bs,
                     const int32_t* a_rows, int a_nrows) -> river_status {
@@ -154,9 +154,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.e_rows = row_idx;
     q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
-    dim3 grid((2 * nh) / 128 + ((2 * nh) % 128 ? 1 : 0), mt, nl);
-    if (small) gemm_nt_kernel<64, true, EPI_CACHE><<<grid, 256, 0, s>>>(q);
-    else gemm_nt_kernel<128, true, EPI_CACHE><<<grid, 256, 0, s>>>(q);
+    gemm_auto<true, EPI_CACHE>(q, nl, s);
     return check_launch("kv_fill projection");
   };
 
@@ -173,9 +171,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     p.A = (const uint16_t*)h; p.lda = ld_h; p.a_bstride = 0; p.a_rows = row_idx; p.a_nrows = n_rows;
     p.B = (const uint16_t*)maps + (int64_t)l0 * d * d; p.ldb = d; p.b_bstride = (int64_t)d * d;
     p.C = xh; p.ldc = d; p.c_bstride = (int64_t)m_max * d;
-    dim3 grid(d / 128 + (d % 128 ? 1 : 0), mt, nl);
-    if (small) gemm_nt_kernel<64, false, EPI_BF16><<<grid, 256, 0, s>>>(p);
-    else gemm_nt_kernel<128, false, EPI_BF16><<<grid, 256, 0, s>>>(p);
+    gemm_auto<false, EPI_BF16>(p, nl, s);
     river_status st = check_launch("kv_fill map");
     if (st != RIVER_OK) return st;
     st = stage2(l0, nl, xh, d, (int64_t)m_max * d, nullptr, m_max);

@@ -341,7 +341,7 @@ river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const v
     g.A = w.Xt; g.lda = n; g.a_nrows = d_in;
     g.B = w.Xt; g.ldb = n;
     g.C = w.G; g.ldc = d_in; g.diag = lambda;
-    gemm_nt_kernel<128, false, EPI_F32><<<dim3((d_in + 127) / 128, (d_in + 127) / 128, 1), 256, 0, s>>>(g);
+    gemm_auto<false, EPI_F32>(g, 1, s);
     if ((st = check_launch("ridge gram")) != RIVER_OK) return st;
   } else {
     const float* Xf = (const float*)X;
@@ -361,20 +361,19 @@ river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const v
       c.A = w.Yt; c.lda = n; c.a_nrows = d_out;
       c.B = w.Xt; c.ldb = n;
       c.C = w.Ct; c.ldc = d_in;
-      gemm_nt_kernel<128, false, EPI_F32><<<dim3((d_in + 127) / 128, (d_out + 127) / 128, 1), 256, 0, s>>>(c);
+      gemm_auto<false, EPI_F32>(c, 1, s);
       split3_kernel<<<grid1d(wsz), 256, 0, s>>>(w.Ct, d_out, d_in, w.Acat, 0b100);
       GemmArgs f{};
       f.M_max = d_out; f.N = d_in; f.K = 3 * d_in;
       f.A = w.Acat; f.lda = 3 * d_in; f.a_nrows = d_out;
       f.B = w.Bcat; f.ldb = 3 * d_in;
       f.ldc = d_in;
-      dim3 grid((d_in + 127) / 128, (d_out + 127) / 128, 1);
       if (wdt == RIVER_BF16) {
         f.C = (uint16_t*)W + t * wsz;
-        gemm_nt_kernel<128, false, EPI_BF16><<<grid, 256, 0, s>>>(f);
+        gemm_auto<false, EPI_BF16>(f, 1, s);
       } else {
         f.C = (float*)W + t * wsz;
-        gemm_nt_kernel<128, false, EPI_F32><<<grid, 256, 0, s>>>(f);
+        gemm_auto<false, EPI_F32>(f, 1, s);
       }
       if ((st = check_launch("ridge target")) != RIVER_OK) return st;
     }

@@ -6,14 +6,14 @@
 // thresholds. TIDE 模块4 fuses RMSNorm and the router into one launch; here
 // the cosine is fused in as well, so h_prev and h_cur are each read once.
 //
-// bf16 path: one workgroup = 4 waves = 16*RT tokens. The four waves split
-// the feature dimension in 32-wide slabs; each wave keeps the 16xRT token
-// rows' partial norms in registers and runs the router down-projection on
-// bf16 MFMA (16x16x32) with the RMSNorm scale applied afterwards in fp32:
+// bf16 path: one workgroup = 8 waves = 16*RT tokens. The waves split the
+// feature dimension in 32-wide slabs; each wave keeps the 16xRT token rows'
+// partial norms in registers and runs the router down-projection on bf16
+// MFMA (16x16x32) with the RMSNorm scale applied afterwards in fp32:
 //   u = r * (W_down . (gamma * h)),   r = 1 / sqrt(mean(h^2) + eps),
 // which never rounds the normalised vector to bf16. gamma != 1 is fed as
 // the exact fp32 product gamma*h split into two bf16 terms (hi + lo).
-// The partial results of the four waves are summed in LDS in a fixed order
+// The partial results of the waves are summed in LDS in a fixed order
 // (deterministic), then the SiLU / w_up / sigmoid epilogue runs per token.
 #include "common.h"
 
@@ -94,18 +94,30 @@ __global__ __launch_bounds__(64) void route_generic_kernel(RouteArgs a) {
 }
 
 // ------------------------------------------------------------ MFMA path
+// WAVES waves split the feature dimension into 32-wide slabs (slab
+// ks = wave + WAVES * j). Each wave streams its slabs of h_prev / h_cur for
+// its 16 * RT token rows through a 4-deep register ring (three slabs in
+// flight while one is used) and its router-weight fragments through a
+// 2-deep ring. Loads past the wave's last slab re-read that slab (L2 hits)
+// so that every iteration issues the same loads and the compiler's wait
+// counts stay exact.
 template <int RT>
-struct SlabRegs {
+struct HSlab {
   u32x4 c[RT], p[RT];
 };
+template <int NT>
+struct WSlab {
+  u32x4 w[NT];
+};
 
-template <int RT, int NT, bool HAS_GAMMA>
-__global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a) {
+template <int RT, int NT, bool HAS_GAMMA, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
   constexpr int T = 16 * RT;          // tokens per workgroup
   constexpr int BW = NT * 16;         // router units held per wave
-  constexpr int TPR = 256 / T;        // epilogue threads per token
-  __shared__ float red[4][T][BW];     // per-wave partial U
-  __shared__ float nrm[4][T][3];      // per-wave partial dot, |a|^2, |b|^2
+  constexpr int NTH = 64 * WAVES;
+  constexpr int TPR = NTH / T;        // epilogue threads per token
+  __shared__ float red[WAVES][T][BW]; // per-wave partial U
+  __shared__ float nrm[WAVES][T][3];  // per-wave partial dot, |a|^2, |b|^2
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row0 = blockIdx.x * T;
@@ -120,23 +132,22 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a) {
 
   const uint16_t* pc[RT];
   const uint16_t* pp[RT];
-  bool rv[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int row = row0 + rt * 16 + fr;
-    rv[rt] = row < n;
-    const int rr = rv[rt] ? row : 0;
+    const int rr = row < n ? row : n - 1;   // rows past n re-read the last row; dropped
     pc[rt] = hc + (int64_t)rr * a.ldc + fk;
     pp[rt] = hp + (int64_t)rr * a.ldp + fk;
   }
   const uint16_t* pw[NT];
-  bool wv[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int j = nt * 16 + fr;
-    wv[nt] = j < b;
-    pw[nt] = wd + (int64_t)(wv[nt] ? j : 0) * d + fk;
+    pw[nt] = wd + (int64_t)(j < b ? j : b - 1) * d + fk;   // units past b: zero below
   }
+  bool wv[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) wv[nt] = nt * 16 + fr < b;
 
   f32x4 acc[RT][NT];
 #pragma unroll
@@ -148,38 +159,34 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a) {
   for (int rt = 0; rt < RT; ++rt) dot[rt] = na[rt] = nb[rt] = 0.f;
 
   const int KS = d / 32;
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  SlabRegs<RT> cur, nxt;
-  int ks = wave;
-  if (ks < KS) {
+  const int J = (KS - wave + WAVES - 1) / WAVES;   // this wave's slabs
+  const int jl = J - 1;
+  auto koff = [&](int j) { return (wave + WAVES * (j < jl ? j : jl)) * 32; };
+  HSlab<RT> hr[4];
+  WSlab<NT> wr[2];
+  auto load_h = [&](HSlab<RT>& h, int j) {
+    const int k = koff(j);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      cur.c[rt] = rv[rt] ? *(const u32x4*)(pc[rt] + ks * 32) : zero4;
-      cur.p[rt] = rv[rt] ? *(const u32x4*)(pp[rt] + ks * 32) : zero4;
+      h.c[rt] = *(const u32x4*)(pc[rt] + k);
+      h.p[rt] = *(const u32x4*)(pp[rt] + k);
     }
-  }
-  for (; ks < KS; ks += 4) {
-    const int k = ks * 32;
-    if (ks + 4 < KS) {
+  };
+  auto load_w = [&](WSlab<NT>& w, int j) {
+    const int k = koff(j);
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        nxt.c[rt] = rv[rt] ? *(const u32x4*)(pc[rt] + k + 128) : zero4;
-        nxt.p[rt] = rv[rt] ? *(const u32x4*)(pp[rt] + k + 128) : zero4;
-      }
-    }
-    u32x4 wb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) wb[nt] = wv[nt] ? *(const u32x4*)(pw[nt] + k) : zero4;
+    for (int nt = 0; nt < NT; ++nt) w.w[nt] = *(const u32x4*)(pw[nt] + k);
+  };
+  auto step = [&](const HSlab<RT>& h, const WSlab<NT>& w, int j) {
+    if (j >= J) return;
     u32x4 g4;
-    if constexpr (HAS_GAMMA) g4 = *(const u32x4*)(gm + k + fk);
-
+    if constexpr (HAS_GAMMA) g4 = *(const u32x4*)(gm + koff(j) + fk);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      // norms from the raw bf16 values
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float c0 = bf16_lo(cur.c[rt][w]), c1 = bf16_hi(cur.c[rt][w]);
-        const float p0 = bf16_lo(cur.p[rt][w]), p1 = bf16_hi(cur.p[rt][w]);
+      for (int q = 0; q < 4; ++q) {
+        const float c0 = bf16_lo(h.c[rt][q]), c1 = bf16_hi(h.c[rt][q]);
+        const float p0 = bf16_lo(h.p[rt][q]), p1 = bf16_hi(h.p[rt][q]);
         dot[rt] = fmaf(p0, c0, dot[rt]); dot[rt] = fmaf(p1, c1, dot[rt]);
         na[rt] = fmaf(p0, p0, na[rt]);   na[rt] = fmaf(p1, p1, na[rt]);
         nb[rt] = fmaf(c0, c0, nb[rt]);   nb[rt] = fmaf(c1, c1, nb[rt]);
@@ -187,31 +194,43 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a) {
       if constexpr (HAS_GAMMA) {
         u32x4 hi4, lo4;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float x0 = bf16_lo(cur.c[rt][w]) * bf16_lo(g4[w]);   // exact in fp32
-          const float x1 = bf16_hi(cur.c[rt][w]) * bf16_hi(g4[w]);
-          const uint32_t h = pack_bf16x2(x0, x1);
-          hi4[w] = h;
-          lo4[w] = pack_bf16x2(x0 - bf16_lo(h), x1 - bf16_hi(h));
+        for (int q = 0; q < 4; ++q) {
+          const float x0 = bf16_lo(h.c[rt][q]) * bf16_lo(g4[q]);   // exact in fp32
+          const float x1 = bf16_hi(h.c[rt][q]) * bf16_hi(g4[q]);
+          const uint32_t hh = pack_bf16x2(x0, x1);
+          hi4[q] = hh;
+          lo4[q] = pack_bf16x2(x0 - bf16_lo(hh), x1 - bf16_hi(hh));
         }
         const bf16x8 ah = __builtin_bit_cast(bf16x8, hi4);
         const bf16x8 al = __builtin_bit_cast(bf16x8, lo4);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const bf16x8 bb = __builtin_bit_cast(bf16x8, wb[nt]);
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, wv[nt] ? w.w[nt] : u32x4{0u, 0u, 0u, 0u});
           acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, acc[rt][nt], 0, 0, 0);
           acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, acc[rt][nt], 0, 0, 0);
         }
       } else {
-        const bf16x8 aa = __builtin_bit_cast(bf16x8, cur.c[rt]);
+        const bf16x8 aa = __builtin_bit_cast(bf16x8, h.c[rt]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          const bf16x8 bb = __builtin_bit_cast(bf16x8, wb[nt]);
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, wv[nt] ? w.w[nt] : u32x4{0u, 0u, 0u, 0u});
           acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aa, bb, acc[rt][nt], 0, 0, 0);
         }
       }
     }
-    cur = nxt;
+  };
+
+  if (J > 0) {
+    load_h(hr[0], 0);
+    load_h(hr[1], 1);
+    load_h(hr[2], 2);
+    load_w(wr[0], 0);
+    for (int j = 0; j < J; j += 4) {
+      load_h(hr[3], j + 3); load_w(wr[1], j + 1); step(hr[0], wr[0], j);
+      load_h(hr[0], j + 4); load_w(wr[0], j + 2); step(hr[1], wr[1], j + 1);
+      load_h(hr[1], j + 5); load_w(wr[1], j + 3); step(hr[2], wr[0], j + 2);
+      load_h(hr[2], j + 6); load_w(wr[0], j + 4); step(hr[3], wr[1], j + 3);
+    }
   }
 
   // lanes fr, fr+16, fr+32, fr+48 hold the same token row
@@ -235,13 +254,19 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(RouteArgs a) {
 
   const int row = tid / TPR, part = tid % TPR;
   const int gi = row0 + row;
-  const float sd = ((nrm[0][row][0] + nrm[1][row][0]) + nrm[2][row][0]) + nrm[3][row][0];
-  const float sa = ((nrm[0][row][1] + nrm[1][row][1]) + nrm[2][row][1]) + nrm[3][row][1];
-  const float sb = ((nrm[0][row][2] + nrm[1][row][2]) + nrm[2][row][2]) + nrm[3][row][2];
+  float sd = 0.f, sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {   // fixed order: deterministic
+    sd += nrm[w][row][0];
+    sa += nrm[w][row][1];
+    sb += nrm[w][row][2];
+  }
   const float r = 1.0f / sqrtf(sb / (float)d + a.eps);
   float zp = 0.f;
   for (int u = part; u < b; u += TPR) {
-    const float s = ((red[0][row][u] + red[1][row][u]) + red[2][row][u]) + red[3][row][u];
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += red[w][row][u];
     const float x = s * r;
     const float act = x * sigmoidf_(x);
     zp = fmaf(act, load_elem<true>(a.wu, u), zp);
@@ -284,12 +309,12 @@ river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int6
       const bool g = gamma != nullptr;
       if (two) {
         dim3 grid((n + 31) / 32);
-        if (g) route_mfma_kernel<2, 8, true><<<grid, 256, 0, s>>>(a);
-        else route_mfma_kernel<2, 8, false><<<grid, 256, 0, s>>>(a);
+        if (g) route_mfma_kernel<2, 8, true, 8><<<grid, 512, 0, s>>>(a);
+        else route_mfma_kernel<2, 8, false, 8><<<grid, 512, 0, s>>>(a);
       } else {
         dim3 grid((n + 15) / 16);
-        if (g) route_mfma_kernel<1, 8, true><<<grid, 256, 0, s>>>(a);
-        else route_mfma_kernel<1, 8, false><<<grid, 256, 0, s>>>(a);
+        if (g) route_mfma_kernel<1, 8, true, 8><<<grid, 512, 0, s>>>(a);
+        else route_mfma_kernel<1, 8, false, 8><<<grid, 512, 0, s>>>(a);
       }
     } else {
       const size_t lds = w_down ? (size_t)d * sizeof(float) : 0;
