@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--rotate", type=int, default=12, help="input/output sets cycled through")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle CPU time")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--projection-only", type=int, default=0,
+                    help="only run this many projection-kernel launches (counter collection)")
     return ap.parse_args()
 
 
@@ -112,6 +116,14 @@ class Workload:
                           s["kc"], s["vc"], m_max=cfg.n_tokens, m_dev=s["counts"][1:],
                           row_idx=s["ext"], maps=self.maps, workspace=self.kws)
 
+    def fill_projection_only(self, s):
+        """The K/V projection kernel alone (identity map, same rows, same
+        output slots): one launch of the kernel that dominates the step."""
+        cfg = self.cfg
+        tee.river_kv_fill(s["hc"], self.slot, self.wk, self.wv, cfg.n_kv_heads, cfg.head_dim,
+                          s["kc"], s["vc"], m_max=cfg.n_tokens, m_dev=s["counts"][1:],
+                          row_idx=s["ext"], maps=None)
+
     def step(self, i):
         s = self.sets[i % len(self.sets)]
         self.route(s)
@@ -162,6 +174,55 @@ def per_call_times(wl, steps):
     return {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
 
 
+def kernel_times(wl, launches):
+    """Average duration of single-kernel calls: ``launches`` back-to-back
+    calls of one kind (rotating sets) between two events on the launch
+    stream, divided by their number. Back to back, the events see the
+    kernels' own durations plus the short dispatch gaps between them, the
+    figure a kernel trace reports as the average duration."""
+    out = {}
+    for k, fn in (("route", wl.route), ("projection", wl.fill_projection_only)):
+        for i in range(len(wl.sets)):
+            fn(wl.sets[i])
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(launches):
+            fn(wl.sets[i % len(wl.sets)])
+        b.record()
+        torch.cuda.synchronize()
+        out[k] = a.elapsed_time(b) / launches
+    return out
+
+
+def source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = ["token_early_exit_amd/csrc/gemm.h", "token_early_exit_amd/csrc/kv_fill.hip",
+                  "token_early_exit_amd/csrc/common.h"]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the projection kernel from the committed
+    rocprofv3 counter summary, or None when the kernel sources changed since
+    the counters were taken."""
+    f = os.path.join(ROOT, "profiles", "kv_projection_gpt2_traffic.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash(KERNEL_SOURCES):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 def cpu_baseline(wl, target_s):
     """The oracle (float64 NumPy, as it stands) on whole steps of the same
     workload, repeated until about ``target_s`` seconds of CPU time."""
@@ -208,7 +269,27 @@ def main():
         sys.exit(2)
     tee.load()
     torch.cuda.set_device(0)
+    if args.copy_probe_mb:
+        # a plain copy of known size: FETCH_SIZE / WRITE_SIZE calibration
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return
     wl = Workload(args.rotate)
+    if args.projection_only:
+        for i in range(len(wl.sets)):
+            wl.step(i)            # the exit lists of every set
+        torch.cuda.synchronize()
+        for i in range(args.projection_only):
+            wl.fill_projection_only(wl.sets[i % len(wl.sets)])
+        torch.cuda.synchronize()
+        print(json.dumps({"projection_launches": args.projection_only,
+                          "exited": int(wl.sets[0]["counts"][1].item())}))
+        return
 
     # warm-up, then the timed region
     for i in range(args.warmup):
@@ -217,21 +298,20 @@ def main():
     ms_step = ms_total / args.steps
     n_exit = int(wl.sets[0]["counts"][1].item())
     calls = per_call_times(wl, max(20, args.steps // 4))
+    kern = kernel_times(wl, max(50, args.steps))
 
     route_b, compact_b, fill_f, fill_b = wl.work(n_exit)
     value = n_exit / (ms_step * 1e-3)
-    # dominant kernel: the call with the largest share of the step
-    dom = max(calls, key=calls.get)
-    if dom == "fill":
-        ach = fill_f / (calls["fill"] * 1e-3) / 1e12
-        roof = {"kernel": "kv_fill (map + W4A16 projection GEMMs)", "bound": "mfma",
-                "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
-    else:
-        by = route_b if dom == "route" else compact_b
-        ach = by / (calls[dom] * 1e-3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None}
+    # dominant kernel: the W4A16 K/V projection GEMM with the cache write
+    # (gemm_nt_kernel<128, int4, cache>); algorithmic flops per launch =
+    # exited rows x layers x 2 x d x (2 n_kv_heads head_dim)
+    cfg = wl.cfg
+    proj_flops = n_exit * wl.nl * 2 * cfg.d * 2 * cfg.hd
+    ach = proj_flops / (kern["projection"] * 1e-3) / 1e12
+    roof = {"kernel": "gemm_nt_kernel<128,int4,cache> (kv_fill K/V projection)", "bound": "mfma",
+            "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(),
+            "flops_per_launch": proj_flops, "avg_launch_us": kern["projection"] * 1e3}
 
     line = {
         "metric": "exited tokens/s (route+compact+kv_fill)",
@@ -251,6 +331,7 @@ def main():
                                "5-12 through ridge maps and int4 (group 64) K/V, 12x64 KV heads",
                    "exited_per_step": n_exit, "rotating_sets": args.rotate},
         "breakdown_us": {k: v * 1e3 for k, v in calls.items()},
+        "route_kernel_us": kern["route"] * 1e3,
         "fill_tflops": fill_f / (calls["fill"] * 1e-3) / 1e12,
         "route_gbs": route_b / (calls["route"] * 1e-3) / 1e9,
         "compact_gbs": compact_b / (calls["compact"] * 1e-3) / 1e9,

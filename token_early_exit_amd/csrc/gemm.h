@@ -164,7 +164,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
   const int n0 = nt * BN;
   (void)tiles_m;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers
   const int wm = wave >> 1, wn = wave & 1;
 
   // DMA block b = i * 4 + wave covers LDS chunks [64 b, 64 b + 64); lane l

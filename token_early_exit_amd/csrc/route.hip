@@ -7,14 +7,17 @@
 // the cosine is fused in as well, so h_prev and h_cur are each read once.
 //
 // bf16 path: one workgroup = 8 waves = 16*RT tokens. The waves split the
-// feature dimension in 32-wide slabs; each wave keeps the 16xRT token rows'
-// partial norms in registers and runs the router down-projection on bf16
-// MFMA (16x16x32) with the RMSNorm scale applied afterwards in fp32:
+// feature dimension into 32-wide slabs (4 groups) and the router units in
+// two halves; each wave keeps partial norms in registers and runs the router
+// down-projection on bf16 MFMA (16x16x32) with the RMSNorm scale applied
+// afterwards in fp32:
 //   u = r * (W_down . (gamma * h)),   r = 1 / sqrt(mean(h^2) + eps),
 // which never rounds the normalised vector to bf16. gamma != 1 is fed as
 // the exact fp32 product gamma*h split into two bf16 terms (hi + lo).
 // The partial results of the waves are summed in LDS in a fixed order
 // (deterministic), then the SiLU / w_up / sigmoid epilogue runs per token.
+#include <type_traits>
+
 #include "common.h"
 
 namespace river {
@@ -94,32 +97,41 @@ __global__ __launch_bounds__(64) void route_generic_kernel(RouteArgs a) {
 }
 
 // ------------------------------------------------------------ MFMA path
-// WAVES waves split the feature dimension into 32-wide slabs (slab
-// ks = wave + WAVES * j). Each wave streams its slabs of h_prev / h_cur for
-// its 16 * RT token rows through a 4-deep register ring (three slabs in
-// flight while one is used) and its router-weight fragments through a
-// 2-deep ring. Loads past the wave's last slab re-read that slab (L2 hits)
-// so that every iteration issues the same loads and the compiler's wait
-// counts stay exact.
+// 8 waves = KG K-groups x UG unit-groups. K-group kg streams the 32-wide
+// feature slabs ks = kg + KG * j; unit-group ug owns router units
+// [64 ug, 64 ug + 64). Each wave keeps its slabs of h_prev / h_cur for the
+// 16 * RT token rows and its router-weight fragments in 4-deep register
+// rings (three slabs in flight while one is used). Loads past the last slab
+// re-read that slab (cache hits) so that every iteration issues the same
+// loads and control flow stays uniform. Unit-group 0 also accumulates the
+// cosine norms.
 template <int RT>
 struct HSlab {
   u32x4 c[RT], p[RT];
+  u32x4 g;            // gamma chunk (when gamma is given)
 };
 template <int NT>
 struct WSlab {
   u32x4 w[NT];
 };
 
-template <int RT, int NT, bool HAS_GAMMA, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
-  constexpr int T = 16 * RT;          // tokens per workgroup
-  constexpr int BW = NT * 16;         // router units held per wave
-  constexpr int NTH = 64 * WAVES;
-  constexpr int TPR = NTH / T;        // epilogue threads per token
-  __shared__ float red[WAVES][T][BW]; // per-wave partial U
-  __shared__ float nrm[WAVES][T][3];  // per-wave partial dot, |a|^2, |b|^2
+constexpr int R_KG = 4, R_UG = 2, R_NT = 4;   // 8 waves, 128 units
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int RT, bool HAS_GAMMA, bool FULLB>
+__global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
+  constexpr int KG = R_KG, UG = R_UG, NT = R_NT;
+  constexpr int T = 16 * RT;          // tokens per workgroup
+  constexpr int BU = UG * NT * 16;    // router units per workgroup (128)
+  constexpr int NTH = 64 * KG * UG;
+  constexpr int TPR = NTH / T;        // epilogue threads per token
+  __shared__ float red[KG][T][BU];    // per-K-group partial U
+  __shared__ float nrm[KG][T][3];     // per-K-group partial dot, |a|^2, |b|^2
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index is uniform across the wave; say so, so that everything
+  // derived from it (slab counts, offsets) lives in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = wave % KG, ug = wave / KG;
   const int row0 = blockIdx.x * T;
   const int d = a.d, b = a.b, n = a.n;
   const int fr = lane & 15;           // fragment row (token) / column (unit)
@@ -140,14 +152,14 @@ __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
     pp[rt] = hp + (int64_t)rr * a.ldp + fk;
   }
   const uint16_t* pw[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int j = nt * 16 + fr;
-    pw[nt] = wd + (int64_t)(j < b ? j : b - 1) * d + fk;   // units past b: zero below
-  }
   bool wv[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wv[nt] = nt * 16 + fr < b;
+  for (int nt = 0; nt < NT; ++nt) {
+    const int j = ug * NT * 16 + nt * 16 + fr;
+    wv[nt] = FULLB || j < b;
+    pw[nt] = wd + (int64_t)(j < b ? j : b - 1) * d + fk;   // units past b: zero below
+  }
+  const bool norms = ug == 0;
 
   f32x4 acc[RT][NT];
 #pragma unroll
@@ -159,44 +171,41 @@ __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
   for (int rt = 0; rt < RT; ++rt) dot[rt] = na[rt] = nb[rt] = 0.f;
 
   const int KS = d / 32;
-  const int J = (KS - wave + WAVES - 1) / WAVES;   // this wave's slabs
+  const int J = (KS - kg + KG - 1) / KG;   // this K-group's slabs (uniform)
   const int jl = J - 1;
-  auto koff = [&](int j) { return (wave + WAVES * (j < jl ? j : jl)) * 32; };
+  auto koff = [&](int j) { return (kg + KG * (j < jl ? j : jl)) * 32; };
   HSlab<RT> hr[4];
-  WSlab<NT> wr[2];
-  auto load_h = [&](HSlab<RT>& h, int j) {
+  WSlab<NT> wr[4];
+  auto load = [&](HSlab<RT>& h, WSlab<NT>& w, int j) {
     const int k = koff(j);
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       h.c[rt] = *(const u32x4*)(pc[rt] + k);
-      h.p[rt] = *(const u32x4*)(pp[rt] + k);
+      if (norms) h.p[rt] = *(const u32x4*)(pp[rt] + k);
     }
-  };
-  auto load_w = [&](WSlab<NT>& w, int j) {
-    const int k = koff(j);
+    if constexpr (HAS_GAMMA) h.g = *(const u32x4*)(gm + k + fk);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) w.w[nt] = *(const u32x4*)(pw[nt] + k);
   };
-  auto step = [&](const HSlab<RT>& h, const WSlab<NT>& w, int j) {
-    if (j >= J) return;
-    u32x4 g4;
-    if constexpr (HAS_GAMMA) g4 = *(const u32x4*)(gm + koff(j) + fk);
+  auto step = [&](const HSlab<RT>& h, const WSlab<NT>& w) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
+      if (norms) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float c0 = bf16_lo(h.c[rt][q]), c1 = bf16_hi(h.c[rt][q]);
-        const float p0 = bf16_lo(h.p[rt][q]), p1 = bf16_hi(h.p[rt][q]);
-        dot[rt] = fmaf(p0, c0, dot[rt]); dot[rt] = fmaf(p1, c1, dot[rt]);
-        na[rt] = fmaf(p0, p0, na[rt]);   na[rt] = fmaf(p1, p1, na[rt]);
-        nb[rt] = fmaf(c0, c0, nb[rt]);   nb[rt] = fmaf(c1, c1, nb[rt]);
+        for (int q = 0; q < 4; ++q) {
+          const float c0 = bf16_lo(h.c[rt][q]), c1 = bf16_hi(h.c[rt][q]);
+          const float p0 = bf16_lo(h.p[rt][q]), p1 = bf16_hi(h.p[rt][q]);
+          dot[rt] = fmaf(p0, c0, dot[rt]); dot[rt] = fmaf(p1, c1, dot[rt]);
+          na[rt] = fmaf(p0, p0, na[rt]);   na[rt] = fmaf(p1, p1, na[rt]);
+          nb[rt] = fmaf(c0, c0, nb[rt]);   nb[rt] = fmaf(c1, c1, nb[rt]);
+        }
       }
       if constexpr (HAS_GAMMA) {
         u32x4 hi4, lo4;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float x0 = bf16_lo(h.c[rt][q]) * bf16_lo(g4[q]);   // exact in fp32
-          const float x1 = bf16_hi(h.c[rt][q]) * bf16_hi(g4[q]);
+          const float x0 = bf16_lo(h.c[rt][q]) * bf16_lo(h.g[q]);   // exact in fp32
+          const float x1 = bf16_hi(h.c[rt][q]) * bf16_hi(h.g[q]);
           const uint32_t hh = pack_bf16x2(x0, x1);
           hi4[q] = hh;
           lo4[q] = pack_bf16x2(x0 - bf16_lo(hh), x1 - bf16_hi(hh));
@@ -221,34 +230,41 @@ __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
   };
 
   if (J > 0) {
-    load_h(hr[0], 0);
-    load_h(hr[1], 1);
-    load_h(hr[2], 2);
-    load_w(wr[0], 0);
-    for (int j = 0; j < J; j += 4) {
-      load_h(hr[3], j + 3); load_w(wr[1], j + 1); step(hr[0], wr[0], j);
-      load_h(hr[0], j + 4); load_w(wr[0], j + 2); step(hr[1], wr[1], j + 1);
-      load_h(hr[1], j + 5); load_w(wr[1], j + 3); step(hr[2], wr[0], j + 2);
-      load_h(hr[2], j + 6); load_w(wr[0], j + 4); step(hr[3], wr[1], j + 3);
+    load(hr[0], wr[0], 0);
+    load(hr[1], wr[1], 1);
+    load(hr[2], wr[2], 2);
+    int j = 0;
+    for (; j + 4 <= J; j += 4) {     // whole groups of four slabs, uniform control flow
+      load(hr[3], wr[3], j + 3); step(hr[0], wr[0]);
+      load(hr[0], wr[0], j + 4); step(hr[1], wr[1]);
+      load(hr[1], wr[1], j + 5); step(hr[2], wr[2]);
+      load(hr[2], wr[2], j + 6); step(hr[3], wr[3]);
     }
+    const int rem = J - j;            // 0..3 slabs left, in ring slots 0..2
+    if (rem > 0) step(hr[0], wr[0]);
+    if (rem > 1) step(hr[1], wr[1]);
+    if (rem > 2) step(hr[2], wr[2]);
   }
 
   // lanes fr, fr+16, fr+32, fr+48 hold the same token row
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    dot[rt] += __shfl_xor(dot[rt], 16, WAVE); dot[rt] += __shfl_xor(dot[rt], 32, WAVE);
-    na[rt] += __shfl_xor(na[rt], 16, WAVE);   na[rt] += __shfl_xor(na[rt], 32, WAVE);
-    nb[rt] += __shfl_xor(nb[rt], 16, WAVE);   nb[rt] += __shfl_xor(nb[rt], 32, WAVE);
-    if (lane < 16) {
-      nrm[wave][rt * 16 + lane][0] = dot[rt];
-      nrm[wave][rt * 16 + lane][1] = na[rt];
-      nrm[wave][rt * 16 + lane][2] = nb[rt];
+    if (norms) {
+      dot[rt] += __shfl_xor(dot[rt], 16, WAVE); dot[rt] += __shfl_xor(dot[rt], 32, WAVE);
+      na[rt] += __shfl_xor(na[rt], 16, WAVE);   na[rt] += __shfl_xor(na[rt], 32, WAVE);
+      nb[rt] += __shfl_xor(nb[rt], 16, WAVE);   nb[rt] += __shfl_xor(nb[rt], 32, WAVE);
+      if (lane < 16) {
+        nrm[kg][rt * 16 + lane][0] = dot[rt];
+        nrm[kg][rt * 16 + lane][1] = na[rt];
+        nrm[kg][rt * 16 + lane][2] = nb[rt];
+      }
     }
     // 16x16 accumulator layout: column = lane % 16, row = 4 * (lane / 16) + i
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][rt * 16 + 4 * (lane >> 4) + i][nt * 16 + fr] = acc[rt][nt][i];
+      for (int i = 0; i < 4; ++i)
+        red[kg][rt * 16 + 4 * (lane >> 4) + i][ug * NT * 16 + nt * 16 + fr] = acc[rt][nt][i];
   }
   __syncthreads();
 
@@ -256,17 +272,17 @@ __global__ __launch_bounds__(64 * WAVES) void route_mfma_kernel(RouteArgs a) {
   const int gi = row0 + row;
   float sd = 0.f, sa = 0.f, sb = 0.f;
 #pragma unroll
-  for (int w = 0; w < WAVES; ++w) {   // fixed order: deterministic
-    sd += nrm[w][row][0];
-    sa += nrm[w][row][1];
-    sb += nrm[w][row][2];
+  for (int k = 0; k < KG; ++k) {      // fixed order: deterministic
+    sd += nrm[k][row][0];
+    sa += nrm[k][row][1];
+    sb += nrm[k][row][2];
   }
   const float r = 1.0f / sqrtf(sb / (float)d + a.eps);
   float zp = 0.f;
   for (int u = part; u < b; u += TPR) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) s += red[w][row][u];
+    for (int k = 0; k < KG; ++k) s += red[k][row][u];
     const float x = s * r;
     const float act = x * sigmoidf_(x);
     zp = fmaf(act, load_elem<true>(a.wu, u), zp);
@@ -307,14 +323,22 @@ river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int6
     if (mfma) {
       const bool two = n >= 8192;   // 32 tokens per workgroup once the grid is large
       const bool g = gamma != nullptr;
+      const bool full = b == 128;
+      auto go = [&](auto rt, auto gam, auto fb) {
+        constexpr int RT = decltype(rt)::value;
+        route_mfma_kernel<RT, decltype(gam)::value, decltype(fb)::value>
+            <<<(n + 16 * RT - 1) / (16 * RT), 512, 0, s>>>(a);
+      };
+      using I1 = std::integral_constant<int, 1>;
+      using I2 = std::integral_constant<int, 2>;
+      using T = std::true_type;
+      using F = std::false_type;
       if (two) {
-        dim3 grid((n + 31) / 32);
-        if (g) route_mfma_kernel<2, 8, true, 8><<<grid, 512, 0, s>>>(a);
-        else route_mfma_kernel<2, 8, false, 8><<<grid, 512, 0, s>>>(a);
+        if (g) { if (full) go(I2{}, T{}, T{}); else go(I2{}, T{}, F{}); }
+        else { if (full) go(I2{}, F{}, T{}); else go(I2{}, F{}, F{}); }
       } else {
-        dim3 grid((n + 15) / 16);
-        if (g) route_mfma_kernel<1, 8, true, 8><<<grid, 512, 0, s>>>(a);
-        else route_mfma_kernel<1, 8, false, 8><<<grid, 512, 0, s>>>(a);
+        if (g) { if (full) go(I1{}, T{}, T{}); else go(I1{}, T{}, F{}); }
+        else { if (full) go(I1{}, F{}, T{}); else go(I1{}, F{}, F{}); }
       }
     } else {
       const size_t lds = w_down ? (size_t)d * sizeof(float) : 0;
