@@ -135,7 +135,7 @@ class Workload:
         cfg = self.cfg
         n, d, b, hd = cfg.n_tokens, cfg.d, cfg.b, cfg.hd
         route_bytes = 2 * n * d * 2 + b * d * 2 + b * 2 + n * 1
-        compact_bytes = n * 1 + n * 4 + 2 * 4 + n * d * 2 + n_exit * d * 2
+        compact_bytes = n * 1 + n * 4 + 2 * 4 + 2 * n_exit * d * 2   # mask, indices, counts, exit rows
         fill_flops = n_exit * self.nl * (2 * d * d + 2 * 2 * d * hd)
         fill_bytes = (self.nl * d * d * 2 + self.nl * 2 * hd * (d // 2 + 2 * 2 * d // cfg.group)
                       + n_exit * d * 2 + self.nl * n_exit * d * 2 * 2

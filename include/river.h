@@ -201,7 +201,11 @@ river_status river_compact(int n, int d, river_dtype dt, const uint8_t* mask,
  *            m_max, d, 0, 0, 1) bytes; the layers are processed in as few
  *            chunks as the given size allows. Without maps none is needed.
  * Only the filled slots are written; every other byte is left unchanged.
- * Requirements (bf16): d % 64 == 0, n_out % 32 == 0, group % 32 == 0.
+ * Paths: bf16 with d % 64 == 0, n_out % 32 == 0, group % 64 == 0, the same
+ * group and scale/zero dtype for wk and wv, and an even number of groups
+ * per row when scale/zero are bf16, runs on MFMA; every other shape (and
+ * fp32) runs a generic fp32 kernel, one workgroup per (row, layer), which
+ * needs d <= 8192 (RIVER_ERR_UNSUPPORTED otherwise).
  */
 river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt,
                            const void* h, int64_t ld_h, int n_rows,
