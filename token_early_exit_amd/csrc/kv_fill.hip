@@ -20,6 +20,7 @@
 // per (token, layer), fp32 throughout.
 #include "common.h"
 #include "gemm.h"
+#include "w4gemm.h"
 
 namespace river {
 
@@ -154,7 +155,12 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.e_rows = row_idx;
     q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
-    gemm_auto<true, EPI_CACHE>(q, nl, s);
+    // whole groups of four K-slabs, 64-column blocks inside one half, and
+    // every operand addressable with 32-bit offsets
+    const bool w4 = d % 256 == 0 && nh % 64 == 0 &&
+                    (int64_t)a_nrows * lda * 2 < ((int64_t)1 << 31) && (int64_t)nh * d < ((int64_t)1 << 31);
+    if (w4) w4_gemm_auto<EPI_CACHE>(q, nl, s);
+    else gemm_auto<true, EPI_CACHE>(q, nl, s);
     return check_launch("kv_fill projection");
   };
 

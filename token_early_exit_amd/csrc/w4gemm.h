@@ -1,0 +1,401 @@
+// W4A16 GEMM on gfx950 MFMA with the K/V cache scatter as its epilogue:
+//   C[z] = A[z] . deq(W[z])^T,   A bf16 [M][K], W int4 [N][K] (K-contiguous)
+// where rows [0, nh) of W come from descriptor 0 (K projection) and
+// [nh, 2 nh) from descriptor 1 (V projection), and
+//   deq(q) = (q - zero) * scale = fma(q, scale, -zero * scale)
+// per group of `group` input channels (a multiple of 64 here).
+//
+// Workgroup tile BM x 256, 4 waves. Wave w owns the 64 output columns
+// [64 w, 64 w + 64) for all BM rows: BM/32 x 2 accumulators of 32x32 fed by
+// v_mfma_f32_32x32x16_bf16. Only A goes through LDS (direct global->LDS
+// loads into a 4-stage ring, three K-slabs ahead); every wave reads the same
+// A fragments. Each lane fetches the 16 bytes of int4 weights it needs per
+// slab (staged through LDS with the A tile, three slabs ahead) and
+// dequantizes them in registers into the MFMA's B operand: no dequantized
+// tile goes through LDS, and each weight is dequantized once per workgroup.
+//
+// The reduction index inside a 64-wide slab is permuted so that one 16-byte
+// load per lane and column fragment covers the whole slab: in sub-step s
+// (16 channels), lane half h = lane / 32 contracts channels
+// 32 h + 8 s .. 32 h + 8 s + 7 (A chunk 4 h + s of its row, dword s of the
+// lane's 16 weight bytes). The sum over the slab is the same sum.
+//
+// Per 64-slab and workgroup (BM = 128): 128 MFMAs of 32 cycles per SIMD
+// (1024 cycles), 64 KB of LDS fragment reads plus 16 KB of DMA writes
+// and 24 KB of weight staging (about 810 cycles at 128 B/clk), 28 KB from
+// L2, and 8 dequant8 per lane.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+#include "gemm.h"
+
+namespace river {
+
+// dword 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit
+// data format, no swizzle, no index stride
+constexpr int RSRC_WORD3 = 0x00020000;
+
+// SIZE bytes per lane from the buffer [base, base + bytes) at byte offset
+// voff + soff straight into LDS (lane l writes lds + SIZE * l); a lane whose
+// bytes lie past the end reads zeros. base, bytes and soff are uniform, so
+// the resource sits in scalar registers and is built once per loop.
+template <int SIZE>   // 16 or 4
+__device__ __forceinline__ void buf_lds(const void* base, int bytes, uint32_t voff, int soff, void* lds) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, RSRC_WORD3);
+  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, soff, 0, 0);
+  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, (int)voff, soff, 0, 0);
+}
+
+// Scheduling hint for the preceding code of a basic block, per sub-step:
+// the LDS reads of the next fragments first (so their latency is covered),
+// then one MFMA at a time with a few VALU instructions (the dequantization
+// of the next fragments) and, every other MFMA, one of N_VMEM global loads,
+// so the matrix unit is fed while the vector unit dequantizes and no burst
+// of loads stalls the wave.
+template <int N_SUB, int MFMA_PER_SUB, int READS, int N_VMEM>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int sub = 0; sub < N_SUB; ++sub) {
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);                 // LDS reads first
+#pragma unroll
+    for (int i = 0; i < MFMA_PER_SUB; ++i) {
+      const int k = sub * MFMA_PER_SUB + i;
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                  // VALU
+      if (k % 2 == 1 && k / 2 < N_VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
+    }
+  }
+}
+
+template <int BM, int EPI, bool SZ_BF16>
+__global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, int batch) {
+  constexpr int BN = 256;
+  constexpr int MI = BM / 32;            // 32-row fragments (all rows of the tile)
+  constexpr int NI = 2;                  // 32-column fragments per wave
+  constexpr int AD = BM * 8 / 256;       // A DMA instructions per thread per slab
+  constexpr int SZB = SZ_BF16 ? 2 : 4;
+  // vector-memory instructions per thread per slab: A DMAs, 2 weight loads,
+  // one scale and one zero load
+  constexpr int PER_SLAB = AD + NI + 2;
+  // one LDS array per pipeline stage: the A tile (BM x 64 bf16, swizzled),
+  // then per wave and column fragment the lanes' 16 weight bytes (64 x 16 B)
+  // and per wave the scale and zero words of its 64 columns (2 x 64 x 4 B).
+  // The weights pass through LDS only so that their loads are waited for
+  // like the A tile's.
+  constexpr int QOFF = BM * 8;                    // in 16-byte units
+  constexpr int ZOFF = QOFF + 4 * NI * 64;
+  constexpr int SSZ = ZOFF + 4 * 32;
+  __shared__ u32x4 S0[SSZ], S1[SSZ], S2[SSZ], S3[SSZ];
+
+  // kernel arguments used below, read up front
+  const int M_max = g.M_max, N = g.N, K = g.K, nh = g.nh, a_nrows = g.a_nrows;
+  const int grp = g.group[0];            // equal for both descriptors here
+  int M = M_max;
+  if (g.M_dev) {
+    const int md = *g.M_dev;
+    M = md < 0 ? 0 : (md < M_max ? md : M_max);
+  }
+  const int tiles_m_act = (M + BM - 1) / BM;
+  const int total = tiles_n * tiles_m_act * batch;
+  // persistent tiles, contiguous per XCD (see gemm_nt_kernel)
+  const int xcd = blockIdx.x & 7, wg_in_xcd = blockIdx.x >> 3;
+  const int per_xcd = (gridDim.x + 7 - xcd) >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int t_end = (xcd + 1) * chunk < total ? (xcd + 1) * chunk : total;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int KT = K / 64;                 // a multiple of 4 on this path
+  const int slabs_per_group = grp >> 6;
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  auto stage = [&](auto st) -> u32x4* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return S0; else if constexpr (S == 1) return S1;
+    else if constexpr (S == 2) return S2; else return S3;
+  };
+
+  for (int tile = xcd * chunk + wg_in_xcd; tile < t_end; tile += per_xcd) {
+    const int nt = tile % tiles_n;
+    const int mt = (tile / tiles_n) % tiles_m_act;
+    const int z = tile / (tiles_n * tiles_m_act);
+    const int m0 = mt * BM, n0 = nt * BN;
+
+    // A: DMA block b = i * 4 + wave covers LDS chunks [64 b, 64 b + 64);
+    // lane l fills chunk p = 64 b + l = (row p / 8, physical chunk p % 8),
+    // which holds logical chunk (p % 8) ^ swz(row) of that row.
+    int a_src_row[AD];
+#pragma unroll
+    for (int i = 0; i < AD; ++i) {
+      const int t = m0 + (((i * 4 + wave) * 64 + lane) >> 3);
+      a_src_row[i] = g.a_rows ? g.a_rows[t < M ? t : M - 1] : t;
+    }
+    // Operands come in through buffer loads straight into LDS: a uniform
+    // resource (base and byte size of the buffer), a fixed 32-bit offset per
+    // lane and a uniform offset per slab, so no per-slab address arithmetic
+    // runs on the vector unit; a read past the stated size returns zeros.
+    // A: row src of this tile's layer, 16-byte chunk c of the slab.
+    const void* a_buf = g.A + (int64_t)z * g.a_bstride;
+    const int a_bytes = (int)(a_nrows * g.lda * 2);
+    uint32_t a_off[AD];
+#pragma unroll
+    for (int i = 0; i < AD; ++i) {
+      const int p = (i * 4 + wave) * 64 + lane;
+      const int r = p >> 3, c = (p & 7) ^ swz(r);
+      int src = a_src_row[i];
+      if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
+      a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
+    }
+    // B: this wave's 64 columns n0 + 64 wave .. + 63 lie wholly in the K or
+    // the V half (nh % 64 == 0): one resource per operand for the layer's
+    // half. Column fragment ni, lane (l % 32, h): weight bytes [16 h, 16 h +
+    // 16) of the 32-byte run of column 32 ni + l % 32 in each slab; scale and
+    // zero: lane l loads the word of column l.
+    const int wc0 = n0 + 64 * wave;                         // uniform
+    const int which = wc0 >= nh ? 1 : 0;
+    const int hc0 = wc0 - which * nh;                       // first column inside the half
+    const int64_t szs = which ? g.sz_bstride[1] : g.sz_bstride[0];
+    const int gpr = K / grp;                                // groups per row
+    const void* q_buf = (which ? g.q[1] : g.q[0]) + (int64_t)z * g.q_bstride;
+    const int q_bytes = nh * (K / 2);
+    const void* s_buf = (const char*)(which ? g.s[1] : g.s[0]) + z * szs * SZB;
+    const void* z_buf = (const char*)(which ? g.zp[1] : g.zp[0]) + z * szs * SZB;
+    const int sz_bytes = nh * gpr * SZB;
+    uint32_t q_off[NI];
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) q_off[ni] = (uint32_t)((hc0 + 32 * ni + (lane & 31)) * (K / 2) + h * 16);
+    const uint32_t sz_off = (uint32_t)((hc0 + lane) * gpr * SZB);
+
+    // every load of K-slab j into LDS stage ST
+    auto issue = [&](auto st, int j) {
+      u32x4* la = stage(st);
+#pragma unroll
+      for (int i = 0; i < AD; ++i) buf_lds<16>(a_buf, a_bytes, a_off[i], j * 128, la + (i * 4 + wave) * 64);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        buf_lds<16>(q_buf, q_bytes, q_off[ni], j * 32, la + QOFF + (wave * NI + ni) * 64);
+      const int gi = j / slabs_per_group;   // uniform
+      // bf16 scale / zero: the aligned word holding group gi (rows hold an
+      // even number of groups, so the word stays inside the row)
+      const int go = (SZ_BF16 ? (gi & ~1) : gi) * SZB;
+      uint32_t* lz = (uint32_t*)(la + ZOFF) + wave * 128;
+      buf_lds<4>(s_buf, sz_bytes, sz_off, go, lz);
+      buf_lds<4>(z_buf, sz_bytes, sz_off, go, lz + 64);
+    };
+    // this lane's weights of slab j (held in stage la) from LDS
+    struct BRegs { u32x4 q[NI]; uint32_t s[NI], zz[NI]; };
+    auto fetch = [&](const u32x4* la, int j, BRegs& b) {
+      const uint32_t* lz = (const uint32_t*)(la + ZOFF) + wave * 128;
+      const int sh = SZ_BF16 ? ((j / slabs_per_group) & 1) * 16 : 0;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        b.q[ni] = la[QOFF + (wave * NI + ni) * 64 + lane];
+        const uint32_t sw = lz[ni * 32 + (lane & 31)];
+        const uint32_t zw = lz[64 + ni * 32 + (lane & 31)];
+        b.s[ni] = SZ_BF16 ? (sw >> sh) & 0xFFFFu : sw;
+        b.zz[ni] = SZ_BF16 ? (zw >> sh) & 0xFFFFu : zw;
+      }
+    };
+    struct SC { float s[NI], c[NI]; };
+    auto scales = [&](const BRegs& b) {
+      SC r;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        r.s[ni] = SZ_BF16 ? __uint_as_float(b.s[ni] << 16) : __uint_as_float(b.s[ni]);
+        const float ze = SZ_BF16 ? __uint_as_float(b.zz[ni] << 16) : __uint_as_float(b.zz[ni]);
+        r.c[ni] = -ze * r.s[ni];
+      }
+      return r;
+    };
+    // the A fragments (from LDS) and dequantized B fragments of sub-step s
+    struct Frag { bf16x8 a[MI], b[NI]; };
+    auto frag = [&](const u32x4* la, const BRegs& b, const SC& sc, int s, Frag& f) {
+      const int ch = 4 * h + s;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int r = mi * 32 + (lane & 31);
+        f.a[mi] = __builtin_bit_cast(bf16x8, la[r * 8 + (ch ^ swz(r))]);
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        uint32_t o[4];
+        dequant8(b.q[ni][s], sc.s[ni], sc.c[ni], o);
+        u32x4 v;
+        v[0] = o[0]; v[1] = o[1]; v[2] = o[2]; v[3] = o[3];
+        f.b[ni] = __builtin_bit_cast(bf16x8, v);
+      }
+    };
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+    auto mfma = [&](const Frag& f) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+    };
+
+    // Pipeline. Slab kt lives in LDS stage kt % 4 and register set kt % 4.
+    // The barrier for slab kt + 1 sits before the last sub-step of slab kt,
+    // so the first fragments of slab kt + 1 are read and dequantized while
+    // the last MFMAs of slab kt run; after it, the stage of slab kt is free
+    // and slab kt + 4 is issued into it. The last four slabs issue nothing
+    // and wait for exactly what is still outstanding.
+    if (tile != xcd * chunk + wg_in_xcd) {
+      // every wave is done with the previous tile's stages
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    // cache slots of the tile's rows for the epilogue: lane l looks up rows
+    // m0 + 64 j + l. The e_rows loads go out before the first slab's (so the
+    // first wait covers them), the slot loads right after it.
+    constexpr int RJ = BM / 64;
+    [[maybe_unused]] int er[RJ], sl[RJ];
+    if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) {
+        const int row = m0 + 64 * j + lane;
+        const int rc = row < M ? row : M - 1;
+        er[j] = g.e_rows ? g.e_rows[rc] : rc;
+      }
+    }
+    issue(I0{}, 0);
+    issue(I1{}, 1);
+    issue(I2{}, 2);
+    wait_barrier<2 * PER_SLAB, true>();   // slab 0 landed
+    if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) {
+        const bool ok = m0 + 64 * j + lane < M && er[j] >= 0 && er[j] < g.e_nrows;
+        const int s_ = ok ? g.slot[er[j]] : -1;
+        sl[j] = s_ >= 0 && s_ < g.n_slots ? s_ : -1;
+      }
+    }
+    Frag f0, f1;
+    BRegs bA, bB;
+    fetch(S0, 0, bA);
+    SC sc = scales(bA);
+    frag(S0, bA, sc, 0, f0);
+
+    // Pipeline. Slab kt lives in LDS stage kt % 4. Iteration kt issues slab
+    // kt + 3 into the stage of slab kt - 1 (free since the previous barrier),
+    // spread between the MFMAs of sub-steps 0..2, so that no wave stalls on
+    // a burst of loads; the barrier for slab kt + 1 sits before the last
+    // sub-step, whose MFMAs then cover the fetch and dequantization of the
+    // first fragments of slab kt + 1. W = loads allowed outstanding at the
+    // barrier (those of the slabs after kt + 1); ISSUE = slab kt + 3 exists.
+    auto iter = [&](auto st, BRegs& cur, BRegs& nxt, int kt, auto w, auto issue_next) {
+      constexpr int ST = decltype(st)::value;
+      using NX = std::integral_constant<int, (ST + 1) & 3>;
+      using PV = std::integral_constant<int, (ST + 3) & 3>;
+      constexpr bool ISS = decltype(issue_next)::value;
+      if constexpr (ISS) issue(PV{}, kt + 3);
+      frag(stage(st), cur, sc, 1, f1);
+      mfma(f0);
+      frag(stage(st), cur, sc, 2, f0);
+      mfma(f1);
+      frag(stage(st), cur, sc, 3, f1);
+      mfma(f0);
+      interleave<3, MI * NI, MI, ISS ? PER_SLAB : 0>();
+      wait_barrier<decltype(w)::value, true>();   // slab kt + 1 landed
+      fetch(stage(NX{}), kt + 1, nxt);           // (spare reads after the last slab)
+      sc = scales(nxt);
+      frag(stage(NX{}), nxt, sc, 0, f0);
+      mfma(f1);
+      interleave<1, MI * NI, MI + 3 * NI, 0>();
+    };
+    using W2 = std::integral_constant<int, 2 * PER_SLAB>;
+    using W1 = std::integral_constant<int, PER_SLAB>;
+    using W0 = std::integral_constant<int, 0>;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    int kt = 0;
+    for (; kt + 4 < KT; kt += 4) {       // every slab here issues slab kt + 3
+      iter(I0{}, bA, bB, kt, W2{}, T_{});
+      iter(I1{}, bB, bA, kt + 1, W2{}, T_{});
+      iter(I2{}, bA, bB, kt + 2, W2{}, T_{});
+      iter(I3{}, bB, bA, kt + 3, W2{}, T_{});
+    }
+    // last four slabs: only the first still has a slab to issue
+    iter(I0{}, bA, bB, kt, W2{}, T_{});
+    iter(I1{}, bB, bA, kt + 1, W1{}, F_{});
+    iter(I2{}, bA, bB, kt + 2, W0{}, F_{});
+    iter(I3{}, bB, bA, kt + 3, W0{}, F_{});
+
+    // ---- epilogue. The transposed 32x32 accumulator gives lane l output
+    // row l % 32 of fragment mi and, for gq = 0..3, the four consecutive
+    // columns 8 gq + 4 (l / 32) + 0..3 of fragment ni. Each wave first writes
+    // its BM x 64 block as bf16 into LDS (its own stage array, free now: the
+    // other waves only make spare reads of stage 0 from here on, whose
+    // values are never used), then stores it row by row: 8 lanes x 16 bytes
+    // cover one row's 64 columns (one 128-byte line), 8 rows per store.
+    {
+      constexpr int EP = 72;                      // row pitch in bf16 (144 B)
+      uint16_t* ep = (uint16_t*)(wave == 0 ? S0 : wave == 1 ? S1 : wave == 2 ? S2 : S3);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int r = mi * 32 + (lane & 31), c = ni * 32 + 8 * gq + 4 * h;
+            *(uint2*)(ep + r * EP + c) = uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
+                                               pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
+          }
+      const int ch = lane & 7;
+      const int col = n0 + 64 * wave + 8 * ch;   // 8 columns, all in K or all in V
+      const bool col_ok = col < N;
+      const bool isv = col >= nh;
+#pragma unroll
+      for (int i = 0; i < BM / 8; ++i) {
+        const int r = i * 8 + (lane >> 3);
+        const u32x4 v = *(const u32x4*)(ep + r * EP + 8 * ch);
+        if constexpr (EPI == EPI_CACHE) {
+          // slot of row r: looked up by lane r % 64 in its register r / 64
+          const int sr = __shfl(sl[(i * 8) / 64], (i * 8) % 64 + (lane >> 3), 64);
+          if (sr < 0 || !col_ok) continue;
+          uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc);
+          *(u32x4*)(dst + (int64_t)z * g.cache_bstride + (int64_t)sr * nh + (isv ? col - nh : col)) = v;
+        } else {
+          const int row = m0 + r;
+          if (row >= M || !col_ok) continue;
+          *(u32x4*)((uint16_t*)g.C + (int64_t)z * g.c_bstride + (int64_t)row * g.ldc + col) = v;
+        }
+      }
+    }
+  }  // tiles
+}
+
+// Launch over a batch of `batch` layers: one workgroup per CU (64 KB of
+// LDS for BM = 128), capped by the tile count and rounded to whole XCDs.
+template <int BM, int EPI>
+inline void w4_gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
+  const int tn = (g.N + 255) / 256;
+  const int tm = (g.M_max + BM - 1) / BM;
+  const int64_t tiles = (int64_t)tn * tm * batch;
+  int grid = (int)(tiles < N_CU ? tiles : N_CU);
+  grid = (grid + 7) / 8 * 8;
+  if (g.sz_bf16[0]) w4_gemm_kernel<BM, EPI, true><<<grid, 256, 0, s>>>(g, tn, batch);
+  else w4_gemm_kernel<BM, EPI, false><<<grid, 256, 0, s>>>(g, tn, batch);
+}
+
+template <int EPI>
+inline void w4_gemm_auto(const GemmArgs& g, int batch, hipStream_t s) {
+  if (g.M_max <= 64) w4_gemm_launch<64, EPI>(g, batch, s);
+  else w4_gemm_launch<128, EPI>(g, batch, s);
+}
+
+}  // namespace river
