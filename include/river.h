@@ -249,9 +249,11 @@ const char* river_last_error(void);
 /* Library version string. */
 const char* river_version(void);
 
-/* Test hook: force the compaction index path (0 = automatic, 1 = single
- * wave ballot, n <= 64; 2 = one workgroup scan; 3 = multi-workgroup scan).
- * Process-wide; the paths give bitwise-identical results. */
+/* Test hook: force the compaction path (0 = automatic; 1 = single wave
+ * ballot, n <= 64; 2 = one workgroup scan; 3 = multi-workgroup scan; 1-3
+ * then copy rows in a second launch; 4 = one fused launch, each workgroup
+ * counting the exits before its 64 tokens itself, the automatic choice for
+ * n <= 65536). Process-wide; the paths give bitwise-identical results. */
 river_status river_debug_set_compact_path(int path);
 
 #ifdef __cplusplus

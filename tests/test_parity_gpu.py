@@ -166,7 +166,7 @@ def compact_gpu(mask, h, row_ids=None, out=None):
     return cont, ext, counts, hc, ridc
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("n", [0, 1, 33, 63, 64, 65, 1023, 1024, 1025, 5000, 8192, 20000])
 def test_compact_all_paths(path, n):
     if path == 1 and n > 64:

@@ -54,7 +54,7 @@ const char* river_last_error(void) { return g_err; }
 const char* river_version(void) { return "river 0.1.0 (gfx950)"; }
 
 river_status river_debug_set_compact_path(int path) {
-  if (path < 0 || path > 3) return fail(RIVER_ERR_ARG, "compact path must be 0..3, got %d", path);
+  if (path < 0 || path > 4) return fail(RIVER_ERR_ARG, "compact path must be 0..4, got %d", path);
   g_compact_path = path;
   return RIVER_OK;
 }
@@ -117,6 +117,7 @@ river_status river_compact(int n, int d, river_dtype dt, const uint8_t* mask, co
   if (n < 0) return fail(RIVER_ERR_ARG, "compact: n = %d < 0", n);
   if (!counts) return fail(RIVER_ERR_ARG, "compact: counts is required");
   if (n > 0 && (!mask || !cont_idx || !exit_idx)) return fail(RIVER_ERR_ARG, "compact: mask, cont_idx and exit_idx are required");
+  if (n > 0 && !aligned16(mask)) return fail(RIVER_ERR_ALIGN, "compact: mask must be 16-byte aligned");
   bool rows = (h_cont || out);
   if (rows) {
     if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "compact: d = %d must be a positive multiple of 8", d);

@@ -6,7 +6,9 @@
 // for large ones; "Exit Scatter" copies exited hidden states back to their
 // original rows of an output buffer.
 //
-// Index kernels (one launch, or two for very large batches):
+// Default for n <= 65536: one fused launch (indices and rows, see below).
+// Otherwise, or when forced for testing, index kernels (one launch, or two
+// for very large batches) then a row kernel:
 //   n <= 64      one wave: ballot + lane-rank (mbcnt)
 //   n <= 16384   one workgroup of 1024 threads: per-thread counts, wave
 //                prefix scans, scan of the 16 wave totals in LDS
@@ -146,6 +148,80 @@ __global__ __launch_bounds__(256) void compact_grid_write_kernel(CompactIdx a, c
   }
 }
 
+// nonzero bytes of a dword (the high bit of each byte of the result is set
+// iff that byte is nonzero)
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+  return __popc((((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u);
+}
+
+// ---------------------------------------------------------- fused path
+// One launch for indices and rows, n <= FUSED_MAX: workgroup c owns tokens
+// [64 c, 64 c + 64). It counts the exits before its chunk itself (16-byte
+// reads of the mask prefix, at most n bytes, L2-resident), ranks its own
+// 64 tokens with a ballot, writes both index lists and then copies its own
+// rows (exited rows to out[row_ids[i]], continuing rows to h_cont).
+constexpr int FCH = 64;
+constexpr int FUSED_MAX = 65536;
+
+__global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const char* h, int64_t ld_h,
+                                                            int row_bytes, char* h_cont, int64_t ld_cont,
+                                                            char* out, int64_t ld_out, int64_t n_out_rows) {
+  __shared__ int s_part[4];
+  __shared__ int64_t s_dst[FCH];   // byte offset of each token's destination row, or -1
+  __shared__ int s_to_out[FCH];    // 1: destination in out, 0: in h_cont
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * FCH;
+  const int n = a.n;
+  // exits in [0, c0)
+  int cnt = 0;
+  const u32x4* m16 = (const u32x4*)a.mask;
+  for (int v = tid; v < (c0 >> 4); v += 256) {
+    const u32x4 w = m16[v];
+    cnt += nonzero_bytes(w[0]) + nonzero_bytes(w[1]) + nonzero_bytes(w[2]) + nonzero_bytes(w[3]);
+  }
+  cnt = (int)row_sum<16>((float)cnt);       // exact: counts stay far below 2^24
+  cnt += __shfl_xor(cnt, 16, WAVE);
+  cnt += __shfl_xor(cnt, 32, WAVE);
+  if (lane == 0) s_part[wave] = cnt;
+  __syncthreads();
+  const int base = s_part[0] + s_part[1] + s_part[2] + s_part[3];
+  if (wave == 0) {
+    const int i = c0 + lane;
+    const bool ex = i < n && a.mask[i] != 0;
+    const uint64_t bits = __ballot(ex);
+    const int rank = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
+    int64_t dst = -1;
+    int to_out = 0;
+    if (i < n) {
+      emit(a, i, ex, rank);
+      if (ex) {
+        const int64_t rid = a.row_ids ? a.row_ids[i] : i;
+        if (out && rid >= 0 && rid < n_out_rows) { dst = rid * ld_out; to_out = 1; }
+      } else if (h_cont) {
+        dst = (int64_t)(i - rank) * ld_cont;
+      }
+    }
+    s_dst[lane] = dst;
+    s_to_out[lane] = to_out;
+    if (c0 + FCH >= n && lane == 0) {          // the last chunk knows the total
+      const int ne = base + __popcll(bits);
+      a.counts[0] = n - ne;
+      a.counts[1] = ne;
+    }
+  }
+  if (!h) return;
+  __syncthreads();
+  const int chunks = row_bytes >> 4;
+  for (int t = wave; t < FCH; t += 4) {        // one row per wave at a time
+    const int64_t dst = s_dst[t];
+    if (dst < 0) continue;
+    const u32x4* src = (const u32x4*)(h + (int64_t)(c0 + t) * ld_h);
+    u32x4* d = (u32x4*)((s_to_out[t] ? out : h_cont) + dst);
+    for (int c = lane; c < chunks; c += 64) d[c] = src[c];
+  }
+}
+
 __global__ void compact_zero_counts_kernel(int32_t* counts) {
   if (threadIdx.x == 0) { counts[0] = 0; counts[1] = 0; }
 }
@@ -212,7 +288,14 @@ river_status launch_compact(int n, int d, river_dtype dt, const uint8_t* mask, c
   }
   CompactIdx a{n, mask, row_ids, cont_idx, exit_idx, counts, row_ids_cont};
   int path = compact_path_override();
-  if (path == 0) path = n <= 64 ? 1 : (n <= CB_THREADS * 16 ? 2 : 3);
+  if (path == 0) path = n <= FUSED_MAX ? 4 : 3;
+  const int64_t es = (int64_t)esize(dt);
+  if (path == 4) {
+    compact_fused_kernel<<<(n + FCH - 1) / FCH, 256, 0, s>>>(
+        a, (h_cont || out) ? (const char*)h : nullptr, ld_h * es, (int)(d * es), (char*)h_cont,
+        ld_cont * es, (char*)out, ld_out * es, n_out_rows);
+    return check_launch("compact fused");
+  }
   if (path == 1) {
     compact_wave_kernel<<<1, 64, 0, s>>>(a);
   } else if (path == 2) {
@@ -228,7 +311,6 @@ river_status launch_compact(int n, int d, river_dtype dt, const uint8_t* mask, c
   }
   river_status st = check_launch("compact index");
   if (st != RIVER_OK || (!h_cont && !out)) return st;
-  const int64_t es = (int64_t)esize(dt);
   CompactRows r{n, (int)(d * es), (const char*)h, ld_h * es, row_ids, cont_idx, exit_idx, counts,
                 (char*)h_cont, ld_cont * es, (char*)out, ld_out * es, n_out_rows};
   compact_rows_kernel<<<(n + ROWS_PER_WG - 1) / ROWS_PER_WG, 256, 0, s>>>(r);

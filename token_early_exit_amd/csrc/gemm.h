@@ -71,27 +71,6 @@ __device__ __forceinline__ void dequant8(uint32_t w, float s, float c, uint32_t*
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS swizzle of 16-byte chunk c of tile row r (8 chunks per row): stored at
-// r * 8 + (c ^ swz(r)). With 64 lanes reading one chunk of 32 consecutive
-// rows, each 16-lane group touches 16 distinct bank groups (measured on
-// gfx950: no bank-conflict cycles, where c ^ (r & 7) costs 4 per read).
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-// s_waitcnt until at most N vector-memory operations of this wave are
-// outstanding (and, with LGKM0, all LDS writes are done), then a
-// workgroup barrier. The empty asm statements keep the compiler from
-// moving memory operations across; unlike __syncthreads() there is no
-// release fence, which would force vmcnt(0) and drain the load pipeline.
-template <int N, bool LGKM0>
-__device__ __forceinline__ void wait_barrier() {
-  constexpr int vm = N > 63 ? 63 : N;
-  constexpr int imm = (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(imm);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // 16 bytes per lane from global memory straight into LDS: lane l of the
 // wave writes lds_base + 16 * l (lds_base is wave-uniform).
 __device__ __forceinline__ void dma16(const void* gptr, void* lds_base) {
@@ -101,17 +80,6 @@ __device__ __forceinline__ void dma16(const void* gptr, void* lds_base) {
 // 4 bytes per lane from global memory into LDS (lane l writes lds_base + 4 l)
 __device__ __forceinline__ void dma4(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 4, 0, 0);
-}
-
-// s_waitcnt until at most N vector-memory operations of this wave are
-// outstanding, no barrier (for data this wave loaded itself).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  constexpr int vm = N > 63 ? 63 : N;
-  constexpr int imm = (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (15 << 8);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(imm);
-  asm volatile("" ::: "memory");
 }
 
 // Four-stage pipeline. Everything a K-slab needs goes to LDS stage

@@ -50,6 +50,12 @@ __device__ __forceinline__ void write_decision(const RouteArgs& a, int i, float 
   a.mask_out[i] = e ? 1 : 0;
 }
 
+// x * sigmoid(x) through the hardware base-2 exponential and reciprocal
+// (about one ulp each; e^-x = 2^(-x log2 e))
+__device__ __forceinline__ float silu_hw(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.44269504088896341f));
+}
+
 // --------------------------------------------------------- generic path
 // One wave per token row. Used for fp32 and for shapes the MFMA path does
 // not take. Dynamic LDS holds the normalised row (d floats) when the
@@ -291,6 +297,224 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
   if (part == 0 && gi < n) write_decision(a, gi, cosine_from(sd, sa, sb), sigmoidf_(z), true);
 }
 
+// ------------------------------------------------------ streaming path
+// d % 256 == 0, bf16, b <= 128: one workgroup = 4 waves = T = 16 RT tokens.
+// The feature dimension is walked in 64-wide slabs. Each slab of W_down
+// (128 units x 64, 16 KB) and of the T rows of h_prev and h_cur goes through
+// LDS by buffer loads (full 128-byte lines, three slabs ahead, rows past n
+// and units past b read as zeros). Wave w owns units [32 w, 32 w + 32) and
+// runs u = W_down . (gamma * h_cur) on 16x16x32 bf16 MFMA over all slabs, so
+// the pre-activations need no cross-wave sum; meanwhile 8 threads per token
+// accumulate, in fp32, the three dot products over 8 features of each slab.
+template <int RT, bool HAS_GAMMA>
+__global__ __launch_bounds__(256) void route_stream_kernel(RouteArgs a) {
+  constexpr int T = 16 * RT;
+  constexpr int WB = 128 * 8;            // W slab: 128 units x 8 chunks of 16 bytes
+  constexpr int HB = T * 8;              // one state slab: T rows x 8 chunks
+  constexpr int SSZ = WB + 2 * HB;       // W, then h_cur, then h_prev
+  constexpr int HD = 2 * HB / 256;       // state DMAs per thread per slab (RT)
+  constexpr int PER_SLAB = 4 + HD;       // buffer loads per thread per slab
+  constexpr int DT = 8 * T;              // threads on the dot products: 8 per token,
+                                         // one 16-byte chunk (8 features) each per slab
+  __shared__ u32x4 S0[SSZ], S1[SSZ], S2[SSZ], S3[SSZ];
+  __shared__ float red[4][T];            // per-wave partial router logits
+  __shared__ float nrm[T][3];            // dot, |h_prev|^2, |h_cur|^2
+  __shared__ uint32_t gam[HAS_GAMMA ? 4096 : 1];   // gamma as bf16 pairs (d <= 8192)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row0 = blockIdx.x * T;
+  const int d = a.d, b = a.b, n = a.n;
+  const int KT = d / 64;
+
+  // w_up of this lane's two units, fetched now for the epilogue (the first
+  // slab wait covers these older loads)
+  float wup[2];
+#pragma unroll
+  for (int uf = 0; uf < 2; ++uf) {
+    const int u = wave * 32 + uf * 16 + (lane & 15);
+    wup[uf] = u < b ? load_elem<true>(a.wu, u) : 0.f;
+  }
+  if constexpr (HAS_GAMMA) {
+    for (int i = tid; i < d / 2; i += 256) gam[i] = ((const uint32_t*)a.gamma)[i];
+    __syncthreads();
+  }
+
+  // buffer offsets: chunk p of a slab holds logical 16-byte chunk
+  // (p % 8) ^ swz(p / 8) of row p / 8 (unit or token)
+  const int w_bytes = b * d * 2;
+  uint32_t w_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = (i * 4 + wave) * 64 + lane;
+    const int u = p >> 3, c = (p & 7) ^ swz(u);
+    w_off[i] = (uint32_t)(u * d * 2 + c * 16);
+  }
+  // state DMA i of this thread: block (i * 4 + wave) of the 2 HB chunks
+  // (h_cur first, then h_prev)
+  uint32_t h_off[HD];
+  bool h_prev[HD];
+#pragma unroll
+  for (int i = 0; i < HD; ++i) {
+    const int p = (i * 4 + wave) * 64 + lane;      // 0 .. 2 HB - 1
+    const bool pv = (i * 4 + wave) * 64 >= HB;       // whole block: uniform
+    const int q = pv ? p - HB : p;
+    const int t = q >> 3, c = (q & 7) ^ swz(t);
+    h_prev[i] = pv;
+    h_off[i] = (uint32_t)((int64_t)(row0 + t) * (pv ? a.ldp : a.ldc) * 2 + c * 16);
+  }
+  const int hc_bytes = (int)((int64_t)n * a.ldc * 2), hp_bytes = (int)((int64_t)n * a.ldp * 2);
+  auto stage = [&](auto st) -> u32x4* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return S0; else if constexpr (S == 1) return S1;
+    else if constexpr (S == 2) return S2; else return S3;
+  };
+  auto issue = [&](auto st, int j) {
+    u32x4* l = stage(st);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) buf_lds<16>(a.wd, w_bytes, w_off[i], j * 128, l + (i * 4 + wave) * 64);
+#pragma unroll
+    for (int i = 0; i < HD; ++i)   // one load per block; the source choice is uniform
+      buf_lds<16>(h_prev[i] ? a.hp : a.hc, h_prev[i] ? hp_bytes : hc_bytes, h_off[i], j * 128,
+                  l + WB + (i * 4 + wave) * 64);
+  };
+
+  f32x4 acc[RT][2];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int uf = 0; uf < 2; ++uf) acc[rt][uf] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dot = 0.f, na = 0.f, nb = 0.f;
+  const int my_t = tid >> 3, my_q = tid & 7;      // dot-product share: token, chunk
+
+  auto compute = [&](const u32x4* l, int j) {
+    const u32x4* lw = l;
+    const u32x4* lc = l + WB;
+    const u32x4* lp = l + WB + HB;
+    // dot products: chunk my_q (features 8 my_q .. 8 my_q + 7) of token my_t
+    // (16-byte reads, which the compiler does not pair into a read2)
+    if (DT == 256 || tid < DT) {
+      const int sw = my_q ^ swz(my_t);
+      const u32x4 x = lp[my_t * 8 + sw], y = lc[my_t * 8 + sw];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = bf16_lo(x[e]), p1 = bf16_hi(x[e]), c0 = bf16_lo(y[e]), c1 = bf16_hi(y[e]);
+        dot = fmaf(p0, c0, dot); dot = fmaf(p1, c1, dot);
+        na = fmaf(p0, p0, na);   na = fmaf(p1, p1, na);
+        nb = fmaf(c0, c0, nb);   nb = fmaf(c1, c1, nb);
+      }
+    }
+    // router: two 32-wide k-steps; A = tokens (lane: row l % 16, chunk
+    // 4 ks + l / 16), B = this wave's units
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = ks * 4 + (lane >> 4);
+      bf16x8 bw[2];
+#pragma unroll
+      for (int uf = 0; uf < 2; ++uf) {
+        const int u = wave * 32 + uf * 16 + (lane & 15);
+        bw[uf] = __builtin_bit_cast(bf16x8, lw[u * 8 + (c ^ swz(u))]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int t = rt * 16 + (lane & 15);
+        const u32x4 hx = lc[t * 8 + (c ^ swz(t))];
+        if constexpr (HAS_GAMMA) {
+          // gamma * h exactly in fp32, fed as hi + lo bf16 terms
+          const int k0 = j * 64 + c * 8;
+          u32x4 hi4, lo4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t gw = gam[(k0 >> 1) + e];
+            const float x0 = bf16_lo(hx[e]) * bf16_lo(gw), x1 = bf16_hi(hx[e]) * bf16_hi(gw);
+            const uint32_t hh = pack_bf16x2(x0, x1);
+            hi4[e] = hh;
+            lo4[e] = pack_bf16x2(x0 - bf16_lo(hh), x1 - bf16_hi(hh));
+          }
+#pragma unroll
+          for (int uf = 0; uf < 2; ++uf) {
+            acc[rt][uf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi4), bw[uf], acc[rt][uf], 0, 0, 0);
+            acc[rt][uf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo4), bw[uf], acc[rt][uf], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int uf = 0; uf < 2; ++uf)
+            acc[rt][uf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hx), bw[uf], acc[rt][uf], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // slab j in stage j % 4; slab j + 3 is issued after the barrier of slab
+  // j (its stage held slab j - 1, which every wave has finished with). KT is
+  // a multiple of 4: the loop body has static stages and no branches, and
+  // the last four slabs wait for exactly what is still in flight.
+  issue(I0{}, 0);
+  issue(I1{}, 1);
+  issue(I2{}, 2);
+  auto iter = [&](auto st, int j, auto w, auto iss) {
+    using NX = std::integral_constant<int, (decltype(st)::value + 3) & 3>;
+    wait_barrier<decltype(w)::value, true>();   // slab j landed; its loads and older ones done
+    if constexpr (decltype(iss)::value) issue(NX{}, j + 3);
+    compute(stage(st), j);
+  };
+  using W2 = std::integral_constant<int, 2 * PER_SLAB>;
+  using W1 = std::integral_constant<int, PER_SLAB>;
+  using W0 = std::integral_constant<int, 0>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int j = 0;
+  for (; j + 4 < KT; j += 4) {
+    iter(I0{}, j, W2{}, T_{});
+    iter(I1{}, j + 1, W2{}, T_{});
+    iter(I2{}, j + 2, W2{}, T_{});
+    iter(I3{}, j + 3, W2{}, T_{});
+  }
+  iter(I0{}, j, W2{}, T_{});
+  iter(I1{}, j + 1, W1{}, F_{});
+  iter(I2{}, j + 2, W0{}, F_{});
+  iter(I3{}, j + 3, W0{}, F_{});
+
+  // dot products: sum over the 8 threads of each token (fixed order)
+  dot = row_sum<8>(dot);
+  na = row_sum<8>(na);
+  nb = row_sum<8>(nb);
+  if (my_q == 0 && tid < DT) { nrm[my_t][0] = dot; nrm[my_t][1] = na; nrm[my_t][2] = nb; }
+  __syncthreads();
+  // router epilogue of this wave's units: 16x16 accumulator layout, lane l
+  // holds unit 16 uf + l % 16 of rows (tokens) 4 (l / 16) + i
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float zp[4] = {0.f, 0.f, 0.f, 0.f}, r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = 1.0f / sqrtf(nrm[rt * 16 + 4 * (lane >> 4) + i][2] / (float)d + a.eps);
+#pragma unroll
+    for (int uf = 0; uf < 2; ++uf) {
+      const bool uok = wave * 32 + uf * 16 + (lane & 15) < b;   // units past b do not exist
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = silu_hw(acc[rt][uf][i] * r[i]) * wup[uf];
+        zp[i] += uok ? c : 0.f;   // a select: a missing unit adds nothing, whatever c is
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = row_sum<16>(zp[i]);
+      if ((lane & 15) == 0) red[wave][rt * 16 + 4 * (lane >> 4) + i] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    const int gi = row0 + tid;
+    const float z = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];   // fixed order
+    if (gi < n) write_decision(a, gi, cosine_from(nrm[tid][0], nrm[tid][1], nrm[tid][2]), sigmoidf_(z), true);
+  }
+}
+
 // ------------------------------------------------------------ batch rule
 // AND of the per-token decisions; for the batch-min rule the AND is then
 // broadcast to every token's mask (River-LLM 方法步骤详情 step 3, TIDE
@@ -320,7 +544,23 @@ river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int6
               cos_out, prob_out, mask_out};
   if (n > 0) {
     const bool mfma = dt == RIVER_BF16 && w_down && d % 32 == 0 && b % 16 == 0 && b <= 128;
-    if (mfma) {
+    // streaming path: groups of four 64-wide slabs, byte offsets of both state arrays and
+    // W_down within 31 bits, gamma (if any) within its LDS copy
+    const bool stream = dt == RIVER_BF16 && w_down && d % 256 == 0 && b <= 128 &&
+                        (int64_t)n * ld_cur * 2 < ((int64_t)1 << 31) &&
+                        (int64_t)n * ld_prev * 2 < ((int64_t)1 << 31) && d <= 8192;
+    if (stream) {
+      const bool two = n >= 8192;
+      const int T = two ? 32 : 16;
+      const dim3 grid((n + T - 1) / T);
+      if (gamma) {
+        if (two) route_stream_kernel<2, true><<<grid, 256, 0, s>>>(a);
+        else route_stream_kernel<1, true><<<grid, 256, 0, s>>>(a);
+      } else {
+        if (two) route_stream_kernel<2, false><<<grid, 256, 0, s>>>(a);
+        else route_stream_kernel<1, false><<<grid, 256, 0, s>>>(a);
+      }
+    } else if (mfma) {
       const bool two = n >= 8192;   // 32 tokens per workgroup once the grid is large
       const bool g = gamma != nullptr;
       const bool full = b == 128;

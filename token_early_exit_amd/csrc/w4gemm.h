@@ -33,21 +33,6 @@
 
 namespace river {
 
-// dword 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit
-// data format, no swizzle, no index stride
-constexpr int RSRC_WORD3 = 0x00020000;
-
-// SIZE bytes per lane from the buffer [base, base + bytes) at byte offset
-// voff + soff straight into LDS (lane l writes lds + SIZE * l); a lane whose
-// bytes lie past the end reads zeros. base, bytes and soff are uniform, so
-// the resource sits in scalar registers and is built once per loop.
-template <int SIZE>   // 16 or 4
-__device__ __forceinline__ void buf_lds(const void* base, int bytes, uint32_t voff, int soff, void* lds) {
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, RSRC_WORD3);
-  if constexpr (SIZE == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, (int)voff, soff, 0, 0);
-  else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, (int)voff, soff, 0, 0);
-}
-
 // Scheduling hint for the preceding code of a basic block, per sub-step:
 // the LDS reads of the next fragments first (so their latency is covered),
 // then one MFMA at a time with a few VALU instructions (the dequantization
