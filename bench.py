@@ -205,8 +205,8 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-KERNEL_SOURCES = ["token_early_exit_amd/csrc/gemm.h", "token_early_exit_amd/csrc/kv_fill.hip",
-                  "token_early_exit_amd/csrc/common.h"]
+KERNEL_SOURCES = ["token_early_exit_amd/csrc/w4gemm.h", "token_early_exit_amd/csrc/gemm.h",
+                  "token_early_exit_amd/csrc/kv_fill.hip", "token_early_exit_amd/csrc/common.h"]
 
 
 def measured_traffic():
@@ -303,12 +303,12 @@ def main():
     route_b, compact_b, fill_f, fill_b = wl.work(n_exit)
     value = n_exit / (ms_step * 1e-3)
     # dominant kernel: the W4A16 K/V projection GEMM with the cache write
-    # (gemm_nt_kernel<128, int4, cache>); algorithmic flops per launch =
+    # (w4_gemm_kernel<128, cache>); algorithmic flops per launch =
     # exited rows x layers x 2 x d x (2 n_kv_heads head_dim)
     cfg = wl.cfg
     proj_flops = n_exit * wl.nl * 2 * cfg.d * 2 * cfg.hd
     ach = proj_flops / (kern["projection"] * 1e-3) / 1e12
-    roof = {"kernel": "gemm_nt_kernel<128,int4,cache> (kv_fill K/V projection)", "bound": "mfma",
+    roof = {"kernel": "w4_gemm_kernel<128,cache> (kv_fill K/V projection)", "bound": "mfma",
             "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(),
             "flops_per_launch": proj_flops, "avg_launch_us": kern["projection"] * 1e3}

@@ -90,12 +90,18 @@ __global__ __launch_bounds__(256) void kv_fill_generic_kernel(FillGeneric a) {
 namespace river_host {
 using namespace river;
 
-static bool fill_mfma_ok(int d, river_dtype dt, int nh, const river_w4* wk, const river_w4* wv) {
-  // group multiple of 64 (one group per K-slab); an even number of groups
-  // per row for bf16 scale/zero (read as aligned 4-byte words)
+// The MFMA path: K-slabs in groups of four (d % 256), 64-column blocks inside
+// the K or the V half (nh % 64), one quantization group per slab or more
+// (group % 64, the same for K and V), an even number of groups per row for
+// bf16 scale/zero (read as aligned 4-byte words), and every operand's byte
+// span addressable with 31-bit offsets.
+static bool fill_mfma_ok(int d, river_dtype dt, int nh, const river_w4* wk, const river_w4* wv,
+                         int64_t a_span, int64_t ws_span) {
   const bool even = wk->sz_dtype == RIVER_F32 || (d / wk->group) % 2 == 0;
-  return dt == RIVER_BF16 && d % 64 == 0 && nh % 32 == 0 && wk->group % 64 == 0 &&
-         wk->group == wv->group && wk->sz_dtype == wv->sz_dtype && even;
+  const int64_t lim = (int64_t)1 << 31;
+  return dt == RIVER_BF16 && d % 256 == 0 && nh % 64 == 0 && wk->group % 64 == 0 &&
+         wk->group == wv->group && wk->sz_dtype == wv->sz_dtype && even &&
+         a_span < lim && ws_span < lim && (int64_t)nh * d < lim && (int64_t)d * d * 2 < lim;
 }
 
 size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt) {
@@ -108,7 +114,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
                             int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
                             int64_t n_slots, void* workspace, size_t ws_bytes, hipStream_t s) {
   const int nh = n_kv_heads * head_dim;
-  if (!fill_mfma_ok(d, dt, nh, wk, wv)) {
+  if (!fill_mfma_ok(d, dt, nh, wk, wv, (int64_t)n_rows * ld_h * 2, (int64_t)m_max * d * 2)) {
     const size_t lds = 2 * (size_t)d * sizeof(float);
     if (lds > 65536) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: d = %d too large for the generic path", d);
     FillGeneric a{m_max, m_dev, d, h, ld_h, n_rows, row_idx, slot, maps,
@@ -155,12 +161,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.e_rows = row_idx;
     q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
-    // whole groups of four K-slabs, 64-column blocks inside one half, and
-    // every operand addressable with 32-bit offsets
-    const bool w4 = d % 256 == 0 && nh % 64 == 0 &&
-                    (int64_t)a_nrows * lda * 2 < ((int64_t)1 << 31) && (int64_t)nh * d < ((int64_t)1 << 31);
-    if (w4) w4_gemm_auto<EPI_CACHE>(q, nl, s);
-    else gemm_auto<true, EPI_CACHE>(q, nl, s);
+    w4_gemm_auto<EPI_CACHE>(q, nl, s);
     return check_launch("kv_fill projection");
   };
 
@@ -177,7 +178,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     p.A = (const uint16_t*)h; p.lda = ld_h; p.a_bstride = 0; p.a_rows = row_idx; p.a_nrows = n_rows;
     p.B = (const uint16_t*)maps + (int64_t)l0 * d * d; p.ldb = d; p.b_bstride = (int64_t)d * d;
     p.C = xh; p.ldc = d; p.c_bstride = (int64_t)m_max * d;
-    gemm_auto<false, EPI_BF16>(p, nl, s);
+    gemm_auto<EPI_BF16>(p, nl, s);
     river_status st = check_launch("kv_fill map");
     if (st != RIVER_OK) return st;
     st = stage2(l0, nl, xh, d, (int64_t)m_max * d, nullptr, m_max);

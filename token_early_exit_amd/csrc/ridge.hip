@@ -95,8 +95,10 @@ __global__ __launch_bounds__(256) void vgemm_kernel(VGemm g) {
 }
 
 // ------------------------------------------------------ elementwise
-__global__ void transpose_bf16_kernel(const uint16_t* in, int R, int C, int64_t ld_in, uint16_t* out,
-                                      int64_t ld_out) {
+// out[c][r] = in[r][c] for r < R; out[c][r] = 0 for R <= r < R_pad (the
+// padding that makes the GEMM's reduction length a multiple of 256)
+__global__ void transpose_bf16_kernel(const uint16_t* in, int R, int R_pad, int C, int64_t ld_in,
+                                      uint16_t* out, int64_t ld_out) {
   __shared__ uint16_t t[64][66];
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
@@ -106,7 +108,7 @@ __global__ void transpose_bf16_kernel(const uint16_t* in, int R, int C, int64_t 
   __syncthreads();
   for (int i = threadIdx.x; i < 64 * 64; i += blockDim.x) {
     const int c = i >> 6, r = i & 63;
-    if (c0 + c < C && r0 + r < R) out[(int64_t)(c0 + c) * ld_out + r0 + r] = t[r][c];
+    if (c0 + c < C && r0 + r < R_pad) out[(int64_t)(c0 + c) * ld_out + r0 + r] = t[r][c];
   }
 }
 
@@ -125,17 +127,21 @@ __global__ void zero_upper_kernel(float* G, int d) {
     if ((i % d) > (i / d)) G[i] = 0.f;
 }
 
-// split fp32 rows into bf16 hi/lo parts laid out as three K-blocks:
+// split fp32 rows into bf16 hi/lo parts laid out as three K-blocks, each
+// row padded with zeros to ld_out columns:
 // out[r][p*C + c] = part(p)(in[r][c]), part = hi when (pattern >> p) & 1 == 0
-__global__ void split3_kernel(const float* in, int R, int C, uint16_t* out, int pattern) {
-  const int64_t n = (int64_t)R * C;
+__global__ void split3_kernel(const float* in, int R, int C, uint16_t* out, int64_t ld_out, int pattern) {
+  const int64_t n = (int64_t)R * ld_out;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = i / C, c = i % C;
-    const float v = in[i];
-    const uint16_t hi = f32_to_bf16(v);
-    const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
-#pragma unroll
-    for (int p = 0; p < 3; ++p) out[r * 3 * C + p * C + c] = ((pattern >> p) & 1) ? lo : hi;
+    const int64_t r = i / ld_out, j = i % ld_out;
+    const int p = (int)(j / C);
+    uint16_t o = 0;
+    if (p < 3) {
+      const float v = in[r * C + j % C];
+      const uint16_t hi = f32_to_bf16(v);
+      o = ((pattern >> p) & 1) ? f32_to_bf16(v - bf16_to_f32(hi)) : hi;
+    }
+    out[i] = o;
   }
 }
 
@@ -258,6 +264,9 @@ struct RidgeWs {
   size_t total;
 };
 
+// reduction lengths of the MFMA GEMMs: multiples of 256 (zero padded)
+static int ridge_pad(int k) { return (k + 255) / 256 * 256; }
+
 static RidgeWs ridge_layout(int n, int d_in, int d_out, river_dtype dt, char* base) {
   RidgeWs w{};
   size_t off = 0;
@@ -270,10 +279,11 @@ static RidgeWs ridge_layout(int n, int d_in, int d_out, river_dtype dt, char* ba
   w.T = (float*)take((size_t)NB * di * 4);
   w.Ct = (float*)take(dd * di * 4);
   if (dt == RIVER_BF16) {
-    w.Xt = (uint16_t*)take(di * nn * 2);
-    w.Yt = (uint16_t*)take(dd * nn * 2);
-    w.Bcat = (uint16_t*)take(di * 3 * di * 2);
-    w.Acat = (uint16_t*)take(dd * 3 * di * 2);
+    const size_t np = ridge_pad(n), k3 = ridge_pad(3 * d_in);
+    w.Xt = (uint16_t*)take(di * np * 2);
+    w.Yt = (uint16_t*)take(dd * np * 2);
+    w.Bcat = (uint16_t*)take(di * k3 * 2);
+    w.Acat = (uint16_t*)take(dd * k3 * 2);
   } else {
     w.Wtmp = (float*)take(dd * di * 4);
   }
@@ -331,17 +341,18 @@ river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const v
   hipError_t he = hipMemsetAsync(w.flag, 0, sizeof(int), s);
   if (he != hipSuccess) return fail(RIVER_ERR_HIP, "ridge_fit: %s", hipGetErrorString(he));
   const int64_t wsz = (int64_t)d_out * d_in;
+  const int np = ridge_pad(n), k3 = ridge_pad(3 * d_in);
 
   if (xdt == RIVER_BF16) {
     const uint16_t* Xb = (const uint16_t*)X;
-    transpose_bf16_kernel<<<dim3((d_in + 63) / 64, (n + 63) / 64), 256, 0, s>>>(Xb, n, d_in, d_in, w.Xt, n);
+    transpose_bf16_kernel<<<dim3((d_in + 63) / 64, np / 64), 256, 0, s>>>(Xb, n, np, d_in, d_in, w.Xt, np);
     if ((st = check_launch("ridge transpose X")) != RIVER_OK) return st;
     GemmArgs g{};
-    g.M_max = d_in; g.N = d_in; g.K = n;
-    g.A = w.Xt; g.lda = n; g.a_nrows = d_in;
-    g.B = w.Xt; g.ldb = n;
+    g.M_max = d_in; g.N = d_in; g.K = np;
+    g.A = w.Xt; g.lda = np; g.a_nrows = d_in;
+    g.B = w.Xt; g.ldb = np;
     g.C = w.G; g.ldc = d_in; g.diag = lambda;
-    gemm_auto<false, EPI_F32>(g, 1, s);
+    gemm_auto<EPI_F32>(g, 1, s);
     if ((st = check_launch("ridge gram")) != RIVER_OK) return st;
   } else {
     const float* Xf = (const float*)X;
@@ -352,28 +363,28 @@ river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const v
   if ((st = factor_and_invert(d_in, w, s)) != RIVER_OK) return st;
 
   if (xdt == RIVER_BF16) {
-    split3_kernel<<<grid1d((int64_t)d_in * d_in), 256, 0, s>>>(w.Gi, d_in, d_in, w.Bcat, 0b010);
+    split3_kernel<<<grid1d((int64_t)d_in * k3), 256, 0, s>>>(w.Gi, d_in, d_in, w.Bcat, k3, 0b010);
     for (int t = 0; t < n_targets; ++t) {
       const uint16_t* Yb = (const uint16_t*)Y + (int64_t)t * n * d_out;
-      transpose_bf16_kernel<<<dim3((d_out + 63) / 64, (n + 63) / 64), 256, 0, s>>>(Yb, n, d_out, d_out, w.Yt, n);
+      transpose_bf16_kernel<<<dim3((d_out + 63) / 64, np / 64), 256, 0, s>>>(Yb, n, np, d_out, d_out, w.Yt, np);
       GemmArgs c{};
-      c.M_max = d_out; c.N = d_in; c.K = n;
-      c.A = w.Yt; c.lda = n; c.a_nrows = d_out;
-      c.B = w.Xt; c.ldb = n;
+      c.M_max = d_out; c.N = d_in; c.K = np;
+      c.A = w.Yt; c.lda = np; c.a_nrows = d_out;
+      c.B = w.Xt; c.ldb = np;
       c.C = w.Ct; c.ldc = d_in;
-      gemm_auto<false, EPI_F32>(c, 1, s);
-      split3_kernel<<<grid1d(wsz), 256, 0, s>>>(w.Ct, d_out, d_in, w.Acat, 0b100);
+      gemm_auto<EPI_F32>(c, 1, s);
+      split3_kernel<<<grid1d((int64_t)d_out * k3), 256, 0, s>>>(w.Ct, d_out, d_in, w.Acat, k3, 0b100);
       GemmArgs f{};
-      f.M_max = d_out; f.N = d_in; f.K = 3 * d_in;
-      f.A = w.Acat; f.lda = 3 * d_in; f.a_nrows = d_out;
-      f.B = w.Bcat; f.ldb = 3 * d_in;
+      f.M_max = d_out; f.N = d_in; f.K = k3;
+      f.A = w.Acat; f.lda = k3; f.a_nrows = d_out;
+      f.B = w.Bcat; f.ldb = k3;
       f.ldc = d_in;
       if (wdt == RIVER_BF16) {
         f.C = (uint16_t*)W + t * wsz;
-        gemm_auto<false, EPI_BF16>(f, 1, s);
+        gemm_auto<EPI_BF16>(f, 1, s);
       } else {
         f.C = (float*)W + t * wsz;
-        gemm_auto<false, EPI_F32>(f, 1, s);
+        gemm_auto<EPI_F32>(f, 1, s);
       }
       if ((st = check_launch("ridge target")) != RIVER_OK) return st;
     }

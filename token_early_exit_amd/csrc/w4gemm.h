@@ -33,27 +33,6 @@
 
 namespace river {
 
-// Scheduling hint for the preceding code of a basic block, per sub-step:
-// the LDS reads of the next fragments first (so their latency is covered),
-// then one MFMA at a time with a few VALU instructions (the dequantization
-// of the next fragments) and, every other MFMA, one of N_VMEM global loads,
-// so the matrix unit is fed while the vector unit dequantizes and no burst
-// of loads stalls the wave.
-template <int N_SUB, int MFMA_PER_SUB, int READS, int N_VMEM>
-__device__ __forceinline__ void interleave() {
-#pragma unroll
-  for (int sub = 0; sub < N_SUB; ++sub) {
-    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);                 // LDS reads first
-#pragma unroll
-    for (int i = 0; i < MFMA_PER_SUB; ++i) {
-      const int k = sub * MFMA_PER_SUB + i;
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);                  // VALU
-      if (k % 2 == 1 && k / 2 < N_VMEM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // load
-    }
-  }
-}
-
 template <int BM, int EPI, bool SZ_BF16>
 __global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, int batch) {
   constexpr int BN = 256;
