@@ -33,24 +33,26 @@
 
 namespace river {
 
-template <int BM, int EPI, bool SZ_BF16>
-__global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, int batch) {
+template <int BM, int EPI, bool SZ_BF16, int NW>
+__global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_n, int batch) {
   constexpr int BN = 256;
   constexpr int MI = BM / 32;            // 32-row fragments (all rows of the tile)
-  constexpr int NI = 2;                  // 32-column fragments per wave
-  constexpr int AD = BM * 8 / 256;       // A DMA instructions per thread per slab
+  constexpr int NI = 8 / NW;             // 32-column fragments per wave (NW = 4 or 8 waves)
+  constexpr int CW = 32 * NI;            // columns per wave
+  constexpr int AD = BM * 8 / (64 * NW); // A DMA instructions per thread per slab
   constexpr int SZB = SZ_BF16 ? 2 : 4;
-  // vector-memory instructions per thread per slab: A DMAs, 2 weight loads,
+  // vector-memory instructions per thread per slab: A DMAs, NI weight loads,
   // one scale and one zero load
   constexpr int PER_SLAB = AD + NI + 2;
   // one LDS array per pipeline stage: the A tile (BM x 64 bf16, swizzled),
   // then per wave and column fragment the lanes' 16 weight bytes (64 x 16 B)
-  // and per wave the scale and zero words of its 64 columns (2 x 64 x 4 B).
+  // and per wave the scale and zero words of 64 columns from its first one
+  // (2 x 64 x 4 B).
   // The weights pass through LDS only so that their loads are waited for
   // like the A tile's.
   constexpr int QOFF = BM * 8;                    // in 16-byte units
-  constexpr int ZOFF = QOFF + 4 * NI * 64;
-  constexpr int SSZ = ZOFF + 4 * 32;
+  constexpr int ZOFF = QOFF + NW * NI * 64;
+  constexpr int SSZ = ZOFF + NW * 32;
   __shared__ u32x4 S0[SSZ], S1[SSZ], S2[SSZ], S3[SSZ];
 
   // kernel arguments used below, read up front
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, i
     int a_src_row[AD];
 #pragma unroll
     for (int i = 0; i < AD; ++i) {
-      const int t = m0 + (((i * 4 + wave) * 64 + lane) >> 3);
+      const int t = m0 + (((i * NW + wave) * 64 + lane) >> 3);
       a_src_row[i] = g.a_rows ? g.a_rows[t < M ? t : M - 1] : t;
     }
     // Operands come in through buffer loads straight into LDS: a uniform
@@ -110,18 +112,18 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, i
     uint32_t a_off[AD];
 #pragma unroll
     for (int i = 0; i < AD; ++i) {
-      const int p = (i * 4 + wave) * 64 + lane;
+      const int p = (i * NW + wave) * 64 + lane;
       const int r = p >> 3, c = (p & 7) ^ swz(r);
       int src = a_src_row[i];
       if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
       a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
     }
-    // B: this wave's 64 columns n0 + 64 wave .. + 63 lie wholly in the K or
-    // the V half (nh % 64 == 0): one resource per operand for the layer's
+    // B: this wave's CW columns n0 + CW wave .. lie wholly in the K or the V
+    // half (nh % 64 == 0): one resource per operand for the layer's
     // half. Column fragment ni, lane (l % 32, h): weight bytes [16 h, 16 h +
     // 16) of the 32-byte run of column 32 ni + l % 32 in each slab; scale and
     // zero: lane l loads the word of column l.
-    const int wc0 = n0 + 64 * wave;                         // uniform
+    const int wc0 = n0 + CW * wave;                         // uniform
     const int which = wc0 >= nh ? 1 : 0;
     const int hc0 = wc0 - which * nh;                       // first column inside the half
     const int64_t szs = which ? g.sz_bstride[1] : g.sz_bstride[0];
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, i
     auto issue = [&](auto st, int j) {
       u32x4* la = stage(st);
 #pragma unroll
-      for (int i = 0; i < AD; ++i) buf_lds<16>(a_buf, a_bytes, a_off[i], j * 128, la + (i * 4 + wave) * 64);
+      for (int i = 0; i < AD; ++i) buf_lds<16>(a_buf, a_bytes, a_off[i], j * 128, la + (i * NW + wave) * 64);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         buf_lds<16>(q_buf, q_bytes, q_off[ni], j * 32, la + QOFF + (wave * NI + ni) * 64);
@@ -244,8 +246,7 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, i
 #pragma unroll
       for (int j = 0; j < RJ; ++j) {
         const bool ok = m0 + 64 * j + lane < M && er[j] >= 0 && er[j] < g.e_nrows;
-        const int s_ = ok ? g.slot[er[j]] : -1;
-        sl[j] = s_ >= 0 && s_ < g.n_slots ? s_ : -1;
+        sl[j] = ok ? g.slot[er[j]] : -1;          // range-checked where it is used
       }
     }
     Frag f0, f1;
@@ -302,13 +303,16 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, i
     // ---- epilogue. The transposed 32x32 accumulator gives lane l output
     // row l % 32 of fragment mi and, for gq = 0..3, the four consecutive
     // columns 8 gq + 4 (l / 32) + 0..3 of fragment ni. Each wave first writes
-    // its BM x 64 block as bf16 into LDS (its own stage array, free now: the
-    // other waves only make spare reads of stage 0 from here on, whose
-    // values are never used), then stores it row by row: 8 lanes x 16 bytes
-    // cover one row's 64 columns (one 128-byte line), 8 rows per store.
+    // its BM x CW block as bf16 into LDS (a region of stage wave / (NW / 4),
+    // free now: the other waves only make spare reads of stage 0 from here
+    // on, whose values are never used), then stores it row by row: LPR lanes
+    // x 16 bytes cover one row's CW columns, 64 / LPR rows per store.
     {
-      constexpr int EP = 72;                      // row pitch in bf16 (144 B)
-      uint16_t* ep = (uint16_t*)(wave == 0 ? S0 : wave == 1 ? S1 : wave == 2 ? S2 : S3);
+      constexpr int EP = CW + 8;                  // row pitch in bf16 (padded)
+      constexpr int LPR = CW / 8;                 // lanes per row
+      constexpr int RPI = 64 / LPR;               // rows per store instruction
+      const int sw = wave / (NW / 4), sub = wave % (NW / 4);
+      uint16_t* ep = (uint16_t*)(sw == 0 ? S0 : sw == 1 ? S1 : sw == 2 ? S2 : S3) + sub * BM * EP;
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -319,18 +323,18 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, i
             *(uint2*)(ep + r * EP + c) = uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
                                                pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
           }
-      const int ch = lane & 7;
-      const int col = n0 + 64 * wave + 8 * ch;   // 8 columns, all in K or all in V
+      const int ch = lane % LPR;
+      const int col = n0 + CW * wave + 8 * ch;   // 8 columns, all in K or all in V
       const bool col_ok = col < N;
       const bool isv = col >= nh;
 #pragma unroll
-      for (int i = 0; i < BM / 8; ++i) {
-        const int r = i * 8 + (lane >> 3);
+      for (int i = 0; i < BM / RPI; ++i) {
+        const int r = i * RPI + lane / LPR;
         const u32x4 v = *(const u32x4*)(ep + r * EP + 8 * ch);
         if constexpr (EPI == EPI_CACHE) {
           // slot of row r: looked up by lane r % 64 in its register r / 64
-          const int sr = __shfl(sl[(i * 8) / 64], (i * 8) % 64 + (lane >> 3), 64);
-          if (sr < 0 || !col_ok) continue;
+          const int sr = __shfl(sl[(i * RPI) / 64], (i * RPI) % 64 + lane / LPR, 64);
+          if (sr < 0 || sr >= g.n_slots || !col_ok) continue;
           uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc);
           *(u32x4*)(dst + (int64_t)z * g.cache_bstride + (int64_t)sr * nh + (isv ? col - nh : col)) = v;
         } else {
@@ -343,8 +347,11 @@ __global__ __launch_bounds__(256) void w4_gemm_kernel(GemmArgs g, int tiles_n, i
   }  // tiles
 }
 
-// Launch over a batch of `batch` layers: one workgroup per CU (64 KB of
+// Launch over a batch of `batch` layers: one workgroup per CU (112 KB of
 // LDS for BM = 128), capped by the tile count and rounded to whole XCDs.
+// W4_WAVES: 4 waves (64 columns each, one per SIMD) or 8 (32 columns each,
+// two per SIMD, which hide each other's latencies).
+constexpr int W4_WAVES = 8;
 template <int BM, int EPI>
 inline void w4_gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 255) / 256;
@@ -352,8 +359,8 @@ inline void w4_gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int64_t tiles = (int64_t)tn * tm * batch;
   int grid = (int)(tiles < N_CU ? tiles : N_CU);
   grid = (grid + 7) / 8 * 8;
-  if (g.sz_bf16[0]) w4_gemm_kernel<BM, EPI, true><<<grid, 256, 0, s>>>(g, tn, batch);
-  else w4_gemm_kernel<BM, EPI, false><<<grid, 256, 0, s>>>(g, tn, batch);
+  if (g.sz_bf16[0]) w4_gemm_kernel<BM, EPI, true, W4_WAVES><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
+  else w4_gemm_kernel<BM, EPI, false, W4_WAVES><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
 }
 
 template <int EPI>
