@@ -5,10 +5,11 @@
 //   deq(q) = (q - zero) * scale = fma(q, scale, -zero * scale)
 // per group of `group` input channels (a multiple of 64 here).
 //
-// Workgroup tile BM x 256, 4 waves. Wave w owns the 64 output columns
-// [64 w, 64 w + 64) for all BM rows: BM/32 x 2 accumulators of 32x32 fed by
-// v_mfma_f32_32x32x16_bf16. Only A goes through LDS (direct global->LDS
-// loads into a 4-stage ring, three K-slabs ahead); every wave reads the same
+// Workgroup tile BM x 256, NW waves (8 by default: two per SIMD, which hide
+// each other's latencies). Wave w owns the CW = 256 / NW output columns
+// [CW w, CW w + CW) for all BM rows: BM/32 x CW/32 accumulators of 32x32 fed
+// by v_mfma_f32_32x32x16_bf16. Only A goes through LDS (buffer loads straight
+// into LDS, a 4-stage ring, three K-slabs ahead); every wave reads the same
 // A fragments. Each lane fetches the 16 bytes of int4 weights it needs per
 // slab (staged through LDS with the A tile, three slabs ahead) and
 // dequantizes them in registers into the MFMA's B operand: no dequantized
@@ -21,9 +22,10 @@
 // lane's 16 weight bytes). The sum over the slab is the same sum.
 //
 // Per 64-slab and workgroup (BM = 128): 128 MFMAs of 32 cycles per SIMD
-// (1024 cycles), 64 KB of LDS fragment reads plus 16 KB of DMA writes
-// and 24 KB of weight staging (about 810 cycles at 128 B/clk), 28 KB from
-// L2, and 8 dequant8 per lane.
+// (1024 cycles), 16 dequant8 per SIMD (about 23 vector instructions each,
+// the binding cost: about 5 vector instructions hide behind one MFMA), 16 KB
+// of A and 12 KB of weight staging written to LDS and 8 x 16 KB of A
+// fragments read from it, 28 KB from L2.
 #pragma once
 
 #include <type_traits>
