@@ -156,10 +156,12 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
 
 // ---------------------------------------------------------- fused path
 // One launch for indices and rows, n <= FUSED_MAX: workgroup c owns tokens
-// [64 c, 64 c + 64). It counts the exits before its chunk itself (16-byte
-// reads of the mask prefix, at most n bytes, L2-resident), ranks its own
-// 64 tokens with a ballot, writes both index lists and then copies its own
-// rows (exited rows to out[row_ids[i]], continuing rows to h_cont).
+// [64 c, 64 c + 64). Every wave reads the chunk's 64 mask bytes and ballots
+// them, so each wave knows which of the chunk's rows exit. Exited rows go to
+// out[row_ids[i]], which does not depend on any rank, so they are copied
+// while the exits before the chunk are still being counted (16-byte reads
+// of the mask prefix, at most n bytes). With that count the workgroup writes
+// both index lists and copies its continuing rows to h_cont.
 constexpr int FCH = 64;
 constexpr int FUSED_MAX = 65536;
 
@@ -167,17 +169,32 @@ __global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const 
                                                             int row_bytes, char* h_cont, int64_t ld_cont,
                                                             char* out, int64_t ld_out, int64_t n_out_rows) {
   __shared__ int s_part[4];
-  __shared__ int64_t s_dst[FCH];   // byte offset of each token's destination row, or -1
-  __shared__ int s_to_out[FCH];    // 1: destination in out, 0: in h_cont
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = blockIdx.x * FCH;
   const int n = a.n;
-  // exits in [0, c0)
+  const int chunks = row_bytes >> 4;
+  // this chunk's tokens, in every wave
+  const int i_own = c0 + lane;
+  const bool ex_own = i_own < n && a.mask[i_own] != 0;
+  const int rid_own = (out && ex_own) ? (a.row_ids ? a.row_ids[i_own] : i_own) : -1;
+  // exits in [0, c0) (loads issued now, summed below)
   int cnt = 0;
   const u32x4* m16 = (const u32x4*)a.mask;
   for (int v = tid; v < (c0 >> 4); v += 256) {
     const u32x4 w = m16[v];
     cnt += nonzero_bytes(w[0]) + nonzero_bytes(w[1]) + nonzero_bytes(w[2]) + nonzero_bytes(w[3]);
+  }
+  const uint64_t bits = __ballot(ex_own);
+  // exit scatter: rows t = wave, wave + 4, ... of the chunk
+  if (h && out) {
+    for (int t = wave; t < FCH; t += 4) {
+      if (!((bits >> t) & 1)) continue;                     // uniform
+      const int rid = __builtin_amdgcn_readlane(rid_own, t);
+      if (rid < 0 || rid >= n_out_rows) continue;
+      const u32x4* src = (const u32x4*)(h + (int64_t)(c0 + t) * ld_h);
+      u32x4* d = (u32x4*)(out + (int64_t)rid * ld_out);
+      for (int c = lane; c < chunks; c += 64) d[c] = src[c];
+    }
   }
   cnt = (int)row_sum<16>((float)cnt);       // exact: counts stay far below 2^24
   cnt += __shfl_xor(cnt, 16, WAVE);
@@ -186,39 +203,24 @@ __global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const 
   __syncthreads();
   const int base = s_part[0] + s_part[1] + s_part[2] + s_part[3];
   if (wave == 0) {
-    const int i = c0 + lane;
-    const bool ex = i < n && a.mask[i] != 0;
-    const uint64_t bits = __ballot(ex);
     const int rank = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
-    int64_t dst = -1;
-    int to_out = 0;
-    if (i < n) {
-      emit(a, i, ex, rank);
-      if (ex) {
-        const int64_t rid = a.row_ids ? a.row_ids[i] : i;
-        if (out && rid >= 0 && rid < n_out_rows) { dst = rid * ld_out; to_out = 1; }
-      } else if (h_cont) {
-        dst = (int64_t)(i - rank) * ld_cont;
-      }
-    }
-    s_dst[lane] = dst;
-    s_to_out[lane] = to_out;
+    if (i_own < n) emit(a, i_own, ex_own, rank);
     if (c0 + FCH >= n && lane == 0) {          // the last chunk knows the total
       const int ne = base + __popcll(bits);
       a.counts[0] = n - ne;
       a.counts[1] = ne;
     }
   }
-  if (!h) return;
-  __syncthreads();
-  const int chunks = row_bytes >> 4;
-  for (int t = wave; t < FCH; t += 4) {        // one row per wave at a time
-    const int64_t dst = s_dst[t];
-    if (dst < 0) continue;
-    const u32x4* src = (const u32x4*)(h + (int64_t)(c0 + t) * ld_h);
-    u32x4* d = (u32x4*)((s_to_out[t] ? out : h_cont) + dst);
-    for (int c = lane; c < chunks; c += 64) d[c] = src[c];
+  // continuing rows: row t goes to h_cont[(c0 + t) - (exits before it)]
+  if (h && h_cont) {
+    for (int t = wave; t < FCH && c0 + t < n; t += 4) {
+      if ((bits >> t) & 1) continue;                        // uniform
+      const int er = base + __popcll(bits & ((1ull << t) - 1));
+      const u32x4* src = (const u32x4*)(h + (int64_t)(c0 + t) * ld_h);
+      u32x4* d = (u32x4*)(h_cont + (int64_t)(c0 + t - er) * ld_cont);
+      for (int c = lane; c < chunks; c += 64) d[c] = src[c];
+    }
   }
 }
 
