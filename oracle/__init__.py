@@ -29,6 +29,7 @@ from .river_oracle import (  # noqa: F401
     RULE_BATCH_MIN,
     route,
     compact,
+    exit_projection,
     dequant_w4,
     kv_fill,
     kv_fill_rows,

@@ -148,6 +148,43 @@ def compact(mask, h, row_ids=None, out=None):
     return res
 
 
+def exit_projection(h, row_idx, m, gamma, eps, out, row_ids=None):
+    """Final RMSNorm of the exited rows, scattered to their original places.
+
+    Source: TIDE, "模块4: 融合 CUDA 内核" -- Exit Projection fuses an RMSNorm
+    with the scatter of exited tokens; "模块3: Post-Hoc Generation" -- an
+    exited token's logits come from the LM head applied to the RMSNorm of
+    its hidden state, so this is the state handed to the LM head.
+
+    Definition, for t = 0..m-1 with r = row_idx[t] (or t when row_idx is
+    None) and dst = row_ids[r] (or r when row_ids is None):
+
+        out[dst][j] = gamma[j] * h[r][j] / sqrt(mean_k(h[r][k]^2) + eps)
+
+    Readings taken: the mean runs over the d features; gamma=None means all
+    ones; rows r outside [0, n) and destinations outside [0, len(out)) are
+    skipped (the library's convention for out-of-range indices); every other
+    row of ``out`` is left as given. A zero row with eps = 0 gives 0/0 = NaN,
+    as IEEE arithmetic does. ``out`` is copied and the copy returned (float64).
+    """
+    h = _f64(h)
+    n, d = h.shape
+    g = np.ones(d) if gamma is None else _f64(gamma)
+    o = _f64(out).copy()
+    for t in range(int(m)):
+        r = t if row_idx is None else int(row_idx[t])
+        if not (0 <= r < n):
+            continue
+        dst = r if row_ids is None else int(row_ids[r])
+        if not (0 <= dst < o.shape[0]):
+            continue
+        x = h[r]
+        ms = np.mean(x * x)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            o[dst] = g * x / np.sqrt(ms + eps)
+    return o
+
+
 def dequant_w4(q, scale, zero, group):
     """Dequantize group-quantized int4 weights: w = (q - zero) * scale.
 

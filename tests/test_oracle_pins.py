@@ -405,6 +405,82 @@ def test_p11_cosine_rises_with_depth():
         assert all(b > a for a, b in zip(means, means[1:]))
 
 
+# ------------------------------------------------- P12 exit projection
+
+def test_p12_exit_projection_closed_forms():
+    """RMSNorm by hand: [3, 4] has mean square 12.5."""
+    z = np.zeros((1, 2))
+    o = O.exit_projection(np.array([[3.0, 4.0]]), None, 1, None, 0.0, z)
+    assert np.allclose(o[0], [3 * math.sqrt(2) / 5, 4 * math.sqrt(2) / 5], atol=1e-15, rtol=0)
+    # eps adds to the mean square: 12.5 + 12.5 = 25
+    o = O.exit_projection(np.array([[3.0, 4.0]]), None, 1, None, 12.5, z)
+    assert np.allclose(o[0], [0.6, 0.8], atol=1e-15, rtol=0)
+    # one feature: 3 / sqrt(9 + 16)
+    o = O.exit_projection(np.array([[3.0]]), None, 1, np.array([2.0]), 16.0, np.zeros((1, 1)))
+    assert np.allclose(o[0], [1.2], atol=1e-15, rtol=0)
+    # a constant row normalizes to gamma (times its sign)
+    g = np.linspace(-2, 3, 16)
+    for c in (-5.0, 0.25, 40.0):
+        o = O.exit_projection(np.full((1, 16), c), None, 1, g, 0.0, np.zeros((1, 16)))
+        assert np.allclose(o[0], np.sign(c) * g, atol=1e-14, rtol=0)
+
+
+def test_p12_exit_projection_unit_rms_and_scale():
+    rng = np.random.default_rng(12)
+    h = rng.standard_normal((9, 48)) * rng.uniform(0.01, 100, (9, 1))
+    z = np.zeros_like(h)
+    o = O.exit_projection(h, None, 9, None, 0.0, z)
+    assert np.allclose(np.mean(o * o, axis=1), 1.0, atol=1e-13, rtol=0)
+    for c in (1e-3, 3.0, 1e5):
+        assert np.allclose(O.exit_projection(c * h, None, 9, None, 0.0, z), o, atol=1e-13, rtol=0)
+    assert np.allclose(O.exit_projection(-h, None, 9, None, 0.0, z), -o, atol=1e-15, rtol=0)
+    # a zero row with eps = 0 is 0/0
+    o0 = O.exit_projection(np.zeros((1, 8)), None, 1, None, 0.0, np.zeros((1, 8)))
+    assert np.isnan(o0).all()
+
+
+def test_p12_exit_projection_matches_torch_rms_norm():
+    import torch.nn.functional as F
+    rng = np.random.default_rng(13)
+    h = rng.standard_normal((30, 64))
+    g = rng.standard_normal(64)
+    eps = 1e-2
+    o = O.exit_projection(h, None, 30, g, eps, np.zeros_like(h))
+    ref = F.rms_norm(torch.from_numpy(h), (64,), weight=torch.from_numpy(g), eps=eps).numpy()
+    assert np.allclose(o, ref, atol=1e-14, rtol=0)
+
+
+def test_p12_exit_projection_scatter():
+    """Rows land at row_ids[r]; everything else keeps its old value."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(14)
+    n, d, n_out = 40, 16, 64
+    h = rng.standard_normal((n, d))
+    g = rng.standard_normal(d)
+    mask = (rng.random(n) < 0.4).astype(np.uint8)
+    row_ids = rng.permutation(n_out)[:n]
+    c = O.compact(mask, h, row_ids)
+    sentinel = np.full((n_out, d), np.nan)
+    o = O.exit_projection(h, c["exit_idx"], c["counts"][1], g, 1e-6, sentinel, row_ids)
+    normed = F.rms_norm(torch.from_numpy(h), (d,), weight=torch.from_numpy(g), eps=1e-6).numpy()
+    ext = set(c["exit_idx"].tolist())
+    for r in range(n):
+        if r in ext:
+            assert np.allclose(o[row_ids[r]], normed[r], atol=1e-14, rtol=0)
+    touched = {int(row_ids[r]) for r in ext}
+    for q in range(n_out):
+        if q not in touched:
+            assert np.isnan(o[q]).all()
+    # m counts rows of row_idx; out-of-range rows and destinations are skipped
+    idx = np.array([3, -1, n + 5, 7, 9])
+    ids = np.arange(n)
+    ids[7] = n_out + 1
+    o = O.exit_projection(h, idx, 4, None, 0.0, np.full((n_out, d), np.nan), ids)
+    plain = F.rms_norm(torch.from_numpy(h[3]), (d,), eps=0.0).numpy()
+    assert np.allclose(o[3], plain, atol=1e-14, rtol=0)
+    assert np.isnan(np.delete(o, 3, axis=0)).all()
+
+
 # --------------------------------------------------------- mutation checks
 
 def _mutant_oracle(old, new):
@@ -451,6 +527,16 @@ MUTANTS = [
      "test_p3_ridge_matches_lstsq_and_sklearn"),
     # ridge result left input-major
     ("out[t] = W.T", "out[t] = W.reshape(W.shape[::-1])", "test_p3_ridge_closed_forms"),
+    # RMSNorm over the sum instead of the mean
+    ("ms = np.mean(x * x)", "ms = np.sum(x * x)", "test_p12_exit_projection_closed_forms"),
+    # eps dropped from the final norm
+    ("np.sqrt(ms + eps)", "np.sqrt(ms)", "test_p12_exit_projection_closed_forms"),
+    # gamma dropped from the final norm
+    ("o[dst] = g * x / np.sqrt(ms + eps)", "o[dst] = x / np.sqrt(ms + eps)",
+     "test_p12_exit_projection_matches_torch_rms_norm"),
+    # scatter ignores the row ids
+    ("dst = r if row_ids is None else int(row_ids[r])", "dst = r",
+     "test_p12_exit_projection_scatter"),
     # off-by-one in the filled layers
     ("filled = sum(n_layers - x for x in e)", "filled = sum(n_layers - x + 1 for x in e)",
      "test_p2_tide_figure2_worked_example"),
