@@ -71,6 +71,7 @@ class Workload:
         self.wk = tuple(t.to(dev) for t in w["wk"]) + (cfg.group,)
         self.wv = tuple(t.to(dev) for t in w["wv"]) + (cfg.group,)
         self.slot = G.slots(cfg, device=dev)
+        self.gamma = G.final_norm_gamma(cfg).to(dev)
         # ridge maps fitted on the GPU from the calibration pass
         X, Y = (t.to(dev) for t in G.calibration(cfg, e))
         self.maps = torch.empty((self.nl, d, d), dtype=torch.bfloat16, device=dev)
@@ -124,6 +125,13 @@ class Workload:
                           s["kc"], s["vc"], m_max=cfg.n_tokens, m_dev=s["counts"][1:],
                           row_idx=s["ext"], maps=None)
 
+    def exit_projection(self, s):
+        """Final RMSNorm of the exited rows into their positions of ``out``
+        (timed on its own: it is not one of the step's three calls)."""
+        cfg = self.cfg
+        tee.river_exit_projection(s["hc"], s["out"], m_max=cfg.n_tokens, m_dev=s["counts"][1:],
+                                  row_idx=s["ext"], gamma=self.gamma, eps=1e-5)
+
     def step(self, i):
         s = self.sets[i % len(self.sets)]
         self.route(s)
@@ -175,24 +183,34 @@ def per_call_times(wl, steps):
 
 
 def kernel_times(wl, launches):
-    """Average duration of single-kernel calls: ``launches`` back-to-back
-    calls of one kind (rotating sets) between two events on the launch
-    stream, divided by their number. Back to back, the events see the
-    kernels' own durations plus the short dispatch gaps between them, the
-    figure a kernel trace reports as the average duration."""
+    """Average duration of single-kernel calls. ``launches`` calls of one
+    kind (rotating sets) are captured into a HIP graph, and one replay is
+    bracketed by two events on the stream it runs on; the total divided by
+    the number of launches is the kernel's own duration plus the short
+    dispatch gap between graph nodes, the figure a kernel trace reports as
+    the average duration. The graph keeps host-side launch cost (the Python
+    binding takes several microseconds per call) out of the figure, which
+    matters for kernels shorter than that."""
     out = {}
-    for k, fn in (("route", wl.route), ("projection", wl.fill_projection_only)):
+    for k, fn in (("route", wl.route), ("projection", wl.fill_projection_only),
+                  ("exit_projection", wl.exit_projection)):
         for i in range(len(wl.sets)):
             fn(wl.sets[i])
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(launches):
+                fn(wl.sets[i % len(wl.sets)])
+        g.replay()
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for i in range(launches):
-            fn(wl.sets[i % len(wl.sets)])
+        g.replay()
         b.record()
         torch.cuda.synchronize()
         out[k] = a.elapsed_time(b) / launches
+        del g
     return out
 
 
@@ -313,6 +331,15 @@ def main():
             "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": measured_traffic(),
             "flops_per_launch": proj_flops, "avg_launch_us": kern["projection"] * 1e3}
 
+    # exit projection: reads and writes each exited row once, plus its two
+    # indices (exit_idx entry, and the identity row id)
+    ep_bytes = n_exit * (2 * cfg.d * 2 + 4)
+    ep_gbs = ep_bytes / (kern["exit_projection"] * 1e-3) / 1e9
+    exit_proj = {"kernel": "exit_proj_kernel<bf16,2> (final RMSNorm + scatter)", "bound": "hbm",
+                 "avg_launch_us": kern["exit_projection"] * 1e3, "bytes_per_launch": ep_bytes,
+                 "achieved": ep_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": ep_gbs / HBM_PEAK_GBS}
+
     line = {
         "metric": "exited tokens/s (route+compact+kv_fill)",
         "value": value,
@@ -336,6 +363,7 @@ def main():
         "route_gbs": route_b / (calls["route"] * 1e-3) / 1e9,
         "compact_gbs": compact_b / (calls["compact"] * 1e-3) / 1e9,
         "ridge_fit_ms_once": wl.ridge_ms,
+        "exit_projection": exit_proj,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -7,6 +7,8 @@
  *   river_route      which tokens exit at this layer
  *   river_compact    stable split of the batch into continuing and exiting
  *                    tokens, plus the exit scatter of hidden states
+ *   river_exit_projection  final RMSNorm of the exited rows, scattered to
+ *                    their original positions (the LM head's input)
  *   river_kv_fill    K/V of every skipped layer written into each exited
  *                    token's own cache slot
  *   river_ridge_fit  the closed-form ridge maps the fill applies
@@ -169,6 +171,41 @@ river_status river_compact(int n, int d, river_dtype dt, const uint8_t* mask,
                            void* workspace, size_t ws_bytes, hipStream_t s);
 
 /*
+ * river_exit_projection -- final RMSNorm of the exited rows, scattered to
+ * their original rows of the output.
+ *
+ * TIDE 模块4: "Exit Projection" fuses an RMSNorm with the scatter of the
+ * exited tokens; TIDE 模块3: an exited token's logits are the LM head
+ * applied to the RMSNorm of its hidden state, so each row written here is
+ * the LM head's input for that token.
+ *
+ * For t = 0..m-1, with r = row_idx[t] (or t) and dst = row_ids[r] (or r):
+ *   out[dst][j] = gamma[j] * h[r][j] / sqrt(mean_k(h[r][k]^2) + eps)
+ * rounded to dt (round to nearest even for bf16); the sum of squares and
+ * the scaling are fp32.
+ *
+ * m        : min(*m_dev, m_max) when m_dev is not NULL (a device int32,
+ *            e.g. counts+1 from river_compact), else m_max.
+ * h        : dt [n_rows][d], leading dim ld_h.
+ * row_idx  : int32 [m_max] rows of h (e.g. exit_idx), or NULL for 0..m-1
+ *            (then m_max <= n_rows). A row outside [0, n_rows) is skipped.
+ * row_ids  : int32 [n_rows] output row of each row of h, or NULL for the
+ *            identity. A destination outside [0, n_out_rows) is skipped.
+ * gamma    : dt [d], or NULL for all ones. eps: finite, >= 0. A zero row
+ *            with eps = 0 gives NaN (0 times an infinite reciprocal RMS).
+ * out      : dt [n_out_rows][d], leading dim ld_out; must not overlap h.
+ *            Destinations of the projected rows must be distinct. Rows
+ *            that receive nothing are left unchanged.
+ * No workspace. Every d that is a multiple of 8 is handled.
+ */
+river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river_dtype dt,
+                                   const void* h, int64_t ld_h, int n_rows,
+                                   const int32_t* row_idx, const int32_t* row_ids,
+                                   const void* gamma, float eps,
+                                   void* out, int64_t ld_out, int64_t n_out_rows,
+                                   hipStream_t s);
+
+/*
  * river_kv_fill -- K/V of every skipped layer for each exited token.
  *
  * River-LLM 方法步骤详情 step 1 and 技术新颖性: the exit path writes the
@@ -201,11 +238,12 @@ river_status river_compact(int n, int d, river_dtype dt, const uint8_t* mask,
  *            m_max, d, 0, 0, 1) bytes; the layers are processed in as few
  *            chunks as the given size allows. Without maps none is needed.
  * Only the filled slots are written; every other byte is left unchanged.
- * Paths: bf16 with d % 64 == 0, n_out % 32 == 0, group % 64 == 0, the same
- * group and scale/zero dtype for wk and wv, and an even number of groups
- * per row when scale/zero are bf16, runs on MFMA; every other shape (and
- * fp32) runs a generic fp32 kernel, one workgroup per (row, layer), which
- * needs d <= 8192 (RIVER_ERR_UNSUPPORTED otherwise).
+ * Paths: bf16 with d % 256 == 0, n_out % 64 == 0, group % 64 == 0, the
+ * same group and scale/zero dtype for wk and wv, an even number of groups
+ * per row when scale/zero are bf16, and operand spans under 2^31 bytes runs
+ * on MFMA; every other shape (and fp32) runs a generic kernel with fp32
+ * arithmetic, one workgroup per (row, layer), which needs d <= 8192
+ * (RIVER_ERR_UNSUPPORTED otherwise). n_layers <= 65535 per call.
  */
 river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt,
                            const void* h, int64_t ld_h, int n_rows,

@@ -14,6 +14,8 @@ tensor does not change when another one is added or dropped):
   States are accumulated in fp32 and each stored layer is rounded to the
   workload dtype.
 * router: W_down ~ N(0, 1/d), W_up ~ N(0, 1/b), gamma = 1 (passed as NULL).
+* final RMSNorm weight (exit projection): gamma = 1 + 0.1 * N(0, 1), the
+  spread of a trained norm's weights around one.
 * K/V weights: W ~ N(0, 1/d) per layer, stored as int4 with a per-group
   scale and zero (round-to-nearest, min-max; see ``quantize_w4``).
 * decode slots: distinct, drawn without replacement; prefill slots are the
@@ -100,6 +102,12 @@ def router_weights(cfg: Config, layer, device="cpu"):
     w_down = _normal((cfg.b, cfg.d), g, device) / math.sqrt(cfg.d)
     w_up = _normal((cfg.b,), g, device) / math.sqrt(cfg.b)
     return w_down.to(dt), w_up.to(dt)
+
+
+def final_norm_gamma(cfg: Config, device="cpu"):
+    """Weight [d] of the final RMSNorm, in the workload dtype."""
+    g = stream(cfg.idx, "final_norm", device)
+    return (1.0 + 0.1 * _normal((cfg.d,), g, device)).to(_DT[cfg.dtype])
 
 
 def quantize_w4(w, group, sz_dtype):

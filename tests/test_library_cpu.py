@@ -86,6 +86,7 @@ def test_kv_fill_and_ridge_argument_errors():
     assert lib.river_kv_fill(*args(maps=16)) == 5                  # maps need a workspace
     assert lib.river_kv_fill(*args(m=9)) == 1                      # more rows than h has
     assert lib.river_kv_fill(*args(kc=None)) == 1
+    assert lib.river_kv_fill(*args(nl=70000)) == 4                 # layers past the grid limit
     r = lib.river_ridge_fit(64, 64, 64, 1, 16, tee.RIVER_BF16, 16, tee.RIVER_F32, 0.1, 16,
                             tee.RIVER_F32, 16, 1 << 30, None)
     assert r == 2                                                  # X, Y dtypes differ
@@ -96,3 +97,33 @@ def test_kv_fill_and_ridge_argument_errors():
                             tee.RIVER_F32, 16, 10, None)
     assert r == 5                                                  # workspace too small
     assert lib.river_debug_set_compact_path(9) == 1
+
+
+def _exit_projection(**kw):
+    lib = tee.load()
+    a = dict(m=8, mdev=None, d=64, dt=tee.RIVER_BF16, h=16, ldh=64, nrows=8, ri=None, rid=None,
+             gamma=None, eps=1e-6, out=16, ldo=64, nout=8, s=None)
+    a.update(kw)
+    return lib.river_exit_projection(*a.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=0), 0),               # empty call, nothing enqueued
+    (dict(m=0, d=12), 1),         # sizes are still checked
+    (dict(dt=3), 2),
+    (dict(m=-1), 1),
+    (dict(nout=-1), 1),
+    (dict(eps=math.nan), 1),
+    (dict(eps=math.inf), 1),
+    (dict(h=None), 1),
+    (dict(out=None), 1),
+    (dict(m=9), 1),               # more rows than h has, no row_idx
+    (dict(h=8), 3),
+    (dict(ldo=60), 3),
+    (dict(ldh=68), 3),            # 136 bytes: not a multiple of 16
+    (dict(gamma=24), 3),
+])
+def test_exit_projection_argument_errors(kw, status):
+    assert _exit_projection(**kw) == status
+    if status:
+        assert len(tee.load().river_last_error()) > 0

@@ -313,6 +313,24 @@ def test_kv_fill_identity_null_equals_explicit_eye():
     check_fill(cfg, k1, v1, h, rows.cpu().numpy(), slot, None, wk, wv)
 
 
+@pytest.mark.parametrize("d,hkv,hd,group", [(200, 3, 24, 40), (512, 3, 24, 64), (264, 2, 32, 8)])
+def test_kv_fill_bf16_generic_shapes(d, hkv, hd, group):
+    """bf16 shapes the MFMA tiles do not take (d not a multiple of 256, an
+    odd number of groups, n_out not a multiple of 64) run the generic
+    kernel, with and without maps."""
+    cfg = get_config(1, d=d, n_kv_heads=hkv, head_dim=hd, group=group, n_tokens=40, n_slots=96)
+    layers = [5, 6, 7]
+    h = G.hidden_states(cfg, cfg.n_tokens, [4])[4].to(DEV)
+    g = torch.Generator().manual_seed(d)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    rows = torch.tensor([1, 7, 39, 0, 22], dtype=torch.int32, device=DEV)
+    maps = G.near_identity_maps(cfg, len(layers)).to(DEV)
+    for mp in (None, maps):
+        kc, vc = fill_gpu(cfg, h, slot, wk, wv, len(layers), row_idx=rows, maps=mp)
+        check_fill(cfg, kc, vc, h, rows.cpu().numpy(), slot, mp, wk, wv)
+
+
 def test_kv_fill_8b_sampled():
     cfg = get_config(3)
     e = 11

@@ -5,8 +5,9 @@ pointers and the current HIP stream to the C interface declared in
 ``include/river.h``; all arithmetic runs in the HIP kernels. There is no
 CPU fallback: if the library is not built, ``load()`` raises.
 
-The four calls keep the C names: ``river_route``, ``river_compact``,
-``river_kv_fill``, ``river_ridge_fit``; plus ``river_workspace_size``.
+The calls keep the C names: ``river_route``, ``river_compact``,
+``river_exit_projection``, ``river_kv_fill``, ``river_ridge_fit``; plus
+``river_workspace_size``.
 """
 
 import ctypes
@@ -22,7 +23,7 @@ OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT = 0, 1, 2, 3
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_DTYPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED",
           5: "ERR_WORKSPACE", 6: "ERR_NOT_SPD", 7: "ERR_HIP"}
 
-EXPORTS = ["river_route", "river_compact", "river_kv_fill", "river_ridge_fit",
+EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fill", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
            "river_debug_set_compact_path"]
 
@@ -60,11 +61,13 @@ def load():
                                 _P, _P, _P, _P, _P]
     lib.river_compact.argtypes = [_I, _I, _I, _P, _P, _L, _P, _P, _P, _P, _P, _L, _P, _P, _L, _L,
                                   _P, _S, _P]
+    lib.river_exit_projection.argtypes = [_I, _P, _I, _I, _P, _L, _I, _P, _P, _P, _F, _P, _L, _L,
+                                          _P]
     lib.river_kv_fill.argtypes = [_I, _P, _I, _I, _P, _L, _I, _P, _P, _I, _P,
                                   ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4), _I, _I,
                                   _P, _P, _L, _P, _S, _P]
     lib.river_ridge_fit.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _S, _P]
-    for f in ("river_route", "river_compact", "river_kv_fill", "river_ridge_fit",
+    for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill", "river_ridge_fit",
               "river_debug_set_compact_path"):
         getattr(lib, f).restype = _I
     lib.river_debug_set_compact_path.argtypes = [_I]
@@ -149,6 +152,16 @@ def river_compact(mask, h, cont_idx, exit_idx, counts, *, row_ids=None, h_cont=N
                                 _ptr(out), _ld(out) if out is not None else 0,
                                 out.shape[0] if out is not None else 0, _ptr(workspace), ws_n,
                                 _stream(stream)))
+
+
+def river_exit_projection(h, out, *, m_max=None, m_dev=None, row_idx=None, row_ids=None,
+                          gamma=None, eps=1e-6, stream=None):
+    n_rows, d = h.shape
+    if m_max is None:
+        m_max = row_idx.shape[0] if row_idx is not None else n_rows
+    _check(load().river_exit_projection(m_max, _ptr(m_dev), d, _dt(h), _ptr(h), _ld(h), n_rows,
+                                        _ptr(row_idx), _ptr(row_ids), _ptr(gamma), eps, _ptr(out),
+                                        _ld(out), out.shape[0], _stream(stream)))
 
 
 def w4(q, scale, zero, group):

@@ -137,6 +137,27 @@ river_status river_compact(int n, int d, river_dtype dt, const uint8_t* mask, co
                         ld_cont, row_ids_cont, out, ld_out, n_out_rows, workspace, ws_bytes, s);
 }
 
+river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river_dtype dt,
+                                   const void* h, int64_t ld_h, int n_rows,
+                                   const int32_t* row_idx, const int32_t* row_ids,
+                                   const void* gamma, float eps, void* out, int64_t ld_out,
+                                   int64_t n_out_rows, hipStream_t s) {
+  g_err[0] = 0;
+  if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "exit_projection: dtype %d is not RIVER_F32 or RIVER_BF16", (int)dt);
+  if (m_max < 0 || n_rows < 0 || n_out_rows < 0) return fail(RIVER_ERR_ARG, "exit_projection: negative size");
+  if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "exit_projection: d = %d must be a positive multiple of 8", d);
+  if (!(eps >= 0.0f) || isinf(eps)) return fail(RIVER_ERR_ARG, "exit_projection: eps must be finite and >= 0");
+  if (m_max == 0) return RIVER_OK;
+  if (!h || !out) return fail(RIVER_ERR_ARG, "exit_projection: h and out are required");
+  if (!row_idx && m_max > n_rows)
+    return fail(RIVER_ERR_ARG, "exit_projection: m_max = %d > n_rows = %d without row_idx", m_max, n_rows);
+  if (!ld_ok(ld_h, d, dt) || !aligned16(h)) return fail(RIVER_ERR_ALIGN, "exit_projection: h misaligned or ld_h invalid");
+  if (!ld_ok(ld_out, d, dt) || !aligned16(out)) return fail(RIVER_ERR_ALIGN, "exit_projection: out misaligned or ld_out invalid");
+  if (gamma && !aligned16(gamma)) return fail(RIVER_ERR_ALIGN, "exit_projection: gamma must be 16-byte aligned");
+  return launch_exit_projection(m_max, m_dev, d, dt, h, ld_h, n_rows, row_idx, row_ids, gamma, eps,
+                                out, ld_out, n_out_rows, s);
+}
+
 river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
                            int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
                            int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
@@ -158,12 +179,8 @@ river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype d
     if (w->group < 2 || d % w->group || w->group % 2) return fail(RIVER_ERR_ARG, "kv_fill: group %d must be even and divide d", w->group);
     if (!aligned16(w->q)) return fail(RIVER_ERR_ALIGN, "kv_fill: int4 weights must be 16-byte aligned");
   }
-  int n_out = n_kv_heads * head_dim;
-  if (dt == RIVER_BF16) {
-    if (d % 64) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: bf16 path needs d %% 64 == 0 (d = %d)", d);
-    if (n_out % 32) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: bf16 path needs n_kv_heads*head_dim %% 32 == 0");
-    if (wk->group % 32 || wv->group % 32) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: bf16 path needs group %% 32 == 0");
-  }
+  if ((int64_t)n_kv_heads * head_dim > (1 << 24)) return fail(RIVER_ERR_ARG, "kv_fill: n_kv_heads * head_dim too large");
+  if (n_layers > 65535) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: at most 65535 layers per call");
   if (!aligned16(k_cache) || !aligned16(v_cache) || (maps && !aligned16(maps)))
     return fail(RIVER_ERR_ALIGN, "kv_fill: caches and maps must be 16-byte aligned");
   if (maps) {

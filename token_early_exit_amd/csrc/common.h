@@ -165,6 +165,12 @@ river_status launch_compact(int n, int d, river_dtype dt, const uint8_t* mask, c
                             int32_t* row_ids_cont, void* out, int64_t ld_out, int64_t n_out_rows,
                             void* workspace, size_t ws_bytes, hipStream_t s);
 
+river_status launch_exit_projection(int m_max, const int32_t* m_dev, int d, river_dtype dt,
+                                    const void* h, int64_t ld_h, int n_rows,
+                                    const int32_t* row_idx, const int32_t* row_ids,
+                                    const void* gamma, float eps, void* out, int64_t ld_out,
+                                    int64_t n_out_rows, hipStream_t s);
+
 size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt);
 river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
                             int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
