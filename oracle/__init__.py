@@ -33,6 +33,8 @@ from .river_oracle import (  # noqa: F401
     dequant_w4,
     kv_fill,
     kv_fill_rows,
+    kv_fill_layer_rows,
+    rope_half,
     ridge_fit,
     exit_schedule_ops,
 )

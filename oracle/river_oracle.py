@@ -246,6 +246,74 @@ def kv_fill_rows(h, row_idx, m, maps, wk, wv):
     return K, V
 
 
+def rope_half(x, cos, sin):
+    """Rotary position embedding of head vectors, half-split pairing.
+
+    Not defined on the pages: this is the standard rotary embedding
+    (RoFormer) in the layout of Llama-family models, the models River-LLM
+    evaluates; it is part of "the layer's own projection" whose output the
+    cache holds (RidgeFill, "思路源头").
+
+    x: [..., hd]; cos, sin: [..., hd/2], broadcast against x. Element i is
+    paired with element i + hd/2 and the pair is turned by the angle whose
+    cosine and sine are cos[i] and sin[i]:
+        y[i] = x[i] cos[i] - x[i + hd/2] sin[i]
+        y[i + hd/2] = x[i] sin[i] + x[i + hd/2] cos[i]
+    """
+    x = _f64(x)
+    half = x.shape[-1] // 2
+    a, b = x[..., :half], x[..., half:]
+    c, s = _f64(cos), _f64(sin)
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def kv_fill_layer_rows(h, row_idx, m, maps, wk, wv, gamma=None, eps=0.0, bk=None, bv=None,
+                       pos=None, cos=None, sin=None, n_kv_heads=None, head_dim=None):
+    """K and V rows of a fill through the skipped layers' full K/V path.
+
+    Sources: RidgeFill, "思路源头": the predicted input of a skipped layer
+    goes through that layer's own projection, which writes the cache as it
+    normally would. River-LLM, "方法步骤详情" step 1: the K/V are those of
+    the skipped layer, at the backbone's addresses.
+
+    Reading taken: the layer's usual K/V path is its input RMSNorm (weight
+    gamma[l], over the d features, as TIDE's RMSNorm), the K and V linear
+    maps with optional biases bk[l], bv[l] (GPT-2-style), then rotary
+    position embedding of K only, per head, at the row's position
+    (``rope_half``; pos is indexed by the row of h, tables cos/sin are
+    [n_pos][head_dim/2]). Any of the three may be absent (None).
+
+    Returns (K, V), each float64 [n_layers][m][n_out].
+    """
+    h = _f64(h)
+    rows = np.arange(m) if row_idx is None else np.asarray(row_idx, dtype=np.int64)[:m]
+    x = h[rows]
+    n_layers = np.asarray(wk["q"]).shape[0]
+    n_out = np.asarray(wk["q"]).shape[1]
+    K = np.empty((n_layers, m, n_out))
+    V = np.empty((n_layers, m, n_out))
+    for l in range(n_layers):
+        xh = x if maps is None else x @ _f64(maps[l]).T        # predicted layer input
+        if gamma is not None:                                  # the layer's input RMSNorm
+            ms = np.mean(xh * xh, axis=1)
+            xh = _f64(gamma[l])[None, :] * xh / np.sqrt(ms + eps)[:, None]
+        Wk = dequant_w4(wk["q"][l], wk["scale"][l], wk["zero"][l], wk["group"])
+        Wv = dequant_w4(wv["q"][l], wv["scale"][l], wv["zero"][l], wv["group"])
+        K[l] = xh @ Wk.T
+        V[l] = xh @ Wv.T
+        if bk is not None:
+            K[l] += _f64(bk[l])[None, :]
+        if bv is not None:
+            V[l] += _f64(bv[l])[None, :]
+        if pos is not None:                                    # RoPE on K, per head
+            p = np.asarray(pos, dtype=np.int64)[rows]
+            k = K[l].reshape(m, n_kv_heads, head_dim)
+            c = _f64(cos)[p][:, None, :]
+            sn = _f64(sin)[p][:, None, :]
+            K[l] = rope_half(k, c, sn).reshape(m, n_out)
+    return K, V
+
+
 def kv_fill(h, row_idx, m, slot, maps, wk, wv, n_kv_heads, head_dim, k_cache, v_cache):
     """Write K/V of every skipped layer into each exited token's own slot.
 

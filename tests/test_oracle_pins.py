@@ -481,6 +481,138 @@ def test_p12_exit_projection_scatter():
     assert np.isnan(np.delete(o, 3, axis=0)).all()
 
 
+# ------------------------------------------- P13 real-layer fill and RoPE
+
+def _rope_tables(n_pos, hd, base):
+    """cos / sin of p * base^(-2i/hd), the standard rotary frequencies."""
+    inv = base ** (-np.arange(0, hd, 2) / hd)
+    ang = np.arange(n_pos)[:, None] * inv[None, :]
+    return np.cos(ang), np.sin(ang)
+
+
+def test_p13_rope_is_complex_rotation():
+    """Pair (x_i, x_{i+hd/2}) as the complex number x_i + j x_{i+hd/2},
+    turned by e^{j angle}."""
+    rng = np.random.default_rng(21)
+    hd = 16
+    x = rng.standard_normal((5, 3, hd))
+    ang = rng.uniform(-7, 7, (5, 1, hd // 2))
+    y = O.rope_half(x, np.cos(ang), np.sin(ang))
+    z = (x[..., : hd // 2] + 1j * x[..., hd // 2:]) * np.exp(1j * ang)
+    assert np.allclose(y[..., : hd // 2], z.real, atol=1e-14, rtol=0)
+    assert np.allclose(y[..., hd // 2:], z.imag, atol=1e-14, rtol=0)
+
+
+def test_p13_rope_relative_position():
+    rng = np.random.default_rng(22)
+    hd = 64
+    cos, sin = _rope_tables(300, hd, 10000.0)
+    q = rng.standard_normal(hd)
+    k = rng.standard_normal(hd)
+    rq = lambda v, p: O.rope_half(v, cos[p], sin[p])
+    for p1, p2, sh in ((3, 10, 100), (50, 7, 33), (0, 0, 250)):
+        a = rq(q, p1) @ rq(k, p2)
+        b = rq(q, p1 + sh) @ rq(k, p2 + sh)
+        assert abs(a - b) <= 1e-10 * (abs(a) + 1)
+    assert np.allclose(rq(q, 0), q, atol=0, rtol=0)                      # position 0
+    assert np.allclose(np.linalg.norm(rq(q, 123)), np.linalg.norm(q), atol=1e-12, rtol=0)
+
+
+def _layer_case(rng, n_layers=2, d=64, hkv=2, hd=16, group=16, n=7):
+    W = rng.standard_normal((2, n_layers, hkv * hd, d)) / math.sqrt(d)
+    ws = []
+    for which in range(2):
+        q, sc, zp = [], [], []
+        for l in range(n_layers):
+            qq, ss, zz = _quant_np(W[which, l], group)
+            q.append(qq)
+            sc.append(ss)
+            zp.append(zz)
+        ws.append({"q": np.stack(q), "scale": np.stack(sc), "zero": np.stack(zp), "group": group})
+    h = rng.standard_normal((n, d))
+    return h, ws[0], ws[1]
+
+
+def _quant_np(w, group):
+    """Round-to-nearest int4 of one [n_out][d] matrix (test data only)."""
+    n_out, d = w.shape
+    g = w.reshape(n_out, d // group, group)
+    lo, hi = g.min(-1), g.max(-1)
+    sc = np.where(hi > lo, (hi - lo) / 15, 1.0)
+    zp = -lo / sc
+    qv = np.clip(np.rint(g / sc[..., None] + zp[..., None]), 0, 15).astype(np.uint8).reshape(n_out, d)
+    return (qv[:, 0::2] | (qv[:, 1::2] << 4)).astype(np.uint8), sc, zp
+
+
+def test_p13_layer_fill_without_extras_is_linear_fill():
+    rng = np.random.default_rng(23)
+    h, wk, wv = _layer_case(rng)
+    maps = rng.standard_normal((2, 64, 64)) / 8
+    rows = np.array([4, 0, 6])
+    K0, V0 = O.kv_fill_rows(h, rows, 3, maps, wk, wv)
+    K1, V1 = O.kv_fill_layer_rows(h, rows, 3, maps, wk, wv)
+    assert np.array_equal(K0, K1) and np.array_equal(V0, V1)
+
+
+def test_p13_layer_fill_matches_torch():
+    """Input RMSNorm, biases and RoPE on K, rebuilt from torch.nn.functional
+    and torch complex arithmetic in float64."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(24)
+    nl, d, hkv, hd = 2, 64, 2, 16
+    h, wk, wv = _layer_case(rng, nl, d, hkv, hd)
+    maps = np.eye(d)[None] + rng.standard_normal((nl, d, d)) / 20
+    gamma = 1 + 0.1 * rng.standard_normal((nl, d))
+    bk = rng.standard_normal((nl, hkv * hd))
+    bv = rng.standard_normal((nl, hkv * hd))
+    cos, sin = _rope_tables(40, hd, 500000.0)
+    pos = rng.permutation(40)[: h.shape[0]]
+    rows = np.array([6, 2, 3, 0])
+    eps = 1e-5
+    K, V = O.kv_fill_layer_rows(h, rows, 4, maps, wk, wv, gamma, eps, bk, bv, pos, cos, sin, hkv, hd)
+    T = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    ang = T(np.arctan2(sin, cos))
+    for l in range(nl):
+        x = T(h[rows]) @ T(maps[l]).T
+        xn = F.rms_norm(x, (d,), weight=T(gamma[l]), eps=eps)
+        Wk = T(O.dequant_w4(wk["q"][l], wk["scale"][l], wk["zero"][l], wk["group"]))
+        Wv = T(O.dequant_w4(wv["q"][l], wv["scale"][l], wv["zero"][l], wv["group"]))
+        k = F.linear(xn, Wk, T(bk[l])).reshape(len(rows), hkv, hd)
+        v = F.linear(xn, Wv, T(bv[l]))
+        zc = torch.complex(k[..., : hd // 2], k[..., hd // 2:])
+        rot = torch.polar(torch.ones_like(ang), ang)[torch.from_numpy(pos[rows])][:, None, :]
+        zr = zc * rot
+        kr = torch.cat([zr.real, zr.imag], dim=-1).reshape(len(rows), hkv * hd)
+        assert np.allclose(K[l], kr.numpy(), atol=1e-12, rtol=0)
+        assert np.allclose(V[l], v.numpy(), atol=1e-12, rtol=0)
+
+
+def test_p13_layer_fill_norm_scale_invariance_and_bias():
+    rng = np.random.default_rng(25)
+    nl, d, hkv, hd = 2, 64, 2, 16
+    h, wk, wv = _layer_case(rng, nl, d, hkv, hd)
+    gamma = 1 + 0.1 * rng.standard_normal((nl, d))
+    K1, V1 = O.kv_fill_layer_rows(h, None, 5, None, wk, wv, gamma, 0.0)
+    K2, V2 = O.kv_fill_layer_rows(37.0 * h, None, 5, None, wk, wv, gamma, 0.0)
+    assert np.allclose(K1, K2, atol=1e-12, rtol=0) and np.allclose(V1, V2, atol=1e-12, rtol=0)
+    # zero weights (q equal to the zero point): K is the rotated bias, V the bias
+    wz = {"q": np.full_like(wk["q"], 0x33), "scale": np.ones_like(wk["scale"]),
+          "zero": np.full_like(wk["zero"], 3.0), "group": wk["group"]}
+    bk = rng.standard_normal((nl, hkv * hd))
+    bv = rng.standard_normal((nl, hkv * hd))
+    cos, sin = _rope_tables(10, hd, 10000.0)
+    pos = np.arange(h.shape[0]) + 2
+    K, V = O.kv_fill_layer_rows(h, None, 5, None, wz, wz, gamma, 1e-6, bk, bv, pos, cos, sin, hkv, hd)
+    for l in range(nl):
+        assert np.array_equal(V[l], np.broadcast_to(bv[l], V[l].shape))
+        for t in range(5):
+            ang = np.arctan2(sin[pos[t]], cos[pos[t]])
+            b = bk[l].reshape(hkv, hd)
+            z = (b[:, : hd // 2] + 1j * b[:, hd // 2:]) * np.exp(1j * ang)
+            assert np.allclose(K[l, t], np.concatenate([z.real, z.imag], axis=1).ravel(),
+                               atol=1e-13, rtol=0)
+
+
 # --------------------------------------------------------- mutation checks
 
 def _mutant_oracle(old, new):
@@ -537,6 +669,20 @@ MUTANTS = [
     # scatter ignores the row ids
     ("dst = r if row_ids is None else int(row_ids[r])", "dst = r",
      "test_p12_exit_projection_scatter"),
+    # rotation with the wrong sign
+    ("np.concatenate([a * c - b * s, a * s + b * c]", "np.concatenate([a * c + b * s, a * s + b * c]",
+     "test_p13_rope_is_complex_rotation"),
+    # interleaved pairs instead of halves
+    ("a, b = x[..., :half], x[..., half:]", "a, b = x[..., 0::2], x[..., 1::2]",
+     "test_p13_layer_fill_matches_torch"),
+    # the layer norm's weight dropped
+    ("xh = _f64(gamma[l])[None, :] * xh / np.sqrt(ms + eps)[:, None]",
+     "xh = xh / np.sqrt(ms + eps)[:, None]", "test_p13_layer_fill_matches_torch"),
+    # every row rotated at position 0
+    ("c = _f64(cos)[p][:, None, :]", "c = _f64(cos)[p * 0][:, None, :]",
+     "test_p13_layer_fill_matches_torch"),
+    # K bias dropped
+    ("K[l] += _f64(bk[l])[None, :]", "K[l] += 0.0", "test_p13_layer_fill_norm_scale_invariance_and_bias"),
     # off-by-one in the filled layers
     ("filled = sum(n_layers - x for x in e)", "filled = sum(n_layers - x + 1 for x in e)",
      "test_p2_tide_figure2_worked_example"),
