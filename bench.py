@@ -72,6 +72,11 @@ class Workload:
         self.wv = tuple(t.to(dev) for t in w["wv"]) + (cfg.group,)
         self.slot = G.slots(cfg, device=dev)
         self.gamma = G.final_norm_gamma(cfg).to(dev)
+        # the skipped layers' own K/V path: input RMSNorm, K/V bias, RoPE
+        self.lgamma = G.layer_norm_gammas(cfg, self.layers).to(dev)
+        self.bk, self.bv = (t.to(dev) for t in G.kv_biases(cfg, self.layers))
+        self.rcos, self.rsin = (t.to(dev) for t in G.rope_tables(cfg, n))
+        self.pos = torch.arange(n, dtype=torch.int32, device=dev)
         # ridge maps fitted on the GPU from the calibration pass
         X, Y = (t.to(dev) for t in G.calibration(cfg, e))
         self.maps = torch.empty((self.nl, d, d), dtype=torch.bfloat16, device=dev)
@@ -100,6 +105,8 @@ class Workload:
                                dtype=torch.uint8, device=dev)
         self.kws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, n, d, 0, 0, self.nl),
                                dtype=torch.uint8, device=dev)
+        self.lws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL_LAYER, n, d, 0, 0, self.nl),
+                               dtype=torch.uint8, device=dev)
 
     # the three calls of one step
     def route(self, s):
@@ -124,6 +131,16 @@ class Workload:
         tee.river_kv_fill(s["hc"], self.slot, self.wk, self.wv, cfg.n_kv_heads, cfg.head_dim,
                           s["kc"], s["vc"], m_max=cfg.n_tokens, m_dev=s["counts"][1:],
                           row_idx=s["ext"], maps=None)
+
+    def fill_layer(self, s):
+        """The fill through the layers' full K/V path (input RMSNorm, K/V
+        bias and RoPE on K), same rows, maps and slots as ``fill``."""
+        cfg = self.cfg
+        tee.river_kv_fill_layer(s["hc"], self.slot, self.wk, self.wv, cfg.n_kv_heads, cfg.head_dim,
+                                s["kc"], s["vc"], m_max=cfg.n_tokens, m_dev=s["counts"][1:],
+                                row_idx=s["ext"], maps=self.maps, norm_gamma=self.lgamma,
+                                norm_eps=1e-5, k_bias=self.bk, v_bias=self.bv, pos=self.pos,
+                                rope_cos=self.rcos, rope_sin=self.rsin, workspace=self.lws)
 
     def exit_projection(self, s):
         """Final RMSNorm of the exited rows into their positions of ``out``
@@ -183,7 +200,9 @@ def per_call_times(wl, steps):
 
 
 def kernel_times(wl, launches):
-    """Average duration of single-kernel calls. ``launches`` calls of one
+    """Average duration of one call of each kind (route, the projection
+    kernel alone, the exit projection, the whole fill with and without the
+    layers' K/V path). ``launches`` calls of one
     kind (rotating sets) are captured into a HIP graph, and one replay is
     bracketed by two events on the stream it runs on; the total divided by
     the number of launches is the kernel's own duration plus the short
@@ -193,7 +212,8 @@ def kernel_times(wl, launches):
     matters for kernels shorter than that."""
     out = {}
     for k, fn in (("route", wl.route), ("projection", wl.fill_projection_only),
-                  ("exit_projection", wl.exit_projection)):
+                  ("exit_projection", wl.exit_projection), ("fill", wl.fill),
+                  ("fill_layer", wl.fill_layer)):
         for i in range(len(wl.sets)):
             fn(wl.sets[i])
         torch.cuda.synchronize()
@@ -364,6 +384,10 @@ def main():
         "compact_gbs": compact_b / (calls["compact"] * 1e-3) / 1e9,
         "ridge_fit_ms_once": wl.ridge_ms,
         "exit_projection": exit_proj,
+        "fill_layer": {"parts": "input RMSNorm + K/V bias + RoPE on K (head_dim 64), ridge maps",
+                       "avg_call_us": kern["fill_layer"] * 1e3,
+                       "plain_fill_avg_call_us": kern["fill"] * 1e3,
+                       "overhead_us": (kern["fill_layer"] - kern["fill"]) * 1e3},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

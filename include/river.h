@@ -11,6 +11,8 @@
  *                    their original positions (the LM head's input)
  *   river_kv_fill    K/V of every skipped layer written into each exited
  *                    token's own cache slot
+ *   river_kv_fill_layer  the same through the layer's full K/V path (input
+ *                    RMSNorm, K/V bias, rotary embedding of K)
  *   river_ridge_fit  the closed-form ridge maps the fill applies
  *
  * Sources (web pages; cited by title and section):
@@ -75,7 +77,8 @@ typedef enum { RIVER_RULE_TOKEN = 0, RIVER_RULE_BATCH_MIN = 1 } river_rule;
 
 /* Operation ids for river_workspace_size. */
 typedef enum {
-  RIVER_OP_ROUTE = 0, RIVER_OP_COMPACT = 1, RIVER_OP_KV_FILL = 2, RIVER_OP_RIDGE_FIT = 3
+  RIVER_OP_ROUTE = 0, RIVER_OP_COMPACT = 1, RIVER_OP_KV_FILL = 2, RIVER_OP_RIDGE_FIT = 3,
+  RIVER_OP_KV_FILL_LAYER = 4
 } river_op;
 
 /*
@@ -255,6 +258,55 @@ river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype d
                            void* workspace, size_t ws_bytes, hipStream_t s);
 
 /*
+ * The rest of a skipped layer's K/V path, for river_kv_fill_layer. Each
+ * part is switched off by a NULL pointer.
+ *
+ * RidgeFill 思路源头: the predicted input of a skipped layer goes through
+ * that layer's own projection, which writes the cache as it normally would.
+ * For the Llama-family models River-LLM evaluates that path is the layer's
+ * input RMSNorm, the K and V projections, and the rotary position embedding
+ * of K; GPT-2-style layers add K and V biases.
+ */
+typedef struct {
+  const void* norm_gamma;   /* dt [n_layers][d]: input RMSNorm weight        */
+  float norm_eps;           /* finite, >= 0                                 */
+  const void* k_bias;       /* dt [n_layers][n_kv_heads * head_dim]         */
+  const void* v_bias;       /* dt [n_layers][n_kv_heads * head_dim]         */
+  const int32_t* pos;       /* int32 [n_rows]: rotary position of each row  */
+  const float* rope_cos;    /* fp32 [n_pos][head_dim / 2]                   */
+  const float* rope_sin;    /* fp32 [n_pos][head_dim / 2]                   */
+  int64_t n_pos;
+} river_layer;
+
+/*
+ * river_kv_fill_layer -- river_kv_fill through the layer's full K/V path.
+ *
+ * For layer l and row r (as in river_kv_fill, x_hat = maps[l] . h[r]):
+ *   x_n = gamma[l] * x_hat / sqrt(mean(x_hat^2) + eps)    (if norm_gamma)
+ *   K = Wk[l] . x_n + k_bias[l],  V = Wv[l] . x_n + v_bias[l]
+ *   if pos: within each head, element i < head_dim/2 is paired with
+ *     i + head_dim/2 and the pair turned by the angle of row pos[r]:
+ *     K'[i]  = K[i] cos[p][i] - K[i + hd/2] sin[p][i]
+ *     K'[i + hd/2] = K[i] sin[p][i] + K[i + hd/2] cos[p][i]
+ * A row whose position is outside [0, n_pos) is skipped (nothing written).
+ * layer may be NULL (then this is river_kv_fill). head_dim must be even
+ * with rotation. workspace: with maps or norm_gamma, at least
+ * river_workspace_size(RIVER_OP_KV_FILL_LAYER, m_max, d, 0, 0, 1) bytes;
+ * the layers are processed in as few chunks as the size allows. The MFMA
+ * path takes the shapes river_kv_fill's does, and head_dim % 32 == 0 with
+ * rotation; every other shape runs the generic kernel (d and n_out with
+ * 2 (d + n_out) + 4 floats of LDS <= 64 KB).
+ */
+river_status river_kv_fill_layer(int m_max, const int32_t* m_dev, int d, river_dtype dt,
+                                 const void* h, int64_t ld_h, int n_rows,
+                                 const int32_t* row_idx, const int32_t* slot,
+                                 int n_layers, const void* maps,
+                                 const river_w4* wk, const river_w4* wv,
+                                 const river_layer* layer, int n_kv_heads, int head_dim,
+                                 void* k_cache, void* v_cache, int64_t n_slots,
+                                 void* workspace, size_t ws_bytes, hipStream_t s);
+
+/*
  * river_ridge_fit -- closed-form ridge maps (RidgeFill, ridge box):
  *
  *   W_t = (X^T X + lambda I)^-1 X^T Y_t     for t = 0..n_targets-1
@@ -277,7 +329,9 @@ river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets,
 
 /* Workspace bytes for an operation (arguments that do not apply are
  * ignored): ROUTE -> 0; COMPACT (n); KV_FILL (n = m_max, d, n_layers; 0
- * layers gives 0, the identity case); RIDGE_FIT (n, d = d_in, d_out,
+ * layers gives 0, the identity case); KV_FILL_LAYER (n = m_max, d,
+ * n_layers; the bytes for n_layers layers, needed with maps or a norm);
+ * RIDGE_FIT (n, d = d_in, d_out,
  * n_targets, and n_layers carries the dtype: RIVER_F32 or RIVER_BF16). */
 size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int n_layers);
 

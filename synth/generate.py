@@ -16,6 +16,10 @@ tensor does not change when another one is added or dropped):
 * router: W_down ~ N(0, 1/d), W_up ~ N(0, 1/b), gamma = 1 (passed as NULL).
 * final RMSNorm weight (exit projection): gamma = 1 + 0.1 * N(0, 1), the
   spread of a trained norm's weights around one.
+* the skipped layers' own K/V path: input RMSNorm weights gamma_l = 1 +
+  0.1 * N(0, 1) per layer, K/V biases N(0, 0.02^2), rotary tables
+  cos/sin(p * base^(-2i/head_dim)) in fp32 (computed in float64), base
+  500000 for the Llama-3-shape workloads and 10000 otherwise.
 * K/V weights: W ~ N(0, 1/d) per layer, stored as int4 with a per-group
   scale and zero (round-to-nearest, min-max; see ``quantize_w4``).
 * decode slots: distinct, drawn without replacement; prefill slots are the
@@ -108,6 +112,41 @@ def final_norm_gamma(cfg: Config, device="cpu"):
     """Weight [d] of the final RMSNorm, in the workload dtype."""
     g = stream(cfg.idx, "final_norm", device)
     return (1.0 + 0.1 * _normal((cfg.d,), g, device)).to(_DT[cfg.dtype])
+
+
+def layer_norm_gammas(cfg: Config, layers, device="cpu"):
+    """Input RMSNorm weights [len(layers)][d] of the given layers."""
+    out = []
+    for l in layers:
+        g = stream(cfg.idx, f"layer_norm/{l}", device)
+        out.append(1.0 + 0.1 * _normal((cfg.d,), g, device))
+    return torch.stack(out).to(_DT[cfg.dtype]).contiguous()
+
+
+def kv_biases(cfg: Config, layers, device="cpu"):
+    """(K bias, V bias), each [len(layers)][n_kv_heads * head_dim]."""
+    n_out = cfg.n_kv_heads * cfg.head_dim
+    res = []
+    for which in ("k", "v"):
+        out = []
+        for l in layers:
+            g = stream(cfg.idx, f"bias/{which}/{l}", device)
+            out.append(0.02 * _normal((n_out,), g, device))
+        res.append(torch.stack(out).to(_DT[cfg.dtype]).contiguous())
+    return tuple(res)
+
+
+def rope_base(cfg: Config):
+    return 500000.0 if cfg.idx in (2, 3) else 10000.0
+
+
+def rope_tables(cfg: Config, n_pos, device="cpu"):
+    """(cos, sin), each fp32 [n_pos][head_dim / 2]."""
+    hd = cfg.head_dim
+    inv = rope_base(cfg) ** (-torch.arange(0, hd, 2, dtype=torch.float64) / hd)
+    ang = torch.arange(n_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    return (torch.cos(ang).float().contiguous().to(device),
+            torch.sin(ang).float().contiguous().to(device))
 
 
 def quantize_w4(w, group, sz_dtype):

@@ -127,3 +127,29 @@ def test_exit_projection_argument_errors(kw, status):
     assert _exit_projection(**kw) == status
     if status:
         assert len(tee.load().river_last_error()) > 0
+
+
+def test_kv_fill_layer_argument_errors():
+    lib = tee.load()
+    w = tee.RiverW4(16, 16, 16, tee.RIVER_BF16, 64)
+
+    def call(layer, **k):
+        a = dict(m=8, mdev=None, d=128, dt=tee.RIVER_BF16, h=16, ld=128, nrows=8, ri=None,
+                 slot=16, nl=2, maps=None, wk=ctypes.byref(w), wv=ctypes.byref(w),
+                 lay=None if layer is None else ctypes.byref(layer), hk=2, hd=64, kc=16, vc=16,
+                 ns=8, ws=None, wsn=0, s=None)
+        a.update(k)
+        return lib.river_kv_fill_layer(*a.values())
+
+    L = tee.RiverLayer
+    assert call(None, m=0) == 0                                         # empty call
+    assert call(L(16, 1e-6, None, None, None, None, None, 0)) == 5      # a norm needs a workspace
+    assert call(L(16, math.nan, None, None, None, None, None, 0), ws=16, wsn=1 << 30) == 1
+    assert call(L(None, 0.0, None, None, 16, None, 16, 64)) == 1        # rotation without cos
+    assert call(L(None, 0.0, None, None, 16, 16, 16, 0)) == 1           # empty tables
+    assert call(L(None, 0.0, None, None, 16, 16, 16, 64), hd=63, hk=2) == 1   # odd head_dim
+    assert call(L(None, 0.0, None, None, 16, 16, 24, 64)) == 3          # misaligned table
+    assert call(L(None, 0.0, 8, None, None, None, None, 0)) == 3        # misaligned bias
+    need = tee.river_workspace_size(tee.OP_KV_FILL_LAYER, 8, 128, 0, 0, 1)
+    assert need >= 8 * 128 * 2 + 2 * 8 * 4
+    assert call(L(16, 1e-6, None, None, None, None, None, 0), ws=16, wsn=need - 1) == 5

@@ -6,7 +6,8 @@ pointers and the current HIP stream to the C interface declared in
 CPU fallback: if the library is not built, ``load()`` raises.
 
 The calls keep the C names: ``river_route``, ``river_compact``,
-``river_exit_projection``, ``river_kv_fill``, ``river_ridge_fit``; plus
+``river_exit_projection``, ``river_kv_fill``, ``river_kv_fill_layer``,
+``river_ridge_fit``; plus
 ``river_workspace_size``.
 """
 
@@ -19,11 +20,12 @@ LIB_PATH = os.path.join(HERE, "libriver.so")
 
 RIVER_F32, RIVER_BF16 = 0, 1
 RULE_TOKEN, RULE_BATCH_MIN = 0, 1
-OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT = 0, 1, 2, 3
+OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT, OP_KV_FILL_LAYER = 0, 1, 2, 3, 4
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_DTYPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED",
           5: "ERR_WORKSPACE", 6: "ERR_NOT_SPD", 7: "ERR_HIP"}
 
-EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fill", "river_ridge_fit",
+EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fill",
+           "river_kv_fill_layer", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
            "river_debug_set_compact_path"]
 
@@ -38,6 +40,13 @@ class RiverError(RuntimeError):
 class RiverW4(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("zero", ctypes.c_void_p),
                 ("sz_dtype", ctypes.c_int), ("group", ctypes.c_int)]
+
+
+class RiverLayer(ctypes.Structure):
+    _fields_ = [("norm_gamma", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("k_bias", ctypes.c_void_p), ("v_bias", ctypes.c_void_p),
+                ("pos", ctypes.c_void_p), ("rope_cos", ctypes.c_void_p),
+                ("rope_sin", ctypes.c_void_p), ("n_pos", ctypes.c_int64)]
 
 
 _lib = None
@@ -66,8 +75,12 @@ def load():
     lib.river_kv_fill.argtypes = [_I, _P, _I, _I, _P, _L, _I, _P, _P, _I, _P,
                                   ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4), _I, _I,
                                   _P, _P, _L, _P, _S, _P]
+    lib.river_kv_fill_layer.argtypes = [_I, _P, _I, _I, _P, _L, _I, _P, _P, _I, _P,
+                                        ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4),
+                                        ctypes.POINTER(RiverLayer), _I, _I, _P, _P, _L, _P, _S, _P]
     lib.river_ridge_fit.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _S, _P]
-    for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill", "river_ridge_fit",
+    for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill",
+              "river_kv_fill_layer", "river_ridge_fit",
               "river_debug_set_compact_path"):
         getattr(lib, f).restype = _I
     lib.river_debug_set_compact_path.argtypes = [_I]
@@ -184,6 +197,29 @@ def river_kv_fill(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, *, m_
                                 ctypes.byref(dk), ctypes.byref(dv), n_kv_heads, head_dim,
                                 _ptr(k_cache), _ptr(v_cache), k_cache.shape[1], _ptr(workspace),
                                 ws_n, _stream(stream)))
+
+
+def river_kv_fill_layer(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, *, m_max=None,
+                        m_dev=None, row_idx=None, maps=None, norm_gamma=None, norm_eps=1e-6,
+                        k_bias=None, v_bias=None, pos=None, rope_cos=None, rope_sin=None,
+                        workspace=None, stream=None):
+    """river_kv_fill through the layer's input RMSNorm, K/V bias and the
+    rotary embedding of K (each off when its tensor is None)."""
+    n_rows, d = h.shape
+    n_layers = wk[0].shape[0]
+    if m_max is None:
+        m_max = row_idx.shape[0] if row_idx is not None else n_rows
+    dk = w4(*wk)
+    dv = w4(*wv)
+    lay = RiverLayer(_ptr(norm_gamma), norm_eps, _ptr(k_bias), _ptr(v_bias), _ptr(pos),
+                     _ptr(rope_cos), _ptr(rope_sin),
+                     rope_cos.shape[0] if rope_cos is not None else 0)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().river_kv_fill_layer(m_max, _ptr(m_dev), d, _dt(h), _ptr(h), _ld(h), n_rows,
+                                      _ptr(row_idx), _ptr(slot), n_layers, _ptr(maps),
+                                      ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(lay),
+                                      n_kv_heads, head_dim, _ptr(k_cache), _ptr(v_cache),
+                                      k_cache.shape[1], _ptr(workspace), ws_n, _stream(stream)))
 
 
 def river_ridge_fit(X, Y, lam, W, *, workspace=None, stream=None):

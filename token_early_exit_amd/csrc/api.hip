@@ -67,6 +67,9 @@ size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int 
     case RIVER_OP_KV_FILL:
       if (n <= 0 || d <= 0 || n_layers <= 0) return 0;
       return kv_fill_workspace(n, d, n_layers, RIVER_BF16);
+    case RIVER_OP_KV_FILL_LAYER:
+      if (n <= 0 || d <= 0 || n_layers <= 0) return 0;
+      return kv_fill_layer_workspace(n, d, n_layers);
     case RIVER_OP_RIDGE_FIT:
       if (n <= 0 || d <= 0 || d_out <= 0) return 0;
       return ridge_workspace(n, d, d_out, n_layers == RIVER_F32 ? RIVER_F32 : RIVER_BF16);
@@ -158,39 +161,77 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
                                 out, ld_out, n_out_rows, s);
 }
 
+static river_status kv_fill_checked(const char* who, int m_max, const int32_t* m_dev, int d,
+                                    river_dtype dt, const void* h, int64_t ld_h, int n_rows,
+                                    const int32_t* row_idx, const int32_t* slot, int n_layers,
+                                    const void* maps, const river_w4* wk, const river_w4* wv,
+                                    const river_layer* L, int n_kv_heads, int head_dim,
+                                    void* k_cache, void* v_cache, int64_t n_slots, void* workspace,
+                                    size_t ws_bytes, hipStream_t s) {
+  g_err[0] = 0;
+  if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "%s: dtype %d is not RIVER_F32 or RIVER_BF16", who, (int)dt);
+  if (m_max < 0 || n_layers < 0 || n_rows < 0) return fail(RIVER_ERR_ARG, "%s: negative size", who);
+  if (m_max == 0 || n_layers == 0) return RIVER_OK;
+  if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "%s: d = %d must be a positive multiple of 8", who, d);
+  if (n_kv_heads < 1 || head_dim < 1) return fail(RIVER_ERR_ARG, "%s: n_kv_heads and head_dim must be >= 1", who);
+  if (!h || !slot || !wk || !wv || !k_cache || !v_cache) return fail(RIVER_ERR_ARG, "%s: a required pointer is NULL", who);
+  if (!row_idx && m_max > n_rows) return fail(RIVER_ERR_ARG, "%s: m_max = %d > n_rows = %d without row_idx", who, m_max, n_rows);
+  if (n_slots < 1) return fail(RIVER_ERR_ARG, "%s: n_slots must be >= 1", who);
+  if (!ld_ok(ld_h, d, dt) || !aligned16(h)) return fail(RIVER_ERR_ALIGN, "%s: h misaligned or ld_h invalid", who);
+  for (const river_w4* w : {wk, wv}) {
+    if (!w->q || !w->scale || !w->zero) return fail(RIVER_ERR_ARG, "%s: int4 descriptor has a NULL pointer", who);
+    if (!dt_ok(w->sz_dtype)) return fail(RIVER_ERR_DTYPE, "%s: scale/zero dtype %d unsupported", who, (int)w->sz_dtype);
+    if (w->group < 2 || d % w->group || w->group % 2) return fail(RIVER_ERR_ARG, "%s: group %d must be even and divide d", who, w->group);
+    if (!aligned16(w->q)) return fail(RIVER_ERR_ALIGN, "%s: int4 weights must be 16-byte aligned", who);
+  }
+  if ((int64_t)n_kv_heads * head_dim > (1 << 24)) return fail(RIVER_ERR_ARG, "%s: n_kv_heads * head_dim too large", who);
+  if (n_layers > 65535) return fail(RIVER_ERR_UNSUPPORTED, "%s: at most 65535 layers per call", who);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || (maps && !aligned16(maps)))
+    return fail(RIVER_ERR_ALIGN, "%s: caches and maps must be 16-byte aligned", who);
+  const bool norm = L && L->norm_gamma;
+  if (L) {
+    if (norm && (!(L->norm_eps >= 0.0f) || isinf(L->norm_eps)))
+      return fail(RIVER_ERR_ARG, "%s: norm_eps must be finite and >= 0", who);
+    if ((L->norm_gamma && !aligned16(L->norm_gamma)) || (L->k_bias && !aligned16(L->k_bias)) ||
+        (L->v_bias && !aligned16(L->v_bias)))
+      return fail(RIVER_ERR_ALIGN, "%s: norm weight and biases must be 16-byte aligned", who);
+    if (L->pos) {
+      if (!L->rope_cos || !L->rope_sin || L->n_pos < 1)
+        return fail(RIVER_ERR_ARG, "%s: rotation needs rope_cos, rope_sin and n_pos >= 1", who);
+      if (head_dim % 2) return fail(RIVER_ERR_ARG, "%s: rotation needs an even head_dim", who);
+      if (!aligned16(L->rope_cos) || !aligned16(L->rope_sin))
+        return fail(RIVER_ERR_ALIGN, "%s: rotary tables must be 16-byte aligned", who);
+    }
+  }
+  if (maps || norm) {
+    const size_t need = L ? kv_fill_layer_workspace(m_max, d, 1) : kv_fill_workspace(m_max, d, 1, dt);
+    if (!workspace || ws_bytes < need)
+      return fail(RIVER_ERR_WORKSPACE, "%s: at least %zu workspace bytes needed, %zu given", who, need, ws_bytes);
+    if (!aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
+  }
+  return launch_kv_fill(m_max, m_dev, d, dt, h, ld_h, n_rows, row_idx, slot, n_layers, maps, wk, wv,
+                        L, n_kv_heads, head_dim, k_cache, v_cache, n_slots, workspace, ws_bytes, s);
+}
+
 river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
                            int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
                            int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
                            int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
                            int64_t n_slots, void* workspace, size_t ws_bytes, hipStream_t s) {
-  g_err[0] = 0;
-  if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "kv_fill: dtype %d is not RIVER_F32 or RIVER_BF16", (int)dt);
-  if (m_max < 0 || n_layers < 0 || n_rows < 0) return fail(RIVER_ERR_ARG, "kv_fill: negative size");
-  if (m_max == 0 || n_layers == 0) return RIVER_OK;
-  if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "kv_fill: d = %d must be a positive multiple of 8", d);
-  if (n_kv_heads < 1 || head_dim < 1) return fail(RIVER_ERR_ARG, "kv_fill: n_kv_heads and head_dim must be >= 1");
-  if (!h || !slot || !wk || !wv || !k_cache || !v_cache) return fail(RIVER_ERR_ARG, "kv_fill: a required pointer is NULL");
-  if (!row_idx && m_max > n_rows) return fail(RIVER_ERR_ARG, "kv_fill: m_max = %d > n_rows = %d without row_idx", m_max, n_rows);
-  if (n_slots < 1) return fail(RIVER_ERR_ARG, "kv_fill: n_slots must be >= 1");
-  if (!ld_ok(ld_h, d, dt) || !aligned16(h)) return fail(RIVER_ERR_ALIGN, "kv_fill: h misaligned or ld_h invalid");
-  for (const river_w4* w : {wk, wv}) {
-    if (!w->q || !w->scale || !w->zero) return fail(RIVER_ERR_ARG, "kv_fill: int4 descriptor has a NULL pointer");
-    if (!dt_ok(w->sz_dtype)) return fail(RIVER_ERR_DTYPE, "kv_fill: scale/zero dtype %d unsupported", (int)w->sz_dtype);
-    if (w->group < 2 || d % w->group || w->group % 2) return fail(RIVER_ERR_ARG, "kv_fill: group %d must be even and divide d", w->group);
-    if (!aligned16(w->q)) return fail(RIVER_ERR_ALIGN, "kv_fill: int4 weights must be 16-byte aligned");
-  }
-  if ((int64_t)n_kv_heads * head_dim > (1 << 24)) return fail(RIVER_ERR_ARG, "kv_fill: n_kv_heads * head_dim too large");
-  if (n_layers > 65535) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: at most 65535 layers per call");
-  if (!aligned16(k_cache) || !aligned16(v_cache) || (maps && !aligned16(maps)))
-    return fail(RIVER_ERR_ALIGN, "kv_fill: caches and maps must be 16-byte aligned");
-  if (maps) {
-    size_t need = kv_fill_workspace(m_max, d, 1, dt);
-    if (!workspace || ws_bytes < need)
-      return fail(RIVER_ERR_WORKSPACE, "kv_fill: at least %zu workspace bytes needed with maps, %zu given", need, ws_bytes);
-    if (!aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "kv_fill: workspace must be 16-byte aligned");
-  }
-  return launch_kv_fill(m_max, m_dev, d, dt, h, ld_h, n_rows, row_idx, slot, n_layers, maps, wk, wv,
-                        n_kv_heads, head_dim, k_cache, v_cache, n_slots, workspace, ws_bytes, s);
+  return kv_fill_checked("kv_fill", m_max, m_dev, d, dt, h, ld_h, n_rows, row_idx, slot, n_layers,
+                         maps, wk, wv, nullptr, n_kv_heads, head_dim, k_cache, v_cache, n_slots,
+                         workspace, ws_bytes, s);
+}
+
+river_status river_kv_fill_layer(int m_max, const int32_t* m_dev, int d, river_dtype dt,
+                                 const void* h, int64_t ld_h, int n_rows, const int32_t* row_idx,
+                                 const int32_t* slot, int n_layers, const void* maps,
+                                 const river_w4* wk, const river_w4* wv, const river_layer* layer,
+                                 int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
+                                 int64_t n_slots, void* workspace, size_t ws_bytes, hipStream_t s) {
+  return kv_fill_checked("kv_fill_layer", m_max, m_dev, d, dt, h, ld_h, n_rows, row_idx, slot,
+                         n_layers, maps, wk, wv, layer, n_kv_heads, head_dim, k_cache, v_cache,
+                         n_slots, workspace, ws_bytes, s);
 }
 
 river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,

@@ -172,11 +172,13 @@ river_status launch_exit_projection(int m_max, const int32_t* m_dev, int d, rive
                                     int64_t n_out_rows, hipStream_t s);
 
 size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt);
+size_t kv_fill_layer_workspace(int m_max, int d, int n_layers);
 river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
                             int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
                             int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
-                            int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
-                            int64_t n_slots, void* workspace, size_t ws_bytes, hipStream_t s);
+                            const river_layer* layer, int n_kv_heads, int head_dim, void* k_cache,
+                            void* v_cache, int64_t n_slots, void* workspace, size_t ws_bytes,
+                            hipStream_t s);
 
 size_t ridge_workspace(int n, int d_in, int d_out, river_dtype dt);
 river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,

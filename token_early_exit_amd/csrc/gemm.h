@@ -30,7 +30,10 @@
 
 namespace river {
 
-enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_CACHE = 2 };
+// EPI_BF16N: bf16 output scaled by gamma[col], plus per-row partial sums
+// of squares of the unscaled result (one per 64-column block): the input
+// of a skipped layer's RMSNorm, applied in the K/V projection's epilogue.
+enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_CACHE = 2, EPI_BF16N = 3 };
 
 struct GemmArgs {
   int M_max;
@@ -52,6 +55,17 @@ struct GemmArgs {
   const int32_t* e_rows;     // slot row of output row t (NULL: t)
   const int32_t* slot; int64_t n_slots; int e_nrows;
   void* kc; void* vc; int64_t cache_bstride;   // elements per layer
+  // EPI_BF16N: gamma [z][N] (bf16), partial sums ss[z][M_max][N / 64]
+  const uint16_t* gamma; int64_t gamma_bstride;
+  float* ss; int64_t ss_bstride;
+  // K/V projection with the rest of the layer's K/V path (w4gemm.h):
+  // row scale 1 / sqrt(sum_p ss_in[z][t][p] / K + eps) when ss_in is set
+  // (ss_parts a multiple of 4, at most 128),
+  // bias[which][z][col] (bf16) when set, rotary embedding of the K half
+  // when pos is set (tables [n_pos][head_dim / 2] fp32, pos per e_row)
+  const float* ss_in; int64_t ss_in_bstride; int ss_parts; float norm_eps;
+  const uint16_t* bias[2]; int64_t bias_bstride;
+  const int32_t* pos; const float* rcos; const float* rsin; int64_t n_pos; int head_dim;
 };
 
 __device__ __forceinline__ float load_sz(const void* p, int64_t i, int bf16) {
@@ -94,7 +108,7 @@ constexpr int N_CU = 256;
 
 template <int BM, int EPI>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, int batch) {
-  static_assert(EPI == EPI_BF16 || EPI == EPI_F32, "bf16 or fp32 output");
+  static_assert(EPI == EPI_BF16 || EPI == EPI_F32 || EPI == EPI_BF16N, "bf16 or fp32 output");
   constexpr int BN = 128;
   constexpr int MI = BM / 64;            // 32-row fragments per wave
   constexpr int NI = 2;                  // 32-column fragments per wave
@@ -272,6 +286,31 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
       constexpr int EP = (64 * ES + 16) / 4;          // row pitch in dwords (padded)
       constexpr int LPR = 64 * ES / 16;               // lanes per row: 8 (bf16) or 16 (f32)
       uint32_t* ep = (uint32_t*)(wave == 0 ? S0 : wave == 1 ? S1 : wave == 2 ? S2 : S3);
+      [[maybe_unused]] uint2 gam[NI][4];
+      if constexpr (EPI == EPI_BF16N) {
+        // gamma of this lane's columns (four consecutive per group)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = n0 + wn * 64 + ni * 32 + 8 * gq + 4 * h;
+            gam[ni][gq] = col < N ? *(const uint2*)(g.gamma + (int64_t)z * g.gamma_bstride + col)
+                                  : uint2{0u, 0u};
+          }
+        // partial sums of squares of this wave's 64 columns, per row
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          float ss = 0.f;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) ss = fmaf(acc[mi][ni][e], acc[mi][ni][e], ss);
+          ss += __shfl_xor(ss, 32, 64);          // the row's other 32 columns
+          const int row = m0 + wm * (BM / 2) + mi * 32 + (lane & 31);
+          if (h == 0 && row < M)
+            g.ss[(int64_t)z * g.ss_bstride + (int64_t)row * (N >> 6) + (n0 >> 6) + wn] = ss;
+        }
+      }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -279,8 +318,14 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq) {
             const int r = mi * 32 + (lane & 31), c = ni * 32 + 8 * gq + 4 * h;
-            const f32x4 v = {acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1], acc[mi][ni][4 * gq + 2],
-                             acc[mi][ni][4 * gq + 3]};
+            f32x4 v = {acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1], acc[mi][ni][4 * gq + 2],
+                       acc[mi][ni][4 * gq + 3]};
+            if constexpr (EPI == EPI_BF16N) {
+              v[0] *= bf16_lo(gam[ni][gq].x);
+              v[1] *= bf16_hi(gam[ni][gq].x);
+              v[2] *= bf16_lo(gam[ni][gq].y);
+              v[3] *= bf16_hi(gam[ni][gq].y);
+            }
             if constexpr (EPI == EPI_F32) {
               *(f32x4*)(ep + r * EP + c) = v;
             } else {

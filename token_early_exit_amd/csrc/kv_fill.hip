@@ -18,6 +18,13 @@
 //
 // Generic path (fp32, or shapes the MFMA tiles do not take): one workgroup
 // per (token, layer), fp32 throughout.
+//
+// river_kv_fill_layer adds the rest of the skipped layer's K/V path: its
+// input RMSNorm (gamma_l), K/V biases and the rotary embedding of K. On the
+// MFMA path the map GEMM multiplies x_hat by gamma_l before rounding it and
+// leaves per-row partial sums of squares (or, without maps, a row kernel
+// writes gamma_l * h and the row sums); the projection's epilogue applies the
+// row scale, the bias and the rotation to its fp32 accumulators.
 #include "common.h"
 #include "gemm.h"
 #include "w4gemm.h"
@@ -32,13 +39,19 @@ struct FillGeneric {
   const uint8_t* q[2]; const void* s[2]; const void* zp[2]; int group[2]; int sz_bf16[2];
   int nh; int64_t n_slots;
   void* kc; void* vc;
+  // the layer's K/V path (all optional)
+  const void* gamma; float eps;              // dt [n_layers][d]
+  const void* bias[2];                       // dt [n_layers][nh]
+  const int32_t* pos; const float* rcos; const float* rsin; int64_t n_pos; int head_dim;
 };
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void kv_fill_generic_kernel(FillGeneric a) {
-  extern __shared__ float sm[];   // x [d], x_hat [d]
+  extern __shared__ float sm[];   // x [d], x_hat [d], outputs [2 nh], partial sums [4]
   float* x = sm;
   float* xh = sm + a.d;
+  float* ko = sm + 2 * a.d;
+  float* red = ko + 2 * a.nh;
   int m = a.m_max;
   if (a.m_dev) {
     const int md = *a.m_dev;
@@ -50,6 +63,8 @@ __global__ __launch_bounds__(256) void kv_fill_generic_kernel(FillGeneric a) {
   if (r < 0 || r >= a.n_rows) return;
   const int sl = a.slot[r];
   if (sl < 0 || sl >= a.n_slots) return;
+  const int p = a.pos ? a.pos[r] : 0;
+  if (a.pos && (p < 0 || p >= a.n_pos)) return;
   const int d = a.d;
   for (int k = threadIdx.x; k < d; k += blockDim.x) x[k] = load_elem<BF16>(a.h, (int64_t)r * a.ld_h + k);
   __syncthreads();
@@ -64,6 +79,17 @@ __global__ __launch_bounds__(256) void kv_fill_generic_kernel(FillGeneric a) {
     for (int k = threadIdx.x; k < d; k += blockDim.x) xh[k] = x[k];
   }
   __syncthreads();
+  if (a.gamma) {   // the layer's input RMSNorm
+    float ss = 0.f;
+    for (int k = threadIdx.x; k < d; k += blockDim.x) ss = fmaf(xh[k], xh[k], ss);
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float rs = rsqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + a.eps);
+    for (int k = threadIdx.x; k < d; k += blockDim.x)
+      xh[k] = xh[k] * rs * load_elem<BF16>(a.gamma, (int64_t)l * d + k);
+    __syncthreads();
+  }
   for (int o = threadIdx.x; o < 2 * a.nh; o += blockDim.x) {
     const int which = o >= a.nh ? 1 : 0;
     const int row = o - which * a.nh;
@@ -79,9 +105,67 @@ __global__ __launch_bounds__(256) void kv_fill_generic_kernel(FillGeneric a) {
       acc = fmaf(((float)(byte & 15) - ze) * sc, xh[k], acc);
       acc = fmaf(((float)(byte >> 4) - ze) * sc, xh[k + 1], acc);
     }
+    if (a.bias[which]) acc += load_elem<BF16>(a.bias[which], (int64_t)l * a.nh + row);
+    ko[o] = acc;
+  }
+  __syncthreads();
+  for (int o = threadIdx.x; o < 2 * a.nh; o += blockDim.x) {
+    const int which = o >= a.nh ? 1 : 0;
+    const int row = o - which * a.nh;
+    float v = ko[o];
+    if (a.pos && which == 0) {   // rotary embedding of K, half-split pairs per head
+      const int hd = a.head_dim, half = hd >> 1;
+      const int i = row % hd;
+      const int f = i < half ? i : i - half;
+      const float c = a.rcos[(int64_t)p * half + f], sn = a.rsin[(int64_t)p * half + f];
+      v = i < half ? ko[o] * c - ko[o + half] * sn : ko[o - half] * sn + ko[o] * c;
+    }
     const int64_t off = ((int64_t)l * a.n_slots + sl) * a.nh + row;
-    if (BF16) ((uint16_t*)(which ? a.vc : a.kc))[off] = f32_to_bf16(acc);
-    else ((float*)(which ? a.vc : a.kc))[off] = acc;
+    if (BF16) ((uint16_t*)(which ? a.vc : a.kc))[off] = f32_to_bf16(v);
+    else ((float*)(which ? a.vc : a.kc))[off] = v;
+  }
+}
+
+// gamma_l * h[row] for every layer of a chunk (bf16) and the row's sum of
+// squares (as four partial sums, the last three zero): the input of the
+// projection when the map is the identity and the layer has an input
+// RMSNorm. One wave per (row t < m, layer): grid (ceil(m_max / 4), layers);
+// the row is read once per layer (from L2 after the first), 16 bytes per
+// lane, and layer 0 also writes the row's sum.
+__global__ __launch_bounds__(256) void norm_rows_kernel(int m_max, const int32_t* __restrict__ m_dev, int d,
+                                                        const uint16_t* __restrict__ h, int64_t ld_h,
+                                                        int n_rows, const int32_t* __restrict__ row_idx,
+                                                        const uint16_t* __restrict__ gamma,
+                                                        uint16_t* __restrict__ xh, int64_t xh_bstride,
+                                                        float* __restrict__ ss) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+  const int lane = threadIdx.x % WAVE;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  const int z = blockIdx.y;
+  if (t >= m_max) return;
+  const int m_in = m_dev ? *m_dev : m_max;
+  const int r = row_idx ? row_idx[t] : (int)t;
+  if (t >= min(max(m_in, 0), m_max) || r < 0 || r >= n_rows) return;
+  const int nch = d / 8;
+  const u32x4* src = (const u32x4*)(h + (int64_t)r * ld_h);
+  const u32x4* gz = (const u32x4*)(gamma + (int64_t)z * d);
+  u32x4* dst = (u32x4*)(xh + (int64_t)z * xh_bstride + t * d);
+  float a = 0.f;
+  for (int c = lane; c < nch; c += WAVE) {
+    const u32x4 v = src[c], gw = gz[c];
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = bf16_lo(v[i]), hi = bf16_hi(v[i]);
+      a = fmaf(lo, lo, a);
+      a = fmaf(hi, hi, a);
+      o[i] = pack_bf16x2(lo * bf16_lo(gw[i]), hi * bf16_hi(gw[i]));
+    }
+    dst[c] = o;
+  }
+  if (z == 0) {
+    a = wave_sum(a);
+    if (lane == 0) *(f32x4*)(ss + 4 * t) = f32x4{a, 0.f, 0.f, 0.f};   // four partials, as the map GEMM leaves
   }
 }
 
@@ -108,20 +192,40 @@ size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt) {
   return align_up((size_t)n_layers * (size_t)m_max * (size_t)d * esize(dt), 256);
 }
 
+// per layer of a chunk: x_hat (bf16 [m_max][d]) and, with an input norm, the
+// partial sums of squares (fp32 [d / 64][m_max])
+static size_t layer_xhat_bytes(int m_max, int d) { return align_up((size_t)m_max * d * 2, 256); }
+static size_t layer_ss_bytes(int m_max, int d) { return align_up((size_t)(d / 64 > 4 ? d / 64 : 4) * m_max * 4, 256); }
+
+size_t kv_fill_layer_workspace(int m_max, int d, int n_layers) {
+  return (size_t)n_layers * (layer_xhat_bytes(m_max, d) + layer_ss_bytes(m_max, d));
+}
+
 river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
                             int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
                             int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
-                            int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
-                            int64_t n_slots, void* workspace, size_t ws_bytes, hipStream_t s) {
+                            const river_layer* L, int n_kv_heads, int head_dim, void* k_cache,
+                            void* v_cache, int64_t n_slots, void* workspace, size_t ws_bytes,
+                            hipStream_t s) {
   const int nh = n_kv_heads * head_dim;
-  if (!fill_mfma_ok(d, dt, nh, wk, wv, (int64_t)n_rows * ld_h * 2, (int64_t)m_max * d * 2)) {
-    const size_t lds = 2 * (size_t)d * sizeof(float);
-    if (lds > 65536) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: d = %d too large for the generic path", d);
+  const void* gamma = L ? L->norm_gamma : nullptr;
+  const bool has_bias = L && (L->k_bias || L->v_bias);
+  const bool rope = L && L->pos;
+  const bool layer = gamma || has_bias || rope;
+  const bool mfma = fill_mfma_ok(d, dt, nh, wk, wv, (int64_t)n_rows * ld_h * 2, (int64_t)m_max * d * 2) &&
+                    (!rope || head_dim % 32 == 0) && (!gamma || d <= 8192);
+  if (!mfma) {
+    const size_t lds = (2 * (size_t)d + 2 * (size_t)nh + 4) * sizeof(float);
+    if (lds > 65536) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: d = %d, n_out = %d too large for the generic path", d, nh);
     FillGeneric a{m_max, m_dev, d, h, ld_h, n_rows, row_idx, slot, maps,
                   {wk->q, wv->q}, {wk->scale, wv->scale}, {wk->zero, wv->zero},
                   {wk->group, wv->group},
                   {wk->sz_dtype == RIVER_BF16, wv->sz_dtype == RIVER_BF16}, nh, n_slots,
-                  k_cache, v_cache};
+                  k_cache, v_cache,
+                  gamma, L ? L->norm_eps : 0.f,
+                  {L ? L->k_bias : nullptr, L ? L->v_bias : nullptr},
+                  rope ? L->pos : nullptr, rope ? L->rope_cos : nullptr,
+                  rope ? L->rope_sin : nullptr, rope ? L->n_pos : 0, head_dim};
     dim3 grid(m_max, n_layers);
     if (dt == RIVER_BF16) kv_fill_generic_kernel<true><<<grid, 256, lds, s>>>(a);
     else kv_fill_generic_kernel<false><<<grid, 256, lds, s>>>(a);
@@ -145,10 +249,16 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
   g.n_slots = n_slots;
   g.e_nrows = n_rows;
   g.cache_bstride = n_slots * nh;
+  if (rope) {
+    g.pos = L->pos; g.rcos = L->rope_cos; g.rsin = L->rope_sin; g.n_pos = L->n_pos;
+    g.head_dim = head_dim;
+  }
 
-
+  // ss: partial sums of squares of this chunk's rows (parts per row, layer
+  // stride ss_bs; 0 when every layer shares one input)
   auto stage2 = [&](int l0, int nl, const uint16_t* A, int64_t lda, int64_t a_bs,
-                    const int32_t* a_rows, int a_nrows) -> river_status {
+                    const int32_t* a_rows, int a_nrows, const float* ss, int64_t ss_bs,
+                    int parts) -> river_status {
     GemmArgs q = g;
     q.N = 2 * nh;
     q.A = A; q.lda = lda; q.a_bstride = a_bs; q.a_rows = a_rows; q.a_nrows = a_nrows;
@@ -161,27 +271,52 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.e_rows = row_idx;
     q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
-    w4_gemm_auto<EPI_CACHE>(q, nl, s);
+    if (!layer) {
+      w4_gemm_auto<EPI_CACHE>(q, nl, s);
+      return check_launch("kv_fill projection");
+    }
+    q.ss_in = ss; q.ss_in_bstride = ss_bs; q.ss_parts = parts; q.norm_eps = L->norm_eps;
+    q.bias[0] = L->k_bias ? (const uint16_t*)L->k_bias + (int64_t)l0 * nh : nullptr;
+    q.bias[1] = L->v_bias ? (const uint16_t*)L->v_bias + (int64_t)l0 * nh : nullptr;
+    q.bias_bstride = nh;
+    w4_gemm_auto<EPI_CACHE, true>(q, nl, s);
     return check_launch("kv_fill projection");
   };
 
-  if (!maps) return stage2(0, n_layers, (const uint16_t*)h, ld_h, 0, row_idx, n_rows);
+  if (!maps && !gamma) return stage2(0, n_layers, (const uint16_t*)h, ld_h, 0, row_idx, n_rows, nullptr, 0, 0);
 
-  const size_t per_layer = (size_t)m_max * d * 2;
-  int chunk = (int)(ws_bytes / per_layer);
+  const size_t xb = layer_xhat_bytes(m_max, d), sb = gamma ? layer_ss_bytes(m_max, d) : 0;
+  int chunk = (int)(ws_bytes / (xb + sb));
   if (chunk > n_layers) chunk = n_layers;
   uint16_t* xh = (uint16_t*)workspace;
+  float* ss = (float*)((char*)workspace + (size_t)chunk * xb);
+  const int parts = maps ? d / 64 : 4;
   for (int l0 = 0; l0 < n_layers; l0 += chunk) {
     const int nl = n_layers - l0 < chunk ? n_layers - l0 : chunk;
-    GemmArgs p = g;
-    p.N = d;
-    p.A = (const uint16_t*)h; p.lda = ld_h; p.a_bstride = 0; p.a_rows = row_idx; p.a_nrows = n_rows;
-    p.B = (const uint16_t*)maps + (int64_t)l0 * d * d; p.ldb = d; p.b_bstride = (int64_t)d * d;
-    p.C = xh; p.ldc = d; p.c_bstride = (int64_t)m_max * d;
-    gemm_auto<EPI_BF16>(p, nl, s);
-    river_status st = check_launch("kv_fill map");
+    river_status st;
+    if (maps) {
+      GemmArgs p = g;
+      p.N = d;
+      p.A = (const uint16_t*)h; p.lda = ld_h; p.a_bstride = 0; p.a_rows = row_idx; p.a_nrows = n_rows;
+      p.B = (const uint16_t*)maps + (int64_t)l0 * d * d; p.ldb = d; p.b_bstride = (int64_t)d * d;
+      p.C = xh; p.ldc = d; p.c_bstride = xb / 2;
+      if (gamma) {
+        p.gamma = (const uint16_t*)gamma + (int64_t)l0 * d; p.gamma_bstride = d;
+        p.ss = ss; p.ss_bstride = sb / 4;
+        gemm_auto<EPI_BF16N>(p, nl, s);
+      } else {
+        gemm_auto<EPI_BF16>(p, nl, s);
+      }
+      st = check_launch("kv_fill map");
+    } else {
+      const dim3 grid((unsigned)(((int64_t)m_max + 3) / 4), (unsigned)nl);
+      norm_rows_kernel<<<grid, 256, 0, s>>>(m_max, m_dev, d, (const uint16_t*)h, ld_h, n_rows, row_idx,
+                                            (const uint16_t*)gamma + (int64_t)l0 * d, xh, xb / 2, ss);
+      st = check_launch("kv_fill norm rows");
+    }
     if (st != RIVER_OK) return st;
-    st = stage2(l0, nl, xh, d, (int64_t)m_max * d, nullptr, m_max);
+    st = stage2(l0, nl, xh, d, xb / 2, nullptr, m_max, gamma ? ss : nullptr,
+                maps ? (int64_t)(sb / 4) : 0, parts);
     if (st != RIVER_OK) return st;
   }
   return RIVER_OK;

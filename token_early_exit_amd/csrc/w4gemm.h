@@ -26,6 +26,14 @@
 // the binding cost: about 5 vector instructions hide behind one MFMA), 16 KB
 // of A and 12 KB of weight staging written to LDS and 8 x 16 KB of A
 // fragments read from it, 28 KB from L2.
+//
+// LAYER adds the rest of a layer's K/V path to the cache epilogue, on the
+// fp32 accumulators: the input RMSNorm's row scale (from per-row partial
+// sums of squares of the layer input), the K/V bias, and the rotary
+// embedding of K. For the rotation each wave computes, instead of 32
+// consecutive output channels, the 16 channels o0 .. o0 + 15 of one head and
+// their partners o0 + hd/2 .. o0 + hd/2 + 15, so that both elements of every
+// rotated pair sit in the same lane (accumulator groups gq and gq + 2).
 #pragma once
 
 #include <type_traits>
@@ -35,8 +43,122 @@
 
 namespace river {
 
-template <int BM, int EPI, bool SZ_BF16, int NW>
+// The rest of a layer's K/V path on the fp32 accumulators of one wave
+// (32 columns, MI fragments of 32 rows): lane l holds row mi * 32 + l % 32
+// and, per group gq, the four consecutive wave columns 8 gq + 4 (l / 32) + i.
+//   v = acc * r_row + bias[chan]                 (r_row = 1 without a norm)
+//   K only, with rotation: for gq < 2 the pair (v[gq][i], v[gq + 2][i]) of
+//   channels (o0 + j, hd/2 + o0 + j), j = 8 gq + 4 (l / 32) + i, turns by the
+//   table angle of frequency o0 + j at the row's position.
+// The row sums of squares are reduced by the whole workgroup into rsum (RG
+// partial sums per row, added in a fixed order), so every wave of the
+// workgroup calls this. A row whose position is outside the table gets
+// slot -1 (not written).
+template <int MI, int BM, int RG, int RCH, int RJ, typename Chan>
+__device__ __forceinline__ void layer_epilogue(const GemmArgs& g, f32x16 (&acc)[MI][1], int z, int m0,
+                                               int M_max, int K, int which, bool cols_ok, int tid,
+                                               int lane, int h, bool rope, int o0, int half,
+                                               float* rsum, Chan chan, const int (&ps)[RJ],
+                                               int (&sl)[RJ]) {
+  const bool rot = rope && which == 0 && cols_ok;
+  // the rotary tables of this lane's rows and the bias of its 16 channels
+  // go out first; the row sums' loads follow, and their first wait covers
+  // every load, so they share one latency
+  f32x4 c[MI][2], s[MI][2];
+  if (rot) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int rr = mi * 32;                    // rows mi * 32 + l % 32 sit in register rr / 64
+      const int p = __shfl(ps[rr / 64], rr % 64 + (lane & 31), 64);
+      const bool pok = p >= 0 && p < g.n_pos;
+      const int64_t base = (int64_t)(pok ? p : 0) * half + o0 + 4 * h;
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq) {
+        c[mi][gq] = *(const f32x4*)(g.rcos + base + 8 * gq);
+        s[mi][gq] = *(const f32x4*)(g.rsin + base + 8 * gq);
+      }
+    }
+  }
+  uint2 bw[4];
+  const uint16_t* bp = g.bias[which];
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq)
+    bw[gq] = (bp && cols_ok) ? *(const uint2*)(bp + (int64_t)z * g.bias_bstride + chan(8 * gq + 4 * h))
+                             : uint2{0u, 0u};
+  // partial sums of the tile's rows: RG threads per row, RCH 16-byte chunks
+  // per thread and round (one round for d <= 64 * 4 * RG * RCH)
+  float a = 0.f;
+  if (g.ss_in) {
+    const int rr = tid % BM, rg = tid / BM;
+    int t = m0 + rr;
+    if (t >= M_max) t = 0;                       // rows past the count are never stored
+    const f32x4* src = (const f32x4*)(g.ss_in + (int64_t)z * g.ss_in_bstride + (int64_t)t * g.ss_parts);
+    const int nchk = g.ss_parts >> 2;
+    for (int c0 = 0; c0 < nchk; c0 += RG * RCH) {
+      f32x4 pv[RCH];
+#pragma unroll
+      for (int i = 0; i < RCH; ++i) {
+        const int ci = c0 + rg + i * RG;
+        pv[i] = ci < nchk ? src[ci] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < RCH; ++i) a += (pv[i][0] + pv[i][1]) + (pv[i][2] + pv[i][3]);
+    }
+  }
+  float rs[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) rs[mi] = 1.0f;
+  if (g.ss_in) {
+    rsum[(tid / BM) * BM + tid % BM] = a;
+    __syncthreads();
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = mi * 32 + (lane & 31);
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < RG; ++q) t += rsum[q * BM + r];
+      rs[mi] = rsqrtf(t / (float)K + g.norm_eps);
+    }
+  }
+  float b[4][4];
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) {
+    b[gq][0] = bf16_lo(bw[gq].x); b[gq][1] = bf16_hi(bw[gq].x);
+    b[gq][2] = bf16_lo(bw[gq].y); b[gq][3] = bf16_hi(bw[gq].y);
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    float v[4][4];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[gq][i] = fmaf(acc[mi][0][4 * gq + i], rs[mi], b[gq][i]);
+    if (rot) {
+#pragma unroll
+      for (int gq = 0; gq < 2; ++gq)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = v[gq][i], hi = v[gq + 2][i];
+          v[gq][i] = lo * c[mi][gq][i] - hi * s[mi][gq][i];
+          v[gq + 2][i] = lo * s[mi][gq][i] + hi * c[mi][gq][i];
+        }
+    }
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mi][0][4 * gq + i] = v[gq][i];
+  }
+  // rows whose position is outside the tables are not written
+  if (rope) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j)
+      if (ps[j] < 0 || ps[j] >= g.n_pos) sl[j] = -1;
+  }
+}
+
+template <int BM, int EPI, bool SZ_BF16, int NW, bool LAYER>
 __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_n, int batch) {
+  static_assert(!LAYER || (NW == 8 && EPI == EPI_CACHE), "the layer epilogue takes 32-column waves");
   constexpr int BN = 256;
   constexpr int MI = BM / 32;            // 32-row fragments (all rows of the tile)
   constexpr int NI = 8 / NW;             // 32-column fragments per wave (NW = 4 or 8 waves)
@@ -56,6 +178,12 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
   constexpr int ZOFF = QOFF + NW * NI * 64;
   constexpr int SSZ = ZOFF + NW * 32;
   __shared__ u32x4 S0[SSZ], S1[SSZ], S2[SSZ], S3[SSZ];
+  // LAYER: per-row sums of squares of the tile's input rows, reduced by the
+  // whole workgroup in the epilogue (RG threads per row, RCH 16-byte chunks
+  // of partial sums per thread and round)
+  constexpr int RG = 64 * NW / BM;
+  constexpr int RCH = 4;
+  __shared__ float RSUM[LAYER ? RG * BM : 1];
 
   // kernel arguments used below, read up front
   const int M_max = g.M_max, N = g.N, K = g.K, nh = g.nh, a_nrows = g.a_nrows;
@@ -138,7 +266,27 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     uint32_t q_off[NI];
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) q_off[ni] = (uint32_t)((hc0 + 32 * ni + (lane & 31)) * (K / 2) + h * 16);
-    const uint32_t sz_off = (uint32_t)((hc0 + lane) * gpr * SZB);
+    [[maybe_unused]] const uint32_t sz_off_plain = (uint32_t)((hc0 + lane) * gpr * SZB);
+    // LAYER with rotary embedding: output channel of wave column j (0..31)
+    // is hb + o0 + j for j < 16 and hb + hd/2 + o0 + j - 16 otherwise
+    [[maybe_unused]] const bool rope = LAYER && g.pos != nullptr;
+    [[maybe_unused]] int hb = 0, o0 = 0, half = 0;
+    if constexpr (LAYER) {
+      if (rope) {
+        const int hd = g.head_dim;
+        half = hd >> 1;
+        hb = hc0 / hd * hd;
+        o0 = ((hc0 - hb) >> 5) << 4;
+      }
+    }
+    auto chan = [&](int j) -> int {    // channel (inside the K or V half) of wave column j
+      if constexpr (LAYER) {
+        if (rope) return hb + o0 + (j < 16 ? j : half + j - 16);
+      }
+      return hc0 + j;
+    };
+    if constexpr (LAYER) q_off[0] = (uint32_t)(chan(lane & 31) * (K / 2) + h * 16);
+    const uint32_t sz_off = LAYER ? (uint32_t)(chan(lane & 31) * gpr * SZB) : sz_off_plain;
 
     // every load of K-slab j into LDS stage ST
     auto issue = [&](auto st, int j) {
@@ -231,7 +379,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     // m0 + 64 j + l. The e_rows loads go out before the first slab's (so the
     // first wait covers them), the slot loads right after it.
     constexpr int RJ = BM / 64;
-    [[maybe_unused]] int er[RJ], sl[RJ];
+    [[maybe_unused]] int er[RJ], sl[RJ], ps[RJ];
     if constexpr (EPI == EPI_CACHE) {
 #pragma unroll
       for (int j = 0; j < RJ; ++j) {
@@ -249,6 +397,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
       for (int j = 0; j < RJ; ++j) {
         const bool ok = m0 + 64 * j + lane < M && er[j] >= 0 && er[j] < g.e_nrows;
         sl[j] = ok ? g.slot[er[j]] : -1;          // range-checked where it is used
+        if constexpr (LAYER) ps[j] = (ok && rope) ? g.pos[er[j]] : 0;
       }
     }
     Frag f0, f1;
@@ -315,6 +464,10 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
       constexpr int RPI = 64 / LPR;               // rows per store instruction
       const int sw = wave / (NW / 4), sub = wave % (NW / 4);
       uint16_t* ep = (uint16_t*)(sw == 0 ? S0 : sw == 1 ? S1 : sw == 2 ? S2 : S3) + sub * BM * EP;
+      // (a wave whose columns lie past N reads no bias; its stores are dropped)
+      if constexpr (LAYER)
+        layer_epilogue<MI, BM, RG, RCH>(g, acc, z, m0, M_max, K, which, wc0 < N, tid, lane, h, rope, o0,
+                                        half, RSUM, chan, ps, sl);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -326,9 +479,10 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
                                                pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
           }
       const int ch = lane % LPR;
-      const int col = n0 + CW * wave + 8 * ch;   // 8 columns, all in K or all in V
+      int col = n0 + CW * wave + 8 * ch;         // 8 columns, all in K or all in V
       const bool col_ok = col < N;
       const bool isv = col >= nh;
+      if constexpr (LAYER) col = (isv ? nh : 0) + chan(8 * ch);
 #pragma unroll
       for (int i = 0; i < BM / RPI; ++i) {
         const int r = i * RPI + lane / LPR;
@@ -354,21 +508,21 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
 // W4_WAVES: 4 waves (64 columns each, one per SIMD) or 8 (32 columns each,
 // two per SIMD, which hide each other's latencies).
 constexpr int W4_WAVES = 8;
-template <int BM, int EPI>
+template <int BM, int EPI, bool LAYER>
 inline void w4_gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 255) / 256;
   const int tm = (g.M_max + BM - 1) / BM;
   const int64_t tiles = (int64_t)tn * tm * batch;
   int grid = (int)(tiles < N_CU ? tiles : N_CU);
   grid = (grid + 7) / 8 * 8;
-  if (g.sz_bf16[0]) w4_gemm_kernel<BM, EPI, true, W4_WAVES><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
-  else w4_gemm_kernel<BM, EPI, false, W4_WAVES><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
+  if (g.sz_bf16[0]) w4_gemm_kernel<BM, EPI, true, W4_WAVES, LAYER><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
+  else w4_gemm_kernel<BM, EPI, false, W4_WAVES, LAYER><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
 }
 
-template <int EPI>
+template <int EPI, bool LAYER = false>
 inline void w4_gemm_auto(const GemmArgs& g, int batch, hipStream_t s) {
-  if (g.M_max <= 64) w4_gemm_launch<64, EPI>(g, batch, s);
-  else w4_gemm_launch<128, EPI>(g, batch, s);
+  if (g.M_max <= 64) w4_gemm_launch<64, EPI, LAYER>(g, batch, s);
+  else w4_gemm_launch<128, EPI, LAYER>(g, batch, s);
 }
 
 }  // namespace river
