@@ -36,5 +36,6 @@ from .river_oracle import (  # noqa: F401
     kv_fill_layer_rows,
     rope_half,
     ridge_fit,
+    decode_step,
     exit_schedule_ops,
 )

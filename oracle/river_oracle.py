@@ -339,6 +339,55 @@ def kv_fill(h, row_idx, m, slot, maps, wk, wv, n_kv_heads, head_dim, k_cache, v_
     return kc, vc
 
 
+def decode_step(checkpoints, n_layers, rule, slot, wk, wv, n_kv_heads, head_dim, k_cache,
+                v_cache, gamma=None, eps=1e-6):
+    """One generation step of the token-level exit loop over checkpoints.
+
+    Source: River-LLM, "方法步骤详情" step 3: during generation each token's
+    state climbs the blocks; after block l the state-transition similarity
+    decides whether the token switches to the exit path, which then writes
+    the K/V of every remaining block at that token's slot (step 1). TIDE
+    "模块4" / formula 4 give the per-token decision with a router; River
+    takes the minimum over the batch (``RULE_BATCH_MIN``).
+
+    checkpoints: list, in increasing layer order, of dicts with
+      layer (e, 1 <= e < L), h_prev (h^(e-1), [n][d]), h_cur (h^(e)),
+      tau, theta, w_down / w_up (None: router off), maps (None: identity,
+      else [L - e][d][d]).
+    wk, wv: int4 descriptors of blocks 1..L (``n_layers`` = L layers);
+    caches: [L][n_slots][Hkv][Dh], cache layer j - 1 holding block j.
+
+    Readings taken: a token takes part in a checkpoint only while it has
+    not exited; it exits at the first checkpoint whose decision passes
+    (under the batch rule: every still-running token passes); its exit state
+    is h_cur of that checkpoint and blocks e+1..L are filled from it as in
+    ``kv_fill``. Tokens that never exit get exit layer L.
+    Returns (exit_layer int64 [n], k_cache, v_cache) (caches copied).
+    """
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    n = np.asarray(checkpoints[0]["h_cur"]).shape[0]
+    alive = np.ones(n, dtype=bool)
+    exit_layer = np.full(n, n_layers, dtype=np.int64)
+    for ck in checkpoints:
+        e = int(ck["layer"])
+        _, _, m, _ = route(ck["h_prev"], ck["h_cur"], gamma, eps, ck.get("w_down"),
+                           ck.get("w_up"), ck["tau"], ck["theta"], RULE_TOKEN)
+        dec = (m != 0) & alive
+        if rule == RULE_BATCH_MIN:
+            every = alive.any() and bool(np.all(dec[alive]))
+            dec = alive & every
+        rows = np.flatnonzero(dec)
+        exit_layer[rows] = e
+        alive &= ~dec
+        if len(rows):
+            sub = lambda w: {"q": np.asarray(w["q"])[e:], "scale": np.asarray(w["scale"])[e:],
+                             "zero": np.asarray(w["zero"])[e:], "group": w["group"]}
+            kc[e:], vc[e:] = kv_fill(ck["h_cur"], rows, len(rows), slot, ck.get("maps"), sub(wk),
+                                     sub(wv), n_kv_heads, head_dim, kc[e:], vc[e:])
+    return exit_layer, kc, vc
+
+
 def ridge_fit(X, Y, lam):
     """Closed-form ridge maps, one per target.
 

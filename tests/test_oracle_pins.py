@@ -613,6 +613,90 @@ def test_p13_layer_fill_norm_scale_invariance_and_bias():
                                atol=1e-13, rtol=0)
 
 
+# ------------------------------------------------------- P14 decode step
+
+def _decode_case(rng, rule=O.RULE_TOKEN, router=False):
+    L, d, Hkv, Dh, n, n_slots = 8, 16, 2, 4, 20, 32
+    slot = rng.permutation(n_slots)[:n]
+    wk = _hand_w4(L, Hkv * Dh, d, 8, rng)
+    wv = _hand_w4(L, Hkv * Dh, d, 8, rng)
+    hs = [rng.standard_normal((n, d))]
+    for l in range(1, L + 1):
+        hs.append(hs[-1] + rng.uniform(0.1, 1.2, (n, 1)) * rng.standard_normal((n, d)))
+    cks = []
+    for e in (2, 3, 5, 6):
+        c = {"layer": e, "h_prev": hs[e - 1], "h_cur": hs[e], "tau": 0.55, "theta": -np.inf,
+             "maps": None if e % 2 else np.eye(d)[None] + 0.05 * rng.standard_normal((L - e, d, d))}
+        if router:
+            c["w_down"] = rng.standard_normal((4, d))
+            c["w_up"] = rng.standard_normal(4)
+            c["tau"], c["theta"] = 0.93, 0.5
+        cks.append(c)
+    kc = np.full((L, n_slots, Hkv, Dh), np.nan)
+    return cks, L, slot, wk, wv, Hkv, Dh, kc
+
+
+def test_p14_decode_step_first_passing_checkpoint_and_integrity():
+    rng = np.random.default_rng(31)
+    cks, L, slot, wk, wv, Hkv, Dh, kc = _decode_case(rng, router=True)
+    ex, K, V = O.decode_step(cks, L, O.RULE_TOKEN, slot, wk, wv, Hkv, Dh, kc, kc)
+    n = len(ex)
+    # each token exits at the first checkpoint its own decision passes
+    for i in range(n):
+        first = L
+        for c in cks:
+            cos, prob, _, _ = O.route(c["h_prev"][i:i + 1], c["h_cur"][i:i + 1], None, 1e-6,
+                                      c.get("w_down"), c.get("w_up"), c["tau"], c["theta"])
+            if cos[0] > c["tau"] and prob[0] > c["theta"]:
+                first = c["layer"]
+                break
+        assert ex[i] == first
+    assert 0 < np.sum(ex < L) < n
+    # Intrinsic KV integrity: slot s of cache layer j is written iff its
+    # token exited before block j + 1; the count matches the schedule's
+    filled = ~np.isnan(K).any(axis=(2, 3))
+    for j in range(L):
+        for i in range(n):
+            assert filled[j, slot[i]] == (ex[i] <= j)
+    assert filled.sum() == O.exit_schedule_ops(ex, L)["filled"]
+    assert np.array_equal(filled, ~np.isnan(V).any(axis=(2, 3)))
+
+
+def test_p14_decode_step_one_checkpoint_is_route_compact_fill():
+    rng = np.random.default_rng(32)
+    cks, L, slot, wk, wv, Hkv, Dh, kc = _decode_case(rng)
+    c = cks[1]
+    ex, K, V = O.decode_step([c], L, O.RULE_TOKEN, slot, wk, wv, Hkv, Dh, kc, kc)
+    _, _, m, _ = O.route(c["h_prev"], c["h_cur"], None, 1e-6, None, None, c["tau"], c["theta"])
+    rows = O.compact(m, None)["exit_idx"]
+    e = c["layer"]
+    sub = lambda w: {"q": w["q"][e:], "scale": w["scale"][e:], "zero": w["zero"][e:], "group": 8}
+    k2, v2 = O.kv_fill(c["h_cur"], rows, len(rows), slot, c["maps"], sub(wk), sub(wv), Hkv, Dh,
+                       kc[e:], kc[e:])
+    assert np.array_equal(np.flatnonzero(ex == e), rows)
+    assert np.array_equal(K[e:], k2, equal_nan=True) and np.array_equal(V[e:], v2, equal_nan=True)
+    assert np.isnan(K[:e]).all()
+
+
+def test_p14_decode_step_batch_rule():
+    """Under the batch rule a checkpoint lets every running token exit or
+    none, and it does so exactly when the smallest cosine of the running
+    tokens passes (River-LLM step 3)."""
+    rng = np.random.default_rng(33)
+    cks, L, slot, wk, wv, Hkv, Dh, kc = _decode_case(rng)
+    n = cks[0]["h_cur"].shape[0]
+    # make one checkpoint pass for everybody: a tiny step keeps cos near 1
+    cks[2]["h_cur"] = cks[2]["h_prev"] * 1.0001
+    ex, K, _ = O.decode_step(cks, L, O.RULE_BATCH_MIN, slot, wk, wv, Hkv, Dh, kc, kc)
+    alive = np.ones(n, bool)
+    for c in cks:
+        cos, _, _, _ = O.route(c["h_prev"], c["h_cur"], None, 1e-6, None, None, -np.inf, -np.inf)
+        passes = alive.any() and cos[alive].min() > c["tau"]
+        assert np.array_equal(ex == c["layer"], alive & passes)
+        alive &= ~passes
+    assert np.all(ex == cks[2]["layer"]) or np.all(ex == cks[0]["layer"]) or np.all(ex == cks[1]["layer"])
+
+
 # --------------------------------------------------------- mutation checks
 
 def _mutant_oracle(old, new):
@@ -683,6 +767,12 @@ MUTANTS = [
      "test_p13_layer_fill_matches_torch"),
     # K bias dropped
     ("K[l] += _f64(bk[l])[None, :]", "K[l] += 0.0", "test_p13_layer_fill_norm_scale_invariance_and_bias"),
+    # an exited token takes part in later checkpoints again
+    ("dec = (m != 0) & alive", "dec = (m != 0)",
+     "test_p14_decode_step_first_passing_checkpoint_and_integrity"),
+    # the batch rule taking any running token instead of every one
+    ("every = alive.any() and bool(np.all(dec[alive]))", "every = bool(np.any(dec[alive]))",
+     "test_p14_decode_step_batch_rule"),
     # off-by-one in the filled layers
     ("filled = sum(n_layers - x for x in e)", "filled = sum(n_layers - x + 1 for x in e)",
      "test_p2_tide_figure2_worked_example"),
