@@ -685,7 +685,10 @@ def test_p14_decode_step_batch_rule():
     rng = np.random.default_rng(33)
     cks, L, slot, wk, wv, Hkv, Dh, kc = _decode_case(rng)
     n = cks[0]["h_cur"].shape[0]
-    # make one checkpoint pass for everybody: a tiny step keeps cos near 1
+    # some but not all tokens pass the first two checkpoints; the third one
+    # passes for everybody (a tiny step keeps cos near 1)
+    for c in cks:
+        c["tau"] = 0.85
     cks[2]["h_cur"] = cks[2]["h_prev"] * 1.0001
     ex, K, _ = O.decode_step(cks, L, O.RULE_BATCH_MIN, slot, wk, wv, Hkv, Dh, kc, kc)
     alive = np.ones(n, bool)
@@ -694,7 +697,7 @@ def test_p14_decode_step_batch_rule():
         passes = alive.any() and cos[alive].min() > c["tau"]
         assert np.array_equal(ex == c["layer"], alive & passes)
         alive &= ~passes
-    assert np.all(ex == cks[2]["layer"]) or np.all(ex == cks[0]["layer"]) or np.all(ex == cks[1]["layer"])
+    assert np.all(ex == cks[2]["layer"])
 
 
 # --------------------------------------------------------- mutation checks
