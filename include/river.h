@@ -13,6 +13,8 @@
  *                    token's own cache slot
  *   river_kv_fill_layer  the same through the layer's full K/V path (input
  *                    RMSNorm, K/V bias, rotary embedding of K)
+ *   river_decode_step  one generation step: route, compact and fill at
+ *                    every checkpoint, graph-capturable
  *   river_ridge_fit  the closed-form ridge maps the fill applies
  *
  * Sources (web pages; cited by title and section):
@@ -78,7 +80,7 @@ typedef enum { RIVER_RULE_TOKEN = 0, RIVER_RULE_BATCH_MIN = 1 } river_rule;
 /* Operation ids for river_workspace_size. */
 typedef enum {
   RIVER_OP_ROUTE = 0, RIVER_OP_COMPACT = 1, RIVER_OP_KV_FILL = 2, RIVER_OP_RIDGE_FIT = 3,
-  RIVER_OP_KV_FILL_LAYER = 4
+  RIVER_OP_KV_FILL_LAYER = 4, RIVER_OP_DECODE_STEP = 5
 } river_op;
 
 /*
@@ -307,6 +309,59 @@ river_status river_kv_fill_layer(int m_max, const int32_t* m_dev, int d, river_d
                                  void* workspace, size_t ws_bytes, hipStream_t s);
 
 /*
+ * One exit checkpoint of river_decode_step: the check after block `layer`.
+ */
+typedef struct {
+  int layer;              /* e: blocks 1..e ran; 1 <= e < n_layers, increasing  */
+  const void* h_prev;     /* dt [n][ld]: h^(e-1), the block's input              */
+  const void* h_cur;      /* dt [n][ld]: h^(e), its output (the exit state)      */
+  float tau, theta;       /* thresholds as in river_route                        */
+  const void* w_down;     /* dt [b][d] router, or NULL (cosine test only)        */
+  const void* w_up;       /* dt [b]                                              */
+  const void* maps;       /* dt [n_layers - e][d][d] (blocks e+1..L), or NULL    */
+} river_checkpoint;
+
+/*
+ * river_decode_step -- one generation step of the token-level exit loop.
+ *
+ * River-LLM 方法步骤详情 step 3: after each checked block the state-transition
+ * similarity decides whether a token leaves the backbone for the exit path,
+ * which writes the K/V of every remaining block at the token's slot (step 1,
+ * 技术新颖性). TIDE formula 3 and 4: the decision may also need the router.
+ *
+ * For checkpoints c = 0..n_ck-1 in order, over the tokens still running:
+ *   decision_i = river_route's decision on (h_prev, h_cur) of row i
+ *   rule TOKEN: token i exits at c if decision_i;
+ *   rule BATCH_MIN: every running token exits at c if all of them decide so
+ *   an exiting token i gets exit_layer[i] = e and blocks e+1..L filled as
+ *   river_kv_fill does from row i of h_cur (with the checkpoint's maps),
+ *   at slot[i] of cache layers e..L-1.
+ * Tokens that never exit get exit_layer[i] = n_layers. Rows of exited tokens
+ * in the states of later checkpoints are read but do not matter.
+ *
+ * wk, wv : host pointers to int4 descriptors of blocks 1..n_layers.
+ * k_cache, v_cache : dt [n_layers][n_slots][n_kv_heads][head_dim]; cache
+ *          layer j - 1 holds block j.
+ * gamma, eps, b : the routers' RMSNorm weight (NULL: ones) and width.
+ * exit_layer : int32 [n], written.
+ * workspace : river_workspace_size(RIVER_OP_DECODE_STEP, n, d, 0, 0,
+ *          n_layers) bytes fill every checkpoint in one pass; with maps at
+ *          least the size for n_layers = 2 is needed.
+ * The call enqueues an ordered sequence of kernels on s and returns: no
+ * host synchronisation, allocation or runtime memset, so it may be captured
+ * into a HIP graph once and the graph replayed for every step. The fill's
+ * shape rules are river_kv_fill's.
+ */
+river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
+                               const river_checkpoint* ck, int n_layers, const void* gamma,
+                               float eps, int b, river_rule rule,
+                               const river_w4* wk, const river_w4* wv,
+                               int n_kv_heads, int head_dim, const int32_t* slot,
+                               void* k_cache, void* v_cache, int64_t n_slots,
+                               int32_t* exit_layer, void* workspace, size_t ws_bytes,
+                               hipStream_t s);
+
+/*
  * river_ridge_fit -- closed-form ridge maps (RidgeFill, ridge box):
  *
  *   W_t = (X^T X + lambda I)^-1 X^T Y_t     for t = 0..n_targets-1
@@ -331,6 +386,7 @@ river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets,
  * ignored): ROUTE -> 0; COMPACT (n); KV_FILL (n = m_max, d, n_layers; 0
  * layers gives 0, the identity case); KV_FILL_LAYER (n = m_max, d,
  * n_layers; the bytes for n_layers layers, needed with maps or a norm);
+ * DECODE_STEP (n, d, n_layers: the blocks of the model);
  * RIDGE_FIT (n, d = d_in, d_out,
  * n_targets, and n_layers carries the dtype: RIVER_F32 or RIVER_BF16). */
 size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int n_layers);

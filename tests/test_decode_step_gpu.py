@@ -1,0 +1,254 @@
+"""GPU parity of one generation step of the token-level exit loop
+(river_decode_step) against the float64 oracle, eagerly and replayed from a
+captured HIP graph.
+
+Bars: exit layers bit-exact for tokens whose cosines and probabilities at
+every checkpoint they reach lie outside the 1e-4 band around the thresholds
+(tokens inside it are excluded and counted; at most an eighth may be); K/V of
+filled slots within the fill's bar (per-row relative L2 <= 1e-2); every
+other slot keeps its NaN sentinel. A graph replay equals the eager call bit
+for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import token_early_exit_amd as tee
+from synth import get_config
+from synth import generate as G
+from helpers import BAND, KV_TOL, f32, kv_row_errors, np64, w4_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+INF = math.inf
+
+
+@pytest.fixture(autouse=True)
+def _lib(gpu_lib):
+    tee.river_debug_set_compact_path(0)
+    yield
+
+
+def _kv(cfg, layers):
+    w = G.kv_weights(cfg, layers, device="cpu" if cfg.d <= 2048 else DEV)
+    return (tuple(t.to(DEV) for t in w["wk"]) + (cfg.group,),
+            tuple(t.to(DEV) for t in w["wv"]) + (cfg.group,))
+
+
+def run_gpu(cks, cfg, wk, wv, slot, rule=O.RULE_TOKEN, caches=None):
+    kc, vc = caches if caches is not None else G.nan_cache(cfg, cfg.L, device=DEV)
+    n = cks[0]["h_cur"].shape[0]
+    ex = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(tee.river_workspace_size(tee.OP_DECODE_STEP, n, cfg.d, 0, 0, cfg.L),
+                     dtype=torch.uint8, device=DEV)
+    tee.river_decode_step(cks, wk, wv, cfg.n_kv_heads, cfg.head_dim, slot, kc, vc, ex, rule=rule,
+                          workspace=ws)
+    torch.cuda.synchronize()
+    return ex, kc, vc
+
+
+def oracle_cks(cks):
+    out = []
+    for c in cks:
+        o = {"layer": c["layer"], "h_prev": np64(c["h_prev"]), "h_cur": np64(c["h_cur"]),
+             "tau": f32(c["tau"]), "theta": f32(c["theta"])}
+        if c.get("w_down") is not None:
+            o["w_down"], o["w_up"] = np64(c["w_down"]), np64(c["w_up"])
+        out.append(o)
+    return out
+
+
+def band_tokens(cks, ex_ref):
+    """Tokens whose cosine or probability at a checkpoint they reached lies
+    within the band around the threshold."""
+    n = len(ex_ref)
+    bad = np.zeros(n, bool)
+    for c in oracle_cks(cks):
+        cos, prob, _, _ = O.route(c["h_prev"], c["h_cur"], None, 1e-6, c.get("w_down"),
+                                  c.get("w_up"), -INF, -INF)
+        reach = ex_ref >= c["layer"]
+        near = np.abs(cos - c["tau"]) < BAND
+        if c.get("w_down") is not None:
+            near |= np.abs(prob - c["theta"]) < BAND
+        bad |= reach & near
+    return bad
+
+
+def check_step(cfg, cks, ex, kc, vc, slot, wk, wv, rule=O.RULE_TOKEN, sample_per_ck=None):
+    """Exit layers against the oracle's; filled slots' K/V against the
+    oracle's fill of the GPU's own exits."""
+    ocks = oracle_cks(cks)
+    n = ex.shape[0]
+    # oracle exit layers (no fill: caches of one layer and one slot)
+    ex_ref = np.full(n, cfg.L)
+    alive = np.ones(n, bool)
+    for c in ocks:
+        _, _, m, _ = O.route(c["h_prev"], c["h_cur"], None, 1e-6, c.get("w_down"), c.get("w_up"),
+                             c["tau"], c["theta"])
+        dec = (m != 0) & alive
+        if rule == O.RULE_BATCH_MIN:
+            dec = alive & (alive.any() and bool(np.all(dec[alive])))
+        ex_ref[dec] = c["layer"]
+        alive &= ~dec
+    bad = band_tokens(cks, ex_ref)
+    assert bad.sum() <= max(2, n // 8), f"{bad.sum()} tokens in the threshold band"
+    exg = ex.cpu().numpy()
+    assert np.array_equal(exg[~bad], ex_ref[~bad])
+    # K/V of the filled slots
+    slot_np = slot.cpu().numpy()
+    for ci, c in enumerate(cks):
+        e = c["layer"]
+        rows = np.flatnonzero((exg == e) & ~bad)
+        if len(rows) == 0:
+            continue
+        if sample_per_ck is not None and len(rows) > sample_per_ck:
+            rows = np.sort(np.random.default_rng(e).choice(rows, sample_per_ck, replace=False))
+        maps = c.get("maps")
+        K, V = O.kv_fill_rows(np64(c["h_cur"]), rows, len(rows),
+                              None if maps is None else maps.float().cpu().numpy(),
+                              w4_np(tuple(t[e:] for t in wk[:3]) + (wk[3],)),
+                              w4_np(tuple(t[e:] for t in wv[:3]) + (wv[3],)))
+        s = torch.from_numpy(slot_np[rows].astype(np.int64)).to(DEV)
+        ek = kv_row_errors(kc[e:, s].reshape(cfg.L - e, len(rows), -1), K)
+        evv = kv_row_errors(vc[e:, s].reshape(cfg.L - e, len(rows), -1), V)
+        assert ek.max() <= KV_TOL and evv.max() <= KV_TOL, (e, ek.max(), evv.max())
+    # exactly the slots of cache layers >= exit layer hold values
+    nan_k = torch.isnan(kc).all(dim=-1).all(dim=-1).cpu().numpy()       # [L][n_slots]
+    nan_v = torch.isnan(vc).all(dim=-1).all(dim=-1).cpu().numpy()
+    want = np.ones_like(nan_k)
+    for i in range(n):
+        want[exg[i]:, slot_np[i]] = False       # the GPU's own exit layers (checked above)
+    assert np.array_equal(nan_k, want) and np.array_equal(nan_v, want)
+    return exg
+
+
+def llama1b_checkpoints(cfg, hs):
+    """Checkpoints after blocks 8..15, router off, tau_l at the midpoint of
+    the two middle oracle cosines of the tokens still running."""
+    n = cfg.n_tokens
+    alive = np.ones(n, bool)
+    cks = []
+    for l in cfg.route_layers:
+        cos, *_ = O.route(np64(hs[l - 1]), np64(hs[l]), None, 1e-6, None, None, -INF, -INF)
+        c = np.sort(cos[alive])
+        m = len(c)
+        tau = 0.5 * (c[(m - 1) // 2] + c[m // 2]) if m > 1 else (c[0] - 1 if m else 0.0)
+        cks.append({"layer": l, "h_prev": hs[l - 1], "h_cur": hs[l], "tau": tau, "theta": -INF})
+        alive &= ~(cos > f32(tau))
+    return cks
+
+
+def test_decode_step_llama1b():
+    cfg = get_config(2)
+    hs = {l: t.to(DEV) for l, t in G.hidden_states(cfg, cfg.n_tokens, range(7, 17)).items()}
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    cks = llama1b_checkpoints(cfg, hs)
+    ex, kc, vc = run_gpu(cks, cfg, wk, wv, slot)
+    exg = check_step(cfg, cks, ex, kc, vc, slot, wk, wv)
+    counts = np.bincount(exg, minlength=cfg.L + 1)[8:]
+    assert counts[0] >= 28 and counts.sum() == cfg.n_tokens      # about half exit at block 8
+
+
+def test_decode_step_llama1b_batch_rule():
+    """Batch rule: the step lets everybody exit at block 11, where tau
+    sits below the smallest cosine, and nobody before."""
+    cfg = get_config(2)
+    hs = {l: t.to(DEV) for l, t in G.hidden_states(cfg, cfg.n_tokens, range(7, 17)).items()}
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    cks = llama1b_checkpoints(cfg, hs)
+    cos, *_ = O.route(np64(hs[10]), np64(hs[11]), None, 1e-6, None, None, -INF, -INF)
+    for c in cks:
+        c["tau"] = 2.0                           # no token passes (cos <= 1)
+    cks[3]["tau"] = float(cos.min()) - 1e-3
+    ex, kc, vc = run_gpu(cks, cfg, wk, wv, slot, rule=O.RULE_BATCH_MIN)
+    exg = check_step(cfg, cks, ex, kc, vc, slot, wk, wv, rule=O.RULE_BATCH_MIN)
+    assert np.all(exg == 11)
+
+
+def test_decode_step_8b_router_and_maps():
+    """Llama-3-8B-shape decode (256 tokens, d = 4096, checkpoints every four
+    blocks with a router each): tau off, theta_11 between the 13th and 14th
+    largest probabilities, theta_31 = -inf, +inf elsewhere; near-identity
+    maps for the fills."""
+    cfg = get_config("3D")
+    n = cfg.n_tokens
+    layers = list(cfg.route_layers)
+    need = sorted({l - 1 for l in layers} | set(layers))
+    hs = G.hidden_states(cfg, n, need, device=DEV)
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    cks = []
+    for l in layers:
+        wd, wu = (t.to(DEV) for t in G.router_weights(cfg, l))
+        c = {"layer": l, "h_prev": hs[l - 1], "h_cur": hs[l], "tau": -INF, "theta": INF,
+             "w_down": wd, "w_up": wu}
+        if l == 11:
+            _, prob, _, _ = O.route(np64(hs[10]), np64(hs[11]), None, 1e-6, np64(wd), np64(wu),
+                                    -INF, -INF)
+            p = np.sort(prob)[::-1]
+            c["theta"] = 0.5 * (p[12] + p[13])
+            c["maps"] = G.near_identity_maps(cfg, cfg.L - l, device=DEV)
+        if l == 31:
+            c["theta"] = -INF
+            c["maps"] = G.near_identity_maps(cfg, cfg.L - l, tag="maps31", device=DEV)
+        cks.append(c)
+    ex, kc, vc = run_gpu(cks, cfg, wk, wv, slot)
+    exg = check_step(cfg, cks, ex, kc, vc, slot, wk, wv, sample_per_ck=12)
+    assert np.sum(exg == 11) == 13 and np.sum(exg == 31) == n - 13
+
+
+def test_decode_step_graph_replay():
+    """The step captured once into a graph and replayed for three steps with
+    new states copied into the captured buffers; each replay equals an eager
+    call on the same states, with eager work between the replays."""
+    cfg = get_config(2)
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    steps = []
+    for k in range(3):
+        hs = G.hidden_states(cfg, cfg.n_tokens, range(7, 17), tag=f"step{k}")
+        steps.append({l: t.to(DEV) for l, t in hs.items()})
+    buf = {l: torch.empty_like(t) for l, t in steps[0].items()}
+    cks = llama1b_checkpoints(cfg, steps[0])
+    gcks = [dict(c, h_prev=buf[c["layer"] - 1], h_cur=buf[c["layer"]]) for c in cks]
+    n = cfg.n_tokens
+    kc, vc = G.nan_cache(cfg, cfg.L, device=DEV)
+    ex = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty(tee.river_workspace_size(tee.OP_DECODE_STEP, n, cfg.d, 0, 0, cfg.L),
+                     dtype=torch.uint8, device=DEV)
+    for l in buf:
+        buf[l].copy_(steps[0][l])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                 # warm-up outside the capture
+        tee.river_decode_step(gcks, wk, wv, cfg.n_kv_heads, cfg.head_dim, slot, kc, vc, ex,
+                              workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        tee.river_decode_step(gcks, wk, wv, cfg.n_kv_heads, cfg.head_dim, slot, kc, vc, ex,
+                              workspace=ws)
+    for k in range(3):
+        for l in buf:
+            buf[l].copy_(steps[k][l])
+        kc.fill_(float("nan"))
+        vc.fill_(float("nan"))
+        ex.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        kr, vr, er = kc.clone(), vc.clone(), ex.clone()
+        # eager call on the same states, fresh outputs
+        eck = [dict(c, h_prev=steps[k][c["layer"] - 1], h_cur=steps[k][c["layer"]]) for c in cks]
+        e2, k2, v2 = run_gpu(eck, cfg, wk, wv, slot)
+        assert torch.equal(er, e2)
+        assert torch.equal(kr.view(torch.int16), k2.view(torch.int16))
+        assert torch.equal(vr.view(torch.int16), v2.view(torch.int16))
+        assert (er < cfg.L).any()

@@ -153,3 +153,33 @@ def test_kv_fill_layer_argument_errors():
     need = tee.river_workspace_size(tee.OP_KV_FILL_LAYER, 8, 128, 0, 0, 1)
     assert need >= 8 * 128 * 2 + 2 * 8 * 4
     assert call(L(16, 1e-6, None, None, None, None, None, 0), ws=16, wsn=need - 1) == 5
+
+
+def test_decode_step_argument_errors():
+    lib = tee.load()
+    w = tee.RiverW4(16, 16, 16, tee.RIVER_BF16, 64)
+    C = tee.RiverCheckpoint
+
+    def call(cks, **k):
+        arr = (C * len(cks))(*cks)
+        a = dict(n=8, d=128, dt=tee.RIVER_BF16, ld=128, nck=len(cks), ck=arr, L=4, gamma=None,
+                 eps=1e-6, b=0, rule=0, wk=ctypes.byref(w), wv=ctypes.byref(w), hk=2, hd=64,
+                 slot=16, kc=16, vc=16, ns=8, ex=16, ws=16, wsn=1 << 30, s=None)
+        a.update(k)
+        return lib.river_decode_step(*a.values())
+
+    ok = C(1, 16, 16, 0.5, -math.inf, None, None, None)
+    assert call([ok], n=0) == 0                                          # empty batch
+    assert call([C(0, 16, 16, 0.5, 0.0, None, None, None)]) == 1         # layer 0
+    assert call([C(4, 16, 16, 0.5, 0.0, None, None, None)]) == 1         # layer L
+    assert call([C(2, 16, 16, 0.5, 0.0, None, None, None), ok]) == 1     # decreasing layers
+    assert call([C(1, None, 16, 0.5, 0.0, None, None, None)]) == 1       # no states
+    assert call([C(1, 16, 16, math.nan, 0.0, None, None, None)]) == 1    # NaN tau
+    assert call([C(1, 16, 16, 0.5, 0.0, 16, None, None)], b=8) == 1     # router without w_up
+    assert call([C(1, 8, 16, 0.5, 0.0, None, None, None)]) == 3          # misaligned state
+    assert call([ok], ws=None, wsn=0) == 5                               # no workspace
+    assert call([ok], ex=None) == 1
+    assert call([ok], rule=3) == 1
+    need = tee.river_workspace_size(tee.OP_DECODE_STEP, 8, 128, 0, 0, 4)
+    assert need > 0
+    assert call([C(1, 16, 16, 0.5, 0.0, None, None, 16)], wsn=need // 8) == 5   # maps need x_hat

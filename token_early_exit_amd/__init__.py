@@ -7,7 +7,7 @@ CPU fallback: if the library is not built, ``load()`` raises.
 
 The calls keep the C names: ``river_route``, ``river_compact``,
 ``river_exit_projection``, ``river_kv_fill``, ``river_kv_fill_layer``,
-``river_ridge_fit``; plus
+``river_decode_step``, ``river_ridge_fit``; plus
 ``river_workspace_size``.
 """
 
@@ -20,12 +20,12 @@ LIB_PATH = os.path.join(HERE, "libriver.so")
 
 RIVER_F32, RIVER_BF16 = 0, 1
 RULE_TOKEN, RULE_BATCH_MIN = 0, 1
-OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT, OP_KV_FILL_LAYER = 0, 1, 2, 3, 4
+OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT, OP_KV_FILL_LAYER, OP_DECODE_STEP = 0, 1, 2, 3, 4, 5
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_DTYPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED",
           5: "ERR_WORKSPACE", 6: "ERR_NOT_SPD", 7: "ERR_HIP"}
 
 EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fill",
-           "river_kv_fill_layer", "river_ridge_fit",
+           "river_kv_fill_layer", "river_decode_step", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
            "river_debug_set_compact_path"]
 
@@ -47,6 +47,12 @@ class RiverLayer(ctypes.Structure):
                 ("k_bias", ctypes.c_void_p), ("v_bias", ctypes.c_void_p),
                 ("pos", ctypes.c_void_p), ("rope_cos", ctypes.c_void_p),
                 ("rope_sin", ctypes.c_void_p), ("n_pos", ctypes.c_int64)]
+
+
+class RiverCheckpoint(ctypes.Structure):
+    _fields_ = [("layer", ctypes.c_int), ("h_prev", ctypes.c_void_p), ("h_cur", ctypes.c_void_p),
+                ("tau", ctypes.c_float), ("theta", ctypes.c_float), ("w_down", ctypes.c_void_p),
+                ("w_up", ctypes.c_void_p), ("maps", ctypes.c_void_p)]
 
 
 _lib = None
@@ -78,9 +84,12 @@ def load():
     lib.river_kv_fill_layer.argtypes = [_I, _P, _I, _I, _P, _L, _I, _P, _P, _I, _P,
                                         ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4),
                                         ctypes.POINTER(RiverLayer), _I, _I, _P, _P, _L, _P, _S, _P]
+    lib.river_decode_step.argtypes = [_I, _I, _I, _L, _I, ctypes.POINTER(RiverCheckpoint), _I, _P, _F,
+                                      _I, _I, ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4), _I,
+                                      _I, _P, _P, _P, _L, _P, _P, _S, _P]
     lib.river_ridge_fit.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _S, _P]
     for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill",
-              "river_kv_fill_layer", "river_ridge_fit",
+              "river_kv_fill_layer", "river_decode_step", "river_ridge_fit",
               "river_debug_set_compact_path"):
         getattr(lib, f).restype = _I
     lib.river_debug_set_compact_path.argtypes = [_I]
@@ -220,6 +229,36 @@ def river_kv_fill_layer(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache,
                                       ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(lay),
                                       n_kv_heads, head_dim, _ptr(k_cache), _ptr(v_cache),
                                       k_cache.shape[1], _ptr(workspace), ws_n, _stream(stream)))
+
+
+def river_decode_step(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, v_cache,
+                      exit_layer, *, gamma=None, eps=1e-6, rule=RULE_TOKEN, workspace=None,
+                      stream=None):
+    """checkpoints: list of dicts with layer, h_prev, h_cur, tau, theta and
+    optionally w_down, w_up, maps; wk, wv: (q, scale, zero, group) of every
+    block; caches [n_layers][n_slots][Hkv][Dh]."""
+    h0 = checkpoints[0]["h_cur"]
+    n, d = h0.shape
+    ld = _ld(h0)
+    b = 0
+    arr = (RiverCheckpoint * len(checkpoints))()
+    for i, c in enumerate(checkpoints):
+        if _ld(c["h_prev"]) != ld or _ld(c["h_cur"]) != ld:
+            raise ValueError("every state must have the same leading dimension")
+        wd = c.get("w_down")
+        if wd is not None:
+            b = wd.shape[0]
+        arr[i] = RiverCheckpoint(int(c["layer"]), _ptr(c["h_prev"]), _ptr(c["h_cur"]),
+                                 float(c["tau"]), float(c["theta"]), _ptr(wd), _ptr(c.get("w_up")),
+                                 _ptr(c.get("maps")))
+    dk = w4(*wk)
+    dv = w4(*wv)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().river_decode_step(n, d, _dt(h0), ld, len(checkpoints), arr, k_cache.shape[0],
+                                    _ptr(gamma), eps, b, rule, ctypes.byref(dk), ctypes.byref(dv),
+                                    n_kv_heads, head_dim, _ptr(slot), _ptr(k_cache), _ptr(v_cache),
+                                    k_cache.shape[1], _ptr(exit_layer), _ptr(workspace), ws_n,
+                                    _stream(stream)))
 
 
 def river_ridge_fit(X, Y, lam, W, *, workspace=None, stream=None):

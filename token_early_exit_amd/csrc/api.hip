@@ -70,6 +70,9 @@ size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int 
     case RIVER_OP_KV_FILL_LAYER:
       if (n <= 0 || d <= 0 || n_layers <= 0) return 0;
       return kv_fill_layer_workspace(n, d, n_layers);
+    case RIVER_OP_DECODE_STEP:
+      if (n <= 0 || d <= 0) return 0;
+      return decode_fixed_workspace(n) + (n_layers > 1 ? kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) : 0);
     case RIVER_OP_RIDGE_FIT:
       if (n <= 0 || d <= 0 || d_out <= 0) return 0;
       return ridge_workspace(n, d, d_out, n_layers == RIVER_F32 ? RIVER_F32 : RIVER_BF16);
@@ -99,7 +102,7 @@ river_status river_route(int n, int d, river_dtype dt, const void* h_prev, int64
   if (n == 0) {
     if (all_exit_out) return launch_route(0, d, dt, nullptr, d, nullptr, d, nullptr, eps, nullptr,
                                           nullptr, b, tau, theta, rule, nullptr, nullptr, nullptr,
-                                          all_exit_out, s);
+                                          all_exit_out, nullptr, s);
     return RIVER_OK;
   }
   if (!h_prev || !h_cur || !mask_out) return fail(RIVER_ERR_ARG, "route: h_prev, h_cur and mask_out are required");
@@ -107,7 +110,7 @@ river_status river_route(int n, int d, river_dtype dt, const void* h_prev, int64
     return fail(RIVER_ERR_ALIGN, "route: leading dims must be >= d and a multiple of 16 bytes");
   if (!aligned16(h_prev) || !aligned16(h_cur)) return fail(RIVER_ERR_ALIGN, "route: hidden states must be 16-byte aligned");
   return launch_route(n, d, dt, h_prev, ld_prev, h_cur, ld_cur, gamma, eps, w_down, w_up, b, tau,
-                      theta, rule, cos_out, prob_out, mask_out, all_exit_out, s);
+                      theta, rule, cos_out, prob_out, mask_out, all_exit_out, nullptr, s);
 }
 
 river_status river_compact(int n, int d, river_dtype dt, const uint8_t* mask, const void* h,
@@ -161,14 +164,14 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
                                 out, ld_out, n_out_rows, s);
 }
 
-static river_status kv_fill_checked(const char* who, int m_max, const int32_t* m_dev, int d,
-                                    river_dtype dt, const void* h, int64_t ld_h, int n_rows,
-                                    const int32_t* row_idx, const int32_t* slot, int n_layers,
-                                    const void* maps, const river_w4* wk, const river_w4* wv,
-                                    const river_layer* L, int n_kv_heads, int head_dim,
-                                    void* k_cache, void* v_cache, int64_t n_slots, void* workspace,
-                                    size_t ws_bytes, hipStream_t s) {
-  g_err[0] = 0;
+// argument checks of a fill (RIVER_OK when the call may go ahead; an empty
+// call is valid)
+static river_status kv_fill_validate(const char* who, int m_max, int d, river_dtype dt, const void* h,
+                                     int64_t ld_h, int n_rows, const int32_t* row_idx,
+                                     const int32_t* slot, int n_layers, const void* maps,
+                                     const river_w4* wk, const river_w4* wv, const river_layer* L,
+                                     int n_kv_heads, int head_dim, void* k_cache, void* v_cache,
+                                     int64_t n_slots, void* workspace, size_t ws_bytes) {
   if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "%s: dtype %d is not RIVER_F32 or RIVER_BF16", who, (int)dt);
   if (m_max < 0 || n_layers < 0 || n_rows < 0) return fail(RIVER_ERR_ARG, "%s: negative size", who);
   if (m_max == 0 || n_layers == 0) return RIVER_OK;
@@ -209,6 +212,21 @@ static river_status kv_fill_checked(const char* who, int m_max, const int32_t* m
       return fail(RIVER_ERR_WORKSPACE, "%s: at least %zu workspace bytes needed, %zu given", who, need, ws_bytes);
     if (!aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "%s: workspace must be 16-byte aligned", who);
   }
+  return RIVER_OK;
+}
+
+static river_status kv_fill_checked(const char* who, int m_max, const int32_t* m_dev, int d,
+                                    river_dtype dt, const void* h, int64_t ld_h, int n_rows,
+                                    const int32_t* row_idx, const int32_t* slot, int n_layers,
+                                    const void* maps, const river_w4* wk, const river_w4* wv,
+                                    const river_layer* L, int n_kv_heads, int head_dim,
+                                    void* k_cache, void* v_cache, int64_t n_slots, void* workspace,
+                                    size_t ws_bytes, hipStream_t s) {
+  g_err[0] = 0;
+  river_status st = kv_fill_validate(who, m_max, d, dt, h, ld_h, n_rows, row_idx, slot, n_layers, maps,
+                                     wk, wv, L, n_kv_heads, head_dim, k_cache, v_cache, n_slots,
+                                     workspace, ws_bytes);
+  if (st != RIVER_OK || m_max == 0 || n_layers == 0) return st;
   return launch_kv_fill(m_max, m_dev, d, dt, h, ld_h, n_rows, row_idx, slot, n_layers, maps, wk, wv,
                         L, n_kv_heads, head_dim, k_cache, v_cache, n_slots, workspace, ws_bytes, s);
 }
@@ -232,6 +250,60 @@ river_status river_kv_fill_layer(int m_max, const int32_t* m_dev, int d, river_d
   return kv_fill_checked("kv_fill_layer", m_max, m_dev, d, dt, h, ld_h, n_rows, row_idx, slot,
                          n_layers, maps, wk, wv, layer, n_kv_heads, head_dim, k_cache, v_cache,
                          n_slots, workspace, ws_bytes, s);
+}
+
+river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
+                               const river_checkpoint* ck, int n_layers, const void* gamma,
+                               float eps, int b, river_rule rule, const river_w4* wk,
+                               const river_w4* wv, int n_kv_heads, int head_dim,
+                               const int32_t* slot, void* k_cache, void* v_cache, int64_t n_slots,
+                               int32_t* exit_layer, void* workspace, size_t ws_bytes,
+                               hipStream_t s) {
+  g_err[0] = 0;
+  if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "decode_step: dtype %d is not RIVER_F32 or RIVER_BF16", (int)dt);
+  if (n < 0 || n_ck < 0) return fail(RIVER_ERR_ARG, "decode_step: negative size");
+  if (n == 0) return RIVER_OK;
+  if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "decode_step: d = %d must be a positive multiple of 8", d);
+  if (n_layers < 2) return fail(RIVER_ERR_ARG, "decode_step: n_layers = %d must be >= 2", n_layers);
+  if (!exit_layer || (n_ck > 0 && !ck)) return fail(RIVER_ERR_ARG, "decode_step: exit_layer and the checkpoints are required");
+  if (!ld_ok(ld, d, dt)) return fail(RIVER_ERR_ALIGN, "decode_step: ld must be >= d and a multiple of 16 bytes");
+  if (rule != RIVER_RULE_TOKEN && rule != RIVER_RULE_BATCH_MIN) return fail(RIVER_ERR_ARG, "decode_step: unknown rule %d", (int)rule);
+  if (!(eps >= 0.0f) || isinf(eps)) return fail(RIVER_ERR_ARG, "decode_step: eps must be finite and >= 0");
+  if (gamma && !aligned16(gamma)) return fail(RIVER_ERR_ALIGN, "decode_step: gamma must be 16-byte aligned");
+  bool any_maps = false;
+  for (int c = 0; c < n_ck; ++c) {
+    const river_checkpoint& k = ck[c];
+    if (k.layer < 1 || k.layer >= n_layers || (c > 0 && k.layer <= ck[c - 1].layer))
+      return fail(RIVER_ERR_ARG, "decode_step: checkpoint %d: layers must increase within [1, n_layers)", c);
+    if (!k.h_prev || !k.h_cur) return fail(RIVER_ERR_ARG, "decode_step: checkpoint %d: states are required", c);
+    if (!aligned16(k.h_prev) || !aligned16(k.h_cur)) return fail(RIVER_ERR_ALIGN, "decode_step: checkpoint %d: states must be 16-byte aligned", c);
+    if (isnan(k.tau) || isnan(k.theta)) return fail(RIVER_ERR_ARG, "decode_step: checkpoint %d: NaN threshold", c);
+    if (k.w_down) {
+      if (b < 1 || b > 512) return fail(RIVER_ERR_ARG, "decode_step: router width b = %d must be in [1, 512]", b);
+      if (!k.w_up) return fail(RIVER_ERR_ARG, "decode_step: checkpoint %d: w_up is NULL while w_down is set", c);
+      if (!aligned16(k.w_down) || !aligned16(k.w_up)) return fail(RIVER_ERR_ALIGN, "decode_step: router weights must be 16-byte aligned");
+    }
+    any_maps |= k.maps != nullptr;
+  }
+  const size_t fixed = decode_fixed_workspace(n);
+  const size_t need = fixed + (any_maps ? kv_fill_workspace(n, d, 1, dt) : 0);
+  if (!workspace || ws_bytes < need)
+    return fail(RIVER_ERR_WORKSPACE, "decode_step: workspace of at least %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "decode_step: workspace must be 16-byte aligned");
+  // the fill of each checkpoint: blocks e+1..L from its exit state
+  for (int c = 0; c < n_ck; ++c) {
+    const int e = ck[c].layer;
+    river_w4 k4, v4;
+    decode_layer_offset(*wk, e, n_kv_heads * head_dim, d, &k4);
+    decode_layer_offset(*wv, e, n_kv_heads * head_dim, d, &v4);
+    river_status st = kv_fill_validate("decode_step", n, d, dt, ck[c].h_cur, ld, n, nullptr, slot,
+                                       n_layers - e, ck[c].maps, &k4, &v4, nullptr, n_kv_heads,
+                                       head_dim, k_cache, v_cache, n_slots,
+                                       (char*)workspace + fixed, ws_bytes - fixed);
+    if (st != RIVER_OK) return st;
+  }
+  return launch_decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads,
+                            head_dim, slot, k_cache, v_cache, n_slots, exit_layer, workspace, ws_bytes, s);
 }
 
 river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,

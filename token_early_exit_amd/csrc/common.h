@@ -152,11 +152,16 @@ int compact_path_override();
 
 // launchers implemented by the kernel files; argument checks are done by
 // the caller (api.hip)
+
+// the running-token state of the generation loop (river_decode_step)
+struct RouteLive {
+  const uint8_t* alive_in; uint8_t* alive_out; int32_t* exit_layer; int exit_value;
+};
 river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int64_t ld_prev,
                           const void* h_cur, int64_t ld_cur, const void* gamma, float eps,
                           const void* w_down, const void* w_up, int b, float tau, float theta,
                           river_rule rule, float* cos_out, float* prob_out, uint8_t* mask_out,
-                          int32_t* all_exit_out, hipStream_t s);
+                          int32_t* all_exit_out, const RouteLive* live, hipStream_t s);
 
 size_t compact_workspace(int n);
 river_status launch_compact(int n, int d, river_dtype dt, const uint8_t* mask, const void* h,
@@ -179,6 +184,16 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
                             const river_layer* layer, int n_kv_heads, int head_dim, void* k_cache,
                             void* v_cache, int64_t n_slots, void* workspace, size_t ws_bytes,
                             hipStream_t s);
+
+size_t decode_fixed_workspace(int n);
+void decode_layer_offset(const river_w4& w, int e, int n_out, int d, river_w4* out);
+river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
+                                const river_checkpoint* ck, int n_layers, const void* gamma,
+                                float eps, int b, river_rule rule, const river_w4* wk,
+                                const river_w4* wv, int n_kv_heads, int head_dim,
+                                const int32_t* slot, void* k_cache, void* v_cache, int64_t n_slots,
+                                int32_t* exit_layer, void* workspace, size_t ws_bytes,
+                                hipStream_t s);
 
 size_t ridge_workspace(int n, int d_in, int d_out, river_dtype dt);
 river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,

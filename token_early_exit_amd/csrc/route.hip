@@ -30,6 +30,12 @@ struct RouteArgs {
   const void* wd; const void* wu;
   float tau, theta;
   float* cos_out; float* prob_out; uint8_t* mask_out;
+  // generation loop (river_decode_step): only tokens with alive_in[i] != 0
+  // take part; under the token rule the decision also writes alive_out and,
+  // for an exiting token, exit_layer (under the batch rule the finish
+  // kernel does, once the batch decision is known)
+  const uint8_t* alive_in; uint8_t* alive_out; int32_t* exit_layer; int exit_value;
+  int batch_min;
 };
 
 __device__ __forceinline__ float cosine_from(float dot, float na, float nb) {
@@ -47,6 +53,14 @@ __device__ __forceinline__ void write_decision(const RouteArgs& a, int i, float 
   bool e = router ? ((c > a.tau) && (p > a.theta)) : (c > a.tau);
   if (a.cos_out) a.cos_out[i] = c;
   if (a.prob_out) a.prob_out[i] = p;
+  if (a.alive_in) {
+    const bool al = a.alive_in[i] != 0;
+    e = e && al;
+    if (!a.batch_min) {
+      a.alive_out[i] = (al && !e) ? 1 : 0;
+      if (e) a.exit_layer[i] = a.exit_value;
+    }
+  }
   a.mask_out[i] = e ? 1 : 0;
 }
 
@@ -519,15 +533,33 @@ __global__ __launch_bounds__(256) void route_stream_kernel(RouteArgs a) {
 // AND of the per-token decisions; for the batch-min rule the AND is then
 // broadcast to every token's mask (River-LLM 方法步骤详情 step 3, TIDE
 // formula 4: exit only when every token of the batch passes).
+// With alive_in (the generation loop) the AND runs over the running tokens
+// only (0 when none runs), and the broadcast also writes alive_out and the
+// exit layer of the tokens that exit.
 __global__ __launch_bounds__(1024) void route_finish_kernel(int n, uint8_t* mask, int32_t* all_out,
-                                                            int batch_min) {
-  int all = 1;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) all &= (mask[i] != 0);
+                                                            int batch_min, const uint8_t* alive_in,
+                                                            uint8_t* alive_out, int32_t* exit_layer,
+                                                            int exit_value) {
+  int all = 1, any = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const bool al = alive_in ? alive_in[i] != 0 : true;
+    if (al) { all &= (mask[i] != 0); any = 1; }
+  }
   all = __syncthreads_and(all);
-  if (n == 0) all = 0;
+  any = __syncthreads_or(any);
+  if (!any) all = 0;
   if (threadIdx.x == 0 && all_out) *all_out = all;
-  if (batch_min)
-    for (int i = threadIdx.x; i < n; i += blockDim.x) mask[i] = (uint8_t)all;
+  if (batch_min) {
+    for (int i = threadIdx.x; i < n; i += blockDim.x) {
+      const bool al = alive_in ? alive_in[i] != 0 : true;
+      const bool ex = al && all;
+      mask[i] = ex ? 1 : 0;
+      if (alive_in) {
+        alive_out[i] = (al && !ex) ? 1 : 0;
+        if (ex) exit_layer[i] = exit_value;
+      }
+    }
+  }
 }
 
 }  // namespace river
@@ -539,9 +571,12 @@ river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int6
                           const void* h_cur, int64_t ld_cur, const void* gamma, float eps,
                           const void* w_down, const void* w_up, int b, float tau, float theta,
                           river_rule rule, float* cos_out, float* prob_out, uint8_t* mask_out,
-                          int32_t* all_exit_out, hipStream_t s) {
+                          int32_t* all_exit_out, const RouteLive* live, hipStream_t s) {
+  const int batch_min = rule == RIVER_RULE_BATCH_MIN;
   RouteArgs a{n, d, b, h_prev, ld_prev, h_cur, ld_cur, gamma, eps, w_down, w_up, tau, theta,
-              cos_out, prob_out, mask_out};
+              cos_out, prob_out, mask_out,
+              live ? live->alive_in : nullptr, live ? live->alive_out : nullptr,
+              live ? live->exit_layer : nullptr, live ? live->exit_value : 0, batch_min};
   if (n > 0) {
     const bool mfma = dt == RIVER_BF16 && w_down && d % 32 == 0 && b % 16 == 0 && b <= 128;
     // streaming path: groups of four 64-wide slabs, byte offsets of both state arrays and
@@ -590,7 +625,8 @@ river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int6
     if (st != RIVER_OK) return st;
   }
   if (rule == RIVER_RULE_BATCH_MIN || all_exit_out) {
-    route_finish_kernel<<<1, 1024, 0, s>>>(n, mask_out, all_exit_out, rule == RIVER_RULE_BATCH_MIN);
+    route_finish_kernel<<<1, 1024, 0, s>>>(n, mask_out, all_exit_out, batch_min, a.alive_in,
+                                           a.alive_out, a.exit_layer, a.exit_value);
     return check_launch("route finish");
   }
   return RIVER_OK;
