@@ -51,6 +51,9 @@ def parse():
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--projection-only", type=int, default=0,
                     help="only run this many projection-kernel launches (counter collection)")
+    ap.add_argument("--decode-only", choices=["2", "3D"], default=None,
+                    help="only time the decode step of one decode workload (2: Llama-3.2-1B, "
+                         "3D: Llama-3-8B) and print its figures")
     return ap.parse_args()
 
 
@@ -234,6 +237,97 @@ def kernel_times(wl, launches):
     return out
 
 
+class DecodeWorkload:
+    """One generation step of the token-level exit loop on a decode shape:
+    Llama-3.2-1B (64 tokens, checks after blocks 8..15, router off, tau_l at
+    the midpoint of the two middle cosines of the tokens still running,
+    identity fill) or Llama-3-8B (256 tokens, a router at every fourth block,
+    tau off, theta_11 between the 13th and 14th largest probabilities,
+    theta_31 = -inf and +inf elsewhere, near-identity maps). The thresholds
+    come from the library's own cosines and probabilities."""
+
+    def __init__(self, key, dev="cuda"):
+        cfg = self.cfg = get_config(key)
+        n = cfg.n_tokens
+        layers = list(cfg.route_layers)
+        need = sorted({l - 1 for l in layers} | set(layers))
+        self.hs = G.hidden_states(cfg, n, need, device=dev)
+        self.slot = G.slots(cfg, device=dev)
+        w = G.kv_weights(cfg, list(range(1, cfg.L + 1)), device=dev)
+        self.wk = tuple(w["wk"]) + (cfg.group,)
+        self.wv = tuple(w["wv"]) + (cfg.group,)
+        self.kc = torch.zeros((cfg.L, cfg.n_slots, cfg.n_kv_heads, cfg.head_dim),
+                              dtype=torch.bfloat16, device=dev)
+        self.vc = torch.zeros_like(self.kc)
+        self.ex = torch.empty(n, dtype=torch.int32, device=dev)
+        self.ws = torch.empty(tee.river_workspace_size(tee.OP_DECODE_STEP, n, cfg.d, 0, 0, cfg.L),
+                              dtype=torch.uint8, device=dev)
+        cos = torch.empty(n, device=dev)
+        prob = torch.empty(n, device=dev)
+        mask = torch.empty(n, dtype=torch.uint8, device=dev)
+        alive = np.ones(n, bool)
+        self.cks = []
+        for l in layers:
+            c = {"layer": l, "h_prev": self.hs[l - 1], "h_cur": self.hs[l]}
+            if cfg.b:
+                wd, wu = (t.to(dev) for t in G.router_weights(cfg, l))
+                c["w_down"], c["w_up"] = wd, wu
+                tee.river_route(self.hs[l - 1], self.hs[l], mask, w_down=wd, w_up=wu,
+                                prob_out=prob)
+                c["tau"] = -math.inf
+                if l == cfg.extra["exit_early"]:
+                    p = np.sort(prob.cpu().numpy())[::-1]
+                    k = int(round(cfg.extra["early_frac"] * n))
+                    c["theta"] = 0.5 * (p[k - 1] + p[k])
+                    c["maps"] = G.near_identity_maps(cfg, cfg.L - l, device=dev)
+                elif l == cfg.extra["exit_late"]:
+                    c["theta"] = -math.inf
+                    c["maps"] = G.near_identity_maps(cfg, cfg.L - l, tag="maps31", device=dev)
+                else:
+                    c["theta"] = math.inf
+            else:
+                tee.river_route(self.hs[l - 1], self.hs[l], mask, cos_out=cos)
+                cv = cos.cpu().numpy()
+                a = np.sort(cv[alive])
+                m = len(a)
+                c["tau"] = 0.5 * (a[(m - 1) // 2] + a[m // 2]) if m > 1 else -math.inf
+                c["theta"] = -math.inf
+                alive &= ~(cv > np.float32(c["tau"]))
+            self.cks.append(c)
+        torch.cuda.synchronize()
+
+    def step(self, i=0):
+        cfg = self.cfg
+        tee.river_decode_step(self.cks, self.wk, self.wv, cfg.n_kv_heads, cfg.head_dim, self.slot,
+                              self.kc, self.vc, self.ex, workspace=self.ws)
+
+
+def decode_times(key, steps):
+    """µs per decode step: eager (each call enqueues the step's kernels from
+    the host) and replayed from one captured graph."""
+    dw = DecodeWorkload(key)
+    for _ in range(3):
+        dw.step()
+    torch.cuda.synchronize()
+    eager = time_region(dw.step, steps) / steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dw.step()
+    g.replay()
+    torch.cuda.synchronize()
+    graph = time_region(lambda i: g.replay(), steps) / steps
+    ex = dw.ex.cpu().numpy()
+    cfg = dw.cfg
+    n_ck = len(dw.cks)
+    launches = 1 + n_ck * (2 + (1 if cfg.b else 0)) + sum(2 if c.get("maps") is not None else 1
+                                                          for c in dw.cks)
+    del g
+    return {"tokens": cfg.n_tokens, "d": cfg.d, "blocks": cfg.L, "checkpoints": n_ck,
+            "exits_per_checkpoint": [int((ex == c["layer"]).sum()) for c in dw.cks],
+            "filled_token_layers": int(sum(cfg.L - e for e in ex)),
+            "kernels_per_step": launches, "eager_us": eager * 1e3, "graph_us": graph * 1e3}
+
+
 def source_hash(files):
     import hashlib
     h = hashlib.sha256()
@@ -317,6 +411,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
         return
+    if args.decode_only:
+        key = 2 if args.decode_only == "2" else "3D"
+        print(json.dumps({"decode_step": decode_times(key, 20)}))
+        return
     wl = Workload(args.rotate)
     if args.projection_only:
         for i in range(len(wl.sets)):
@@ -389,6 +487,12 @@ def main():
                        "plain_fill_avg_call_us": kern["fill"] * 1e3,
                        "overhead_us": (kern["fill_layer"] - kern["fill"]) * 1e3},
         "roofline": roof,
+    }
+    line["decode_step"] = {
+        "llama3.2-1b decode: 64 tokens, d=2048, checks after blocks 8..15 (router off), identity fill":
+            decode_times(2, 50),
+        "llama3-8b decode: 256 tokens, d=4096, 8 router checkpoints, maps for the exits at 11 and 31":
+            decode_times("3D", 20),
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
