@@ -37,5 +37,7 @@ from .river_oracle import (  # noqa: F401
     rope_half,
     ridge_fit,
     decode_step,
+    router_labels,
+    router_fit,
     exit_schedule_ops,
 )

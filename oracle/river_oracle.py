@@ -388,6 +388,87 @@ def decode_step(checkpoints, n_layers, rule, slot, wk, wv, n_kv_heads, head_dim,
     return exit_layer, kc, vc
 
 
+def router_labels(h_k, h_final, tau_c=0.98):
+    """Calibration labels of one checkpoint.
+
+    Source: TIDE, "模块1: 离线校准": a token counts as converged at checkpoint
+    k when the cosine between its state there and its final-layer state
+    exceeds the convergence threshold (0.98 by default, "关键公式" formula 1).
+    Returns uint8 [n] (1 = converged); the cosine follows ``route``'s rules
+    (zero norm gives 0, NaN compares false).
+    """
+    cos, _, _, _ = route(h_final, h_k, None, 0.0, None, None, tau_c, -np.inf)
+    return (cos > tau_c).astype(np.uint8)
+
+
+def router_fit(h, labels, w_down, w_up, epochs, batch, order=None, gamma=None, eps=1e-6,
+               lr=1e-3, beta1=0.9, beta2=0.999, adam_eps=1e-8):
+    """Train one checkpoint's router with binary cross-entropy and Adam.
+
+    Source: TIDE, "模块1: 离线校准" and the experiment settings: the two-layer
+    router of formula 3 (RMSNorm, W_down, SiLU, w_up, sigmoid) is trained on
+    the calibration states with the BCE loss and Adam (lr = 1e-3) for 100
+    epochs.
+
+    Readings taken: mini-batches of ``batch`` tokens in the order ``order[e]``
+    (a permutation per epoch, drawn by the caller; None: 0..n-1), the last
+    batch of an epoch possibly shorter; the loss of a batch is the mean of
+    -[y log p + (1 - y) log(1 - p)] over its tokens; Adam as published by
+    Kingma and Ba (first and second moments, bias correction with the global
+    step count, no weight decay), defaults beta1 = 0.9, beta2 = 0.999,
+    eps = 1e-8; the RMSNorm weight is fixed (not trained: the router's
+    parameters are the two matrices). Gradients are the chain rule through
+    z = w_up . SiLU(u), u = W_down . x, x = gamma * h / rms(h):
+        dL/dz_i = (sigmoid(z_i) - y_i) / B
+        dL/dw_up = sum_i dL/dz_i SiLU(u_i)
+        dL/du_i = dL/dz_i * w_up * SiLU'(u_i),  SiLU'(u) = s(u) (1 + u (1 - s(u)))
+        dL/dW_down = sum_i dL/du_i x_i^T
+
+    Returns (w_down [b][d], w_up [b], mean loss per epoch [epochs]), float64.
+    """
+    h = _f64(h)
+    n, d = h.shape
+    y = np.asarray(labels, dtype=np.float64)
+    g = np.ones(d) if gamma is None else _f64(gamma)
+    W = _f64(w_down).copy()
+    w = _f64(w_up).copy()
+    mW, vW = np.zeros_like(W), np.zeros_like(W)
+    mw, vw = np.zeros_like(w), np.zeros_like(w)
+    r = 1.0 / np.sqrt(np.mean(h * h, axis=1) + eps)
+    X = h * g[None, :] * r[:, None]                  # RMSNorm of every token
+    t = 0
+    losses = np.zeros(epochs)
+    for e in range(epochs):
+        idx = np.arange(n) if order is None else np.asarray(order[e], dtype=np.int64)
+        total = 0.0
+        for s0 in range(0, n, batch):
+            rows = idx[s0:s0 + batch]
+            B = len(rows)
+            x, yy = X[rows], y[rows]
+            u = x @ W.T                                # [B][b]
+            su = _sigmoid(u)
+            a = u * su                                 # SiLU
+            z = a @ w                                  # [B]
+            p = _sigmoid(z)
+            # BCE from the logit: softplus(z) - y z
+            total += float(np.sum(np.logaddexp(0.0, z) - yy * z))
+            gz = (p - yy) / B
+            gw = a.T @ gz
+            gu = gz[:, None] * w[None, :] * (su * (1.0 + u * (1.0 - su)))
+            gW = gu.T @ x
+            t += 1
+            for P, G, M, V in ((W, gW, mW, vW), (w, gw, mw, vw)):
+                M *= beta1
+                M += (1.0 - beta1) * G
+                V *= beta2
+                V += (1.0 - beta2) * G * G
+                mh = M / (1.0 - beta1 ** t)
+                vh = V / (1.0 - beta2 ** t)
+                P -= lr * mh / (np.sqrt(vh) + adam_eps)
+        losses[e] = total / n
+    return W, w, losses
+
+
 def ridge_fit(X, Y, lam):
     """Closed-form ridge maps, one per target.
 

@@ -700,6 +700,102 @@ def test_p14_decode_step_batch_rule():
     assert np.all(ex == cks[2]["layer"])
 
 
+# ------------------------------------------------ P15 router calibration
+
+def _calib_case(rng, n=96, d=24, b=6):
+    h = rng.standard_normal((n, d)) * rng.uniform(0.5, 2.0, (n, 1))
+    v = rng.standard_normal(d)
+    y = ((h @ v) / np.linalg.norm(h, axis=1) > 0.1).astype(np.uint8)     # learnable from h
+    W0 = rng.standard_normal((b, d)) / math.sqrt(d)
+    w0 = rng.standard_normal(b) / math.sqrt(b)
+    return h, y, W0, w0
+
+
+def test_p15_router_fit_matches_torch_adam():
+    """The same model, loss and optimizer built from torch.nn.functional,
+    autograd and torch.optim.Adam in float64."""
+    import torch.nn.functional as F
+    rng = np.random.default_rng(41)
+    h, y, W0, w0 = _calib_case(rng)
+    n, d = h.shape
+    gam = 1 + 0.1 * rng.standard_normal(d)
+    orders = np.stack([rng.permutation(n) for _ in range(3)])
+    W, w, loss = O.router_fit(h, y, W0, w0, 3, 20, orders, gam, 1e-5, lr=1e-2)
+    Wt = torch.tensor(W0, dtype=torch.float64, requires_grad=True)
+    wt = torch.tensor(w0, dtype=torch.float64, requires_grad=True)
+    opt = torch.optim.Adam([Wt, wt], lr=1e-2, betas=(0.9, 0.999), eps=1e-8)
+    H = torch.from_numpy(h)
+    Y = torch.from_numpy(y.astype(np.float64))
+    tl = []
+    for e in range(3):
+        tot = 0.0
+        for s0 in range(0, n, 20):
+            rows = torch.from_numpy(orders[e][s0:s0 + 20])
+            x = F.rms_norm(H[rows], (d,), weight=torch.from_numpy(gam), eps=1e-5)
+            z = F.linear(F.silu(F.linear(x, Wt)), wt[None])[:, 0]
+            lb = F.binary_cross_entropy_with_logits(z, Y[rows])
+            opt.zero_grad()
+            lb.backward()
+            opt.step()
+            tot += float(lb.detach()) * len(rows)
+        tl.append(tot / n)
+    assert np.allclose(W, Wt.detach().numpy(), atol=1e-12, rtol=0)
+    assert np.allclose(w, wt.detach().numpy(), atol=1e-12, rtol=0)
+    assert np.allclose(loss, tl, atol=1e-12, rtol=0)
+    assert loss[-1] < loss[0]
+
+
+def test_p15_router_fit_first_step_is_signed_lr():
+    """Adam's first update is -lr g / (|g| + eps): -lr sign(g) wherever the
+    gradient is well above eps; the gradient's sign from central finite
+    differences of the mean BCE."""
+    rng = np.random.default_rng(42)
+    h, y, W0, w0 = _calib_case(rng, n=40, d=10, b=3)
+    lr = 1e-3
+    W1, w1, _ = O.router_fit(h, y, W0, w0, 1, 40, lr=lr)
+
+    def loss(W, w):
+        x = h / np.sqrt(np.mean(h * h, axis=1) + 1e-6)[:, None]
+        u = x @ W.T
+        z = (u / (1 + np.exp(-u))) @ w
+        return float(np.mean(np.logaddexp(0, z) - y * z))
+    step = 1e-6
+    for (i, j) in [(0, 0), (1, 4), (2, 9), (0, 7)]:
+        Wp, Wm = W0.copy(), W0.copy()
+        Wp[i, j] += step
+        Wm[i, j] -= step
+        gfd = (loss(Wp, w0) - loss(Wm, w0)) / (2 * step)
+        assert abs(gfd) > 1e-5
+        assert np.isclose(W1[i, j] - W0[i, j], -lr * np.sign(gfd), rtol=1e-3, atol=0)
+    for k in range(3):
+        wp, wm = w0.copy(), w0.copy()
+        wp[k] += step
+        wm[k] -= step
+        gfd = (loss(W0, wp) - loss(W0, wm)) / (2 * step)
+        assert np.isclose(w1[k] - w0[k], -lr * np.sign(gfd), rtol=1e-3, atol=0)
+
+
+def test_p15_router_zero_up_projection():
+    """With w_up = 0 every probability is 1/2: the first epoch's loss is
+    log 2 and W_down gets no gradient in the first step."""
+    rng = np.random.default_rng(43)
+    h, y, W0, _ = _calib_case(rng, n=30)
+    W1, w1, loss = O.router_fit(h, y, W0, np.zeros(6), 1, 30)
+    assert abs(loss[0] - math.log(2)) < 1e-15
+    assert np.array_equal(W1, W0)
+    assert np.all(np.abs(np.abs(w1) - 1e-3) < 1e-9)
+
+
+def test_p15_router_labels_match_scipy_cosine():
+    from scipy.spatial.distance import cosine
+    rng = np.random.default_rng(44)
+    hk = rng.standard_normal((50, 12))
+    hL = hk + rng.uniform(0, 0.5, (50, 1)) * rng.standard_normal((50, 12))
+    y = O.router_labels(hk, hL, 0.98)
+    ref = np.array([1 - cosine(hk[i], hL[i]) > 0.98 for i in range(50)], dtype=np.uint8)
+    assert np.array_equal(y, ref) and 0 < y.sum() < 50
+
+
 # --------------------------------------------------------- mutation checks
 
 def _mutant_oracle(old, new):
@@ -776,6 +872,16 @@ MUTANTS = [
     # the batch rule taking any running token instead of every one
     ("every = alive.any() and bool(np.all(dec[alive]))", "every = bool(np.any(dec[alive]))",
      "test_p14_decode_step_batch_rule"),
+    # SiLU's derivative without its second term
+    ("gu = gz[:, None] * w[None, :] * (su * (1.0 + u * (1.0 - su)))",
+     "gu = gz[:, None] * w[None, :] * su", "test_p15_router_fit_matches_torch_adam"),
+    # Adam without bias correction
+    ("mh = M / (1.0 - beta1 ** t)", "mh = M", "test_p15_router_fit_first_step_is_signed_lr"),
+    # batch loss averaged over the whole set instead of the batch
+    ("gz = (p - yy) / B", "gz = (p - yy) / n", "test_p15_router_fit_matches_torch_adam"),
+    # label threshold not strict
+    ("return (cos > tau_c).astype(np.uint8)", "return (cos >= 0.9).astype(np.uint8)",
+     "test_p15_router_labels_match_scipy_cosine"),
     # off-by-one in the filled layers
     ("filled = sum(n_layers - x for x in e)", "filled = sum(n_layers - x + 1 for x in e)",
      "test_p2_tide_figure2_worked_example"),
