@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--decode-only", choices=["2", "3D"], default=None,
                     help="only time the decode step of one decode workload (2: Llama-3.2-1B, "
                          "3D: Llama-3-8B) and print its figures")
+    ap.add_argument("--router-fit-only", action="store_true",
+                    help="only time router calibration (both shapes) and print its figures")
     return ap.parse_args()
 
 
@@ -328,6 +330,50 @@ def decode_times(key, steps):
             "kernels_per_step": launches, "eager_us": eager * 1e3, "graph_us": graph * 1e3}
 
 
+def router_fit_times(key, n, epochs=100, batch=256):
+    """One checkpoint's router trained on n synthetic calibration tokens
+    (labels from the library's cosine test at 0.98), timed whole between two
+    events: the page's setting of 100 epochs, Adam lr 1e-3."""
+    cfg = get_config(key)
+    k = cfg.route_layers[0]
+    hk, hf = (t.to("cuda") for t in G.router_calibration(cfg, k, n, device="cuda"))
+    y = torch.empty(n, dtype=torch.uint8, device="cuda")
+    tee.river_route(hf, hk, y, tau=0.98)
+    wd, wu = G.router_weights(cfg, k)
+    W0 = wd.float().cuda()
+    w0 = wu.float().cuda()
+    ws = torch.empty(tee.river_workspace_size(tee.OP_ROUTER_FIT, n, cfg.d, cfg.b, batch, epochs),
+                     dtype=torch.uint8, device="cuda")
+    loss = torch.empty(epochs, device="cuda")
+    W, w = W0.clone(), w0.clone()
+    tee.river_router_fit(hk, y, W, w, epochs=1, batch=batch, loss_out=loss, workspace=ws)  # warm-up
+    W, w = W0.clone(), w0.clone()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record()
+    tee.river_router_fit(hk, y, W, w, epochs=epochs, batch=batch, loss_out=loss, workspace=ws)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    steps = epochs * ((n + batch - 1) // batch)
+    lo = loss.cpu().numpy()
+    return {"tokens": n, "d": cfg.d, "b": cfg.b, "epochs": epochs, "batch": batch,
+            "adam_steps": steps, "ms": ms, "us_per_step": ms * 1e3 / steps,
+            "host_enqueue_ms": host_ms, "token_epochs_per_s": n * epochs / (ms * 1e-3),
+            "converged_fraction": float(y.float().mean().item()),
+            "loss_first_last_epoch": [float(lo[0]), float(lo[-1])]}
+
+
+def router_fit_all():
+    return {
+        "gpt2-small shape: checkpoint 4, 2048 calibration tokens": router_fit_times(1, 2048),
+        "llama3-8b shape: checkpoint 3, 8192 calibration tokens": router_fit_times(3, 8192),
+    }
+
+
 def source_hash(files):
     import hashlib
     h = hashlib.sha256()
@@ -410,6 +456,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return
+    if args.router_fit_only:
+        print(json.dumps({"router_fit": router_fit_all()}))
         return
     if args.decode_only:
         key = 2 if args.decode_only == "2" else "3D"
@@ -494,6 +543,7 @@ def main():
         "llama3-8b decode: 256 tokens, d=4096, 8 router checkpoints, maps for the exits at 11 and 31":
             decode_times("3D", 20),
     }
+    line["router_fit"] = router_fit_all()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line))

@@ -16,6 +16,8 @@
  *   river_decode_step  one generation step: route, compact and fill at
  *                    every checkpoint, graph-capturable
  *   river_ridge_fit  the closed-form ridge maps the fill applies
+ *   river_router_fit training of a checkpoint's router (BCE + Adam) on
+ *                    calibration states (offline)
  *
  * Sources (web pages; cited by title and section):
  *   River-LLM -- "River-LLM: Large Language Model Seamless Exit Based on
@@ -80,7 +82,7 @@ typedef enum { RIVER_RULE_TOKEN = 0, RIVER_RULE_BATCH_MIN = 1 } river_rule;
 /* Operation ids for river_workspace_size. */
 typedef enum {
   RIVER_OP_ROUTE = 0, RIVER_OP_COMPACT = 1, RIVER_OP_KV_FILL = 2, RIVER_OP_RIDGE_FIT = 3,
-  RIVER_OP_KV_FILL_LAYER = 4, RIVER_OP_DECODE_STEP = 5
+  RIVER_OP_KV_FILL_LAYER = 4, RIVER_OP_DECODE_STEP = 5, RIVER_OP_ROUTER_FIT = 6
 } river_op;
 
 /*
@@ -382,11 +384,51 @@ river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets,
                              void* W, river_dtype wdt,
                              void* workspace, size_t ws_bytes, hipStream_t s);
 
+/*
+ * river_router_fit -- train one checkpoint's router on calibration states.
+ *
+ * TIDE 模块1 (offline calibration): the router of formula 3,
+ *   p = sigmoid(w_up . SiLU(W_down . RMSNorm(h))),
+ * is trained with binary cross-entropy and Adam (lr 1e-3 on the page) for
+ * a number of epochs (100 on the page). The labels are 1 for tokens whose
+ * cosine to their final-layer state exceeds 0.98 (formula 1): river_route
+ * with h_prev = final states, h_cur = checkpoint states, tau = 0.98 and the
+ * router off writes exactly these labels as its mask.
+ *
+ * Per epoch e the tokens are taken in the order order[e][0..n) (NULL: 0..n-1)
+ * in mini-batches of `batch` (the last one possibly shorter); each batch's
+ * loss is the mean BCE over its tokens, and one Adam step follows:
+ *   m = beta1 m + (1 - beta1) g,  v = beta2 v + (1 - beta2) g^2,
+ *   w -= lr (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + adam_eps),
+ * t counting steps from 1 over the whole fit. The RMSNorm weight gamma is
+ * fixed (NULL: ones); only W_down and w_up are trained.
+ *
+ * h       : dt [n][d] checkpoint states, leading dim ld_h.
+ * labels  : uint8 [n], 0 or non-zero.
+ * w_down  : fp32 [b][d], the initial weights in, the trained ones out.
+ * w_up    : fp32 [b], likewise.
+ * loss_out: fp32 [epochs], the mean training loss of each epoch (the sum of
+ *           its batches' per-token losses over n), or NULL.
+ * workspace: river_workspace_size(RIVER_OP_ROUTER_FIT, n, d, b, batch,
+ *           epochs) bytes.
+ * Arithmetic is fp32 with reductions in a fixed order: a fit is
+ * deterministic. The call enqueues two kernels per batch and returns.
+ * Requirements: d % 8 == 0, b in [1, 512], batch in [1, 1000], epochs >= 1,
+ * finite lr > 0, beta1 and beta2 in [0, 1), adam_eps > 0.
+ */
+river_status river_router_fit(int n, int d, river_dtype dt, const void* h, int64_t ld_h,
+                              const uint8_t* labels, const void* gamma, float eps, int b,
+                              float* w_down, float* w_up, int epochs, int batch,
+                              const int32_t* order, float lr, float beta1, float beta2,
+                              float adam_eps, float* loss_out, void* workspace, size_t ws_bytes,
+                              hipStream_t s);
+
 /* Workspace bytes for an operation (arguments that do not apply are
  * ignored): ROUTE -> 0; COMPACT (n); KV_FILL (n = m_max, d, n_layers; 0
  * layers gives 0, the identity case); KV_FILL_LAYER (n = m_max, d,
  * n_layers; the bytes for n_layers layers, needed with maps or a norm);
- * DECODE_STEP (n, d, n_layers: the blocks of the model);
+ * DECODE_STEP (n, d, n_layers: the blocks of the model); ROUTER_FIT (n, d,
+ * d_out = b, n_targets = batch, n_layers = epochs);
  * RIDGE_FIT (n, d = d_in, d_out,
  * n_targets, and n_layers carries the dtype: RIVER_F32 or RIVER_BF16). */
 size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int n_layers);

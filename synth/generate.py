@@ -24,6 +24,11 @@ tensor does not change when another one is added or dropped):
   scale and zero (round-to-nearest, min-max; see ``quantize_w4``).
 * decode slots: distinct, drawn without replacement; prefill slots are the
   token positions.
+* router calibration states (one checkpoint): h_k from the calibration
+  walk; the drift to the final layer is s_i * |h_k| / sqrt(d) * N(0, I) with
+  s_i = 0.25 * exp(-q_i), q_i = sqrt(d) * <h_k / |h_k|, v> for a fixed unit
+  direction v. About 40% of the tokens then end within cosine 0.98 of
+  their final state, and which ones is learnable from h_k alone.
 """
 
 import math
@@ -198,6 +203,23 @@ def kv_weights(cfg: Config, layers, device="cpu"):
     for which in ("k", "v"):
         res["w" + which] = tuple(torch.stack(x).contiguous() for x in qs[which])
     return res
+
+
+def router_calibration(cfg: Config, k, n=None, device="cpu"):
+    """(h_k, h_final), each [n][d] in the workload dtype, for training the
+    router at checkpoint k."""
+    n = cfg.n_calib if n is None else n
+    hk = hidden_states(cfg, n, [k], tag="router_calib", device=device, dtype=torch.float32)[k]
+    g = stream(cfg.idx, f"router_calib/{k}", device)
+    v = _normal((cfg.d,), g, device)
+    v = v / v.norm()
+    nrm = hk.norm(dim=1, keepdim=True)
+    q = (hk @ v)[:, None] / nrm * math.sqrt(cfg.d)
+    s = 0.25 * torch.exp(-q)
+    drift = _normal((n, cfg.d), g, device)
+    hf = hk + s * drift * nrm / math.sqrt(cfg.d)
+    dt = _DT[cfg.dtype]
+    return hk.to(dt).contiguous(), hf.to(dt).contiguous()
 
 
 def slots(cfg: Config, n=None, device="cpu"):

@@ -183,3 +183,28 @@ def test_decode_step_argument_errors():
     need = tee.river_workspace_size(tee.OP_DECODE_STEP, 8, 128, 0, 0, 4)
     assert need > 0
     assert call([C(1, 16, 16, 0.5, 0.0, None, None, 16)], wsn=need // 8) == 5   # maps need x_hat
+
+
+def test_router_fit_argument_errors():
+    lib = tee.load()
+
+    def call(**k):
+        a = dict(n=64, d=128, dt=tee.RIVER_BF16, h=16, ld=128, y=16, gamma=None, eps=1e-6, b=16,
+                 wd=16, wu=16, epochs=2, batch=32, order=None, lr=1e-3, b1=0.9, b2=0.999,
+                 aeps=1e-8, loss=None, ws=16, wsn=1 << 30, s=None)
+        a.update(k)
+        return lib.river_router_fit(*a.values())
+
+    assert call(n=0) == 1
+    assert call(epochs=0) == 1
+    assert call(b=513) == 1
+    assert call(batch=1001) == 1
+    assert call(lr=0.0) == 1
+    assert call(b1=1.0) == 1
+    assert call(aeps=0.0) == 1
+    assert call(y=None) == 1
+    assert call(h=8) == 3
+    assert call(ws=None, wsn=0) == 5
+    need = tee.river_workspace_size(tee.OP_ROUTER_FIT, 64, 128, 16, 32, 2)
+    assert need >= 3 * 128 * 16 * 4
+    assert call(wsn=need - 1) == 5

@@ -7,7 +7,7 @@ CPU fallback: if the library is not built, ``load()`` raises.
 
 The calls keep the C names: ``river_route``, ``river_compact``,
 ``river_exit_projection``, ``river_kv_fill``, ``river_kv_fill_layer``,
-``river_decode_step``, ``river_ridge_fit``; plus
+``river_decode_step``, ``river_router_fit``, ``river_ridge_fit``; plus
 ``river_workspace_size``.
 """
 
@@ -20,12 +20,13 @@ LIB_PATH = os.path.join(HERE, "libriver.so")
 
 RIVER_F32, RIVER_BF16 = 0, 1
 RULE_TOKEN, RULE_BATCH_MIN = 0, 1
-OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT, OP_KV_FILL_LAYER, OP_DECODE_STEP = 0, 1, 2, 3, 4, 5
+(OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT, OP_KV_FILL_LAYER, OP_DECODE_STEP,
+ OP_ROUTER_FIT) = 0, 1, 2, 3, 4, 5, 6
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_DTYPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED",
           5: "ERR_WORKSPACE", 6: "ERR_NOT_SPD", 7: "ERR_HIP"}
 
 EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fill",
-           "river_kv_fill_layer", "river_decode_step", "river_ridge_fit",
+           "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
            "river_debug_set_compact_path"]
 
@@ -87,9 +88,11 @@ def load():
     lib.river_decode_step.argtypes = [_I, _I, _I, _L, _I, ctypes.POINTER(RiverCheckpoint), _I, _P, _F,
                                       _I, _I, ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4), _I,
                                       _I, _P, _P, _P, _L, _P, _P, _S, _P]
+    lib.river_router_fit.argtypes = [_I, _I, _I, _P, _L, _P, _P, _F, _I, _P, _P, _I, _I, _P, _F, _F,
+                                     _F, _F, _P, _P, _S, _P]
     lib.river_ridge_fit.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _S, _P]
     for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill",
-              "river_kv_fill_layer", "river_decode_step", "river_ridge_fit",
+              "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
               "river_debug_set_compact_path"):
         getattr(lib, f).restype = _I
     lib.river_debug_set_compact_path.argtypes = [_I]
@@ -259,6 +262,21 @@ def river_decode_step(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, 
                                     n_kv_heads, head_dim, _ptr(slot), _ptr(k_cache), _ptr(v_cache),
                                     k_cache.shape[1], _ptr(exit_layer), _ptr(workspace), ws_n,
                                     _stream(stream)))
+
+
+def river_router_fit(h, labels, w_down, w_up, *, epochs=100, batch=256, order=None, gamma=None,
+                     eps=1e-6, lr=1e-3, beta1=0.9, beta2=0.999, adam_eps=1e-8, loss_out=None,
+                     workspace=None, stream=None):
+    """w_down (fp32 [b][d]) and w_up (fp32 [b]) are trained in place."""
+    n, d = h.shape
+    b = w_down.shape[0]
+    if workspace is None:
+        raise ValueError("river_router_fit needs a workspace (river_workspace_size(OP_ROUTER_FIT, ...))")
+    ws_n = workspace.numel() * workspace.element_size()
+    _check(load().river_router_fit(n, d, _dt(h), _ptr(h), _ld(h), _ptr(labels), _ptr(gamma), eps, b,
+                                   _ptr(w_down), _ptr(w_up), epochs, batch, _ptr(order), lr, beta1,
+                                   beta2, adam_eps, _ptr(loss_out), _ptr(workspace), ws_n,
+                                   _stream(stream)))
 
 
 def river_ridge_fit(X, Y, lam, W, *, workspace=None, stream=None):

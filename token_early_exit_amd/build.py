@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libriver.so")
 
-SOURCES = ["api.hip", "route.hip", "compact.hip", "exit_proj.hip", "kv_fill.hip", "ridge.hip", "decode.hip"]
+SOURCES = ["api.hip", "route.hip", "compact.hip", "exit_proj.hip", "kv_fill.hip", "ridge.hip", "decode.hip", "calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -73,6 +73,9 @@ size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int 
     case RIVER_OP_DECODE_STEP:
       if (n <= 0 || d <= 0) return 0;
       return decode_fixed_workspace(n) + (n_layers > 1 ? kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) : 0);
+    case RIVER_OP_ROUTER_FIT:
+      if (n <= 0 || d <= 0 || d_out <= 0 || n_targets <= 0 || n_layers <= 0) return 0;
+      return calib_workspace(n, d, d_out, n_targets, n_layers);
     case RIVER_OP_RIDGE_FIT:
       if (n <= 0 || d <= 0 || d_out <= 0) return 0;
       return ridge_workspace(n, d, d_out, n_layers == RIVER_F32 ? RIVER_F32 : RIVER_BF16);
@@ -304,6 +307,35 @@ river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_c
   }
   return launch_decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads,
                             head_dim, slot, k_cache, v_cache, n_slots, exit_layer, workspace, ws_bytes, s);
+}
+
+river_status river_router_fit(int n, int d, river_dtype dt, const void* h, int64_t ld_h,
+                              const uint8_t* labels, const void* gamma, float eps, int b,
+                              float* w_down, float* w_up, int epochs, int batch,
+                              const int32_t* order, float lr, float beta1, float beta2,
+                              float adam_eps, float* loss_out, void* workspace, size_t ws_bytes,
+                              hipStream_t s) {
+  g_err[0] = 0;
+  if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "router_fit: dtype %d is not RIVER_F32 or RIVER_BF16", (int)dt);
+  if (n < 1 || epochs < 1) return fail(RIVER_ERR_ARG, "router_fit: n and epochs must be >= 1");
+  if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "router_fit: d = %d must be a positive multiple of 8", d);
+  if (b < 1 || b > 512) return fail(RIVER_ERR_ARG, "router_fit: b = %d must be in [1, 512]", b);
+  if (batch < 1 || batch > 1000) return fail(RIVER_ERR_ARG, "router_fit: batch = %d must be in [1, 1000]", batch);
+  if (!(lr > 0.0f) || isinf(lr)) return fail(RIVER_ERR_ARG, "router_fit: lr must be finite and > 0");
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(RIVER_ERR_ARG, "router_fit: beta1 and beta2 must be in [0, 1)");
+  if (!(adam_eps > 0.0f) || isinf(adam_eps)) return fail(RIVER_ERR_ARG, "router_fit: adam_eps must be finite and > 0");
+  if (!(eps >= 0.0f) || isinf(eps)) return fail(RIVER_ERR_ARG, "router_fit: eps must be finite and >= 0");
+  if (!h || !labels || !w_down || !w_up) return fail(RIVER_ERR_ARG, "router_fit: h, labels, w_down and w_up are required");
+  if (!ld_ok(ld_h, d, dt) || !aligned16(h)) return fail(RIVER_ERR_ALIGN, "router_fit: h misaligned or ld_h invalid");
+  if (gamma && !aligned16(gamma)) return fail(RIVER_ERR_ALIGN, "router_fit: gamma must be 16-byte aligned");
+  if ((int64_t)n * epochs > ((int64_t)1 << 31)) return fail(RIVER_ERR_UNSUPPORTED, "router_fit: n * epochs must stay below 2^31");
+  const size_t need = calib_workspace(n, d, b, batch, epochs);
+  if (!workspace || ws_bytes < need)
+    return fail(RIVER_ERR_WORKSPACE, "router_fit: workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  if (!aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "router_fit: workspace must be 16-byte aligned");
+  return launch_router_fit(n, d, dt, h, ld_h, labels, gamma, eps, b, w_down, w_up, epochs, batch, order,
+                           lr, beta1, beta2, adam_eps, loss_out, workspace, s);
 }
 
 river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,

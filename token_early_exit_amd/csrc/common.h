@@ -195,6 +195,13 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
                                 int32_t* exit_layer, void* workspace, size_t ws_bytes,
                                 hipStream_t s);
 
+size_t calib_workspace(int n, int d, int b, int batch, int epochs);
+river_status launch_router_fit(int n, int d, river_dtype dt, const void* h, int64_t ld_h,
+                               const uint8_t* labels, const void* gamma, float eps, int b,
+                               float* w_down, float* w_up, int epochs, int batch,
+                               const int32_t* order, float lr, float beta1, float beta2,
+                               float adam_eps, float* loss_out, void* workspace, hipStream_t s);
+
 size_t ridge_workspace(int n, int d_in, int d_out, river_dtype dt);
 river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,
                               river_dtype xdt, const void* Y, float lambda, void* W,
