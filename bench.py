@@ -262,8 +262,10 @@ class DecodeWorkload:
                               dtype=torch.bfloat16, device=dev)
         self.vc = torch.zeros_like(self.kc)
         self.ex = torch.empty(n, dtype=torch.int32, device=dev)
-        self.ws = torch.empty(tee.river_workspace_size(tee.OP_DECODE_STEP, n, cfg.d, 0, 0, cfg.L),
-                              dtype=torch.uint8, device=dev)
+        # with room for the fills' split reduction (n <= 64)
+        wsn = tee.river_workspace_size(tee.OP_DECODE_STEP, n, cfg.d, cfg.n_kv_heads * cfg.head_dim,
+                                       0, cfg.L)
+        self.ws = torch.empty(wsn, dtype=torch.uint8, device=dev)
         cos = torch.empty(n, device=dev)
         prob = torch.empty(n, device=dev)
         mask = torch.empty(n, dtype=torch.uint8, device=dev)
@@ -365,6 +367,109 @@ def router_fit_times(key, n, epochs=100, batch=256):
             "host_enqueue_ms": host_ms, "token_epochs_per_s": n * epochs / (ms * 1e-3),
             "converged_fraction": float(y.float().mean().item()),
             "loss_first_last_epoch": [float(lo[0]), float(lo[-1])]}
+
+
+def route_compact_8b(reps=20):
+    """route and compact at the Llama-3-8B prefill shape (8192 tokens,
+    d = 4096, router b = 128 at checkpoint 11): µs per call (graph of
+    back-to-back calls between two events) and HBM GB/s on the algorithmic
+    bytes (route: both state rows of every token and W_down; compact: the
+    mask, the index lists and the exited rows read and written)."""
+    cfg = get_config(3)
+    n, d, b = cfg.n_tokens, cfg.d, cfg.b
+    e = 11
+    hs = G.hidden_states(cfg, n, [e - 1, e], device="cuda")
+    wd, wu = (t.to("cuda") for t in G.router_weights(cfg, e))
+    mask = torch.empty(n, dtype=torch.uint8, device="cuda")
+    prob = torch.empty(n, device="cuda")
+    tee.river_route(hs[e - 1], hs[e], mask, w_down=wd, w_up=wu, prob_out=prob)
+    p = np.sort(prob.cpu().numpy())[::-1]
+    k = int(round(cfg.extra["early_frac"] * n))
+    theta = float(0.5 * (p[k - 1] + p[k]))
+    cont = torch.empty(n, dtype=torch.int32, device="cuda")
+    ext = torch.empty(n, dtype=torch.int32, device="cuda")
+    counts = torch.empty(2, dtype=torch.int32, device="cuda")
+    out = torch.empty((n, d), dtype=torch.bfloat16, device="cuda")
+    cws = torch.empty(max(256, tee.river_workspace_size(tee.OP_COMPACT, n)), dtype=torch.uint8,
+                      device="cuda")
+    route = lambda i: tee.river_route(hs[e - 1], hs[e], mask, w_down=wd, w_up=wu, tau=-math.inf,
+                                      theta=theta)
+    compact = lambda i: tee.river_compact(mask, hs[e], cont, ext, counts, out=out, workspace=cws)
+    res = {}
+    for name, fn in (("route", route), ("compact", compact)):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        res[name] = time_region(lambda i: g.replay(), 1) / reps
+        del g
+    ne = int(counts[1].item())
+    route_b = 2 * n * d * 2 + b * d * 2 + b * 2 + n
+    compact_b = n + 4 * n + 8 + 2 * ne * d * 2
+    return {"tokens": n, "d": d, "exited": ne,
+            "route_us": res["route"] * 1e3, "route_gbs": route_b / (res["route"] * 1e-3) / 1e9,
+            "route_frac_hbm": route_b / (res["route"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "compact_us": res["compact"] * 1e3,
+            "compact_gbs": compact_b / (res["compact"] * 1e-3) / 1e9,
+            "route_compact_frac_hbm": (route_b + compact_b) / ((res["route"] + res["compact"]) * 1e-3)
+                                      / 1e9 / HBM_PEAK_GBS}
+
+
+def fill_long_context(reps=3):
+    """The fill at the long-context prefill shape (d = 5120, exit after block
+    16 of 64, the 30,704 rows between the first 16 and the last 2048 of a
+    32K-token prompt, 48 filled layers, near-identity maps, int4 group 128,
+    8 x 128 KV heads): the shape where the GEMMs fill the GPU. Whole fill
+    and projection alone, each averaged over ``reps`` calls between two
+    events."""
+    cfg = get_config(4)
+    e = 16
+    layers = list(range(e + 1, cfg.L + 1))
+    nl = len(layers)
+    n, d = cfg.n_tokens, cfg.d
+    h = G.hidden_states(cfg, n, [e], device="cuda")[e]
+    slot = G.slots(cfg, device="cuda")
+    w = G.kv_weights(cfg, layers, device="cuda")
+    wk = tuple(w["wk"]) + (cfg.group,)
+    wv = tuple(w["wv"]) + (cfg.group,)
+    maps = G.near_identity_maps(cfg, nl, device="cuda")
+    rows = torch.arange(cfg.fill_lo, n - cfg.fill_tail, dtype=torch.int32, device="cuda")
+    m = rows.numel()
+    kc = torch.empty((nl, cfg.n_slots, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16,
+                     device="cuda")
+    vc = torch.empty_like(kc)
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, m, d, 0, 0, nl), dtype=torch.uint8,
+                     device="cuda")
+
+    def fill(with_maps):
+        tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=m,
+                          row_idx=rows, maps=maps if with_maps else None,
+                          workspace=ws if with_maps else None)
+
+    out = {}
+    for key, wm in (("fill_ms", True), ("projection_ms", False)):
+        fill(wm)
+        torch.cuda.synchronize()
+        out[key] = time_region(lambda i: fill(wm), reps) / reps
+    n_out = 2 * cfg.n_kv_heads * cfg.head_dim
+    map_flops = 2.0 * m * d * d * nl
+    proj_flops = 2.0 * m * d * n_out * nl
+    map_ms = out["fill_ms"] - out["projection_ms"]
+    del maps, ws, kc, vc
+    torch.cuda.empty_cache()
+    return {"rows": m, "d": d, "layers": nl, "n_out": n_out,
+            "fill_ms": out["fill_ms"], "projection_ms": out["projection_ms"],
+            "map_gemm_ms": map_ms,
+            "map_gemm_tflops": map_flops / (map_ms * 1e-3) / 1e12,
+            "projection_tflops": proj_flops / (out["projection_ms"] * 1e-3) / 1e12,
+            "fill_tflops": (map_flops + proj_flops) / (out["fill_ms"] * 1e-3) / 1e12,
+            "fill_frac_of_bf16_peak": (map_flops + proj_flops) / (out["fill_ms"] * 1e-3) / 1e12
+                                      / MFMA_BF16_PEAK_TFLOPS,
+            "exited_tokens_per_s": m / (out["fill_ms"] * 1e-3)}
 
 
 def router_fit_all():
@@ -544,6 +649,8 @@ def main():
             decode_times("3D", 20),
     }
     line["router_fit"] = router_fit_all()
+    line["fill_long_context"] = fill_long_context()
+    line["route_compact_8b_prefill"] = route_compact_8b()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line))

@@ -244,6 +244,12 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
  * workspace: with maps, at least river_workspace_size(RIVER_OP_KV_FILL,
  *            m_max, d, 0, 0, 1) bytes; the layers are processed in as few
  *            chunks as the given size allows. Without maps none is needed.
+ *            For m_max <= 64, river_workspace_size(RIVER_OP_KV_FILL, m_max,
+ *            d, n_kv_heads * head_dim, 0, n_layers) bytes also hold the
+ *            fp32 partial sums of a projection whose reduction over d is
+ *            split into parts (so that a few rows still occupy every CU);
+ *            the parts are added in a fixed order, so results do not
+ *            depend on the split. With less, the reduction is not split.
  * Only the filled slots are written; every other byte is left unchanged.
  * Paths: bf16 with d % 256 == 0, n_out % 64 == 0, group % 64 == 0, the
  * same group and scale/zero dtype for wk and wv, an even number of groups
@@ -348,7 +354,9 @@ typedef struct {
  * exit_layer : int32 [n], written.
  * workspace : river_workspace_size(RIVER_OP_DECODE_STEP, n, d, 0, 0,
  *          n_layers) bytes fill every checkpoint in one pass; with maps at
- *          least the size for n_layers = 2 is needed.
+ *          least the size for n_layers = 2 is needed. Passing d_out =
+ *          n_kv_heads * head_dim adds room for the split reduction that
+ *          river_kv_fill describes (n <= 64).
  * The call enqueues an ordered sequence of kernels on s and returns: no
  * host synchronisation, allocation or runtime memset, so it may be captured
  * into a HIP graph once and the graph replayed for every step. The fill's
@@ -425,9 +433,11 @@ river_status river_router_fit(int n, int d, river_dtype dt, const void* h, int64
 
 /* Workspace bytes for an operation (arguments that do not apply are
  * ignored): ROUTE -> 0; COMPACT (n); KV_FILL (n = m_max, d, n_layers; 0
- * layers gives 0, the identity case); KV_FILL_LAYER (n = m_max, d,
+ * layers gives 0, the identity case; optional d_out = n_kv_heads *
+ * head_dim); KV_FILL_LAYER (n = m_max, d,
  * n_layers; the bytes for n_layers layers, needed with maps or a norm);
- * DECODE_STEP (n, d, n_layers: the blocks of the model); ROUTER_FIT (n, d,
+ * DECODE_STEP (n, d, n_layers: the blocks of the model; optional d_out as
+ * for KV_FILL); ROUTER_FIT (n, d,
  * d_out = b, n_targets = batch, n_layers = epochs);
  * RIDGE_FIT (n, d = d_in, d_out,
  * n_targets, and n_layers carries the dtype: RIVER_F32 or RIVER_BF16). */

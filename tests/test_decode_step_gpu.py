@@ -39,12 +39,18 @@ def _kv(cfg, layers):
             tuple(t.to(DEV) for t in w["wv"]) + (cfg.group,))
 
 
-def run_gpu(cks, cfg, wk, wv, slot, rule=O.RULE_TOKEN, caches=None):
+def step_workspace(cfg, n, split=True):
+    """split: room for the split reduction of the fills (n <= 64)."""
+    d_out = cfg.n_kv_heads * cfg.head_dim if split else 0
+    return torch.empty(tee.river_workspace_size(tee.OP_DECODE_STEP, n, cfg.d, d_out, 0, cfg.L),
+                       dtype=torch.uint8, device=DEV)
+
+
+def run_gpu(cks, cfg, wk, wv, slot, rule=O.RULE_TOKEN, caches=None, split=True):
     kc, vc = caches if caches is not None else G.nan_cache(cfg, cfg.L, device=DEV)
     n = cks[0]["h_cur"].shape[0]
     ex = torch.full((n,), -7, dtype=torch.int32, device=DEV)
-    ws = torch.empty(tee.river_workspace_size(tee.OP_DECODE_STEP, n, cfg.d, 0, 0, cfg.L),
-                     dtype=torch.uint8, device=DEV)
+    ws = step_workspace(cfg, n, split)
     tee.river_decode_step(cks, wk, wv, cfg.n_kv_heads, cfg.head_dim, slot, kc, vc, ex, rule=rule,
                           workspace=ws)
     torch.cuda.synchronize()
@@ -142,13 +148,15 @@ def llama1b_checkpoints(cfg, hs):
     return cks
 
 
-def test_decode_step_llama1b():
+@pytest.mark.parametrize("split", [True, False])
+def test_decode_step_llama1b(split):
+    """split: the fills' reduction over d runs in parts (64 rows at most)."""
     cfg = get_config(2)
     hs = {l: t.to(DEV) for l, t in G.hidden_states(cfg, cfg.n_tokens, range(7, 17)).items()}
     slot = G.slots(cfg, device=DEV)
     wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
     cks = llama1b_checkpoints(cfg, hs)
-    ex, kc, vc = run_gpu(cks, cfg, wk, wv, slot)
+    ex, kc, vc = run_gpu(cks, cfg, wk, wv, slot, split=split)
     exg = check_step(cfg, cks, ex, kc, vc, slot, wk, wv)
     counts = np.bincount(exg, minlength=cfg.L + 1)[8:]
     assert counts[0] >= 28 and counts.sum() == cfg.n_tokens      # about half exit at block 8
@@ -220,8 +228,7 @@ def test_decode_step_graph_replay():
     n = cfg.n_tokens
     kc, vc = G.nan_cache(cfg, cfg.L, device=DEV)
     ex = torch.full((n,), -7, dtype=torch.int32, device=DEV)
-    ws = torch.empty(tee.river_workspace_size(tee.OP_DECODE_STEP, n, cfg.d, 0, 0, cfg.L),
-                     dtype=torch.uint8, device=DEV)
+    ws = step_workspace(cfg, n)
     for l in buf:
         buf[l].copy_(steps[0][l])
     torch.cuda.synchronize()

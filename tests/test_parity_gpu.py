@@ -313,6 +313,45 @@ def test_kv_fill_identity_null_equals_explicit_eye():
     check_fill(cfg, k1, v1, h, rows.cpu().numpy(), slot, None, wk, wv)
 
 
+@pytest.mark.parametrize("n_layers,m", [(8, 37), (1, 64), (3, 1)])
+def test_kv_fill_split_reduction_small_rows(n_layers, m):
+    """At most 64 rows with room for partial sums: the reduction over d runs
+    in parts whose fp32 sums a second kernel adds in a fixed order. Eight
+    layers of the Llama-3.2-1B shape give 8 parts of 256 channels, one layer
+    8 parts as well, three layers 2 parts. Within the K/V bar of the oracle,
+    untouched slots unchanged, the same bits on a second call and the same
+    rows as the unsplit projection to within bf16 rounding of the sum."""
+    cfg = get_config(2)
+    layers = list(range(cfg.L - n_layers + 1, cfg.L + 1))
+    h = G.hidden_states(cfg, cfg.n_tokens, [cfg.L - n_layers])[cfg.L - n_layers].to(DEV)
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, layers)
+    g = torch.Generator().manual_seed(m)
+    sel = torch.randperm(cfg.n_tokens, generator=g)[:m].to(torch.int32)
+    rows = torch.full((64,), -1, dtype=torch.int32)
+    rows[:m] = sel
+    rows = rows.to(DEV)
+    m_dev = torch.tensor([m], dtype=torch.int32, device=DEV)
+    nh = cfg.n_kv_heads * cfg.head_dim
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, 64, cfg.d, nh, 0, n_layers),
+                     dtype=torch.uint8, device=DEV)
+    out = []
+    for w in (ws, ws, None):
+        kc, vc = G.nan_cache(cfg, n_layers, device=DEV)
+        tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=64,
+                          m_dev=m_dev, row_idx=rows, workspace=w)
+        torch.cuda.synchronize()
+        out.append((kc, vc))
+    (k1, v1), (k2, v2), (k0, v0) = out
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+    check_fill(cfg, k1, v1, h, sel.numpy(), slot, None, wk, wv)
+    s = slot[sel.long().to(DEV)].long()
+    for a, b in ((k1, k0), (v1, v0)):
+        a, b = a[:, s].float(), b[:, s].float()
+        assert torch.all((a - b).abs() <= 2 ** -7 * b.abs() + 1e-4)
+
+
 @pytest.mark.parametrize("d,hkv,hd,group", [(200, 3, 24, 40), (512, 3, 24, 64), (264, 2, 32, 8)])
 def test_kv_fill_bf16_generic_shapes(d, hkv, hd, group):
     """bf16 shapes the MFMA tiles do not take (d not a multiple of 256, an

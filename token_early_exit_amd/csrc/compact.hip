@@ -165,6 +165,28 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
 constexpr int FCH = 64;
 constexpr int FUSED_MAX = 65536;
 
+// One row of `chunks` 16-byte pieces copied by one wave: up to 8 loads per
+// lane in flight before their stores, so a long row costs one memory
+// latency per 8 x 1 KB instead of one per kilobyte.
+__device__ __forceinline__ void copy_row(u32x4* __restrict__ d, const u32x4* __restrict__ src, int chunks,
+                                         int lane) {
+  for (int c0 = 0; c0 < chunks; c0 += 8 * 64) {
+    u32x4 v[8];
+    // unconditional loads (a lane past the row reloads its last piece), so
+    // that no branch makes the wave wait between them
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = c0 + lane + 64 * i;
+      v[i] = src[c < chunks ? c : chunks - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = c0 + lane + 64 * i;
+      if (c < chunks) d[c] = v[i];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const char* h, int64_t ld_h,
                                                             int row_bytes, char* h_cont, int64_t ld_cont,
                                                             char* out, int64_t ld_out, int64_t n_out_rows) {
@@ -175,8 +197,12 @@ __global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const 
   const int chunks = row_bytes >> 4;
   // this chunk's tokens, in every wave
   const int i_own = c0 + lane;
-  const bool ex_own = i_own < n && a.mask[i_own] != 0;
-  const int rid_own = (out && ex_own) ? (a.row_ids ? a.row_ids[i_own] : i_own) : -1;
+  // the mask byte and the row id load together (the id is used only for
+  // exits)
+  const bool in = i_own < n;
+  const bool ex_own = in && a.mask[i_own] != 0;
+  const int rid_all = (out && in) ? (a.row_ids ? a.row_ids[i_own] : i_own) : -1;
+  const int rid_own = ex_own ? rid_all : -1;
   // exits in [0, c0) (loads issued now, summed below)
   int cnt = 0;
   const u32x4* m16 = (const u32x4*)a.mask;
@@ -191,9 +217,8 @@ __global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const 
       if (!((bits >> t) & 1)) continue;                     // uniform
       const int rid = __builtin_amdgcn_readlane(rid_own, t);
       if (rid < 0 || rid >= n_out_rows) continue;
-      const u32x4* src = (const u32x4*)(h + (int64_t)(c0 + t) * ld_h);
-      u32x4* d = (u32x4*)(out + (int64_t)rid * ld_out);
-      for (int c = lane; c < chunks; c += 64) d[c] = src[c];
+      copy_row((u32x4*)(out + (int64_t)rid * ld_out), (const u32x4*)(h + (int64_t)(c0 + t) * ld_h),
+               chunks, lane);
     }
   }
   cnt = (int)row_sum<16>((float)cnt);       // exact: counts stay far below 2^24
@@ -217,9 +242,8 @@ __global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const 
     for (int t = wave; t < FCH && c0 + t < n; t += 4) {
       if ((bits >> t) & 1) continue;                        // uniform
       const int er = base + __popcll(bits & ((1ull << t) - 1));
-      const u32x4* src = (const u32x4*)(h + (int64_t)(c0 + t) * ld_h);
-      u32x4* d = (u32x4*)(h_cont + (int64_t)(c0 + t - er) * ld_cont);
-      for (int c = lane; c < chunks; c += 64) d[c] = src[c];
+      copy_row((u32x4*)(h_cont + (int64_t)(c0 + t - er) * ld_cont),
+               (const u32x4*)(h + (int64_t)(c0 + t) * ld_h), chunks, lane);
     }
   }
 }

@@ -33,7 +33,9 @@ namespace river {
 // EPI_BF16N: bf16 output scaled by gamma[col], plus per-row partial sums
 // of squares of the unscaled result (one per 64-column block): the input
 // of a skipped layer's RMSNorm, applied in the K/V projection's epilogue.
-enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_CACHE = 2, EPI_BF16N = 3 };
+// EPI_PART: fp32 partial sums of a split reduction, [ksplit][batch][M_max][N]
+// (the W4 projection at small row counts; a finishing kernel adds them).
+enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_CACHE = 2, EPI_BF16N = 3, EPI_PART = 4 };
 
 struct GemmArgs {
   int M_max;
@@ -66,6 +68,8 @@ struct GemmArgs {
   const float* ss_in; int64_t ss_in_bstride; int ss_parts; float norm_eps;
   const uint16_t* bias[2]; int64_t bias_bstride;
   const int32_t* pos; const float* rcos; const float* rsin; int64_t n_pos; int head_dim;
+  // split reduction (EPI_PART): K is cut into ksplit parts of K / ksplit
+  int ksplit; float* part;
 };
 
 __device__ __forceinline__ float load_sz(const void* p, int64_t i, int bf16) {

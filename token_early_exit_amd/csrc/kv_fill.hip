@@ -197,6 +197,26 @@ size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt) {
 static size_t layer_xhat_bytes(int m_max, int d) { return align_up((size_t)m_max * d * 2, 256); }
 static size_t layer_ss_bytes(int m_max, int d) { return align_up((size_t)(d / 64 > 4 ? d / 64 : 4) * m_max * 4, 256); }
 
+// Parts of the reduction for a projection of at most 64 rows: enough
+// workgroups to fill the CUs, each part a multiple of 256 input channels,
+// the fp32 partial sums within the space left in the workspace.
+static int choose_ksplit(int m_max, int N, int K, int nl, size_t avail) {
+  if (m_max > 64) return 1;
+  const int tiles = ((N + 255) / 256) * nl;
+  const int kt = K / 64;
+  int ks = 1;
+  while (ks < 8 && ks * 2 * tiles <= N_CU && kt % (ks * 2 * 4) == 0 &&
+         (size_t)(ks * 2) * nl * m_max * N * 4 <= avail)
+    ks *= 2;
+  return ks;
+}
+
+// fp32 partial sums of up to 8 parts, K and V, for n_layers layers
+size_t kv_fill_split_workspace(int m_max, int n_out, int n_layers) {
+  if (m_max > 64 || n_out <= 0 || n_layers <= 0) return 0;
+  return align_up((size_t)8 * n_layers * m_max * 2 * n_out * 4, 256);
+}
+
 size_t kv_fill_layer_workspace(int m_max, int d, int n_layers) {
   return (size_t)n_layers * (layer_xhat_bytes(m_max, d) + layer_ss_bytes(m_max, d));
 }
@@ -256,6 +276,9 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
 
   // ss: partial sums of squares of this chunk's rows (parts per row, layer
   // stride ss_bs; 0 when every layer shares one input)
+  // part_ws: workspace left for the partial sums of a split reduction
+  char* part_ws = nullptr;
+  size_t part_bytes = 0;
   auto stage2 = [&](int l0, int nl, const uint16_t* A, int64_t lda, int64_t a_bs,
                     const int32_t* a_rows, int a_nrows, const float* ss, int64_t ss_bs,
                     int parts) -> river_status {
@@ -272,6 +295,17 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
     if (!layer) {
+      const int ks = choose_ksplit(m_max, q.N, d, nl, part_bytes);
+      if (ks > 1) {
+        q.ksplit = ks;
+        q.part = (float*)part_ws;
+        w4_gemm_launch<64, EPI_PART, false>(q, nl, s);
+        river_status st = check_launch("kv_fill projection parts");
+        if (st != RIVER_OK) return st;
+        const int64_t threads = (int64_t)nl * m_max * (q.N / 8);
+        w4_part_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(q, nl);
+        return check_launch("kv_fill projection sum");
+      }
       w4_gemm_auto<EPI_CACHE>(q, nl, s);
       return check_launch("kv_fill projection");
     }
@@ -283,13 +317,19 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     return check_launch("kv_fill projection");
   };
 
-  if (!maps && !gamma) return stage2(0, n_layers, (const uint16_t*)h, ld_h, 0, row_idx, n_rows, nullptr, 0, 0);
+  if (!maps && !gamma) {
+    part_ws = (char*)workspace;
+    part_bytes = workspace ? ws_bytes : 0;
+    return stage2(0, n_layers, (const uint16_t*)h, ld_h, 0, row_idx, n_rows, nullptr, 0, 0);
+  }
 
   const size_t xb = layer_xhat_bytes(m_max, d), sb = gamma ? layer_ss_bytes(m_max, d) : 0;
   int chunk = (int)(ws_bytes / (xb + sb));
   if (chunk > n_layers) chunk = n_layers;
   uint16_t* xh = (uint16_t*)workspace;
   float* ss = (float*)((char*)workspace + (size_t)chunk * xb);
+  part_ws = (char*)workspace + (size_t)chunk * (xb + sb);
+  part_bytes = ws_bytes - (size_t)chunk * (xb + sb);
   const int parts = maps ? d / 64 : 4;
   for (int l0 = 0; l0 < n_layers; l0 += chunk) {
     const int nl = n_layers - l0 < chunk ? n_layers - l0 : chunk;

@@ -159,6 +159,7 @@ __device__ __forceinline__ void layer_epilogue(const GemmArgs& g, f32x16 (&acc)[
 template <int BM, int EPI, bool SZ_BF16, int NW, bool LAYER>
 __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_n, int batch) {
   static_assert(!LAYER || (NW == 8 && EPI == EPI_CACHE), "the layer epilogue takes 32-column waves");
+  static_assert(EPI == EPI_CACHE || EPI == EPI_PART, "cache or partial-sum output");
   constexpr int BN = 256;
   constexpr int MI = BM / 32;            // 32-row fragments (all rows of the tile)
   constexpr int NI = 8 / NW;             // 32-column fragments per wave (NW = 4 or 8 waves)
@@ -194,7 +195,8 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     M = md < 0 ? 0 : (md < M_max ? md : M_max);
   }
   const int tiles_m_act = (M + BM - 1) / BM;
-  const int total = tiles_n * tiles_m_act * batch;
+  const int ksplit = EPI == EPI_PART ? g.ksplit : 1;
+  const int total = tiles_n * tiles_m_act * batch * ksplit;
   // persistent tiles, contiguous per XCD (see gemm_nt_kernel)
   const int xcd = blockIdx.x & 7, wg_in_xcd = blockIdx.x >> 3;
   const int per_xcd = (gridDim.x + 7 - xcd) >> 3;
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5;
-  const int KT = K / 64;                 // a multiple of 4 on this path
+  const int KT = K / 64 / ksplit;        // slabs per tile, a multiple of 4 on this path
   const int slabs_per_group = grp >> 6;
 
   using I0 = std::integral_constant<int, 0>;
@@ -220,7 +222,9 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
   for (int tile = xcd * chunk + wg_in_xcd; tile < t_end; tile += per_xcd) {
     const int nt = tile % tiles_n;
     const int mt = (tile / tiles_n) % tiles_m_act;
-    const int z = tile / (tiles_n * tiles_m_act);
+    const int z = (tile / (tiles_n * tiles_m_act)) % batch;
+    const int ks = tile / (tiles_n * tiles_m_act * batch);   // part of the reduction
+    const int j0 = ks * KT;                                  // its first slab
     const int m0 = mt * BM, n0 = nt * BN;
 
     // A: DMA block b = i * 4 + wave covers LDS chunks [64 b, 64 b + 64);
@@ -388,9 +392,9 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
         er[j] = g.e_rows ? g.e_rows[rc] : rc;
       }
     }
-    issue(I0{}, 0);
-    issue(I1{}, 1);
-    issue(I2{}, 2);
+    issue(I0{}, j0);
+    issue(I1{}, j0 + 1);
+    issue(I2{}, j0 + 2);
     wait_barrier<2 * PER_SLAB, true>();   // slab 0 landed
     if constexpr (EPI == EPI_CACHE) {
 #pragma unroll
@@ -402,7 +406,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     }
     Frag f0, f1;
     BRegs bA, bB;
-    fetch(S0, 0, bA);
+    fetch(S0, j0, bA);
     SC sc = scales(bA);
     frag(S0, bA, sc, 0, f0);
 
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
       using NX = std::integral_constant<int, (ST + 1) & 3>;
       using PV = std::integral_constant<int, (ST + 3) & 3>;
       constexpr bool ISS = decltype(issue_next)::value;
-      if constexpr (ISS) issue(PV{}, kt + 3);
+      if constexpr (ISS) issue(PV{}, j0 + kt + 3);
       frag(stage(st), cur, sc, 1, f1);
       mfma(f0);
       frag(stage(st), cur, sc, 2, f0);
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
       mfma(f0);
       interleave<3, MI * NI, MI, ISS ? PER_SLAB : 0>();
       wait_barrier<decltype(w)::value, true>();   // slab kt + 1 landed
-      fetch(stage(NX{}), kt + 1, nxt);           // (spare reads after the last slab)
+      fetch(stage(NX{}), j0 + kt + 1, nxt);      // (spare reads after the last slab)
       sc = scales(nxt);
       frag(stage(NX{}), nxt, sc, 0, f0);
       mfma(f1);
@@ -450,6 +454,25 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     iter(I1{}, bB, bA, kt + 1, W1{}, F_{});
     iter(I2{}, bA, bB, kt + 2, W0{}, F_{});
     iter(I3{}, bB, bA, kt + 3, W0{}, F_{});
+
+    if constexpr (EPI == EPI_PART) {
+      // fp32 partial sums straight from the accumulators: lane l holds row
+      // mi * 32 + l % 32 and the four columns 8 gq + 4 (l / 32) + 0..3
+      float* P = g.part + ((int64_t)ks * batch + z) * M_max * N;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int r = m0 + mi * 32 + (lane & 31);
+            const int c = n0 + CW * wave + ni * 32 + 8 * gq + 4 * h;
+            if (r < M && c < N)
+              *(f32x4*)(P + (int64_t)r * N + c) = f32x4{acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1],
+                                                        acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3]};
+          }
+      continue;                                  // next tile
+    }
 
     // ---- epilogue. The transposed 32x32 accumulator gives lane l output
     // row l % 32 of fragment mi and, for gq = 0..3, the four consecutive
@@ -508,11 +531,50 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
 // W4_WAVES: 4 waves (64 columns each, one per SIMD) or 8 (32 columns each,
 // two per SIMD, which hide each other's latencies).
 constexpr int W4_WAVES = 8;
+// The parts of a split reduction added in order, rounded to bf16 and
+// written to each row's cache slot (the EPI_CACHE epilogue's addressing):
+// one thread per 8 columns of a row.
+__global__ __launch_bounds__(256) void w4_part_finish_kernel(GemmArgs g, int batch) {
+  int M = g.M_max;
+  if (g.M_dev) {
+    const int md = *g.M_dev;
+    M = md < 0 ? 0 : (md < g.M_max ? md : g.M_max);
+  }
+  const int N = g.N, nh = g.nh;
+  const int per = N / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int p = (int)(idx % per);
+  const int t = (int)((idx / per) % g.M_max);
+  const int z = (int)(idx / ((int64_t)per * g.M_max));
+  if (z >= batch || t >= M) return;
+  const int e = g.e_rows ? g.e_rows[t] : t;
+  if (e < 0 || e >= g.e_nrows) return;
+  const int sl = g.slot[e];
+  if (sl < 0 || sl >= g.n_slots) return;
+  const int col = 8 * p;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < g.ksplit; ++ks) {
+    const float* src = g.part + (((int64_t)ks * batch + z) * g.M_max + t) * N + col;
+    const f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] += a[i];
+      v[4 + i] += b[i];
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  const bool isv = col >= nh;
+  uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc);
+  *(u32x4*)(dst + (int64_t)z * g.cache_bstride + (int64_t)sl * nh + (isv ? col - nh : col)) = o;
+}
+
 template <int BM, int EPI, bool LAYER>
 inline void w4_gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 255) / 256;
   const int tm = (g.M_max + BM - 1) / BM;
-  const int64_t tiles = (int64_t)tn * tm * batch;
+  const int64_t tiles = (int64_t)tn * tm * batch * (EPI == EPI_PART ? g.ksplit : 1);
   int grid = (int)(tiles < N_CU ? tiles : N_CU);
   grid = (grid + 7) / 8 * 8;
   if (g.sz_bf16[0]) w4_gemm_kernel<BM, EPI, true, W4_WAVES, LAYER><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
