@@ -452,9 +452,17 @@ const char* river_version(void);
 /* Test hook: force the compaction path (0 = automatic; 1 = single wave
  * ballot, n <= 64; 2 = one workgroup scan; 3 = multi-workgroup scan; 1-3
  * then copy rows in a second launch; 4 = one fused launch, each workgroup
- * counting the exits before its 64 tokens itself, the automatic choice for
- * n <= 65536). Process-wide; the paths give bitwise-identical results. */
+ * counting the exits before its 16 (n <= 16384) or 64 tokens itself, the
+ * automatic choice for n <= 65536). Process-wide; the paths give
+ * bitwise-identical results. */
 river_status river_debug_set_compact_path(int path);
+
+/* Test hook: force the tile of the fill's bf16 map GEMM (0 = automatic:
+ * 256 x 256 once that gives at least two tiles per compute unit, else
+ * 128 x 128; 1 = 128 x 128; 2 = 256 x 256). Process-wide. The two tiles
+ * group the reduction over d into MFMA steps differently, so their results
+ * agree to fp32 rounding, not bit for bit. */
+river_status river_debug_set_gemm_path(int path);
 
 #ifdef __cplusplus
 }

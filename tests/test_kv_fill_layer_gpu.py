@@ -130,10 +130,20 @@ def test_layer_fill_parts_with_maps(norm, bias, rope):
     check_layer(cfg, kc, vc, h, rows.cpu().numpy(), slot, maps, wk, wv, parts, pos)
 
 
-@pytest.mark.parametrize("ws_layers", [8, 3])
-def test_layer_fill_gpt2_ridge_maps_norm_bias(ws_layers):
+@pytest.mark.parametrize("ws_layers,gemm_path", [(8, 0), (3, 0), (8, 2)])
+def test_layer_fill_gpt2_ridge_maps_norm_bias(ws_layers, gemm_path):
     """GPT-2-shape prefill: ridge maps, input RMSNorm and K/V biases (no
-    rotary embedding), half of the 4096 tokens, count on the device."""
+    rotary embedding), half of the 4096 tokens, count on the device; with
+    gemm_path 2 the map GEMM (with its RMSNorm epilogue) runs on 256 x 256
+    tiles."""
+    tee.river_debug_set_gemm_path(gemm_path)
+    try:
+        _gpt2_ridge_maps_norm_bias(ws_layers)
+    finally:
+        tee.river_debug_set_gemm_path(0)
+
+
+def _gpt2_ridge_maps_norm_bias(ws_layers):
     cfg = get_config(1)
     e = 4
     layers = list(range(e + 1, cfg.L + 1))

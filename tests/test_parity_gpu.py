@@ -206,6 +206,35 @@ def test_compact_all_paths(path, n):
         assert torch.equal(again[0][:nc], cont[:nc]) and torch.equal(again[1][:ne], ext[:ne])
 
 
+@pytest.mark.parametrize("n", [4096, 16385])
+@pytest.mark.parametrize("d,dt", [(8, torch.bfloat16), (72, torch.bfloat16), (768, torch.bfloat16),
+                                  (4096, torch.bfloat16), (1000, torch.float32)])
+def test_compact_fused_row_lengths(n, d, dt):
+    """The fused launch (16 tokens per workgroup up to 16384 tokens, 64
+    beyond) on rows of one 16-byte piece, a ragged number of pieces, and
+    rows needing several passes, with gathered continuing rows and
+    scattered exits, against the oracle."""
+    tee.river_debug_set_compact_path(0)
+    g = torch.Generator().manual_seed(n + d)
+    h = torch.randn(n, d, generator=g).to(dt).to(DEV)
+    rid = torch.randperm(n + 5, generator=g)[:n].to(torch.int32).to(DEV)
+    m = torch.rand(n, generator=g) < 0.13
+    mask = m.to(torch.uint8).to(DEV)
+    out = torch.full((n + 5, d), float("nan"), dtype=dt, device=DEV)
+    cont, ext, counts, hc, ridc = compact_gpu(mask, h, rid, out)
+    ref = O.compact(mask.cpu().numpy(), h.cpu().float().numpy(), rid.cpu().numpy(),
+                    out.cpu().float().numpy())
+    nc, ne = (int(x) for x in ref["counts"])
+    assert counts.cpu().tolist() == [nc, ne]
+    assert np.array_equal(cont.cpu().numpy()[:nc], ref["cont_idx"])
+    assert np.array_equal(ext.cpu().numpy()[:ne], ref["exit_idx"])
+    iv = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert torch.equal(hc[:nc].view(iv), h[torch.from_numpy(ref["cont_idx"]).to(DEV)].view(iv))
+    o = out.cpu().float().numpy()
+    assert np.array_equal(np.isnan(o), np.isnan(ref["out"]))
+    assert np.array_equal(np.nan_to_num(o), np.nan_to_num(ref["out"]))
+
+
 def test_compact_row_id_out_of_range_is_skipped():
     n, d = 10, 64
     h = torch.randn(n, d).bfloat16().to(DEV)
@@ -296,6 +325,39 @@ def test_kv_fill_gpt2_ridge_maps_device_count(ws_layers):
                       m_max=cfg.n_tokens, maps=maps, ws_layers=ws_layers)
     pick = np.random.default_rng(0).choice(sel.numel(), 256, replace=False)
     check_fill(cfg, kc, vc, h, sel.numpy(), slot, maps, wk, wv, sample=np.sort(pick))
+
+
+@pytest.mark.parametrize("gemm_path", [1, 2])
+def test_kv_fill_map_gemm_tiles(gemm_path):
+    """The map GEMM on 128 x 128 and on 256 x 256 tiles (forced), d = 1024,
+    three layers, 300 of 640 rows (a ragged last row tile in both) with the
+    count on the device: every filled row within the K/V bar, the two tiles
+    within bf16 rounding of each other."""
+    cfg = get_config(1, d=1024, n_tokens=640, n_slots=700)
+    layers = [5, 6, 7]
+    h = G.hidden_states(cfg, cfg.n_tokens, [4])[4].to(DEV)
+    g = torch.Generator().manual_seed(1024)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    maps = G.near_identity_maps(cfg, len(layers)).to(DEV)
+    sel = torch.sort(torch.randperm(cfg.n_tokens, generator=g)[:300]).values.to(torch.int32)
+    rows = torch.full((cfg.n_tokens,), -1, dtype=torch.int32)
+    rows[:300] = sel
+    m_dev = torch.tensor([300], dtype=torch.int32, device=DEV)
+    out = {}
+    try:
+        for p in (gemm_path, 3 - gemm_path):
+            tee.river_debug_set_gemm_path(p)
+            out[p] = fill_gpu(cfg, h, slot, wk, wv, len(layers), row_idx=rows.to(DEV), m_dev=m_dev,
+                              m_max=cfg.n_tokens, maps=maps)
+    finally:
+        tee.river_debug_set_gemm_path(0)
+    kc, vc = out[gemm_path]
+    check_fill(cfg, kc, vc, h, sel.numpy(), slot, maps, wk, wv)
+    s = slot[sel.long().to(DEV)].long()
+    for a, b in zip(out[1], out[2]):
+        a, b = a[:, s].float(), b[:, s].float()
+        assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-2 * b.abs().amax(dim=-1, keepdim=True))
 
 
 def test_kv_fill_identity_null_equals_explicit_eye():

@@ -12,6 +12,7 @@ namespace river_host {
 
 static thread_local char g_err[512] = "";
 static int g_compact_path = 0;
+static int g_gemm_path = 0;
 
 void set_error(const char* fmt, ...) {
   va_list ap;
@@ -35,6 +36,7 @@ river_status check_launch(const char* what) {
 }
 
 int compact_path_override() { return g_compact_path; }
+int gemm_path_override() { return g_gemm_path; }
 
 static bool dt_ok(river_dtype dt) { return dt == RIVER_F32 || dt == RIVER_BF16; }
 
@@ -56,6 +58,12 @@ const char* river_version(void) { return "river 0.1.0 (gfx950)"; }
 river_status river_debug_set_compact_path(int path) {
   if (path < 0 || path > 4) return fail(RIVER_ERR_ARG, "compact path must be 0..4, got %d", path);
   g_compact_path = path;
+  return RIVER_OK;
+}
+
+river_status river_debug_set_gemm_path(int path) {
+  if (path < 0 || path > 2) return fail(RIVER_ERR_ARG, "gemm path must be 0..2, got %d", path);
+  g_gemm_path = path;
   return RIVER_OK;
 }
 

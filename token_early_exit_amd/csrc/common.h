@@ -123,6 +123,15 @@ __device__ __forceinline__ void wait_vm() {
 // data format, no swizzle, no index stride
 constexpr int RSRC_WORD3 = 0x00020000;
 
+// 16 bytes per lane from the buffer [base, base + bytes) at byte offset voff
+// into registers; a lane whose 16 bytes lie past the end reads zeros and
+// touches no memory (bytes and voff multiples of 16). No branch guards the
+// load, so a wave keeps several in flight.
+__device__ __forceinline__ u32x4 buf_load16(const void* base, int bytes, uint32_t voff) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, RSRC_WORD3);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
 // SIZE bytes per lane from the buffer [base, base + bytes) at byte offset
 // voff + soff straight into LDS (lane l writes lds + SIZE * l); a lane whose
 // bytes lie past the end reads zeros. base, bytes and soff are uniform, so
@@ -149,6 +158,7 @@ inline size_t esize(river_dtype dt) { return dt == RIVER_BF16 ? 2 : 4; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int compact_path_override();
+int gemm_path_override();
 
 // launchers implemented by the kernel files; argument checks are done by
 // the caller (api.hip)

@@ -155,71 +155,77 @@ __device__ __forceinline__ int nonzero_bytes(uint32_t w) {
 }
 
 // ---------------------------------------------------------- fused path
-// One launch for indices and rows, n <= FUSED_MAX: workgroup c owns tokens
-// [64 c, 64 c + 64). Every wave reads the chunk's 64 mask bytes and ballots
-// them, so each wave knows which of the chunk's rows exit. Exited rows go to
-// out[row_ids[i]], which does not depend on any rank, so they are copied
-// while the exits before the chunk are still being counted (16-byte reads
-// of the mask prefix, at most n bytes). With that count the workgroup writes
-// both index lists and copies its continuing rows to h_cont.
-constexpr int FCH = 64;
+// One launch for indices and rows, n <= FUSED_MAX: workgroup c owns the
+// FCH tokens [FCH c, FCH c + FCH). Every wave reads the chunk's mask bytes
+// and ballots them. The rows to copy (exits when `out` is set, continuing
+// rows when `h_cont` is) are dealt round-robin to the four waves, and each
+// wave issues the loads of all its rows before the count of the exits
+// before the chunk (16-byte reads of the mask prefix, issued first) is
+// reduced: a row costs one memory latency for its loads and one for its
+// stores, whatever the number of rows per wave. The workgroup then writes
+// both index lists and stores the rows: an exited row to out[row_ids[i]],
+// a continuing one to h_cont[i - (exits before i)]. Rows longer than
+// 64 KP 16-byte pieces per lane go in several passes.
 constexpr int FUSED_MAX = 65536;
 
-// One row of `chunks` 16-byte pieces copied by one wave: up to 8 loads per
-// lane in flight before their stores, so a long row costs one memory
-// latency per 8 x 1 KB instead of one per kilobyte.
-__device__ __forceinline__ void copy_row(u32x4* __restrict__ d, const u32x4* __restrict__ src, int chunks,
-                                         int lane) {
-  for (int c0 = 0; c0 < chunks; c0 += 8 * 64) {
-    u32x4 v[8];
-    // unconditional loads (a lane past the row reloads its last piece), so
-    // that no branch makes the wave wait between them
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = c0 + lane + 64 * i;
-      v[i] = src[c < chunks ? c : chunks - 1];
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = c0 + lane + 64 * i;
-      if (c < chunks) d[c] = v[i];
-    }
-  }
-}
-
+template <int FCH>
 __global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const char* h, int64_t ld_h,
                                                             int row_bytes, char* h_cont, int64_t ld_cont,
                                                             char* out, int64_t ld_out, int64_t n_out_rows) {
+  constexpr int RW = FCH / 4;                     // row slots per wave
+  constexpr int KP = FCH <= 16 ? 2 : 1;           // 16-byte pieces per lane, row and pass
   __shared__ int s_part[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c0 = blockIdx.x * FCH;
   const int n = a.n;
   const int chunks = row_bytes >> 4;
-  // this chunk's tokens, in every wave
+  // this chunk's tokens: lane l < FCH of every wave holds token c0 + l; the
+  // mask byte and the row id load together (the id is used only for exits)
   const int i_own = c0 + lane;
-  // the mask byte and the row id load together (the id is used only for
-  // exits)
-  const bool in = i_own < n;
+  const bool in = lane < FCH && i_own < n;
   const bool ex_own = in && a.mask[i_own] != 0;
-  const int rid_all = (out && in) ? (a.row_ids ? a.row_ids[i_own] : i_own) : -1;
-  const int rid_own = ex_own ? rid_all : -1;
-  // exits in [0, c0) (loads issued now, summed below)
-  int cnt = 0;
-  const u32x4* m16 = (const u32x4*)a.mask;
-  for (int v = tid; v < (c0 >> 4); v += 256) {
-    const u32x4 w = m16[v];
-    cnt += nonzero_bytes(w[0]) + nonzero_bytes(w[1]) + nonzero_bytes(w[2]) + nonzero_bytes(w[3]);
+  const int rid_own = (out && in) ? (a.row_ids ? a.row_ids[i_own] : i_own) : -1;
+  const uint64_t bits = __ballot(ex_own);         // exits of the chunk
+  const uint64_t valid = __ballot(in);            // tokens of the chunk
+  const uint64_t need = (h && out ? bits : 0ull) | (h && h_cont ? valid & ~bits : 0ull);
+  // slot j of this wave: the row of rank 4 j + wave among the rows to copy
+  const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(need >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)need, 0u));
+  const bool mine = lane < FCH && ((need >> lane) & 1);
+  int row[RW];
+#pragma unroll
+  for (int j = 0; j < RW; ++j) {
+    const uint64_t b = __ballot(mine && rank == 4 * j + wave);
+    row[j] = b ? __builtin_ctzll(b) : -1;
   }
-  const uint64_t bits = __ballot(ex_own);
-  // exit scatter: rows t = wave, wave + 4, ... of the chunk
-  if (h && out) {
-    for (int t = wave; t < FCH; t += 4) {
-      if (!((bits >> t) & 1)) continue;                     // uniform
-      const int rid = __builtin_amdgcn_readlane(rid_own, t);
-      if (rid < 0 || rid >= n_out_rows) continue;
-      copy_row((u32x4*)(out + (int64_t)rid * ld_out), (const u32x4*)(h + (int64_t)(c0 + t) * ld_h),
-               chunks, lane);
-    }
+  const bool any = row[0] >= 0;                   // uniform
+  // every load below is unconditional: a free slot's buffer has no bytes,
+  // and a piece past the end of a buffer reads zeros without a memory access
+  const char* src[RW];
+  int sbytes[RW];
+#pragma unroll
+  for (int j = 0; j < RW; ++j) {
+    src[j] = h + (int64_t)(c0 + (row[j] >= 0 ? row[j] : 0)) * ld_h;
+    sbytes[j] = row[j] >= 0 ? row_bytes : 0;
+  }
+  u32x4 v[RW][KP];
+#pragma unroll
+  for (int j = 0; j < RW; ++j)
+#pragma unroll
+    for (int k = 0; k < KP; ++k) v[j][k] = buf_load16(src[j], sbytes[j], (uint32_t)(lane + 64 * k) * 16);
+  // exits in [0, c0): its first 16-byte pieces load with the rows, the rest
+  // (prefixes over 16 KB) in a loop
+  constexpr int PF = 4;
+  u32x4 pm[PF];
+#pragma unroll
+  for (int k = 0; k < PF; ++k) pm[k] = buf_load16(a.mask, c0, (uint32_t)(tid + 256 * k) * 16);
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < PF; ++k)
+    cnt += nonzero_bytes(pm[k][0]) + nonzero_bytes(pm[k][1]) + nonzero_bytes(pm[k][2]) + nonzero_bytes(pm[k][3]);
+  const u32x4* m16 = (const u32x4*)a.mask;
+  for (int q = tid + 256 * PF; q < (c0 >> 4); q += 256) {
+    const u32x4 w = m16[q];
+    cnt += nonzero_bytes(w[0]) + nonzero_bytes(w[1]) + nonzero_bytes(w[2]) + nonzero_bytes(w[3]);
   }
   cnt = (int)row_sum<16>((float)cnt);       // exact: counts stay far below 2^24
   cnt += __shfl_xor(cnt, 16, WAVE);
@@ -228,23 +234,45 @@ __global__ __launch_bounds__(256) void compact_fused_kernel(CompactIdx a, const 
   __syncthreads();
   const int base = s_part[0] + s_part[1] + s_part[2] + s_part[3];
   if (wave == 0) {
-    const int rank = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
-    if (i_own < n) emit(a, i_own, ex_own, rank);
+    const int rk = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(bits >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
+    if (in) emit(a, i_own, ex_own, rk);
     if (c0 + FCH >= n && lane == 0) {          // the last chunk knows the total
       const int ne = base + __popcll(bits);
       a.counts[0] = n - ne;
       a.counts[1] = ne;
     }
   }
-  // continuing rows: row t goes to h_cont[(c0 + t) - (exits before it)]
-  if (h && h_cont) {
-    for (int t = wave; t < FCH && c0 + t < n; t += 4) {
-      if ((bits >> t) & 1) continue;                        // uniform
+  if (!any) return;
+  // destination of each slot's row (null: nothing to store)
+  u32x4* dst[RW];
+#pragma unroll
+  for (int j = 0; j < RW; ++j) {
+    dst[j] = nullptr;
+    const int t = row[j];
+    if (t < 0) continue;
+    if ((bits >> t) & 1) {
+      const int rid = __builtin_amdgcn_readlane(rid_own, t);
+      if (rid >= 0 && rid < n_out_rows) dst[j] = (u32x4*)(out + (int64_t)rid * ld_out);
+    } else {
       const int er = base + __popcll(bits & ((1ull << t) - 1));
-      copy_row((u32x4*)(h_cont + (int64_t)(c0 + t - er) * ld_cont),
-               (const u32x4*)(h + (int64_t)(c0 + t) * ld_h), chunks, lane);
+      dst[j] = (u32x4*)(h_cont + (int64_t)(c0 + t - er) * ld_cont);
     }
+  }
+  for (int p0 = 0;;) {
+#pragma unroll
+    for (int j = 0; j < RW; ++j)
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        const int c = p0 + lane + 64 * k;
+        if (dst[j] && c < chunks) dst[j][c] = v[j][k];
+      }
+    p0 += 64 * KP;
+    if (p0 >= chunks) break;
+#pragma unroll
+    for (int j = 0; j < RW; ++j)
+#pragma unroll
+      for (int k = 0; k < KP; ++k) v[j][k] = buf_load16(src[j], sbytes[j], (uint32_t)(p0 + lane + 64 * k) * 16);
   }
 }
 
@@ -317,9 +345,15 @@ river_status launch_compact(int n, int d, river_dtype dt, const uint8_t* mask, c
   if (path == 0) path = n <= FUSED_MAX ? 4 : 3;
   const int64_t es = (int64_t)esize(dt);
   if (path == 4) {
-    compact_fused_kernel<<<(n + FCH - 1) / FCH, 256, 0, s>>>(
-        a, (h_cont || out) ? (const char*)h : nullptr, ld_h * es, (int)(d * es), (char*)h_cont,
-        ld_cont * es, (char*)out, ld_out * es, n_out_rows);
+    // 16 tokens per workgroup while the mask prefixes the workgroups read
+    // stay small (n^2 / 32 bytes in all), 64 beyond
+    const char* hh = (h_cont || out) ? (const char*)h : nullptr;
+    if (n <= 16384)
+      compact_fused_kernel<16><<<(n + 15) / 16, 256, 0, s>>>(a, hh, ld_h * es, (int)(d * es), (char*)h_cont,
+                                                             ld_cont * es, (char*)out, ld_out * es, n_out_rows);
+    else
+      compact_fused_kernel<64><<<(n + 63) / 64, 256, 0, s>>>(a, hh, ld_h * es, (int)(d * es), (char*)h_cont,
+                                                             ld_cont * es, (char*)out, ld_out * es, n_out_rows);
     return check_launch("compact fused");
   }
   if (path == 1) {

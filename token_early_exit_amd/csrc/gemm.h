@@ -128,11 +128,11 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
     const int md = *g.M_dev;
     M = md < 0 ? 0 : (md < M_max ? md : M_max);
   }
-  // Persistent tiles: only the tiles of the M rows that exist are visited.
-  // Tile t = (z * tiles_m_active + mt) * tiles_n + nt. Workgroups are
+  // Persistent tiles: only the tiles of the M rows that exist are visited,
+  // tiles_n * tiles_m_active of them per batch entry z. Workgroups are
   // dispatched round-robin over the 8 XCDs; XCD x walks the contiguous range
-  // [x * chunk, (x + 1) * chunk) so that neighbouring tiles (same A rows,
-  // same batch entry) share that XCD's L2.
+  // [x * chunk, (x + 1) * chunk) so that neighbouring tiles (one batch
+  // entry, a few row and column tiles) share that XCD's L2.
   const int tiles_m_act = (M + BM - 1) / BM;
   const int total = tiles_n * tiles_m_act * batch;
   const int xcd = blockIdx.x & 7, wg_in_xcd = blockIdx.x >> 3;
@@ -157,9 +157,18 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
   };
 
   for (int tile = xcd * chunk + wg_in_xcd; tile < t_end; tile += per_xcd) {
-    const int nt = tile % tiles_n;
-    const int mt = (tile / tiles_n) % tiles_m_act;
+    // Inside a batch entry the tiles go in groups of GM row tiles, column
+    // tile by column tile, so the 32 tiles an XCD runs at once cover about
+    // 4 row tiles x 8 column tiles: 12 operand tiles to bring into its L2
+    // instead of 33 for one row tile across 32 column tiles.
+    constexpr int GM = 4;
     const int z = tile / (tiles_n * tiles_m_act);
+    const int tz = tile - z * tiles_n * tiles_m_act;
+    const int g0 = tz / (GM * tiles_n) * GM;                 // first row tile of the group
+    const int gsz = tiles_m_act - g0 < GM ? tiles_m_act - g0 : GM;
+    const int tg = tz - g0 * tiles_n;
+    const int mt = g0 + tg % gsz;
+    const int nt = tg / gsz;
     const int m0 = mt * BM, n0 = nt * BN;
 
     // load i of this thread fills LDS chunk p = (i * 4 + wave) * 64 + lane of

@@ -27,6 +27,7 @@
 // row scale, the bias and the rotation to its fp32 accumulators.
 #include "common.h"
 #include "gemm.h"
+#include "gemm_big.h"
 #include "w4gemm.h"
 
 namespace river {
@@ -343,9 +344,9 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
       if (gamma) {
         p.gamma = (const uint16_t*)gamma + (int64_t)l0 * d; p.gamma_bstride = d;
         p.ss = ss; p.ss_bstride = sb / 4;
-        gemm_auto<EPI_BF16N>(p, nl, s);
+        gemm_bf16_auto<EPI_BF16N>(p, nl, s);
       } else {
-        gemm_auto<EPI_BF16>(p, nl, s);
+        gemm_bf16_auto<EPI_BF16>(p, nl, s);
       }
       st = check_launch("kv_fill map");
     } else {
