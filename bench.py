@@ -488,8 +488,11 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
+# the projection kernel's own code: the kernel and its launch (w4gemm.h), the
+# dequantization and scheduling helpers (gemm.h) and the device helpers
+# (common.h)
 KERNEL_SOURCES = ["token_early_exit_amd/csrc/w4gemm.h", "token_early_exit_amd/csrc/gemm.h",
-                  "token_early_exit_amd/csrc/kv_fill.hip", "token_early_exit_amd/csrc/common.h"]
+                  "token_early_exit_amd/csrc/common.h"]
 
 
 def measured_traffic():

@@ -464,6 +464,13 @@ river_status river_debug_set_compact_path(int path);
  * agree to fp32 rounding, not bit for bit. */
 river_status river_debug_set_gemm_path(int path);
 
+/* Test hook: 1 forces river_decode_step onto its per-checkpoint launches
+ * (route, compact, fill per checkpoint) where it would take the two
+ * decision launches for all checkpoints (routers off, n <= 1024, at most
+ * 32 checkpoints); 0 = automatic. Process-wide; both give bit-identical
+ * results. */
+river_status river_debug_set_decode_path(int path);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,6 +162,35 @@ def test_decode_step_llama1b(split):
     assert counts[0] >= 28 and counts.sum() == cfg.n_tokens      # about half exit at block 8
 
 
+@pytest.mark.parametrize("rule", [O.RULE_TOKEN, O.RULE_BATCH_MIN])
+def test_decode_step_two_launch_equals_per_checkpoint(rule):
+    """Routers off: the two decision launches for all checkpoints and the
+    per-checkpoint route/compact launches give the same bits (exit blocks
+    and caches)."""
+    cfg = get_config(2)
+    hs = {l: t.to(DEV) for l, t in G.hidden_states(cfg, cfg.n_tokens, range(7, 17)).items()}
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    cks = llama1b_checkpoints(cfg, hs)
+    if rule == O.RULE_BATCH_MIN:
+        cos, *_ = O.route(np64(hs[10]), np64(hs[11]), None, 1e-6, None, None, -INF, -INF)
+        for c in cks:
+            c["tau"] = 2.0
+        cks[3]["tau"] = float(cos.min()) - 1e-3
+    out = []
+    try:
+        for path in (0, 1):
+            tee.river_debug_set_decode_path(path)
+            out.append(run_gpu(cks, cfg, wk, wv, slot, rule=rule))
+    finally:
+        tee.river_debug_set_decode_path(0)
+    (e0, k0, v0), (e1, k1, v1) = out
+    assert torch.equal(e0, e1)
+    assert torch.equal(k0.view(torch.int16), k1.view(torch.int16))
+    assert torch.equal(v0.view(torch.int16), v1.view(torch.int16))
+    assert (e0 < cfg.L).any()
+
+
 def test_decode_step_llama1b_batch_rule():
     """Batch rule: the step lets everybody exit at block 11, where tau
     sits below the smallest cosine, and nobody before."""

@@ -98,6 +98,7 @@ def test_kv_fill_and_ridge_argument_errors():
     assert r == 5                                                  # workspace too small
     assert lib.river_debug_set_compact_path(9) == 1
     assert lib.river_debug_set_gemm_path(3) == 1
+    assert lib.river_debug_set_decode_path(2) == 1
 
 
 def _exit_projection(**kw):

@@ -28,7 +28,8 @@ STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_DTYPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPO
 EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fill",
            "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
-           "river_debug_set_compact_path", "river_debug_set_gemm_path"]
+           "river_debug_set_compact_path", "river_debug_set_gemm_path",
+           "river_debug_set_decode_path"]
 
 
 class RiverError(RuntimeError):
@@ -93,10 +94,11 @@ def load():
     lib.river_ridge_fit.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _S, _P]
     for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill",
               "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
-              "river_debug_set_compact_path", "river_debug_set_gemm_path"):
+              "river_debug_set_compact_path", "river_debug_set_gemm_path", "river_debug_set_decode_path"):
         getattr(lib, f).restype = _I
     lib.river_debug_set_compact_path.argtypes = [_I]
     lib.river_debug_set_gemm_path.argtypes = [_I]
+    lib.river_debug_set_decode_path.argtypes = [_I]
     lib.river_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.river_workspace_size.restype = _S
     lib.river_last_error.restype = ctypes.c_char_p
@@ -152,6 +154,10 @@ def river_debug_set_compact_path(path):
 
 def river_debug_set_gemm_path(path):
     _check(load().river_debug_set_gemm_path(path))
+
+
+def river_debug_set_decode_path(path):
+    _check(load().river_debug_set_decode_path(path))
 
 
 def river_route(h_prev, h_cur, mask_out, *, gamma=None, eps=1e-6, w_down=None, w_up=None,

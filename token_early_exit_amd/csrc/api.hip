@@ -13,6 +13,7 @@ namespace river_host {
 static thread_local char g_err[512] = "";
 static int g_compact_path = 0;
 static int g_gemm_path = 0;
+static int g_decode_path = 0;
 
 void set_error(const char* fmt, ...) {
   va_list ap;
@@ -37,6 +38,7 @@ river_status check_launch(const char* what) {
 
 int compact_path_override() { return g_compact_path; }
 int gemm_path_override() { return g_gemm_path; }
+int decode_path_override() { return g_decode_path; }
 
 static bool dt_ok(river_dtype dt) { return dt == RIVER_F32 || dt == RIVER_BF16; }
 
@@ -67,6 +69,12 @@ river_status river_debug_set_gemm_path(int path) {
   return RIVER_OK;
 }
 
+river_status river_debug_set_decode_path(int path) {
+  if (path < 0 || path > 1) return fail(RIVER_ERR_ARG, "decode path must be 0..1, got %d", path);
+  g_decode_path = path;
+  return RIVER_OK;
+}
+
 size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int n_layers) {
   (void)n_targets;
   switch (op) {
@@ -80,7 +88,7 @@ size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int 
       return kv_fill_layer_workspace(n, d, n_layers);
     case RIVER_OP_DECODE_STEP:
       if (n <= 0 || d <= 0) return 0;
-      return decode_fixed_workspace(n) + (n_layers > 1 ? kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) : 0) +
+      return decode_fixed_workspace(n, n_layers) + (n_layers > 1 ? kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) : 0) +
              (n_layers > 1 ? kv_fill_split_workspace(n, d_out, n_layers - 1) : 0);
     case RIVER_OP_ROUTER_FIT:
       if (n <= 0 || d <= 0 || d_out <= 0 || n_targets <= 0 || n_layers <= 0) return 0;
@@ -297,7 +305,7 @@ river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_c
     }
     any_maps |= k.maps != nullptr;
   }
-  const size_t fixed = decode_fixed_workspace(n);
+  const size_t fixed = decode_fixed_workspace(n, n_layers);
   const size_t need = fixed + (any_maps ? kv_fill_workspace(n, d, 1, dt) : 0);
   if (!workspace || ws_bytes < need)
     return fail(RIVER_ERR_WORKSPACE, "decode_step: workspace of at least %zu bytes needed, %zu given", need, ws_bytes);

@@ -1,5 +1,5 @@
-// Shared device helpers and host-side plumbing of the river library
-// (gfx950 / CDNA4, wave64).
+// Shared device helpers of the river library (gfx950 / CDNA4, wave64); the
+// host-side plumbing is in host.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -146,76 +146,4 @@ __device__ __forceinline__ void buf_lds(const void* base, int bytes, uint32_t vo
 
 }  // namespace river
 
-// ------------------------------------------------------------ host plumbing
-namespace river_host {
-
-void set_error(const char* fmt, ...);
-river_status fail(river_status st, const char* fmt, ...);
-river_status check_launch(const char* what);
-
-inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-inline size_t esize(river_dtype dt) { return dt == RIVER_BF16 ? 2 : 4; }
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-int compact_path_override();
-int gemm_path_override();
-
-// launchers implemented by the kernel files; argument checks are done by
-// the caller (api.hip)
-
-// the running-token state of the generation loop (river_decode_step)
-struct RouteLive {
-  const uint8_t* alive_in; uint8_t* alive_out; int32_t* exit_layer; int exit_value;
-};
-river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int64_t ld_prev,
-                          const void* h_cur, int64_t ld_cur, const void* gamma, float eps,
-                          const void* w_down, const void* w_up, int b, float tau, float theta,
-                          river_rule rule, float* cos_out, float* prob_out, uint8_t* mask_out,
-                          int32_t* all_exit_out, const RouteLive* live, hipStream_t s);
-
-size_t compact_workspace(int n);
-river_status launch_compact(int n, int d, river_dtype dt, const uint8_t* mask, const void* h,
-                            int64_t ld_h, const int32_t* row_ids, int32_t* cont_idx,
-                            int32_t* exit_idx, int32_t* counts, void* h_cont, int64_t ld_cont,
-                            int32_t* row_ids_cont, void* out, int64_t ld_out, int64_t n_out_rows,
-                            void* workspace, size_t ws_bytes, hipStream_t s);
-
-river_status launch_exit_projection(int m_max, const int32_t* m_dev, int d, river_dtype dt,
-                                    const void* h, int64_t ld_h, int n_rows,
-                                    const int32_t* row_idx, const int32_t* row_ids,
-                                    const void* gamma, float eps, void* out, int64_t ld_out,
-                                    int64_t n_out_rows, hipStream_t s);
-
-size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt);
-size_t kv_fill_layer_workspace(int m_max, int d, int n_layers);
-size_t kv_fill_split_workspace(int m_max, int n_out, int n_layers);
-river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
-                            int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
-                            int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
-                            const river_layer* layer, int n_kv_heads, int head_dim, void* k_cache,
-                            void* v_cache, int64_t n_slots, void* workspace, size_t ws_bytes,
-                            hipStream_t s);
-
-size_t decode_fixed_workspace(int n);
-void decode_layer_offset(const river_w4& w, int e, int n_out, int d, river_w4* out);
-river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
-                                const river_checkpoint* ck, int n_layers, const void* gamma,
-                                float eps, int b, river_rule rule, const river_w4* wk,
-                                const river_w4* wv, int n_kv_heads, int head_dim,
-                                const int32_t* slot, void* k_cache, void* v_cache, int64_t n_slots,
-                                int32_t* exit_layer, void* workspace, size_t ws_bytes,
-                                hipStream_t s);
-
-size_t calib_workspace(int n, int d, int b, int batch, int epochs);
-river_status launch_router_fit(int n, int d, river_dtype dt, const void* h, int64_t ld_h,
-                               const uint8_t* labels, const void* gamma, float eps, int b,
-                               float* w_down, float* w_up, int epochs, int batch,
-                               const int32_t* order, float lr, float beta1, float beta2,
-                               float adam_eps, float* loss_out, void* workspace, hipStream_t s);
-
-size_t ridge_workspace(int n, int d_in, int d_out, river_dtype dt);
-river_status launch_ridge_fit(int n, int d_in, int d_out, int n_targets, const void* X,
-                              river_dtype xdt, const void* Y, float lambda, void* W,
-                              river_dtype wdt, void* workspace, size_t ws_bytes, hipStream_t s);
-
-}  // namespace river_host
+#include "host.h"

@@ -19,6 +19,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "cosine.h"
 
 namespace river {
 
@@ -38,15 +39,6 @@ struct RouteArgs {
   int batch_min;
 };
 
-__device__ __forceinline__ float cosine_from(float dot, float na, float nb) {
-  // NaN propagates (comparisons with NaN are false), zero norm gives 0
-  if (isnan(dot) || isnan(na) || isnan(nb)) return __builtin_nanf("");
-  if (!(na > 0.0f) || !(nb > 0.0f)) return 0.0f;
-  float c = dot / (sqrtf(na) * sqrtf(nb));
-  c = c > 1.0f ? 1.0f : c;
-  c = c < -1.0f ? -1.0f : c;
-  return c;
-}
 
 __device__ __forceinline__ void write_decision(const RouteArgs& a, int i, float c, float p,
                                                bool router) {
@@ -117,66 +109,18 @@ __global__ __launch_bounds__(64) void route_generic_kernel(RouteArgs a) {
 }
 
 // ------------------------------------------------------ cosine only
-// The router switched off: one wave per token, four tokens per workgroup.
-// Both rows are loaded whole into registers (KPL 16-byte chunks per lane,
-// every load issued before the first product), so a token costs one memory
-// latency; KPL = 0 streams any width.
-template <bool BF16>
-__device__ __forceinline__ void dot3(const u32x4& p, const u32x4& c, float& dot, float& na, float& nb) {
-  if constexpr (BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x0 = bf16_lo(p[i]), x1 = bf16_hi(p[i]), y0 = bf16_lo(c[i]), y1 = bf16_hi(c[i]);
-      dot = fmaf(x0, y0, dot); dot = fmaf(x1, y1, dot);
-      na = fmaf(x0, x0, na); na = fmaf(x1, x1, na);
-      nb = fmaf(y0, y0, nb); nb = fmaf(y1, y1, nb);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float x = __uint_as_float(p[i]), y = __uint_as_float(c[i]);
-      dot = fmaf(x, y, dot);
-      na = fmaf(x, x, na);
-      nb = fmaf(y, y, nb);
-    }
-  }
-}
-
+// The router switched off: one wave per token, four tokens per workgroup
+// (token_cosine, cosine.h).
 template <bool BF16, int KPL>
 __global__ __launch_bounds__(256) void route_cos_kernel(RouteArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
   const int lane = threadIdx.x % WAVE;
   const int i = blockIdx.x * 4 + wave;
   if (i >= a.n) return;
-  constexpr int E = BF16 ? 8 : 4;
   constexpr int ES = BF16 ? 2 : 4;
-  const int nch = a.d / E;
-  const u32x4* hp = (const u32x4*)((const char*)a.hp + (int64_t)i * a.ldp * ES);
-  const u32x4* hc = (const u32x4*)((const char*)a.hc + (int64_t)i * a.ldc * ES);
-  float dot = 0.f, na = 0.f, nb = 0.f;
-  if constexpr (KPL > 0) {
-    u32x4 p[KPL], c[KPL];
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    // clamped addresses keep every load unconditional; chunks past the row
-    // are zeroed after they land
-#pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-      const int ch = lane + WAVE * k;
-      p[k] = hp[ch < nch ? ch : nch - 1];
-      c[k] = hc[ch < nch ? ch : nch - 1];
-    }
-#pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-      const bool in = lane + WAVE * k < nch;
-      dot3<BF16>(in ? p[k] : z, in ? c[k] : z, dot, na, nb);
-    }
-  } else {
-    for (int ch = lane; ch < nch; ch += WAVE) dot3<BF16>(hp[ch], hc[ch], dot, na, nb);
-  }
-  dot = wave_sum(dot);
-  na = wave_sum(na);
-  nb = wave_sum(nb);
-  if (lane == 0) write_decision(a, i, cosine_from(dot, na, nb), 1.0f, false);
+  const float c = token_cosine<BF16, KPL>((const char*)a.hp + (int64_t)i * a.ldp * ES,
+                                          (const char*)a.hc + (int64_t)i * a.ldc * ES, a.d, lane);
+  if (lane == 0) write_decision(a, i, c, 1.0f, false);
 }
 
 // ------------------------------------------------------------ MFMA path
