@@ -323,13 +323,20 @@ def decode_times(key, steps):
     ex = dw.ex.cpu().numpy()
     cfg = dw.cfg
     n_ck = len(dw.cks)
-    launches = 1 + n_ck * (2 + (1 if cfg.b else 0)) + sum(2 if c.get("maps") is not None else 1
-                                                          for c in dw.cks)
+    # the launch sequence the library takes for this workload
+    if not cfg.b and cfg.n_tokens <= 1024 and n_ck <= 32:
+        if all(c.get("maps") is None for c in dw.cks):
+            path = ("routers off, no maps: cosines of all checkpoints, one decision workgroup, "
+                    "gather of the exit states, one projection over all filled blocks")
+        else:
+            path = "routers off: cosines of all checkpoints, one decision workgroup, a fill per checkpoint"
+    else:
+        path = "per checkpoint: route, compact, fill"
     del g
     return {"tokens": cfg.n_tokens, "d": cfg.d, "blocks": cfg.L, "checkpoints": n_ck,
             "exits_per_checkpoint": [int((ex == c["layer"]).sum()) for c in dw.cks],
             "filled_token_layers": int(sum(cfg.L - e for e in ex)),
-            "kernels_per_step": launches, "eager_us": eager * 1e3, "graph_us": graph * 1e3}
+            "path": path, "eager_us": eager * 1e3, "graph_us": graph * 1e3}
 
 
 def router_fit_times(key, n, epochs=100, batch=256):

@@ -88,7 +88,7 @@ size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int 
       return kv_fill_layer_workspace(n, d, n_layers);
     case RIVER_OP_DECODE_STEP:
       if (n <= 0 || d <= 0) return 0;
-      return decode_fixed_workspace(n, n_layers) + (n_layers > 1 ? kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) : 0) +
+      return decode_fixed_workspace(n, d, RIVER_F32, n_layers) + (n_layers > 1 ? kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) : 0) +
              (n_layers > 1 ? kv_fill_split_workspace(n, d_out, n_layers - 1) : 0);
     case RIVER_OP_ROUTER_FIT:
       if (n <= 0 || d <= 0 || d_out <= 0 || n_targets <= 0 || n_layers <= 0) return 0;
@@ -305,7 +305,7 @@ river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_c
     }
     any_maps |= k.maps != nullptr;
   }
-  const size_t fixed = decode_fixed_workspace(n, n_layers);
+  const size_t fixed = decode_fixed_workspace(n, d, dt, n_layers);
   const size_t need = fixed + (any_maps ? kv_fill_workspace(n, d, 1, dt) : 0);
   if (!workspace || ws_bytes < need)
     return fail(RIVER_ERR_WORKSPACE, "decode_step: workspace of at least %zu bytes needed, %zu given", need, ws_bytes);

@@ -16,10 +16,17 @@
 // instead of 3 per checkpoint: the cosines of every (checkpoint, token)
 // pair, then one workgroup that walks the checkpoints in order (running
 // flags, token or batch rule, the exiting rows of each checkpoint in token
-// order); the fills follow. Both give bit-identical results (same cosine
-// code, same decisions). Nothing waits on the host, allocates or sets
-// memory through the runtime, so the whole step can be captured once into
-// a HIP graph and replayed for every generated token.
+// order), with the same cosine code and so the same decisions. Without
+// maps the fills of all checkpoints then become one: block e + 1 needs the
+// exits of every checkpoint before it, which (listed checkpoint by
+// checkpoint) form a prefix of one exit order, so after a gather of each
+// exiting token's state one projection over blocks e_0 + 1..L, with a row
+// count per block, writes them all. It computes every (token, block) value
+// as the per-checkpoint fill does when both split the reduction over d
+// into the same parts (bit-identical then; to rounding otherwise).
+// Nothing waits on the host, allocates or sets memory through the runtime,
+// so the whole step can be captured once into a HIP graph and replayed for
+// every generated token.
 #include "common.h"
 #include "cosine.h"
 
@@ -70,6 +77,13 @@ struct DecodePlan {
   int idx_stride;
   int32_t* counts;                // [n_ck][64]: {running or done before, exiting} (compact's layout)
   int32_t* exit_layer;            // [n]
+  // one fill for all checkpoints (NULL: not wanted): the exits of all
+  // checkpoints in checkpoint order, the checkpoint of each token's exit
+  // (-1: none) and, for block layer[0] + 1 + j, the number of exits at
+  // checkpoints before it (a prefix of ord)
+  int32_t* ord;                   // [n]
+  int32_t* ck_of;                 // [n]
+  int32_t* m_layer;               // [n_layers - layer[0]]
 };
 
 // One workgroup, token i in thread i: the checkpoints in order. Under the
@@ -79,10 +93,12 @@ struct DecodePlan {
 // a ballot per wave and the wave totals.
 __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
   __shared__ int wsum[DC_TOKENS / WAVE];
+  __shared__ int tot[DC_MAX];
   const int i = threadIdx.x, lane = i % WAVE, wave = i / WAVE;
   const int n = p.n;
   bool alive = i < n;
-  int el = p.n_layers;
+  int el = p.n_layers, my_ck = -1;
+  int off = 0;                                // exits of the checkpoints before c
   for (int c = 0; c < p.n_ck; ++c) {
     bool e = alive && p.cos[(int64_t)c * n + (i < n ? i : 0)] > p.tau[c];
     if (p.batch_min) {
@@ -104,15 +120,62 @@ __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
     if (e) {
       const int r = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
       p.exit_idx[(int64_t)c * p.idx_stride + r] = i;
+      if (p.ord) p.ord[off + r] = i;
+      my_ck = c;
     }
     if (i == 0) {
       p.counts[c * 64] = n - total;
       p.counts[c * 64 + 1] = total;
+      tot[c] = total;
     }
+    off += total;
     __syncthreads();                          // wsum is rewritten next round
     alive = alive && !e;
   }
-  if (i < n) p.exit_layer[i] = el;
+  if (i < n) {
+    p.exit_layer[i] = el;
+    if (p.ck_of) p.ck_of[i] = my_ck;
+  }
+  if (p.m_layer && p.n_ck > 0) {
+    const int first = p.layer[0] + 1;         // first filled block
+    for (int j = i; j < p.n_layers + 1 - first; j += DC_TOKENS) {
+      int m = 0;
+      for (int c = 0; c < p.n_ck; ++c) m += p.layer[c] < first + j ? tot[c] : 0;
+      p.m_layer[j] = m;
+    }
+  }
+}
+
+struct DecodeGather {
+  int n, row_bytes;               // row_bytes a multiple of 16
+  int64_t ld_bytes;               // source leading dimension in bytes
+  const void* hc[DC_MAX];
+  const int32_t* ck_of;
+  char* x;                        // [n][row_bytes]
+};
+
+// x[i] = the state of token i at its exit checkpoint (workgroup i, 64 lanes;
+// up to four 16-byte pieces per lane in flight)
+__global__ __launch_bounds__(64) void decode_gather_kernel(DecodeGather a) {
+  const int i = blockIdx.x, lane = threadIdx.x;
+  const int c = a.ck_of[i];
+  if (c < 0) return;
+  const u32x4* src = (const u32x4*)((const char*)a.hc[c] + (int64_t)i * a.ld_bytes);
+  u32x4* dst = (u32x4*)(a.x + (int64_t)i * a.row_bytes);
+  const int nch = a.row_bytes >> 4;
+  for (int c0 = 0; c0 < nch; c0 += 4 * WAVE) {
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = c0 + lane + WAVE * k;
+      v[k] = src[q < nch ? q : nch - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = c0 + lane + WAVE * k;
+      if (q < nch) dst[q] = v[k];
+    }
+  }
 }
 
 }  // namespace river
@@ -126,12 +189,18 @@ using namespace river;
 static size_t a256(size_t x) { return align_up(x, 256); }
 
 // the two-launch path: per checkpoint (at most n_layers - 1) the cosines,
-// the exiting rows and the counts
+// the exiting rows and the counts; then for the single fill the exit
+// states [n][d] (sized for fp32), the exit order, the exit checkpoints and
+// the per-block row counts
 static size_t plan_ck_bytes(int n) { return 2 * a256(4 * (size_t)n) + 256; }
+static size_t plan_fill_bytes(int n, int d, int n_layers) {
+  return a256((size_t)n * d * 4) + 2 * a256(4 * (size_t)n) + a256(4 * (size_t)n_layers);
+}
 
-size_t decode_fixed_workspace(int n, int n_layers) {
+size_t decode_fixed_workspace(int n, int d, river_dtype dt, int n_layers) {
+  (void)dt;
   return a256(2 * (size_t)n) + a256((size_t)n) + 2 * a256(4 * (size_t)n) + 256 + compact_workspace(n) +
-         (size_t)(n_layers > 1 ? n_layers - 1 : 0) * plan_ck_bytes(n);
+         (size_t)(n_layers > 1 ? n_layers - 1 : 0) * plan_ck_bytes(n) + plan_fill_bytes(n, d, n_layers);
 }
 
 // descriptor of blocks e+1..L inside one that covers blocks 1..L
@@ -166,6 +235,14 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
   w += cws_bytes;
   char* plan = w;                                   // [n_ck] x (cos, exit rows, counts)
   w += (size_t)(n_layers - 1) * plan_ck_bytes(n);
+  char* xs = w;                                     // exit states of the single fill
+  w += a256((size_t)n * d * 4);
+  int32_t* ord = (int32_t*)w;
+  w += a256(4 * (size_t)n);
+  int32_t* ck_of = (int32_t*)w;
+  w += a256(4 * (size_t)n);
+  int32_t* m_layer = (int32_t*)w;
+  w += a256(4 * (size_t)n_layers);
   void* fws = w;
   const size_t fixed = (size_t)(w - (char*)workspace);
   const size_t fws_bytes = ws_bytes - fixed;
@@ -199,8 +276,21 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
       st = check_launch("decode_step cosines");
       if (st != RIVER_OK) return st;
     }
+    // one fill for all checkpoints when none has maps and the plain MFMA
+    // projection takes the shape: block e_0 + 1 + j projects the first
+    // m_layer[j] rows of the exit order, gathered from each token's exit
+    // checkpoint
+    river_w4 k0, v0;
+    bool single = n_ck > 0;
+    for (int c = 0; c < n_ck; ++c) single = single && !ck[c].maps;
+    if (single) {
+      decode_layer_offset(*wk, ck[0].layer, n_out, d, &k0);
+      decode_layer_offset(*wv, ck[0].layer, n_out, d, &v0);
+      single = kv_fill_plain_mfma(n, d, dt, n, d, &k0, &v0, n_out);
+    }
     DecodePlan q{};
     q.n = n; q.n_ck = n_ck; q.batch_min = rule == RIVER_RULE_BATCH_MIN; q.n_layers = n_layers;
+    if (single) { q.ord = ord; q.ck_of = ck_of; q.m_layer = m_layer; }
     q.cos = (const float*)plan;
     for (int c = 0; c < n_ck; ++c) { q.tau[c] = ck[c].tau; q.layer[c] = ck[c].layer; }
     char* rec = plan + (size_t)n_ck * CO;
@@ -211,6 +301,19 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     decode_plan_kernel<<<1, DC_TOKENS, 0, s>>>(q);
     st = check_launch("decode_step plan");
     if (st != RIVER_OK) return st;
+    if (single) {
+      DecodeGather gq{};
+      gq.n = n; gq.row_bytes = (int)(d * esize(dt)); gq.ld_bytes = ld * (int64_t)esize(dt);
+      for (int c = 0; c < n_ck; ++c) gq.hc[c] = ck[c].h_cur;
+      gq.ck_of = ck_of; gq.x = xs;
+      decode_gather_kernel<<<n, WAVE, 0, s>>>(gq);
+      st = check_launch("decode_step gather");
+      if (st != RIVER_OK) return st;
+      const int e0 = ck[0].layer;
+      return launch_kv_fill(n, nullptr, d, dt, xs, d, n, ord, slot, n_layers - e0, nullptr, &k0, &v0, nullptr,
+                            n_kv_heads, head_dim, (char*)k_cache + e0 * cache_layer,
+                            (char*)v_cache + e0 * cache_layer, n_slots, fws, fws_bytes, s, m_layer);
+    }
     for (int c = 0; c < n_ck; ++c) {
       const river_checkpoint& k = ck[c];
       const int e = k.layer;

@@ -40,6 +40,7 @@ enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_CACHE = 2, EPI_BF16N = 3, EPI_PART = 4 };
 struct GemmArgs {
   int M_max;
   const int32_t* M_dev;      // rows = clamp(*M_dev, 0, M_max) when set
+  const int32_t* M_dev_z;    // W4 kernel: rows of batch entry z = clamp(M_dev_z[z], 0, M_max) when set
   int N, K;
   // A operand, bf16
   const uint16_t* A; int64_t lda; int64_t a_bstride;

@@ -57,9 +57,13 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
                             int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
                             const river_layer* layer, int n_kv_heads, int head_dim, void* k_cache,
                             void* v_cache, int64_t n_slots, void* workspace, size_t ws_bytes,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t* m_dev_layer = nullptr);
+// m_dev_layer: rows of layer j = clamp(m_dev_layer[j], 0, m_max) instead of
+// one count (the plain MFMA path only: no maps, no layer parts)
+bool kv_fill_plain_mfma(int m_max, int d, river_dtype dt, int n_rows, int64_t ld_h, const river_w4* wk,
+                        const river_w4* wv, int nh);
 
-size_t decode_fixed_workspace(int n, int n_layers);
+size_t decode_fixed_workspace(int n, int d, river_dtype dt, int n_layers);
 void decode_layer_offset(const river_w4& w, int e, int n_out, int d, river_w4* out);
 river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
                                 const river_checkpoint* ck, int n_layers, const void* gamma,

@@ -189,6 +189,11 @@ static bool fill_mfma_ok(int d, river_dtype dt, int nh, const river_w4* wk, cons
          a_span < lim && ws_span < lim && (int64_t)nh * d < lim && (int64_t)d * d * 2 < lim;
 }
 
+bool kv_fill_plain_mfma(int m_max, int d, river_dtype dt, int n_rows, int64_t ld_h, const river_w4* wk,
+                        const river_w4* wv, int nh) {
+  return fill_mfma_ok(d, dt, nh, wk, wv, (int64_t)n_rows * ld_h * 2, (int64_t)m_max * d * 2);
+}
+
 size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt) {
   return align_up((size_t)n_layers * (size_t)m_max * (size_t)d * esize(dt), 256);
 }
@@ -227,7 +232,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
                             int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
                             const river_layer* L, int n_kv_heads, int head_dim, void* k_cache,
                             void* v_cache, int64_t n_slots, void* workspace, size_t ws_bytes,
-                            hipStream_t s) {
+                            hipStream_t s, const int32_t* m_dev_layer) {
   const int nh = n_kv_heads * head_dim;
   const void* gamma = L ? L->norm_gamma : nullptr;
   const bool has_bias = L && (L->k_bias || L->v_bias);
@@ -235,6 +240,8 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
   const bool layer = gamma || has_bias || rope;
   const bool mfma = fill_mfma_ok(d, dt, nh, wk, wv, (int64_t)n_rows * ld_h * 2, (int64_t)m_max * d * 2) &&
                     (!rope || head_dim % 32 == 0) && (!gamma || d <= 8192);
+  if (m_dev_layer && (!mfma || layer || maps))
+    return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: per-layer row counts need the plain MFMA path");
   if (!mfma) {
     const size_t lds = (2 * (size_t)d + 2 * (size_t)nh + 4) * sizeof(float);
     if (lds > 65536) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: d = %d, n_out = %d too large for the generic path", d, nh);
@@ -257,6 +264,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
   g.K = d;
   g.M_max = m_max;
   g.M_dev = m_dev;
+  g.M_dev_z = m_dev_layer;
   g.q[0] = wk->q; g.q[1] = wv->q;
   g.s[0] = wk->scale; g.s[1] = wv->scale;
   g.zp[0] = wk->zero; g.zp[1] = wv->zero;

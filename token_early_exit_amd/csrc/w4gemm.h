@@ -194,7 +194,9 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     const int md = *g.M_dev;
     M = md < 0 ? 0 : (md < M_max ? md : M_max);
   }
-  const int tiles_m_act = (M + BM - 1) / BM;
+  // with per-entry row counts every entry walks the row tiles of M_max and
+  // skips those past its own count
+  const int tiles_m_act = ((g.M_dev_z ? M_max : M) + BM - 1) / BM;
   const int ksplit = EPI == EPI_PART ? g.ksplit : 1;
   const int total = tiles_n * tiles_m_act * batch * ksplit;
   // persistent tiles, contiguous per XCD (see gemm_nt_kernel)
@@ -226,6 +228,11 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     const int ks = tile / (tiles_n * tiles_m_act * batch);   // part of the reduction
     const int j0 = ks * KT;                                  // its first slab
     const int m0 = mt * BM, n0 = nt * BN;
+    if (g.M_dev_z) {                                         // uniform
+      const int mz = g.M_dev_z[z];
+      M = mz < 0 ? 0 : (mz < M_max ? mz : M_max);
+      if (m0 >= M) continue;
+    }
 
     // A: DMA block b = i * 4 + wave covers LDS chunks [64 b, 64 b + 64);
     // lane l fills chunk p = 64 b + l = (row p / 8, physical chunk p % 8),
@@ -535,18 +542,20 @@ constexpr int W4_WAVES = 8;
 // written to each row's cache slot (the EPI_CACHE epilogue's addressing):
 // one thread per 8 columns of a row.
 __global__ __launch_bounds__(256) void w4_part_finish_kernel(GemmArgs g, int batch) {
-  int M = g.M_max;
-  if (g.M_dev) {
-    const int md = *g.M_dev;
-    M = md < 0 ? 0 : (md < g.M_max ? md : g.M_max);
-  }
   const int N = g.N, nh = g.nh;
   const int per = N / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int p = (int)(idx % per);
   const int t = (int)((idx / per) % g.M_max);
   const int z = (int)(idx / ((int64_t)per * g.M_max));
-  if (z >= batch || t >= M) return;
+  if (z >= batch) return;
+  int M = g.M_max;
+  const int32_t* md_p = g.M_dev_z ? g.M_dev_z + z : g.M_dev;
+  if (md_p) {
+    const int md = *md_p;
+    M = md < 0 ? 0 : (md < g.M_max ? md : g.M_max);
+  }
+  if (t >= M) return;
   const int e = g.e_rows ? g.e_rows[t] : t;
   if (e < 0 || e >= g.e_nrows) return;
   const int sl = g.slot[e];
