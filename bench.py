@@ -39,6 +39,11 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0 # MI355X dense bf16 MFMA, TFLOP/s
 
 
+def progress(msg):
+    """One line on stderr per finished part (stdout carries only the JSON line)."""
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,12 +329,13 @@ def decode_times(key, steps):
     cfg = dw.cfg
     n_ck = len(dw.cks)
     # the launch sequence the library takes for this workload
-    if not cfg.b and cfg.n_tokens <= 1024 and n_ck <= 32:
+    if cfg.n_tokens <= 1024 and n_ck <= (16 if cfg.b else 32):
+        scores = "one route launch for all checkpoints" if cfg.b else "cosines of all checkpoints"
         if all(c.get("maps") is None for c in dw.cks):
-            path = ("routers off, no maps: cosines of all checkpoints, one decision workgroup, "
-                    "gather of the exit states, one projection over all filled blocks")
+            path = (f"{scores}, one decision workgroup, gather of the exit states, one projection "
+                    "over all filled blocks")
         else:
-            path = "routers off: cosines of all checkpoints, one decision workgroup, a fill per checkpoint"
+            path = f"{scores}, one decision workgroup, a fill per checkpoint"
     else:
         path = "per checkpoint: route, compact, fill"
     del g
@@ -472,6 +478,7 @@ def fill_long_context(reps=3):
             "fill_ms": out["fill_ms"], "projection_ms": out["projection_ms"],
             "map_gemm_ms": map_ms,
             "map_gemm_tflops": map_flops / (map_ms * 1e-3) / 1e12,
+            "map_gemm_frac_of_bf16_peak": map_flops / (map_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "projection_tflops": proj_flops / (out["projection_ms"] * 1e-3) / 1e12,
             "fill_tflops": (map_flops + proj_flops) / (out["fill_ms"] * 1e-3) / 1e12,
             "fill_frac_of_bf16_peak": (map_flops + proj_flops) / (out["fill_ms"] * 1e-3) / 1e12
@@ -597,8 +604,10 @@ def main():
     ms_total = time_region(wl.step, args.steps)
     ms_step = ms_total / args.steps
     n_exit = int(wl.sets[0]["counts"][1].item())
+    progress(f"{args.steps} timed steps: {ms_step * 1e3:.1f} us per step")
     calls = per_call_times(wl, max(20, args.steps // 4))
     kern = kernel_times(wl, max(50, args.steps))
+    progress("per-call and per-kernel timing done")
 
     route_b, compact_b, fill_f, fill_b = wl.work(n_exit)
     value = n_exit / (ms_step * 1e-3)
@@ -658,11 +667,16 @@ def main():
         "llama3-8b decode: 256 tokens, d=4096, 8 router checkpoints, maps for the exits at 11 and 31":
             decode_times("3D", 20),
     }
+    progress("decode steps done")
     line["router_fit"] = router_fit_all()
+    progress("router calibration done")
     line["fill_long_context"] = fill_long_context()
+    progress("long-context fill done")
     line["route_compact_8b_prefill"] = route_compact_8b()
+    progress("8B route and compact done")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        progress("cpu baseline done")
     print(json.dumps(line))
 
 

@@ -466,8 +466,10 @@ river_status river_debug_set_gemm_path(int path);
 
 /* Test hook: 1 forces river_decode_step onto its per-checkpoint launches
  * (route, compact, fill per checkpoint) where it would take the two
- * decision launches for all checkpoints (routers off, n <= 1024, at most
- * 32 checkpoints); 0 = automatic. Process-wide. The decisions are
+ * decision launches for all checkpoints (n <= 1024, and the routers off at
+ * every checkpoint with at most 32 checkpoints, or on at every checkpoint
+ * with at most 16 and bf16 states of d % 256 == 0, d <= 8192, b <= 128);
+ * 0 = automatic. Process-wide. The decisions are
  * bit-identical; the caches too when both paths split the projection's
  * reduction into the same parts (otherwise they agree to rounding). */
 river_status river_debug_set_decode_path(int path);

@@ -208,6 +208,54 @@ def test_decode_step_llama1b_batch_rule():
     assert np.all(exg == 11)
 
 
+def llama8b_checkpoints(cfg, hs):
+    """Router checkpoints every four blocks: tau off, theta_11 between the
+    13th and 14th largest probabilities, theta_31 = -inf, +inf elsewhere;
+    near-identity maps for the fills at 11 and 31."""
+    cks = []
+    for l in cfg.route_layers:
+        wd, wu = (t.to(DEV) for t in G.router_weights(cfg, l))
+        c = {"layer": l, "h_prev": hs[l - 1], "h_cur": hs[l], "tau": -INF, "theta": INF,
+             "w_down": wd, "w_up": wu}
+        if l == 11:
+            _, prob, _, _ = O.route(np64(hs[10]), np64(hs[11]), None, 1e-6, np64(wd), np64(wu),
+                                    -INF, -INF)
+            p = np.sort(prob)[::-1]
+            c["theta"] = 0.5 * (p[12] + p[13])
+            c["maps"] = G.near_identity_maps(cfg, cfg.L - l, device=DEV)
+        if l == 31:
+            c["theta"] = -INF
+            c["maps"] = G.near_identity_maps(cfg, cfg.L - l, tag="maps31", device=DEV)
+        cks.append(c)
+    return cks
+
+
+def test_decode_step_8b_two_launch_equals_per_checkpoint():
+    """Routers on at every checkpoint: one route launch for all checkpoints
+    plus the decision workgroup give the same bits as the per-checkpoint
+    route and compact launches."""
+    cfg = get_config("3D")
+    n = cfg.n_tokens
+    layers = list(cfg.route_layers)
+    need = sorted({l - 1 for l in layers} | set(layers))
+    hs = G.hidden_states(cfg, n, need, device=DEV)
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    cks = llama8b_checkpoints(cfg, hs)
+    out = []
+    try:
+        for path in (0, 1):
+            tee.river_debug_set_decode_path(path)
+            out.append(run_gpu(cks, cfg, wk, wv, slot))
+    finally:
+        tee.river_debug_set_decode_path(0)
+    (e0, k0, v0), (e1, k1, v1) = out
+    assert torch.equal(e0, e1)
+    assert torch.equal(k0.view(torch.int16), k1.view(torch.int16))
+    assert torch.equal(v0.view(torch.int16), v1.view(torch.int16))
+    assert np.sum(e0.cpu().numpy() == 11) == 13
+
+
 def test_decode_step_8b_router_and_maps():
     """Llama-3-8B-shape decode (256 tokens, d = 4096, checkpoints every four
     blocks with a router each): tau off, theta_11 between the 13th and 14th

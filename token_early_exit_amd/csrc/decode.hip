@@ -7,16 +7,18 @@
 // decision also needs the router's probability; River's batch rule exits
 // only when every running token passes.
 //
-// The step is an ordered sequence of launches on one stream. With a router
-// at any checkpoint (or more than 1024 tokens): an init kernel, then per
-// checkpoint route (over all n rows, with the running flags of the
-// previous checkpoint), compact (the exiting rows in order) and the fill
-// of blocks e+1..L for those rows, whose count stays on the device. With
-// the routers off, the decisions of all checkpoints take two launches
-// instead of 3 per checkpoint: the cosines of every (checkpoint, token)
-// pair, then one workgroup that walks the checkpoints in order (running
+// The step is an ordered sequence of launches on one stream. In general
+// (more than 1024 tokens, routers at some checkpoints only, or router
+// shapes off the streaming route): an init kernel, then per checkpoint
+// route (over all n rows, with the running flags of the previous
+// checkpoint), compact (the exiting rows in order) and the fill of blocks
+// e+1..L for those rows, whose count stays on the device. Otherwise the
+// decisions of all checkpoints take two launches instead of 3 per
+// checkpoint: the cosines (and, with routers, the probabilities) of every
+// (checkpoint, token) pair, by the same kernel code as the per-checkpoint
+// route, then one workgroup that walks the checkpoints in order (running
 // flags, token or batch rule, the exiting rows of each checkpoint in token
-// order), with the same cosine code and so the same decisions. Without
+// order): the same decisions. Without
 // maps the fills of all checkpoints then become one: block e + 1 needs the
 // exits of every checkpoint before it, which (listed checkpoint by
 // checkpoint) form a prefix of one exit order, so after a gather of each
@@ -71,7 +73,9 @@ __global__ __launch_bounds__(256) void decode_cos_kernel(DecodeCos a) {
 struct DecodePlan {
   int n, n_ck, batch_min, n_layers;
   const float* cos;               // [n_ck][n]
+  const float* prob;              // [n_ck][n] router probabilities (NULL: routers off)
   float tau[DC_MAX];
+  float theta[DC_MAX];
   int layer[DC_MAX];
   int32_t* exit_idx;              // [n_ck][idx_stride]: the exiting rows of checkpoint c in order
   int idx_stride;
@@ -87,7 +91,8 @@ struct DecodePlan {
 };
 
 // One workgroup, token i in thread i: the checkpoints in order. Under the
-// token rule a running token exits where its cosine passes tau; under the
+// token rule a running token exits where its cosine passes tau (and, with
+// routers, its probability theta); under the
 // batch rule every running token exits where all of them pass (and at
 // least one runs). Each checkpoint's exits are listed in token order from
 // a ballot per wave and the wave totals.
@@ -100,7 +105,9 @@ __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
   int el = p.n_layers, my_ck = -1;
   int off = 0;                                // exits of the checkpoints before c
   for (int c = 0; c < p.n_ck; ++c) {
-    bool e = alive && p.cos[(int64_t)c * n + (i < n ? i : 0)] > p.tau[c];
+    const int64_t at = (int64_t)c * n + (i < n ? i : 0);
+    // the route's decision: cos > tau, and p > theta with a router
+    bool e = alive && p.cos[at] > p.tau[c] && (!p.prob || p.prob[at] > p.theta[c]);
     if (p.batch_min) {
       const int all = __syncthreads_and(!alive || e);
       const int any = __syncthreads_or(alive);
@@ -189,10 +196,11 @@ using namespace river;
 static size_t a256(size_t x) { return align_up(x, 256); }
 
 // the two-launch path: per checkpoint (at most n_layers - 1) the cosines,
-// the exiting rows and the counts; then for the single fill the exit
+// the exiting rows, the counts, the router probabilities and the route's
+// (unused) masks; then for the single fill the exit
 // states [n][d] (sized for fp32), the exit order, the exit checkpoints and
 // the per-block row counts
-static size_t plan_ck_bytes(int n) { return 2 * a256(4 * (size_t)n) + 256; }
+static size_t plan_ck_bytes(int n) { return 3 * a256(4 * (size_t)n) + a256((size_t)n) + 256; }
 static size_t plan_fill_bytes(int n, int d, int n_layers) {
   return a256((size_t)n * d * 4) + 2 * a256(4 * (size_t)n) + a256(4 * (size_t)n_layers);
 }
@@ -249,14 +257,26 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
 
   const int n_out = n_kv_heads * head_dim;
   const int64_t cache_layer = n_slots * n_out * (int64_t)esize(dt);   // bytes per cache layer
-  bool two_launch = n <= DC_TOKENS && n_ck <= DC_MAX && decode_path_override() == 0;
-  for (int c = 0; c < n_ck; ++c) two_launch = two_launch && !ck[c].w_down;
+  bool routers_off = true, routers_on = n_ck > 0;
+  for (int c = 0; c < n_ck; ++c) {
+    routers_off = routers_off && !ck[c].w_down;
+    routers_on = routers_on && ck[c].w_down;
+  }
+  routers_on = routers_on && route_scores_ok(n, d, dt, b, ld, n_ck);
+  const bool two_launch = n <= DC_TOKENS && n_ck <= DC_MAX && decode_path_override() == 0 &&
+                          (routers_off || routers_on);
   if (two_launch) {
     // plan area: cosines [n_ck][n], then the exit rows of each checkpoint
-    // (CO bytes apart), then its counts (256 bytes apart)
+    // (CO bytes apart), then its counts (256 bytes apart), then the router
+    // probabilities [n_ck][n] and the route's masks (n bytes apart)
     const size_t CO = a256(4 * (size_t)n);
+    float* prob = (float*)(plan + (size_t)n_ck * (2 * CO + 256));
+    uint8_t* masks = (uint8_t*)(plan + (size_t)n_ck * (3 * CO + 256));
     river_status st = RIVER_OK;
-    if (n_ck > 0) {
+    if (routers_on) {
+      st = launch_route_scores(n, d, dt, ld, n_ck, ck, gamma, eps, b, (float*)plan, prob, masks, s);
+      if (st != RIVER_OK) return st;
+    } else if (n_ck > 0) {
       DecodeCos a{};
       a.n = n; a.d = d; a.ld = ld;
       for (int c = 0; c < n_ck; ++c) { a.hp[c] = ck[c].h_prev; a.hc[c] = ck[c].h_cur; }
@@ -292,7 +312,8 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     q.n = n; q.n_ck = n_ck; q.batch_min = rule == RIVER_RULE_BATCH_MIN; q.n_layers = n_layers;
     if (single) { q.ord = ord; q.ck_of = ck_of; q.m_layer = m_layer; }
     q.cos = (const float*)plan;
-    for (int c = 0; c < n_ck; ++c) { q.tau[c] = ck[c].tau; q.layer[c] = ck[c].layer; }
+    q.prob = routers_on ? prob : nullptr;
+    for (int c = 0; c < n_ck; ++c) { q.tau[c] = ck[c].tau; q.theta[c] = ck[c].theta; q.layer[c] = ck[c].layer; }
     char* rec = plan + (size_t)n_ck * CO;
     q.exit_idx = (int32_t*)rec;
     q.idx_stride = (int)(CO / 4);

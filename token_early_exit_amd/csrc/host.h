@@ -63,6 +63,13 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
 bool kv_fill_plain_mfma(int m_max, int d, river_dtype dt, int n_rows, int64_t ld_h, const river_w4* wk,
                         const river_w4* wv, int nh);
 
+// cosine and router probability of every token at every checkpoint (all
+// with a router) in one launch, [n_ck][n] each; mask_scratch [n_ck][n]
+bool route_scores_ok(int n, int d, river_dtype dt, int b, int64_t ld, int n_ck);
+river_status launch_route_scores(int n, int d, river_dtype dt, int64_t ld, int n_ck, const river_checkpoint* ck,
+                                 const void* gamma, float eps, int b, float* cos_out, float* prob_out,
+                                 uint8_t* mask_scratch, hipStream_t s);
+
 size_t decode_fixed_workspace(int n, int d, river_dtype dt, int n_layers);
 void decode_layer_offset(const river_w4& w, int e, int n_out, int d, river_w4* out);
 river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,

@@ -328,7 +328,7 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
 // the pre-activations need no cross-wave sum; meanwhile 8 threads per token
 // accumulate, in fp32, the three dot products over 8 features of each slab.
 template <int RT, bool HAS_GAMMA>
-__global__ __launch_bounds__(256) void route_stream_kernel(RouteArgs a) {
+__device__ __forceinline__ void route_stream_body(const RouteArgs& a) {
   constexpr int T = 16 * RT;
   constexpr int WB = 128 * 8;            // W slab: 128 units x 8 chunks of 16 bytes
   constexpr int HB = T * 8;              // one state slab: T rows x 8 chunks
@@ -536,6 +536,23 @@ __global__ __launch_bounds__(256) void route_stream_kernel(RouteArgs a) {
   }
 }
 
+template <int RT, bool HAS_GAMMA>
+__global__ __launch_bounds__(256) void route_stream_kernel(RouteArgs a) {
+  route_stream_body<RT, HAS_GAMMA>(a);
+}
+
+// The router checkpoints of a decode step in one launch: blockIdx.y picks
+// the checkpoint (cosine and probability only; the decision is the
+// caller's).
+constexpr int RM_MAX = 16;
+struct RouteMulti { RouteArgs a[RM_MAX]; };
+static_assert(sizeof(RouteMulti) <= 4000, "kernel arguments are limited to 4 KB");
+
+template <int RT, bool HAS_GAMMA>
+__global__ __launch_bounds__(256) void route_stream_multi_kernel(RouteMulti m) {
+  route_stream_body<RT, HAS_GAMMA>(m.a[blockIdx.y]);
+}
+
 // ------------------------------------------------------------ batch rule
 // AND of the per-token decisions; for the batch-min rule the AND is then
 // broadcast to every token's mask (River-LLM 方法步骤详情 step 3, TIDE
@@ -574,6 +591,41 @@ __global__ __launch_bounds__(1024) void route_finish_kernel(int n, uint8_t* mask
 namespace river_host {
 using namespace river;
 
+// the streaming path's conditions (launch_route takes it whenever they hold)
+static bool stream_ok(int n, int d, river_dtype dt, int b, int64_t ld_prev, int64_t ld_cur) {
+  return dt == RIVER_BF16 && d % 256 == 0 && b <= 128 && (int64_t)n * ld_cur * 2 < ((int64_t)1 << 31) &&
+         (int64_t)n * ld_prev * 2 < ((int64_t)1 << 31) && d <= 8192;
+}
+
+bool route_scores_ok(int n, int d, river_dtype dt, int b, int64_t ld, int n_ck) {
+  return n_ck <= RM_MAX && stream_ok(n, d, dt, b, ld, ld);
+}
+
+river_status launch_route_scores(int n, int d, river_dtype dt, int64_t ld, int n_ck, const river_checkpoint* ck,
+                                 const void* gamma, float eps, int b, float* cos_out, float* prob_out,
+                                 uint8_t* mask_scratch, hipStream_t s) {
+  if (n <= 0 || n_ck <= 0) return RIVER_OK;
+  if (!route_scores_ok(n, d, dt, b, ld, n_ck))
+    return fail(RIVER_ERR_UNSUPPORTED, "route scores: shape outside the streaming path");
+  RouteMulti m{};
+  for (int c = 0; c < n_ck; ++c)
+    m.a[c] = RouteArgs{n, d, b, ck[c].h_prev, ld, ck[c].h_cur, ld, gamma, eps, ck[c].w_down, ck[c].w_up,
+                       __builtin_inff(), __builtin_inff(), cos_out + (int64_t)c * n, prob_out + (int64_t)c * n,
+                       mask_scratch + (int64_t)c * n, nullptr, nullptr, nullptr, 0, 0};
+  // the same tile as launch_route at this n, so the same values
+  const bool two = n >= 8192;
+  const int T = two ? 32 : 16;
+  const dim3 grid((unsigned)((n + T - 1) / T), (unsigned)n_ck);
+  if (gamma) {
+    if (two) route_stream_multi_kernel<2, true><<<grid, 256, 0, s>>>(m);
+    else route_stream_multi_kernel<1, true><<<grid, 256, 0, s>>>(m);
+  } else {
+    if (two) route_stream_multi_kernel<2, false><<<grid, 256, 0, s>>>(m);
+    else route_stream_multi_kernel<1, false><<<grid, 256, 0, s>>>(m);
+  }
+  return check_launch("route scores");
+}
+
 river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int64_t ld_prev,
                           const void* h_cur, int64_t ld_cur, const void* gamma, float eps,
                           const void* w_down, const void* w_up, int b, float tau, float theta,
@@ -588,9 +640,7 @@ river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int6
     const bool mfma = dt == RIVER_BF16 && w_down && d % 32 == 0 && b % 16 == 0 && b <= 128;
     // streaming path: groups of four 64-wide slabs, byte offsets of both state arrays and
     // W_down within 31 bits, gamma (if any) within its LDS copy
-    const bool stream = dt == RIVER_BF16 && w_down && d % 256 == 0 && b <= 128 &&
-                        (int64_t)n * ld_cur * 2 < ((int64_t)1 << 31) &&
-                        (int64_t)n * ld_prev * 2 < ((int64_t)1 << 31) && d <= 8192;
+    const bool stream = w_down && stream_ok(n, d, dt, b, ld_prev, ld_cur);
     if (stream) {
       const bool two = n >= 8192;
       const int T = two ? 32 : 16;
