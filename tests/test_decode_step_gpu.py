@@ -288,6 +288,89 @@ def test_decode_step_8b_router_and_maps():
     assert np.sum(exg == 11) == 13 and np.sum(exg == 31) == n - 13
 
 
+@pytest.mark.parametrize("case", ["ragged-37", "200-no-split", "router-off-maps", "fp32-tiny",
+                                  "mixed-routers"])
+def test_decode_step_paths_and_shapes(case):
+    """Shapes around the step's paths, each against the oracle and against
+    the per-checkpoint launches: 37 tokens (single fill, split reduction,
+    ragged tiles), 200 tokens (single fill without the split), maps at two
+    router-off checkpoints (two decision launches, a fill per checkpoint),
+    fp32 states (the generic fill), and routers at some checkpoints only
+    (per-checkpoint launches). Exit layers agree bit for bit; so do the
+    caches wherever both paths fill with the same launches."""
+    bitwise = case != "ragged-37"
+    if case == "ragged-37":
+        cfg = get_config(2, n_tokens=37)
+    elif case == "200-no-split":
+        cfg = get_config(2, n_tokens=200)
+    elif case == "router-off-maps":
+        cfg = get_config(2)
+    elif case == "fp32-tiny":
+        cfg = get_config(0)
+    else:
+        cfg = get_config("3D", n_tokens=64)
+    layers = list(cfg.route_layers)
+    need = sorted({l - 1 for l in layers} | set(layers))
+    hs = {l: t.to(DEV) for l, t in G.hidden_states(cfg, cfg.n_tokens, need).items()}
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    cks = llama1b_checkpoints(cfg, hs)
+    if case == "fp32-tiny":
+        # cosines a few 1e-5 apart: tau at the middle of the widest gap among
+        # the running tokens keeps them out of the band
+        alive = np.ones(cfg.n_tokens, bool)
+        for c in cks:
+            cos, *_ = O.route(np64(c["h_prev"]), np64(c["h_cur"]), None, 1e-6, None, None, -INF, -INF)
+            v = np.sort(cos[alive])
+            if len(v) < 4:
+                c["tau"] = 2.0                 # nobody left to split
+                continue
+            lo, hi = len(v) // 4, len(v) - len(v) // 4      # keep tokens on both sides
+            g = lo + int(np.argmax(np.diff(v)[lo:hi]))
+            # no gap twice the band wide: nobody exits here
+            c["tau"] = 0.5 * (v[g] + v[g + 1]) if v[g + 1] - v[g] > 2.5 * BAND else 2.0
+            alive &= ~(cos > f32(c["tau"]))
+    if case == "router-off-maps":
+        for c in cks:
+            if c["layer"] in (8, 12):
+                c["maps"] = G.near_identity_maps(cfg, cfg.L - c["layer"], tag=f"m{c['layer']}").to(DEV)
+    if case == "mixed-routers":
+        # the 8B shape's cosines differ in the 8th digit: routers at every
+        # other checkpoint decide (tau off, theta at the middle of the widest
+        # gap of the running tokens' probabilities); nobody exits elsewhere
+        alive = np.ones(cfg.n_tokens, bool)
+        for k, c in enumerate(cks):
+            c["tau"] = 2.0
+            if k % 2:
+                continue
+            wd, wu = (t.to(DEV) for t in G.router_weights(cfg, c["layer"]))
+            c["w_down"], c["w_up"], c["tau"] = wd, wu, -INF
+            _, prob, _, _ = O.route(np64(c["h_prev"]), np64(c["h_cur"]), None, 1e-6, np64(wd), np64(wu),
+                                    -INF, -INF)
+            v = np.sort(prob[alive])
+            c["theta"] = INF
+            if len(v) >= 4:
+                lo, hi = len(v) // 4, len(v) - len(v) // 4
+                g = lo + int(np.argmax(np.diff(v)[lo:hi]))
+                if v[g + 1] - v[g] > 2.5 * BAND:
+                    c["theta"] = 0.5 * (v[g] + v[g + 1])
+            alive &= ~(prob > f32(c["theta"]))
+    out = []
+    try:
+        for path in (0, 1):
+            tee.river_debug_set_decode_path(path)
+            out.append(run_gpu(cks, cfg, wk, wv, slot))
+    finally:
+        tee.river_debug_set_decode_path(0)
+    (e0, k0, v0), (e1, k1, v1) = out
+    assert torch.equal(e0, e1)
+    if bitwise:
+        iv = torch.int16 if k0.dtype == torch.bfloat16 else torch.int32
+        assert torch.equal(k0.view(iv), k1.view(iv)) and torch.equal(v0.view(iv), v1.view(iv))
+    exg = check_step(cfg, cks, e0, k0, v0, slot, wk, wv)
+    assert (exg < cfg.L).any()
+
+
 def test_decode_step_graph_replay():
     """The step captured once into a graph and replayed for three steps with
     new states copied into the captured buffers; each replay equals an eager
