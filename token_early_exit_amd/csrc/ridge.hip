@@ -271,7 +271,7 @@ static RidgeWs ridge_layout(int n, int d_in, int d_out, river_dtype dt, char* ba
   RidgeWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { char* p = base ? base + off : nullptr; off += align_up(bytes, 256); return p; };
-  const size_t di = d_in, dd = d_out, nn = n;
+  const size_t di = d_in, dd = d_out;
   w.flag = (int*)take(256);
   w.G = (float*)take(di * di * 4);
   w.Xi = (float*)take(di * di * 4);
