@@ -455,13 +455,13 @@ def fill_long_context(reps=3):
     kc = torch.empty((nl, cfg.n_slots, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16,
                      device="cuda")
     vc = torch.empty_like(kc)
-    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, m, d, 0, 0, nl), dtype=torch.uint8,
-                     device="cuda")
+    # with room for the projection on dequantised weights
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, m, d, cfg.n_kv_heads * cfg.head_dim, 0, nl),
+                     dtype=torch.uint8, device="cuda")
 
     def fill(with_maps):
         tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=m,
-                          row_idx=rows, maps=maps if with_maps else None,
-                          workspace=ws if with_maps else None)
+                          row_idx=rows, maps=maps if with_maps else None, workspace=ws)
 
     out = {}
     for key, wm in (("fill_ms", True), ("projection_ms", False)):

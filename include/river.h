@@ -244,12 +244,16 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
  * workspace: with maps, at least river_workspace_size(RIVER_OP_KV_FILL,
  *            m_max, d, 0, 0, 1) bytes; the layers are processed in as few
  *            chunks as the given size allows. Without maps none is needed.
- *            For m_max <= 64, river_workspace_size(RIVER_OP_KV_FILL, m_max,
- *            d, n_kv_heads * head_dim, 0, n_layers) bytes also hold the
- *            fp32 partial sums of a projection whose reduction over d is
- *            split into parts (so that a few rows still occupy every CU);
- *            the parts are added in a fixed order, so results do not
- *            depend on the split. With less, the reduction is not split.
+ *            river_workspace_size(RIVER_OP_KV_FILL, m_max, d,
+ *            n_kv_heads * head_dim, 0, n_layers) bytes also hold, for
+ *            m_max <= 64, the fp32 partial sums of a projection whose
+ *            reduction over d is split into parts (so that a few rows still
+ *            occupy every CU; the parts are added in a fixed order, so
+ *            results do not depend on the split), and for row counts that
+ *            give at least two 256 x 256 tiles per CU the weights
+ *            dequantised to bf16 (the values the int4 path forms in
+ *            registers), which a 256 x 256 bf16 GEMM then projects. With
+ *            less, the projection dequantises in registers, unsplit.
  * Only the filled slots are written; every other byte is left unchanged.
  * Paths: bf16 with d % 256 == 0, n_out % 64 == 0, group % 64 == 0, the
  * same group and scale/zero dtype for wk and wv, an even number of groups
@@ -461,11 +465,13 @@ const char* river_version(void);
  * bitwise-identical results. */
 river_status river_debug_set_compact_path(int path);
 
-/* Test hook: force the tile of the fill's bf16 map GEMM (0 = automatic:
- * 256 x 256 once that gives at least two tiles per compute unit, else
- * 128 x 128; 1 = 128 x 128; 2 = 256 x 256). Process-wide. The two tiles
- * group the reduction over d into MFMA steps differently, so their results
- * agree to fp32 rounding, not bit for bit. */
+/* Test hook: force the tiles of the fill's GEMMs (0 = automatic: 256 x 256
+ * once that gives at least two tiles per compute unit, else 128 x 128;
+ * 1 = 128 x 128 for the map GEMM and the int4 projection; 2 = 256 x 256
+ * for the map GEMM and, with room in the workspace and more than 64 rows,
+ * the projection on dequantised weights). Process-wide. The tiles group the
+ * reduction over d into MFMA steps differently, so their results agree to
+ * fp32 rounding, not bit for bit. */
 river_status river_debug_set_gemm_path(int path);
 
 /* Test hook: 1 forces river_decode_step onto its per-checkpoint launches

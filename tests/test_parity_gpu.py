@@ -360,6 +360,50 @@ def test_kv_fill_map_gemm_tiles(gemm_path):
         assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-2 * b.abs().amax(dim=-1, keepdim=True))
 
 
+@pytest.mark.parametrize("maps", [False, True])
+def test_kv_fill_dequantised_projection(maps):
+    """The projection as a 256 x 256 bf16 GEMM on weights dequantised into
+    the workspace (forced; at large row counts it is the automatic choice),
+    d = 1024, 300 of 640 rows with the count on the device, with and without
+    maps: every filled row within the K/V bar, untouched slots unchanged, and
+    within bf16 rounding of the int4 kernel's fill."""
+    cfg = get_config(1, d=1024, n_tokens=640, n_slots=700)
+    layers = [5, 6, 7]
+    nl = len(layers)
+    h = G.hidden_states(cfg, cfg.n_tokens, [4])[4].to(DEV)
+    g = torch.Generator().manual_seed(77)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    mp = G.near_identity_maps(cfg, nl).to(DEV) if maps else None
+    sel = torch.sort(torch.randperm(cfg.n_tokens, generator=g)[:300]).values.to(torch.int32)
+    rows = torch.full((cfg.n_tokens,), -1, dtype=torch.int32)
+    rows[:300] = sel
+    rows = rows.to(DEV)
+    m_dev = torch.tensor([300], dtype=torch.int32, device=DEV)
+    nh = cfg.n_kv_heads * cfg.head_dim
+    # the automatic size holds the dequantised weights only where they would
+    # be chosen; forcing them here needs their [nl][2 nh][d] bf16 on top
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, cfg.n_tokens, cfg.d, nh, 0, nl)
+                     + nl * 2 * nh * cfg.d * 2, dtype=torch.uint8, device=DEV)
+    out = {}
+    try:
+        for p in (2, 1):
+            tee.river_debug_set_gemm_path(p)
+            kc, vc = G.nan_cache(cfg, nl, device=DEV)
+            tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=cfg.n_tokens,
+                              m_dev=m_dev, row_idx=rows, maps=mp, workspace=ws)
+            torch.cuda.synchronize()
+            out[p] = (kc, vc)
+    finally:
+        tee.river_debug_set_gemm_path(0)
+    kc, vc = out[2]
+    check_fill(cfg, kc, vc, h, sel.numpy(), slot, mp, wk, wv)
+    s_ = slot[sel.long().to(DEV)].long()
+    for a, b in zip(out[2], out[1]):
+        a, b = a[:, s_].float(), b[:, s_].float()
+        assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-2 * b.abs().amax(dim=-1, keepdim=True))
+
+
 def test_kv_fill_identity_null_equals_explicit_eye():
     cfg = get_config(2)
     layers = list(range(9, 17))

@@ -1,7 +1,9 @@
 // bf16 GEMM for large row counts: C[z] = A[z] . B[z]^T (both operands
 // K-contiguous, "NT"), fp32 accumulation, K a multiple of 128, bf16 output
 // (EPI_BF16, or EPI_BF16N with the per-column gamma and the per-row partial
-// sums of squares; see gemm.h).
+// sums of squares; see gemm.h), or EPI_CACHE: columns [0, nh) to the K
+// cache and [nh, 2 nh) to the V cache at the slot of each row (the K/V
+// projection on weights dequantised to bf16 beforehand).
 //
 // Workgroup tile 256 x 256, 512 threads = 8 waves in a 2 x 4 grid; each
 // wave owns a 128 x 64 block: 4 x 2 accumulators of 32x32 fed by
@@ -32,7 +34,7 @@ __device__ __forceinline__ int swz4(int r) { return (r >> 2) & 3; }
 
 template <int EPI>
 __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_n, int batch) {
-  static_assert(EPI == EPI_BF16 || EPI == EPI_BF16N, "bf16 output");
+  static_assert(EPI == EPI_BF16 || EPI == EPI_BF16N || EPI == EPI_CACHE, "bf16 output");
   constexpr int BM = 256, BN = 256;
   constexpr int MI = 4, NI = 2;          // 32x32 fragments per wave
   constexpr int AD = BM * 4 / 512;       // A loads per thread per slab (2)
@@ -81,6 +83,18 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_n, 
     const int mt = g0 + tg % gsz;
     const int nt = tg / gsz;
     const int m0 = mt * BM, n0 = nt * BN;
+
+    // EPI_CACHE: the row ids of this lane's four output rows go out now, the
+    // slots once the first slab has landed (its wait covers these loads)
+    [[maybe_unused]] int er[MI], sl[MI];
+    if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = m0 + wm * 128 + mi * 32 + (lane & 31);
+        const int rc = row < M ? row : M - 1;
+        er[mi] = g.e_rows ? g.e_rows[rc] : rc;
+      }
+    }
 
     // load i of this thread fills LDS chunk p = (i * 8 + wave) * 64 + lane
     // of the A (or B) rows: row p / 4, physical chunk p % 4, which holds
@@ -160,6 +174,14 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_n, 
     issue(I1{}, 1);
     issue(I2{}, 2);
     wait_barrier<2 * PER_SLAB, true>();   // slab 0 landed
+    if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = m0 + wm * 128 + mi * 32 + (lane & 31);
+        const bool ok = row < M && er[mi] >= 0 && er[mi] < g.e_nrows;
+        sl[mi] = ok ? g.slot[er[mi]] : -1;          // range-checked where it is used
+      }
+    }
     Frag f0, f1;
     frag(S0, 0, f0);
 
@@ -225,6 +247,27 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_n, 
           if (h == 0 && row < M && cb < N)
             g.ss[(int64_t)z * g.ss_bstride + (int64_t)row * (N >> 6) + (cb >> 6)] = ss;
         }
+      }
+      if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const int row = rb + mi * 32 + (lane & 31);
+          const int slot = sl[mi];
+          if (row >= M || slot < 0 || slot >= g.n_slots) continue;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = cb + ni * 32 + 8 * gq + 4 * h;   // four columns, all in K or all in V
+              if (col >= N) continue;
+              const bool isv = col >= g.nh;
+              uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc) + (int64_t)z * g.cache_bstride +
+                              (int64_t)slot * g.nh + (isv ? col - g.nh : col);
+              *(uint2*)dst = uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
+                                   pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
+            }
+        }
+        continue;                                  // next tile
       }
       uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.c_bstride;
 #pragma unroll

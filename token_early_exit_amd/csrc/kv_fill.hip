@@ -170,6 +170,28 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(int m_max, const int32_t
   }
 }
 
+// bf16 copies of a chunk's int4 K/V weights, [nl][2 nh][K]: the values the
+// W4 kernel forms in registers (dequant8, the same scale and -zero * scale),
+// one thread per 8 weights
+__global__ __launch_bounds__(256) void w4_dequant_kernel(GemmArgs g, int nl, uint16_t* out) {
+  const int K = g.K, nh = g.nh, N = 2 * nh;
+  const int per_row = K / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)nl * N * per_row) return;
+  const int k8 = (int)(idx % per_row);
+  const int col = (int)((idx / per_row) % N);
+  const int z = (int)(idx / ((int64_t)per_row * N));
+  const int which = col >= nh ? 1 : 0, hc = col - which * nh;
+  const uint32_t w = *(const uint32_t*)(g.q[which] + z * g.q_bstride + (int64_t)hc * (K / 2) + k8 * 4);
+  const int gpr = K / g.group[which];
+  const int64_t si = z * g.sz_bstride[which] + (int64_t)hc * gpr + (k8 * 8) / g.group[which];
+  const float sc = load_sz(g.s[which], si, g.sz_bf16[which]);
+  const float ze = load_sz(g.zp[which], si, g.sz_bf16[which]);
+  uint32_t o[4];
+  dequant8(w, sc, -ze * sc, o);
+  *(u32x4*)(out + ((int64_t)z * N + col) * K + k8 * 8) = u32x4{o[0], o[1], o[2], o[3]};
+}
+
 }  // namespace river
 
 namespace river_host {
@@ -218,10 +240,24 @@ static int choose_ksplit(int m_max, int N, int K, int nl, size_t avail) {
 }
 
 // fp32 partial sums of up to 8 parts, K and V, for n_layers layers
-size_t kv_fill_split_workspace(int m_max, int n_out, int n_layers) {
-  if (m_max > 64 || n_out <= 0 || n_layers <= 0) return 0;
-  return align_up((size_t)8 * n_layers * m_max * 2 * n_out * 4, 256);
+// At large row counts (two 256x256 tiles per CU or more) the projection
+// runs as the 256x256 bf16 GEMM on weights dequantised into the workspace
+// beforehand: each weight is then dequantised once per call instead of once
+// per row tile, and the GEMM reads half the LDS bytes per MFMA.
+static bool dequant_wanted(int m_max, int N, int nl) {
+  return m_max > 64 && (int64_t)((N + 255) / 256) * ((m_max + 255) / 256) * nl >= 2 * N_CU;
 }
+
+// the projection's own workspace: fp32 partial sums of up to 8 parts, K and
+// V, for at most 64 rows; the bf16 weights of n_layers layers where they are
+// dequantised beforehand; nothing otherwise
+size_t kv_fill_proj_workspace(int m_max, int d, int n_out, int n_layers) {
+  if (n_out <= 0 || n_layers <= 0 || m_max <= 0) return 0;
+  if (m_max <= 64) return align_up((size_t)8 * n_layers * m_max * 2 * n_out * 4, 256);
+  if (dequant_wanted(m_max, 2 * n_out, n_layers)) return align_up((size_t)n_layers * 2 * n_out * d * 2, 256);
+  return 0;
+}
+
 
 size_t kv_fill_layer_workspace(int m_max, int d, int n_layers) {
   return (size_t)n_layers * (layer_xhat_bytes(m_max, d) + layer_ss_bytes(m_max, d));
@@ -304,6 +340,19 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
     if (!layer) {
+      const int path = gemm_path_override();
+      if (path != 1 && m_max > 64 && !q.M_dev_z && (path == 2 || dequant_wanted(m_max, q.N, nl)) &&
+          part_bytes >= (size_t)nl * q.N * d * 2) {
+        uint16_t* dq = (uint16_t*)part_ws;
+        const int64_t threads = (int64_t)nl * q.N * (d / 8);
+        w4_dequant_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(q, nl, dq);
+        river_status st = check_launch("kv_fill weight dequantisation");
+        if (st != RIVER_OK) return st;
+        GemmArgs p = q;
+        p.B = dq; p.ldb = d; p.b_bstride = (int64_t)q.N * d;
+        gemm_big_launch<EPI_CACHE>(p, nl, s);
+        return check_launch("kv_fill projection (bf16)");
+      }
       const int ks = choose_ksplit(m_max, q.N, d, nl, part_bytes);
       if (ks > 1) {
         q.ksplit = ks;
