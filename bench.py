@@ -382,6 +382,51 @@ def router_fit_times(key, n, epochs=100, batch=256):
             "loss_first_last_epoch": [float(lo[0]), float(lo[-1])]}
 
 
+def fill_8b_prefill(reps=3):
+    """The fill at the Llama-3-8B prefill shape (8192 tokens, d = 4096,
+    8 x 128 KV heads, int4 group 128, near-identity maps): the 5% of tokens
+    that exit at block 11 (410 rows, blocks 12..32) and the rest at block 31
+    (7782 rows, block 32). ms per call averaged over ``reps`` calls between
+    two events, and TFLOP/s on the algorithmic flops (map GEMM and
+    projection)."""
+    cfg = get_config(3)
+    n, d = cfg.n_tokens, cfg.d
+    nh = cfg.n_kv_heads * cfg.head_dim
+    hs = G.hidden_states(cfg, n, [11, 31], device="cuda")
+    slot = G.slots(cfg, device="cuda")
+    n_early = int(round(cfg.extra["early_frac"] * n))
+    perm = torch.randperm(n, generator=torch.Generator().manual_seed(3))
+    early = torch.sort(perm[:n_early]).values.to(torch.int32).to("cuda")
+    late = torch.sort(perm[n_early:]).values.to(torch.int32).to("cuda")
+    out = {}
+    for name, e, rows in (("exit_at_11", 11, early), ("exit_at_31", 31, late)):
+        layers = list(range(e + 1, cfg.L + 1))
+        nl = len(layers)
+        w = G.kv_weights(cfg, layers, device="cuda")
+        wk = tuple(w["wk"]) + (cfg.group,)
+        wv = tuple(w["wv"]) + (cfg.group,)
+        maps = G.near_identity_maps(cfg, nl, tag=f"maps{e}", device="cuda")
+        m = rows.numel()
+        kc = torch.empty((nl, cfg.n_slots, cfg.n_kv_heads, cfg.head_dim), dtype=torch.bfloat16,
+                         device="cuda")
+        vc = torch.empty_like(kc)
+        ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, m, d, nh, 0, nl), dtype=torch.uint8,
+                         device="cuda")
+
+        def fill(i):
+            tee.river_kv_fill(hs[e], slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=m,
+                              row_idx=rows, maps=maps, workspace=ws)
+        fill(0)
+        torch.cuda.synchronize()
+        ms = time_region(fill, reps) / reps
+        flops = 2.0 * m * nl * (d * d + d * 2 * nh)
+        out[name] = {"rows": m, "layers": nl, "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+                     "frac_of_bf16_peak": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+        del w, wk, wv, maps, kc, vc, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def route_compact_8b(reps=20):
     """route and compact at the Llama-3-8B prefill shape (8192 tokens,
     d = 4096, router b = 128 at checkpoint 11): µs per call (graph of
@@ -673,7 +718,8 @@ def main():
     line["fill_long_context"] = fill_long_context()
     progress("long-context fill done")
     line["route_compact_8b_prefill"] = route_compact_8b()
-    progress("8B route and compact done")
+    line["fill_8b_prefill"] = fill_8b_prefill()
+    progress("8B route, compact and fill done")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
         progress("cpu baseline done")

@@ -249,8 +249,8 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
  *            m_max <= 64, the fp32 partial sums of a projection whose
  *            reduction over d is split into parts (so that a few rows still
  *            occupy every CU; the parts are added in a fixed order, so
- *            results do not depend on the split), and for row counts that
- *            give at least two 256 x 256 tiles per CU the weights
+ *            results do not depend on the split), and for m_max >= 2048
+ *            with at least half a 256 x 256 tile per CU the weights
  *            dequantised to bf16 (the values the int4 path forms in
  *            registers), which a 256 x 256 bf16 GEMM then projects. With
  *            less, the projection dequantises in registers, unsplit.
@@ -466,7 +466,8 @@ const char* river_version(void);
 river_status river_debug_set_compact_path(int path);
 
 /* Test hook: force the tiles of the fill's GEMMs (0 = automatic: 256 x 256
- * once that gives at least two tiles per compute unit, else 128 x 128;
+ * from 1024 rows (2048 for the projection) when that gives enough tiles to
+ * occupy the compute units, else 128 x 128;
  * 1 = 128 x 128 for the map GEMM and the int4 projection; 2 = 256 x 256
  * for the map GEMM and, with room in the workspace and more than 64 rows,
  * the projection on dequantised weights). Process-wide. The tiles group the

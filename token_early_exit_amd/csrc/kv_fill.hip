@@ -240,12 +240,16 @@ static int choose_ksplit(int m_max, int N, int K, int nl, size_t avail) {
 }
 
 // fp32 partial sums of up to 8 parts, K and V, for n_layers layers
-// At large row counts (two 256x256 tiles per CU or more) the projection
-// runs as the 256x256 bf16 GEMM on weights dequantised into the workspace
-// beforehand: each weight is then dequantised once per call instead of once
-// per row tile, and the GEMM reads half the LDS bytes per MFMA.
+// At large row counts the projection runs as the 256x256 bf16 GEMM on
+// weights dequantised into the workspace beforehand: each weight is then
+// dequantised once per call instead of once per row tile, and the GEMM
+// reads 0.75 KB of LDS per MFMA instead of about 1.1. The dequantisation
+// costs (1/2 + 2) bytes of traffic per weight, against 2 m flops per weight
+// for m rows: from 2048 rows on it is a few percent of the GEMM (at 410
+// rows and 21 layers it made the projection slower). At least half a tile
+// per CU.
 static bool dequant_wanted(int m_max, int N, int nl) {
-  return m_max > 64 && (int64_t)((N + 255) / 256) * ((m_max + 255) / 256) * nl >= 2 * N_CU;
+  return m_max >= 2048 && (int64_t)((N + 255) / 256) * ((m_max + 255) / 256) * nl >= N_CU / 2;
 }
 
 // the projection's own workspace: fp32 partial sums of up to 8 parts, K and
