@@ -6,14 +6,17 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "common.h"
 
 namespace river_host {
 
 static thread_local char g_err[512] = "";
-static int g_compact_path = 0;
-static int g_gemm_path = 0;
-static int g_decode_path = 0;
+// test hooks (process-wide; read by every launch, so atomics)
+static std::atomic<int> g_compact_path{0};
+static std::atomic<int> g_gemm_path{0};
+static std::atomic<int> g_decode_path{0};
 
 void set_error(const char* fmt, ...) {
   va_list ap;
@@ -36,9 +39,9 @@ river_status check_launch(const char* what) {
   return RIVER_OK;
 }
 
-int compact_path_override() { return g_compact_path; }
-int gemm_path_override() { return g_gemm_path; }
-int decode_path_override() { return g_decode_path; }
+int compact_path_override() { return g_compact_path.load(std::memory_order_relaxed); }
+int gemm_path_override() { return g_gemm_path.load(std::memory_order_relaxed); }
+int decode_path_override() { return g_decode_path.load(std::memory_order_relaxed); }
 
 static bool dt_ok(river_dtype dt) { return dt == RIVER_F32 || dt == RIVER_BF16; }
 
@@ -59,19 +62,19 @@ const char* river_version(void) { return "river 0.1.0 (gfx950)"; }
 
 river_status river_debug_set_compact_path(int path) {
   if (path < 0 || path > 4) return fail(RIVER_ERR_ARG, "compact path must be 0..4, got %d", path);
-  g_compact_path = path;
+  g_compact_path.store(path, std::memory_order_relaxed);
   return RIVER_OK;
 }
 
 river_status river_debug_set_gemm_path(int path) {
   if (path < 0 || path > 2) return fail(RIVER_ERR_ARG, "gemm path must be 0..2, got %d", path);
-  g_gemm_path = path;
+  g_gemm_path.store(path, std::memory_order_relaxed);
   return RIVER_OK;
 }
 
 river_status river_debug_set_decode_path(int path) {
   if (path < 0 || path > 1) return fail(RIVER_ERR_ARG, "decode path must be 0..1, got %d", path);
-  g_decode_path = path;
+  g_decode_path.store(path, std::memory_order_relaxed);
   return RIVER_OK;
 }
 
