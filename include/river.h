@@ -246,10 +246,12 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
  *            chunks as the given size allows. Without maps none is needed.
  *            river_workspace_size(RIVER_OP_KV_FILL, m_max, d,
  *            n_kv_heads * head_dim, 0, n_layers) bytes also hold, for
- *            m_max <= 64, the fp32 partial sums of a projection whose
- *            reduction over d is split into parts (so that a few rows still
- *            occupy every CU; the parts are added in a fixed order, so
- *            results do not depend on the split), and for m_max >= 2048
+ *            m_max <= 64 (and up to 256 when the projection has few
+ *            tiles: at most 128 of 64 rows x 256 outputs x layers), the
+ *            fp32 partial sums of a projection whose reduction over d is
+ *            split into parts (so that a few rows still occupy every CU;
+ *            the parts are added in a fixed order, so a result does not
+ *            depend on which thread finishes first), and for m_max >= 2048
  *            with at least half a 256 x 256 tile per CU the weights
  *            dequantised to bf16 (the values the int4 path forms in
  *            registers), which a 256 x 256 bf16 GEMM then projects. With
@@ -360,7 +362,7 @@ typedef struct {
  *          n_layers) bytes fill every checkpoint in one pass; with maps at
  *          least the size for n_layers = 2 is needed. Passing d_out =
  *          n_kv_heads * head_dim adds room for the split reduction that
- *          river_kv_fill describes (n <= 64).
+ *          river_kv_fill describes (n <= 256).
  * The call enqueues an ordered sequence of kernels on s and returns: no
  * host synchronisation, allocation or runtime memset, so it may be captured
  * into a HIP graph once and the graph replayed for every step. The fill's

@@ -288,21 +288,24 @@ def test_decode_step_8b_router_and_maps():
     assert np.sum(exg == 11) == 13 and np.sum(exg == 31) == n - 13
 
 
-@pytest.mark.parametrize("case", ["ragged-37", "200-no-split", "router-off-maps", "fp32-tiny",
-                                  "mixed-routers"])
+@pytest.mark.parametrize("case", ["ragged-37", "200-split", "300-no-split", "router-off-maps",
+                                  "fp32-tiny", "mixed-routers"])
 def test_decode_step_paths_and_shapes(case):
     """Shapes around the step's paths, each against the oracle and against
     the per-checkpoint launches: 37 tokens (single fill, split reduction,
-    ragged tiles), 200 tokens (single fill without the split), maps at two
+    ragged tiles), 200 tokens (the split over 64-row tiles, in parts that
+    differ between the paths), 300 tokens (no split), maps at two
     router-off checkpoints (two decision launches, a fill per checkpoint),
     fp32 states (the generic fill), and routers at some checkpoints only
     (per-checkpoint launches). Exit layers agree bit for bit; so do the
     caches wherever both paths fill with the same launches."""
-    bitwise = case != "ragged-37"
+    bitwise = case not in ("ragged-37", "200-split")
     if case == "ragged-37":
         cfg = get_config(2, n_tokens=37)
-    elif case == "200-no-split":
+    elif case == "200-split":
         cfg = get_config(2, n_tokens=200)
+    elif case == "300-no-split":
+        cfg = get_config(2, n_tokens=300)
     elif case == "router-off-maps":
         cfg = get_config(2)
     elif case == "fp32-tiny":

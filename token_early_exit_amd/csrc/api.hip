@@ -92,7 +92,7 @@ size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int 
     case RIVER_OP_DECODE_STEP:
       if (n <= 0 || d <= 0) return 0;
       return decode_fixed_workspace(n, d, RIVER_F32, n_layers) + (n_layers > 1 ? kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) : 0) +
-             (n_layers > 1 && n <= 64 ? kv_fill_proj_workspace(n, d, d_out, n_layers - 1) : 0);
+             decode_proj_workspace(n, d, d_out, n_layers);
     case RIVER_OP_ROUTER_FIT:
       if (n <= 0 || d <= 0 || d_out <= 0 || n_targets <= 0 || n_layers <= 0) return 0;
       return calib_workspace(n, d, d_out, n_targets, n_layers);

@@ -34,7 +34,8 @@ namespace river {
 // of squares of the unscaled result (one per 64-column block): the input
 // of a skipped layer's RMSNorm, applied in the K/V projection's epilogue.
 // EPI_PART: fp32 partial sums of a split reduction, [ksplit][batch][M_max][N]
-// (the W4 projection at small row counts; a finishing kernel adds them).
+// (the map GEMM and the W4 projection at small row counts; a finishing
+// kernel adds them in a fixed order).
 enum { EPI_BF16 = 0, EPI_F32 = 1, EPI_CACHE = 2, EPI_BF16N = 3, EPI_PART = 4 };
 
 struct GemmArgs {
@@ -113,7 +114,8 @@ constexpr int N_CU = 256;
 
 template <int BM, int EPI>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, int batch) {
-  static_assert(EPI == EPI_BF16 || EPI == EPI_F32 || EPI == EPI_BF16N, "bf16 or fp32 output");
+  static_assert(EPI == EPI_BF16 || EPI == EPI_F32 || EPI == EPI_BF16N || EPI == EPI_PART,
+                "bf16 or fp32 output, or fp32 partial sums");
   constexpr int BN = 128;
   constexpr int MI = BM / 64;            // 32-row fragments per wave
   constexpr int NI = 2;                  // 32-column fragments per wave
@@ -135,7 +137,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
   // [x * chunk, (x + 1) * chunk) so that neighbouring tiles (one batch
   // entry, a few row and column tiles) share that XCD's L2.
   const int tiles_m_act = (M + BM - 1) / BM;
-  const int total = tiles_n * tiles_m_act * batch;
+  const int ksplit = EPI == EPI_PART ? g.ksplit : 1;
+  const int total = tiles_n * tiles_m_act * batch * ksplit;
   const int xcd = blockIdx.x & 7, wg_in_xcd = blockIdx.x >> 3;
   const int per_xcd = (gridDim.x + 7 - xcd) >> 3;
   const int chunk = (total + 7) >> 3;
@@ -145,7 +148,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int h = lane >> 5;
-  const int KT = K / 64;                 // a multiple of 4
+  const int KT = K / 64 / ksplit;        // slabs per tile, a multiple of 4
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -163,8 +166,11 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
     // 4 row tiles x 8 column tiles: 12 operand tiles to bring into its L2
     // instead of 33 for one row tile across 32 column tiles.
     constexpr int GM = 4;
-    const int z = tile / (tiles_n * tiles_m_act);
-    const int tz = tile - z * tiles_n * tiles_m_act;
+    const int ks = tile / (tiles_n * tiles_m_act * batch);   // part of the reduction
+    const int tb = tile - ks * tiles_n * tiles_m_act * batch;
+    const uint32_t k_off = (uint32_t)ks * KT * 128;           // its first slab, in bytes
+    const int z = tb / (tiles_n * tiles_m_act);
+    const int tz = tb - z * tiles_n * tiles_m_act;
     const int g0 = tz / (GM * tiles_n) * GM;                 // first row tile of the group
     const int gsz = tiles_m_act - g0 < GM ? tiles_m_act - g0 : GM;
     const int tg = tz - g0 * tiles_n;
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
       const int r = p >> 3, c = (p & 7) ^ swz(r);
       int src = a_src_row[i];
       if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
-      a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
+      a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2) + k_off;
     }
     const void* b_buf = g.B + (int64_t)z * g.b_bstride;
     const int b_bytes = (int)(N * g.ldb * 2);                   // rows past N read zeros
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
     for (int i = 0; i < BD; ++i) {
       const int p = (i * 4 + wave) * 64 + lane;
       const int r = p >> 3, c = (p & 7) ^ swz(r);
-      b_off[i] = (uint32_t)(((int64_t)(n0 + r) * g.ldb + c * 8) * 2);
+      b_off[i] = (uint32_t)(((int64_t)(n0 + r) * g.ldb + c * 8) * 2) + k_off;
     }
     auto issue = [&](auto st, int j) {
       u32x4* l = stage(st);
@@ -296,7 +302,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
     // here on, whose values are never used), then writes whole rows of its
     // 64 columns with 16-byte stores.
     {
-      constexpr int ES = EPI == EPI_F32 ? 4 : 2;      // output element size
+      constexpr bool F32OUT = EPI == EPI_F32 || EPI == EPI_PART;
+      constexpr int ES = F32OUT ? 4 : 2;              // output element size
       constexpr int EP = (64 * ES + 16) / 4;          // row pitch in dwords (padded)
       constexpr int LPR = 64 * ES / 16;               // lanes per row: 8 (bf16) or 16 (f32)
       uint32_t* ep = (uint32_t*)(wave == 0 ? S0 : wave == 1 ? S1 : wave == 2 ? S2 : S3);
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
               v[2] *= bf16_lo(gam[ni][gq].y);
               v[3] *= bf16_hi(gam[ni][gq].y);
             }
-            if constexpr (EPI == EPI_F32) {
+            if constexpr (F32OUT) {
               *(f32x4*)(ep + r * EP + c) = v;
             } else {
               *(uint2*)(ep + r * EP + c / 2) = uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -358,6 +365,8 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
           f32x4 o = __builtin_bit_cast(f32x4, v);
           if (row >= col && row < col + 4) o[row - col] += g.diag;
           *(f32x4*)((float*)g.C + (int64_t)z * g.c_bstride + (int64_t)row * g.ldc + col) = o;
+        } else if constexpr (EPI == EPI_PART) {
+          *(u32x4*)(g.part + (((int64_t)ks * batch + z) * M_max + row) * N + col) = v;
         } else {
           *(u32x4*)((uint16_t*)g.C + (int64_t)z * g.c_bstride + (int64_t)row * g.ldc + col) = v;
         }
@@ -376,7 +385,7 @@ template <int BM, int EPI>
 inline void gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 127) / 128;
   const int tm = (g.M_max + BM - 1) / BM;
-  const int64_t tiles = (int64_t)tn * tm * batch;
+  const int64_t tiles = (int64_t)tn * tm * batch * (EPI == EPI_PART ? g.ksplit : 1);
   int grid = (int)(tiles < N_CU ? tiles : N_CU);
   grid = (grid + 7) / 8 * 8;
   gemm_nt_kernel<BM, EPI><<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);

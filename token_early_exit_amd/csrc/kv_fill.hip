@@ -170,6 +170,38 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(int m_max, const int32_t
   }
 }
 
+// The parts of the map GEMM's split reduction (EPI_PART) added in order,
+// rounded to bf16 into C: thread (z, row, 8-column piece).
+__global__ __launch_bounds__(256) void gemm_part_finish_kernel(GemmArgs g, int batch) {
+  const int N = g.N, per = N / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int p = (int)(idx % per);
+  const int t = (int)((idx / per) % g.M_max);
+  const int z = (int)(idx / ((int64_t)per * g.M_max));
+  if (z >= batch) return;
+  int M = g.M_max;
+  if (g.M_dev) {
+    const int md = *g.M_dev;
+    M = md < 0 ? 0 : (md < g.M_max ? md : g.M_max);
+  }
+  if (t >= M) return;
+  const int col = 8 * p;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int ks = 0; ks < g.ksplit; ++ks) {
+    const float* src = g.part + (((int64_t)ks * batch + z) * g.M_max + t) * N + col;
+    const f32x4 a = *(const f32x4*)src, b = *(const f32x4*)(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] += a[i];
+      v[4 + i] += b[i];
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  *(u32x4*)((uint16_t*)g.C + (int64_t)z * g.c_bstride + (int64_t)t * g.ldc + col) = o;
+}
+
 // bf16 copies of a chunk's int4 K/V weights, [nl][2 nh][K]: the values the
 // W4 kernel forms in registers (dequant8, the same scale and -zero * scale),
 // one thread per 8 weights
@@ -225,12 +257,14 @@ size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt) {
 static size_t layer_xhat_bytes(int m_max, int d) { return align_up((size_t)m_max * d * 2, 256); }
 static size_t layer_ss_bytes(int m_max, int d) { return align_up((size_t)(d / 64 > 4 ? d / 64 : 4) * m_max * 4, 256); }
 
-// Parts of the reduction for a projection of at most 64 rows: enough
-// workgroups to fill the CUs, each part a multiple of 256 input channels,
-// the fp32 partial sums within the space left in the workspace.
+// Parts of the reduction for a projection of at most 256 rows (64-row
+// tiles): enough workgroups to fill the CUs, each part a multiple of 256
+// input channels, the fp32 partial sums within the space left in the
+// workspace. Only a projection with few tiles is split (ks * tiles <= half
+// the CUs): at 256 rows, up to 4 layers of 2048 outputs.
 static int choose_ksplit(int m_max, int N, int K, int nl, size_t avail) {
-  if (m_max > 64) return 1;
-  const int tiles = ((N + 255) / 256) * nl;
+  if (m_max > 256) return 1;
+  const int tiles = ((N + 255) / 256) * ((m_max + 63) / 64) * nl;
   const int kt = K / 64;
   int ks = 1;
   while (ks < 8 && ks * 2 * tiles <= N_CU && kt % (ks * 2 * 4) == 0 &&
@@ -239,7 +273,20 @@ static int choose_ksplit(int m_max, int N, int K, int nl, size_t avail) {
   return ks;
 }
 
-// fp32 partial sums of up to 8 parts, K and V, for n_layers layers
+// Parts of the reduction for the map GEMM (d x d per layer) with few tiles,
+// chosen like the projection's: at most one tile per CU, each part a
+// multiple of 256 input channels, the partial sums within avail bytes.
+static int choose_map_ksplit(int m_max, int d, int nl, size_t avail) {
+  const int bm = m_max <= 64 ? 64 : 128;
+  const int64_t tiles = (int64_t)((d + 127) / 128) * ((m_max + bm - 1) / bm) * nl;
+  const int kt = d / 64;
+  int ks = 1;
+  while (ks < 8 && ks * 2 * tiles <= N_CU && kt % (ks * 2 * 4) == 0 &&
+         (size_t)(ks * 2) * nl * m_max * d * 4 <= avail)
+    ks *= 2;
+  return ks;
+}
+
 // At large row counts the projection runs as the 256x256 bf16 GEMM on
 // weights dequantised into the workspace beforehand: each weight is then
 // dequantised once per call instead of once per row tile, and the GEMM
@@ -253,15 +300,31 @@ static bool dequant_wanted(int m_max, int N, int nl) {
 }
 
 // the projection's own workspace: fp32 partial sums of up to 8 parts, K and
-// V, for at most 64 rows; the bf16 weights of n_layers layers where they are
-// dequantised beforehand; nothing otherwise
+// V, for at most 64 rows, and of the parts chosen for 65 to 256 rows; the
+// bf16 weights of n_layers layers where they are dequantised beforehand;
+// nothing otherwise
 size_t kv_fill_proj_workspace(int m_max, int d, int n_out, int n_layers) {
   if (n_out <= 0 || n_layers <= 0 || m_max <= 0) return 0;
   if (m_max <= 64) return align_up((size_t)8 * n_layers * m_max * 2 * n_out * 4, 256);
+  if (m_max <= 256) {
+    const int ks = choose_ksplit(m_max, 2 * n_out, d, n_layers, SIZE_MAX);
+    if (ks > 1) return align_up((size_t)ks * n_layers * m_max * 2 * n_out * 4, 256);
+  }
   if (dequant_wanted(m_max, 2 * n_out, n_layers)) return align_up((size_t)n_layers * 2 * n_out * d * 2, 256);
   return 0;
 }
 
+// the split space any fill of a decode step may use: blocks e + 1 .. L for a
+// checkpoint e, 1 to n_layers - 1 layers of at most n rows each
+size_t decode_proj_workspace(int n, int d, int n_out, int n_layers) {
+  if (n > 256) return 0;
+  size_t m = 0;
+  for (int nl = 1; nl < n_layers; ++nl) {
+    const size_t b = kv_fill_proj_workspace(n, d, n_out, nl);
+    if (b > m) m = b;
+  }
+  return m;
+}
 
 size_t kv_fill_layer_workspace(int m_max, int d, int n_layers) {
   return (size_t)n_layers * (layer_xhat_bytes(m_max, d) + layer_ss_bytes(m_max, d));
@@ -402,14 +465,29 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
       p.A = (const uint16_t*)h; p.lda = ld_h; p.a_bstride = 0; p.a_rows = row_idx; p.a_nrows = n_rows;
       p.B = (const uint16_t*)maps + (int64_t)l0 * d * d; p.ldb = d; p.b_bstride = (int64_t)d * d;
       p.C = xh; p.ldc = d; p.c_bstride = xb / 2;
+      const int mks = gamma || gemm_path_override() != 0 ? 1 : choose_map_ksplit(m_max, d, nl, part_bytes);
       if (gamma) {
         p.gamma = (const uint16_t*)gamma + (int64_t)l0 * d; p.gamma_bstride = d;
         p.ss = ss; p.ss_bstride = sb / 4;
         gemm_bf16_auto<EPI_BF16N>(p, nl, s);
+        st = check_launch("kv_fill map");
+      } else if (mks > 1) {
+        // few tiles (a decode-sized batch): the reduction over d in parts,
+        // their fp32 sums in the space after the maps' outputs, added in order
+        p.ksplit = mks;
+        p.part = (float*)part_ws;
+        if (m_max <= 64) gemm_launch<64, EPI_PART>(p, nl, s);
+        else gemm_launch<128, EPI_PART>(p, nl, s);
+        st = check_launch("kv_fill map parts");
+        if (st == RIVER_OK) {
+          const int64_t threads = (int64_t)nl * m_max * (d / 8);
+          gemm_part_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(p, nl);
+          st = check_launch("kv_fill map sum");
+        }
       } else {
         gemm_bf16_auto<EPI_BF16>(p, nl, s);
+        st = check_launch("kv_fill map");
       }
-      st = check_launch("kv_fill map");
     } else {
       const dim3 grid((unsigned)(((int64_t)m_max + 3) / 4), (unsigned)nl);
       norm_rows_kernel<<<grid, 256, 0, s>>>(m_max, m_dev, d, (const uint16_t*)h, ld_h, n_rows, row_idx,
