@@ -458,6 +458,51 @@ def test_kv_fill_split_reduction_small_rows(n_layers, m):
         assert torch.all((a - b).abs() <= 2 ** -7 * b.abs() + 1e-4)
 
 
+@pytest.mark.parametrize("n_layers,m,m_max", [(2, 150, 200), (1, 243, 256)])
+def test_kv_fill_split_maps_and_projection(n_layers, m, m_max):
+    """65 to 256 rows with few tiles and room for partial sums: the map GEMM
+    and the projection both split the reduction over d (the map's parts are
+    added before x-hat is rounded to bf16). Llama-3.2-1B shape with maps, the
+    row count on the device and a ragged last row tile. Within the K/V bar
+    of the oracle, the same bits on a second call, and the same rows as the
+    unsplit fill (a workspace with room for the maps' outputs only) to
+    within the bar."""
+    cfg = get_config(2, n_tokens=m_max)
+    layers = list(range(cfg.L - n_layers + 1, cfg.L + 1))
+    h = G.hidden_states(cfg, cfg.n_tokens, [cfg.L - n_layers])[cfg.L - n_layers].to(DEV)
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, layers)
+    maps = G.near_identity_maps(cfg, n_layers, tag=f"split{m}").to(DEV)
+    g = torch.Generator().manual_seed(m)
+    sel = torch.randperm(cfg.n_tokens, generator=g)[:m].to(torch.int32)
+    rows = torch.full((m_max,), -1, dtype=torch.int32)
+    rows[:m] = sel
+    rows = rows.to(DEV)
+    m_dev = torch.tensor([m], dtype=torch.int32, device=DEV)
+    nh = cfg.n_kv_heads * cfg.head_dim
+    big = tee.river_workspace_size(tee.OP_KV_FILL, m_max, cfg.d, nh, 0, n_layers)
+    small = tee.river_workspace_size(tee.OP_KV_FILL, m_max, cfg.d, 0, 0, n_layers)
+    assert big > small
+    out = []
+    for size in (big, big, small):
+        ws = torch.empty(size, dtype=torch.uint8, device=DEV)
+        kc, vc = G.nan_cache(cfg, n_layers, device=DEV)
+        tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=m_max,
+                          m_dev=m_dev, row_idx=rows, maps=maps, workspace=ws)
+        torch.cuda.synchronize()
+        out.append((kc, vc))
+    (k1, v1), (k2, v2), (k0, v0) = out
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+    check_fill(cfg, k1, v1, h, sel.numpy(), slot, maps, wk, wv)
+    check_fill(cfg, k0, v0, h, sel.numpy(), slot, maps, wk, wv)
+    s = slot[sel.long().to(DEV)].long()
+    for a, b in ((k1, k0), (v1, v0)):
+        a, b = a[:, s].float(), b[:, s].float()
+        rel = (a - b).norm(dim=-1).norm(dim=-1) / b.norm(dim=-1).norm(dim=-1)
+        assert float(rel.max()) <= 1e-2
+
+
 @pytest.mark.parametrize("d,hkv,hd,group", [(200, 3, 24, 40), (512, 3, 24, 64), (264, 2, 32, 8)])
 def test_kv_fill_bf16_generic_shapes(d, hkv, hd, group):
     """bf16 shapes the MFMA tiles do not take (d not a multiple of 256, an
