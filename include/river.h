@@ -472,9 +472,10 @@ river_status river_debug_set_compact_path(int path);
  * occupy the compute units, else 128 x 128;
  * 1 = 128 x 128 for the map GEMM and the int4 projection; 2 = 256 x 256
  * for the map GEMM and, with room in the workspace and more than 64 rows,
- * the projection on dequantised weights). Process-wide. The tiles group the
- * reduction over d into MFMA steps differently, so their results agree to
- * fp32 rounding, not bit for bit. */
+ * the projection on dequantised weights; 1 and 2 also keep the map GEMM
+ * from splitting its reduction at small row counts). Process-wide. The
+ * tiles group the reduction over d into MFMA steps differently, so their
+ * results agree to fp32 rounding, not bit for bit. */
 river_status river_debug_set_gemm_path(int path);
 
 /* Test hook: 1 forces river_decode_step onto its per-checkpoint launches
