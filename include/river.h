@@ -252,8 +252,9 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
  *            split into parts (so that a few rows still occupy every CU;
  *            the parts are added in a fixed order, so a result does not
  *            depend on which thread finishes first), and for m_max >= 2048
- *            with at least half a 256 x 256 tile per CU the weights
- *            dequantised to bf16 (the values the int4 path forms in
+ *            rows given on the host (m_dev NULL) with at least half a
+ *            256 x 256 tile per CU the weights dequantised to bf16 (the
+ *            values the int4 path forms in
  *            registers), which a 256 x 256 bf16 GEMM then projects. With
  *            less, the projection dequantises in registers, unsplit.
  * Only the filled slots are written; every other byte is left unchanged.
@@ -469,7 +470,9 @@ river_status river_debug_set_compact_path(int path);
 
 /* Test hook: force the tiles of the fill's GEMMs (0 = automatic: 256 x 256
  * from 1024 rows (2048 for the projection) when that gives enough tiles to
- * occupy the compute units, else 128 x 128;
+ * occupy the compute units, else 128 x 128; with the row count on the
+ * device only for the map GEMM and only at two 256 x 256 tiles per CU
+ * for the row bound;
  * 1 = 128 x 128 for the map GEMM and the int4 projection; 2 = 256 x 256
  * for the map GEMM and, with room in the workspace and more than 64 rows,
  * the projection on dequantised weights; 1 and 2 also keep the map GEMM

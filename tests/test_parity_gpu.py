@@ -458,6 +458,38 @@ def test_kv_fill_split_reduction_small_rows(n_layers, m):
         assert torch.all((a - b).abs() <= 2 ** -7 * b.abs() + 1e-4)
 
 
+@pytest.mark.parametrize("m_small", [1, 20, 32])
+def test_kv_fill_few_rows_on_device(m_small):
+    """A count on the device of at most 32 rows under a bound of 200 (128-row
+    tiles): the projection runs its loop on the first row fragment only.
+    Within the K/V bar of the oracle, and bit for bit the rows that a count
+    of 40 (the whole-tile loop) writes for the same first rows; other slots
+    untouched."""
+    cfg = get_config(1)
+    n_layers, m_max, m_big = 3, 200, 40
+    layers = list(range(cfg.L - n_layers + 1, cfg.L + 1))
+    h = G.hidden_states(cfg, cfg.n_tokens, [cfg.L - n_layers])[cfg.L - n_layers].to(DEV)
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, layers)
+    g = torch.Generator().manual_seed(7 + m_small)
+    sel = torch.randperm(cfg.n_tokens, generator=g)[:m_big].to(torch.int32)
+    rows = torch.full((m_max,), -1, dtype=torch.int32)
+    rows[:m_big] = sel
+    rows = rows.to(DEV)
+    out = []
+    for m in (m_small, m_big):
+        kc, vc = G.nan_cache(cfg, n_layers, device=DEV)
+        tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=m_max,
+                          m_dev=torch.tensor([m], dtype=torch.int32, device=DEV), row_idx=rows)
+        torch.cuda.synchronize()
+        out.append((kc, vc))
+    (k1, v1), (k2, v2) = out
+    check_fill(cfg, k1, v1, h, sel[:m_small].numpy(), slot, None, wk, wv)
+    s = slot[sel[:m_small].long().to(DEV)].long()
+    assert torch.equal(k1[:, s].view(torch.int16), k2[:, s].view(torch.int16))
+    assert torch.equal(v1[:, s].view(torch.int16), v2[:, s].view(torch.int16))
+
+
 @pytest.mark.parametrize("n_layers,m,m_max", [(2, 150, 200), (1, 243, 256)])
 def test_kv_fill_split_maps_and_projection(n_layers, m, m_max):
     """65 to 256 rows with few tiles and room for partial sums: the map GEMM

@@ -408,7 +408,9 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
     if (!layer) {
       const int path = gemm_path_override();
-      if (path != 1 && m_max > 64 && !q.M_dev_z && (path == 2 || dequant_wanted(m_max, q.N, nl)) &&
+      // (with the row count on the device, 2048 may bound a few hundred rows:
+      // no automatic dequantisation there)
+      if (path != 1 && m_max > 64 && !q.M_dev_z && (path == 2 || (!m_dev && dequant_wanted(m_max, q.N, nl))) &&
           part_bytes >= (size_t)nl * q.N * d * 2) {
         uint16_t* dq = (uint16_t*)part_ws;
         const int64_t threads = (int64_t)nl * q.N * (d / 8);

@@ -221,316 +221,330 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     else if constexpr (S == 2) return S2; else return S3;
   };
 
-  for (int tile = xcd * chunk + wg_in_xcd; tile < t_end; tile += per_xcd) {
-    const int nt = tile % tiles_n;
-    const int mt = (tile / tiles_n) % tiles_m_act;
-    const int z = (tile / (tiles_n * tiles_m_act)) % batch;
-    const int ks = tile / (tiles_n * tiles_m_act * batch);   // part of the reduction
-    const int j0 = ks * KT;                                  // its first slab
-    const int m0 = mt * BM, n0 = nt * BN;
-    if (g.M_dev_z) {                                         // uniform
-      const int mz = g.M_dev_z[z];
-      M = mz < 0 ? 0 : (mz < M_max ? mz : M_max);
-      if (m0 >= M) continue;
-    }
-
-    // A: DMA block b = i * 4 + wave covers LDS chunks [64 b, 64 b + 64);
-    // lane l fills chunk p = 64 b + l = (row p / 8, physical chunk p % 8),
-    // which holds logical chunk (p % 8) ^ swz(row) of that row.
-    int a_src_row[AD];
-#pragma unroll
-    for (int i = 0; i < AD; ++i) {
-      const int t = m0 + (((i * NW + wave) * 64 + lane) >> 3);
-      a_src_row[i] = g.a_rows ? g.a_rows[t < M ? t : M - 1] : t;
-    }
-    // Operands come in through buffer loads straight into LDS: a uniform
-    // resource (base and byte size of the buffer), a fixed 32-bit offset per
-    // lane and a uniform offset per slab, so no per-slab address arithmetic
-    // runs on the vector unit; a read past the stated size returns zeros.
-    // A: row src of this tile's layer, 16-byte chunk c of the slab.
-    const void* a_buf = g.A + (int64_t)z * g.a_bstride;
-    const int a_bytes = (int)(a_nrows * g.lda * 2);
-    uint32_t a_off[AD];
-#pragma unroll
-    for (int i = 0; i < AD; ++i) {
-      const int p = (i * NW + wave) * 64 + lane;
-      const int r = p >> 3, c = (p & 7) ^ swz(r);
-      int src = a_src_row[i];
-      if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
-      a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
-    }
-    // B: this wave's CW columns n0 + CW wave .. lie wholly in the K or the V
-    // half (nh % 64 == 0): one resource per operand for the layer's
-    // half. Column fragment ni, lane (l % 32, h): weight bytes [16 h, 16 h +
-    // 16) of the 32-byte run of column 32 ni + l % 32 in each slab; scale and
-    // zero: lane l loads the word of column l.
-    const int wc0 = n0 + CW * wave;                         // uniform
-    const int which = wc0 >= nh ? 1 : 0;
-    const int hc0 = wc0 - which * nh;                       // first column inside the half
-    const int64_t szs = which ? g.sz_bstride[1] : g.sz_bstride[0];
-    const int gpr = K / grp;                                // groups per row
-    const void* q_buf = (which ? g.q[1] : g.q[0]) + (int64_t)z * g.q_bstride;
-    const int q_bytes = nh * (K / 2);
-    const void* s_buf = (const char*)(which ? g.s[1] : g.s[0]) + z * szs * SZB;
-    const void* z_buf = (const char*)(which ? g.zp[1] : g.zp[0]) + z * szs * SZB;
-    const int sz_bytes = nh * gpr * SZB;
-    uint32_t q_off[NI];
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) q_off[ni] = (uint32_t)((hc0 + 32 * ni + (lane & 31)) * (K / 2) + h * 16);
-    [[maybe_unused]] const uint32_t sz_off_plain = (uint32_t)((hc0 + lane) * gpr * SZB);
-    // LAYER with rotary embedding: output channel of wave column j (0..31)
-    // is hb + o0 + j for j < 16 and hb + hd/2 + o0 + j - 16 otherwise
-    [[maybe_unused]] const bool rope = LAYER && g.pos != nullptr;
-    [[maybe_unused]] int hb = 0, o0 = 0, half = 0;
-    if constexpr (LAYER) {
-      if (rope) {
-        const int hd = g.head_dim;
-        half = hd >> 1;
-        hb = hc0 / hd * hd;
-        o0 = ((hc0 - hb) >> 5) << 4;
+  // MA: the row fragments the loop computes. A launch whose row count (on
+  // the device) is at most 32 runs every tile on its first row fragment
+  // only: a quarter of the MFMAs and A reads at BM = 128, the same
+  // dequantisation; the other fragments stay zero, their rows are past the
+  // count and not stored.
+  auto run = [&](auto ma) {
+    constexpr int MA = decltype(ma)::value;
+    for (int tile = xcd * chunk + wg_in_xcd; tile < t_end; tile += per_xcd) {
+      const int nt = tile % tiles_n;
+      const int mt = (tile / tiles_n) % tiles_m_act;
+      const int z = (tile / (tiles_n * tiles_m_act)) % batch;
+      const int ks = tile / (tiles_n * tiles_m_act * batch);   // part of the reduction
+      const int j0 = ks * KT;                                  // its first slab
+      const int m0 = mt * BM, n0 = nt * BN;
+      if (g.M_dev_z) {                                         // uniform
+        const int mz = g.M_dev_z[z];
+        M = mz < 0 ? 0 : (mz < M_max ? mz : M_max);
+        if (m0 >= M) continue;
       }
-    }
-    auto chan = [&](int j) -> int {    // channel (inside the K or V half) of wave column j
+
+      // A: DMA block b = i * 4 + wave covers LDS chunks [64 b, 64 b + 64);
+      // lane l fills chunk p = 64 b + l = (row p / 8, physical chunk p % 8),
+      // which holds logical chunk (p % 8) ^ swz(row) of that row.
+      int a_src_row[AD];
+#pragma unroll
+      for (int i = 0; i < AD; ++i) {
+        const int t = m0 + (((i * NW + wave) * 64 + lane) >> 3);
+        a_src_row[i] = g.a_rows ? g.a_rows[t < M ? t : M - 1] : t;
+      }
+      // Operands come in through buffer loads straight into LDS: a uniform
+      // resource (base and byte size of the buffer), a fixed 32-bit offset per
+      // lane and a uniform offset per slab, so no per-slab address arithmetic
+      // runs on the vector unit; a read past the stated size returns zeros.
+      // A: row src of this tile's layer, 16-byte chunk c of the slab.
+      const void* a_buf = g.A + (int64_t)z * g.a_bstride;
+      const int a_bytes = (int)(a_nrows * g.lda * 2);
+      uint32_t a_off[AD];
+#pragma unroll
+      for (int i = 0; i < AD; ++i) {
+        const int p = (i * NW + wave) * 64 + lane;
+        const int r = p >> 3, c = (p & 7) ^ swz(r);
+        int src = a_src_row[i];
+        if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
+        a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
+      }
+      // B: this wave's CW columns n0 + CW wave .. lie wholly in the K or the V
+      // half (nh % 64 == 0): one resource per operand for the layer's
+      // half. Column fragment ni, lane (l % 32, h): weight bytes [16 h, 16 h +
+      // 16) of the 32-byte run of column 32 ni + l % 32 in each slab; scale and
+      // zero: lane l loads the word of column l.
+      const int wc0 = n0 + CW * wave;                         // uniform
+      const int which = wc0 >= nh ? 1 : 0;
+      const int hc0 = wc0 - which * nh;                       // first column inside the half
+      const int64_t szs = which ? g.sz_bstride[1] : g.sz_bstride[0];
+      const int gpr = K / grp;                                // groups per row
+      const void* q_buf = (which ? g.q[1] : g.q[0]) + (int64_t)z * g.q_bstride;
+      const int q_bytes = nh * (K / 2);
+      const void* s_buf = (const char*)(which ? g.s[1] : g.s[0]) + z * szs * SZB;
+      const void* z_buf = (const char*)(which ? g.zp[1] : g.zp[0]) + z * szs * SZB;
+      const int sz_bytes = nh * gpr * SZB;
+      uint32_t q_off[NI];
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) q_off[ni] = (uint32_t)((hc0 + 32 * ni + (lane & 31)) * (K / 2) + h * 16);
+      [[maybe_unused]] const uint32_t sz_off_plain = (uint32_t)((hc0 + lane) * gpr * SZB);
+      // LAYER with rotary embedding: output channel of wave column j (0..31)
+      // is hb + o0 + j for j < 16 and hb + hd/2 + o0 + j - 16 otherwise
+      [[maybe_unused]] const bool rope = LAYER && g.pos != nullptr;
+      [[maybe_unused]] int hb = 0, o0 = 0, half = 0;
       if constexpr (LAYER) {
-        if (rope) return hb + o0 + (j < 16 ? j : half + j - 16);
-      }
-      return hc0 + j;
-    };
-    if constexpr (LAYER) q_off[0] = (uint32_t)(chan(lane & 31) * (K / 2) + h * 16);
-    const uint32_t sz_off = LAYER ? (uint32_t)(chan(lane & 31) * gpr * SZB) : sz_off_plain;
-
-    // every load of K-slab j into LDS stage ST
-    auto issue = [&](auto st, int j) {
-      u32x4* la = stage(st);
-#pragma unroll
-      for (int i = 0; i < AD; ++i) buf_lds<16>(a_buf, a_bytes, a_off[i], j * 128, la + (i * NW + wave) * 64);
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        buf_lds<16>(q_buf, q_bytes, q_off[ni], j * 32, la + QOFF + (wave * NI + ni) * 64);
-      const int gi = j / slabs_per_group;   // uniform
-      // bf16 scale / zero: the aligned word holding group gi (rows hold an
-      // even number of groups, so the word stays inside the row)
-      const int go = (SZ_BF16 ? (gi & ~1) : gi) * SZB;
-      uint32_t* lz = (uint32_t*)(la + ZOFF) + wave * 128;
-      buf_lds<4>(s_buf, sz_bytes, sz_off, go, lz);
-      buf_lds<4>(z_buf, sz_bytes, sz_off, go, lz + 64);
-    };
-    // this lane's weights of slab j (held in stage la) from LDS
-    struct BRegs { u32x4 q[NI]; uint32_t s[NI], zz[NI]; };
-    auto fetch = [&](const u32x4* la, int j, BRegs& b) {
-      const uint32_t* lz = (const uint32_t*)(la + ZOFF) + wave * 128;
-      const int sh = SZ_BF16 ? ((j / slabs_per_group) & 1) * 16 : 0;
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        b.q[ni] = la[QOFF + (wave * NI + ni) * 64 + lane];
-        const uint32_t sw = lz[ni * 32 + (lane & 31)];
-        const uint32_t zw = lz[64 + ni * 32 + (lane & 31)];
-        b.s[ni] = SZ_BF16 ? (sw >> sh) & 0xFFFFu : sw;
-        b.zz[ni] = SZ_BF16 ? (zw >> sh) & 0xFFFFu : zw;
-      }
-    };
-    struct SC { float s[NI], c[NI]; };
-    auto scales = [&](const BRegs& b) {
-      SC r;
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        r.s[ni] = SZ_BF16 ? __uint_as_float(b.s[ni] << 16) : __uint_as_float(b.s[ni]);
-        const float ze = SZ_BF16 ? __uint_as_float(b.zz[ni] << 16) : __uint_as_float(b.zz[ni]);
-        r.c[ni] = -ze * r.s[ni];
-      }
-      return r;
-    };
-    // the A fragments (from LDS) and dequantized B fragments of sub-step s
-    struct Frag { bf16x8 a[MI], b[NI]; };
-    auto frag = [&](const u32x4* la, const BRegs& b, const SC& sc, int s, Frag& f) {
-      const int ch = 4 * h + s;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int r = mi * 32 + (lane & 31);
-        f.a[mi] = __builtin_bit_cast(bf16x8, la[r * 8 + (ch ^ swz(r))]);
-      }
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) {
-        uint32_t o[4];
-        dequant8(b.q[ni][s], sc.s[ni], sc.c[ni], o);
-        u32x4 v;
-        v[0] = o[0]; v[1] = o[1]; v[2] = o[2]; v[3] = o[3];
-        f.b[ni] = __builtin_bit_cast(bf16x8, v);
-      }
-    };
-
-    f32x16 acc[MI][NI];
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
-    auto mfma = [&](const Frag& f) {
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
-    };
-
-    // Pipeline. Slab kt lives in LDS stage kt % 4 and register set kt % 4.
-    // The barrier for slab kt + 1 sits before the last sub-step of slab kt,
-    // so the first fragments of slab kt + 1 are read and dequantized while
-    // the last MFMAs of slab kt run; after it, the stage of slab kt is free
-    // and slab kt + 4 is issued into it. The last four slabs issue nothing
-    // and wait for exactly what is still outstanding.
-    if (tile != xcd * chunk + wg_in_xcd) {
-      // every wave is done with the previous tile's stages
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    }
-    // cache slots of the tile's rows for the epilogue: lane l looks up rows
-    // m0 + 64 j + l. The e_rows loads go out before the first slab's (so the
-    // first wait covers them), the slot loads right after it.
-    constexpr int RJ = BM / 64;
-    [[maybe_unused]] int er[RJ], sl[RJ], ps[RJ];
-    if constexpr (EPI == EPI_CACHE) {
-#pragma unroll
-      for (int j = 0; j < RJ; ++j) {
-        const int row = m0 + 64 * j + lane;
-        const int rc = row < M ? row : M - 1;
-        er[j] = g.e_rows ? g.e_rows[rc] : rc;
-      }
-    }
-    issue(I0{}, j0);
-    issue(I1{}, j0 + 1);
-    issue(I2{}, j0 + 2);
-    wait_barrier<2 * PER_SLAB, true>();   // slab 0 landed
-    if constexpr (EPI == EPI_CACHE) {
-#pragma unroll
-      for (int j = 0; j < RJ; ++j) {
-        const bool ok = m0 + 64 * j + lane < M && er[j] >= 0 && er[j] < g.e_nrows;
-        sl[j] = ok ? g.slot[er[j]] : -1;          // range-checked where it is used
-        if constexpr (LAYER) ps[j] = (ok && rope) ? g.pos[er[j]] : 0;
-      }
-    }
-    Frag f0, f1;
-    BRegs bA, bB;
-    fetch(S0, j0, bA);
-    SC sc = scales(bA);
-    frag(S0, bA, sc, 0, f0);
-
-    // Pipeline. Slab kt lives in LDS stage kt % 4. Iteration kt issues slab
-    // kt + 3 into the stage of slab kt - 1 (free since the previous barrier),
-    // spread between the MFMAs of sub-steps 0..2, so that no wave stalls on
-    // a burst of loads; the barrier for slab kt + 1 sits before the last
-    // sub-step, whose MFMAs then cover the fetch and dequantization of the
-    // first fragments of slab kt + 1. W = loads allowed outstanding at the
-    // barrier (those of the slabs after kt + 1); ISSUE = slab kt + 3 exists.
-    auto iter = [&](auto st, BRegs& cur, BRegs& nxt, int kt, auto w, auto issue_next) {
-      constexpr int ST = decltype(st)::value;
-      using NX = std::integral_constant<int, (ST + 1) & 3>;
-      using PV = std::integral_constant<int, (ST + 3) & 3>;
-      constexpr bool ISS = decltype(issue_next)::value;
-      if constexpr (ISS) issue(PV{}, j0 + kt + 3);
-      frag(stage(st), cur, sc, 1, f1);
-      mfma(f0);
-      frag(stage(st), cur, sc, 2, f0);
-      mfma(f1);
-      frag(stage(st), cur, sc, 3, f1);
-      mfma(f0);
-      interleave<3, MI * NI, MI, ISS ? PER_SLAB : 0>();
-      wait_barrier<decltype(w)::value, true>();   // slab kt + 1 landed
-      fetch(stage(NX{}), j0 + kt + 1, nxt);      // (spare reads after the last slab)
-      sc = scales(nxt);
-      frag(stage(NX{}), nxt, sc, 0, f0);
-      mfma(f1);
-      interleave<1, MI * NI, MI + 3 * NI, 0>();
-    };
-    using W2 = std::integral_constant<int, 2 * PER_SLAB>;
-    using W1 = std::integral_constant<int, PER_SLAB>;
-    using W0 = std::integral_constant<int, 0>;
-    using T_ = std::true_type;
-    using F_ = std::false_type;
-    int kt = 0;
-    for (; kt + 4 < KT; kt += 4) {       // every slab here issues slab kt + 3
-      iter(I0{}, bA, bB, kt, W2{}, T_{});
-      iter(I1{}, bB, bA, kt + 1, W2{}, T_{});
-      iter(I2{}, bA, bB, kt + 2, W2{}, T_{});
-      iter(I3{}, bB, bA, kt + 3, W2{}, T_{});
-    }
-    // last four slabs: only the first still has a slab to issue
-    iter(I0{}, bA, bB, kt, W2{}, T_{});
-    iter(I1{}, bB, bA, kt + 1, W1{}, F_{});
-    iter(I2{}, bA, bB, kt + 2, W0{}, F_{});
-    iter(I3{}, bB, bA, kt + 3, W0{}, F_{});
-
-    if constexpr (EPI == EPI_PART) {
-      // fp32 partial sums straight from the accumulators: lane l holds row
-      // mi * 32 + l % 32 and the four columns 8 gq + 4 (l / 32) + 0..3
-      float* P = g.part + ((int64_t)ks * batch + z) * M_max * N;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int r = m0 + mi * 32 + (lane & 31);
-            const int c = n0 + CW * wave + ni * 32 + 8 * gq + 4 * h;
-            if (r < M && c < N)
-              *(f32x4*)(P + (int64_t)r * N + c) = f32x4{acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1],
-                                                        acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3]};
-          }
-      continue;                                  // next tile
-    }
-
-    // ---- epilogue. The transposed 32x32 accumulator gives lane l output
-    // row l % 32 of fragment mi and, for gq = 0..3, the four consecutive
-    // columns 8 gq + 4 (l / 32) + 0..3 of fragment ni. Each wave first writes
-    // its BM x CW block as bf16 into LDS (a region of stage wave / (NW / 4),
-    // free now: the other waves only make spare reads of stage 0 from here
-    // on, whose values are never used), then stores it row by row: LPR lanes
-    // x 16 bytes cover one row's CW columns, 64 / LPR rows per store.
-    {
-      constexpr int EP = CW + 8;                  // row pitch in bf16 (padded)
-      constexpr int LPR = CW / 8;                 // lanes per row
-      constexpr int RPI = 64 / LPR;               // rows per store instruction
-      const int sw = wave / (NW / 4), sub = wave % (NW / 4);
-      uint16_t* ep = (uint16_t*)(sw == 0 ? S0 : sw == 1 ? S1 : sw == 2 ? S2 : S3) + sub * BM * EP;
-      // (a wave whose columns lie past N reads no bias; its stores are dropped)
-      if constexpr (LAYER)
-        layer_epilogue<MI, BM, RG, RCH>(g, acc, z, m0, M_max, K, which, wc0 < N, tid, lane, h, rope, o0,
-                                        half, RSUM, chan, ps, sl);
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int r = mi * 32 + (lane & 31), c = ni * 32 + 8 * gq + 4 * h;
-            *(uint2*)(ep + r * EP + c) = uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
-                                               pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
-          }
-      const int ch = lane % LPR;
-      int col = n0 + CW * wave + 8 * ch;         // 8 columns, all in K or all in V
-      const bool col_ok = col < N;
-      const bool isv = col >= nh;
-      if constexpr (LAYER) col = (isv ? nh : 0) + chan(8 * ch);
-#pragma unroll
-      for (int i = 0; i < BM / RPI; ++i) {
-        const int r = i * RPI + lane / LPR;
-        const u32x4 v = *(const u32x4*)(ep + r * EP + 8 * ch);
-        if constexpr (EPI == EPI_CACHE) {
-          // slot of row r: looked up by lane r % 64 in its register r / 64
-          const int sr = __shfl(sl[(i * RPI) / 64], (i * RPI) % 64 + lane / LPR, 64);
-          if (sr < 0 || sr >= g.n_slots || !col_ok) continue;
-          uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc);
-          *(u32x4*)(dst + (int64_t)z * g.cache_bstride + (int64_t)sr * nh + (isv ? col - nh : col)) = v;
-        } else {
-          const int row = m0 + r;
-          if (row >= M || !col_ok) continue;
-          *(u32x4*)((uint16_t*)g.C + (int64_t)z * g.c_bstride + (int64_t)row * g.ldc + col) = v;
+        if (rope) {
+          const int hd = g.head_dim;
+          half = hd >> 1;
+          hb = hc0 / hd * hd;
+          o0 = ((hc0 - hb) >> 5) << 4;
         }
       }
-    }
-  }  // tiles
+      auto chan = [&](int j) -> int {    // channel (inside the K or V half) of wave column j
+        if constexpr (LAYER) {
+          if (rope) return hb + o0 + (j < 16 ? j : half + j - 16);
+        }
+        return hc0 + j;
+      };
+      if constexpr (LAYER) q_off[0] = (uint32_t)(chan(lane & 31) * (K / 2) + h * 16);
+      const uint32_t sz_off = LAYER ? (uint32_t)(chan(lane & 31) * gpr * SZB) : sz_off_plain;
+
+      // every load of K-slab j into LDS stage ST
+      auto issue = [&](auto st, int j) {
+        u32x4* la = stage(st);
+#pragma unroll
+        for (int i = 0; i < AD; ++i) buf_lds<16>(a_buf, a_bytes, a_off[i], j * 128, la + (i * NW + wave) * 64);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          buf_lds<16>(q_buf, q_bytes, q_off[ni], j * 32, la + QOFF + (wave * NI + ni) * 64);
+        const int gi = j / slabs_per_group;   // uniform
+        // bf16 scale / zero: the aligned word holding group gi (rows hold an
+        // even number of groups, so the word stays inside the row)
+        const int go = (SZ_BF16 ? (gi & ~1) : gi) * SZB;
+        uint32_t* lz = (uint32_t*)(la + ZOFF) + wave * 128;
+        buf_lds<4>(s_buf, sz_bytes, sz_off, go, lz);
+        buf_lds<4>(z_buf, sz_bytes, sz_off, go, lz + 64);
+      };
+      // this lane's weights of slab j (held in stage la) from LDS
+      struct BRegs { u32x4 q[NI]; uint32_t s[NI], zz[NI]; };
+      auto fetch = [&](const u32x4* la, int j, BRegs& b) {
+        const uint32_t* lz = (const uint32_t*)(la + ZOFF) + wave * 128;
+        const int sh = SZ_BF16 ? ((j / slabs_per_group) & 1) * 16 : 0;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          b.q[ni] = la[QOFF + (wave * NI + ni) * 64 + lane];
+          const uint32_t sw = lz[ni * 32 + (lane & 31)];
+          const uint32_t zw = lz[64 + ni * 32 + (lane & 31)];
+          b.s[ni] = SZ_BF16 ? (sw >> sh) & 0xFFFFu : sw;
+          b.zz[ni] = SZ_BF16 ? (zw >> sh) & 0xFFFFu : zw;
+        }
+      };
+      struct SC { float s[NI], c[NI]; };
+      auto scales = [&](const BRegs& b) {
+        SC r;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          r.s[ni] = SZ_BF16 ? __uint_as_float(b.s[ni] << 16) : __uint_as_float(b.s[ni]);
+          const float ze = SZ_BF16 ? __uint_as_float(b.zz[ni] << 16) : __uint_as_float(b.zz[ni]);
+          r.c[ni] = -ze * r.s[ni];
+        }
+        return r;
+      };
+      // the A fragments (from LDS) and dequantized B fragments of sub-step s
+      struct Frag { bf16x8 a[MI], b[NI]; };
+      auto frag = [&](const u32x4* la, const BRegs& b, const SC& sc, int s, Frag& f) {
+        const int ch = 4 * h + s;
+#pragma unroll
+        for (int mi = 0; mi < MA; ++mi) {
+          const int r = mi * 32 + (lane & 31);
+          f.a[mi] = __builtin_bit_cast(bf16x8, la[r * 8 + (ch ^ swz(r))]);
+        }
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          uint32_t o[4];
+          dequant8(b.q[ni][s], sc.s[ni], sc.c[ni], o);
+          u32x4 v;
+          v[0] = o[0]; v[1] = o[1]; v[2] = o[2]; v[3] = o[3];
+          f.b[ni] = __builtin_bit_cast(bf16x8, v);
+        }
+      };
+
+      f32x16 acc[MI][NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+      auto mfma = [&](const Frag& f) {
+#pragma unroll
+        for (int mi = 0; mi < MA; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+      };
+
+      // Pipeline. Slab kt lives in LDS stage kt % 4 and register set kt % 4.
+      // The barrier for slab kt + 1 sits before the last sub-step of slab kt,
+      // so the first fragments of slab kt + 1 are read and dequantized while
+      // the last MFMAs of slab kt run; after it, the stage of slab kt is free
+      // and slab kt + 4 is issued into it. The last four slabs issue nothing
+      // and wait for exactly what is still outstanding.
+      if (tile != xcd * chunk + wg_in_xcd) {
+        // every wave is done with the previous tile's stages
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      // cache slots of the tile's rows for the epilogue: lane l looks up rows
+      // m0 + 64 j + l. The e_rows loads go out before the first slab's (so the
+      // first wait covers them), the slot loads right after it.
+      constexpr int RJ = BM / 64;
+      [[maybe_unused]] int er[RJ], sl[RJ], ps[RJ];
+      if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+          const int row = m0 + 64 * j + lane;
+          const int rc = row < M ? row : M - 1;
+          er[j] = g.e_rows ? g.e_rows[rc] : rc;
+        }
+      }
+      issue(I0{}, j0);
+      issue(I1{}, j0 + 1);
+      issue(I2{}, j0 + 2);
+      wait_barrier<2 * PER_SLAB, true>();   // slab 0 landed
+      if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+        for (int j = 0; j < RJ; ++j) {
+          const bool ok = m0 + 64 * j + lane < M && er[j] >= 0 && er[j] < g.e_nrows;
+          sl[j] = ok ? g.slot[er[j]] : -1;          // range-checked where it is used
+          if constexpr (LAYER) ps[j] = (ok && rope) ? g.pos[er[j]] : 0;
+        }
+      }
+      Frag f0, f1;
+      BRegs bA, bB;
+      fetch(S0, j0, bA);
+      SC sc = scales(bA);
+      frag(S0, bA, sc, 0, f0);
+
+      // Pipeline. Slab kt lives in LDS stage kt % 4. Iteration kt issues slab
+      // kt + 3 into the stage of slab kt - 1 (free since the previous barrier),
+      // spread between the MFMAs of sub-steps 0..2, so that no wave stalls on
+      // a burst of loads; the barrier for slab kt + 1 sits before the last
+      // sub-step, whose MFMAs then cover the fetch and dequantization of the
+      // first fragments of slab kt + 1. W = loads allowed outstanding at the
+      // barrier (those of the slabs after kt + 1); ISSUE = slab kt + 3 exists.
+      auto iter = [&](auto st, BRegs& cur, BRegs& nxt, int kt, auto w, auto issue_next) {
+        constexpr int ST = decltype(st)::value;
+        using NX = std::integral_constant<int, (ST + 1) & 3>;
+        using PV = std::integral_constant<int, (ST + 3) & 3>;
+        constexpr bool ISS = decltype(issue_next)::value;
+        if constexpr (ISS) issue(PV{}, j0 + kt + 3);
+        frag(stage(st), cur, sc, 1, f1);
+        mfma(f0);
+        frag(stage(st), cur, sc, 2, f0);
+        mfma(f1);
+        frag(stage(st), cur, sc, 3, f1);
+        mfma(f0);
+        interleave<3, MA * NI, MA, ISS ? PER_SLAB : 0>();
+        wait_barrier<decltype(w)::value, true>();   // slab kt + 1 landed
+        fetch(stage(NX{}), j0 + kt + 1, nxt);      // (spare reads after the last slab)
+        sc = scales(nxt);
+        frag(stage(NX{}), nxt, sc, 0, f0);
+        mfma(f1);
+        interleave<1, MA * NI, MA + 3 * NI, 0>();
+      };
+      using W2 = std::integral_constant<int, 2 * PER_SLAB>;
+      using W1 = std::integral_constant<int, PER_SLAB>;
+      using W0 = std::integral_constant<int, 0>;
+      using T_ = std::true_type;
+      using F_ = std::false_type;
+      int kt = 0;
+      for (; kt + 4 < KT; kt += 4) {       // every slab here issues slab kt + 3
+        iter(I0{}, bA, bB, kt, W2{}, T_{});
+        iter(I1{}, bB, bA, kt + 1, W2{}, T_{});
+        iter(I2{}, bA, bB, kt + 2, W2{}, T_{});
+        iter(I3{}, bB, bA, kt + 3, W2{}, T_{});
+      }
+      // last four slabs: only the first still has a slab to issue
+      iter(I0{}, bA, bB, kt, W2{}, T_{});
+      iter(I1{}, bB, bA, kt + 1, W1{}, F_{});
+      iter(I2{}, bA, bB, kt + 2, W0{}, F_{});
+      iter(I3{}, bB, bA, kt + 3, W0{}, F_{});
+
+      if constexpr (EPI == EPI_PART) {
+        // fp32 partial sums straight from the accumulators: lane l holds row
+        // mi * 32 + l % 32 and the four columns 8 gq + 4 (l / 32) + 0..3
+        float* P = g.part + ((int64_t)ks * batch + z) * M_max * N;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int r = m0 + mi * 32 + (lane & 31);
+              const int c = n0 + CW * wave + ni * 32 + 8 * gq + 4 * h;
+              if (r < M && c < N)
+                *(f32x4*)(P + (int64_t)r * N + c) = f32x4{acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1],
+                                                          acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3]};
+            }
+        continue;                                  // next tile
+      }
+
+      // ---- epilogue. The transposed 32x32 accumulator gives lane l output
+      // row l % 32 of fragment mi and, for gq = 0..3, the four consecutive
+      // columns 8 gq + 4 (l / 32) + 0..3 of fragment ni. Each wave first writes
+      // its BM x CW block as bf16 into LDS (a region of stage wave / (NW / 4),
+      // free now: the other waves only make spare reads of stage 0 from here
+      // on, whose values are never used), then stores it row by row: LPR lanes
+      // x 16 bytes cover one row's CW columns, 64 / LPR rows per store.
+      {
+        constexpr int EP = CW + 8;                  // row pitch in bf16 (padded)
+        constexpr int LPR = CW / 8;                 // lanes per row
+        constexpr int RPI = 64 / LPR;               // rows per store instruction
+        const int sw = wave / (NW / 4), sub = wave % (NW / 4);
+        uint16_t* ep = (uint16_t*)(sw == 0 ? S0 : sw == 1 ? S1 : sw == 2 ? S2 : S3) + sub * BM * EP;
+        // (a wave whose columns lie past N reads no bias; its stores are dropped)
+        if constexpr (LAYER)
+          layer_epilogue<MI, BM, RG, RCH>(g, acc, z, m0, M_max, K, which, wc0 < N, tid, lane, h, rope, o0,
+                                          half, RSUM, chan, ps, sl);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int r = mi * 32 + (lane & 31), c = ni * 32 + 8 * gq + 4 * h;
+              *(uint2*)(ep + r * EP + c) = uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
+                                                 pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
+            }
+        const int ch = lane % LPR;
+        int col = n0 + CW * wave + 8 * ch;         // 8 columns, all in K or all in V
+        const bool col_ok = col < N;
+        const bool isv = col >= nh;
+        if constexpr (LAYER) col = (isv ? nh : 0) + chan(8 * ch);
+#pragma unroll
+        for (int i = 0; i < BM / RPI; ++i) {
+          const int r = i * RPI + lane / LPR;
+          const u32x4 v = *(const u32x4*)(ep + r * EP + 8 * ch);
+          if constexpr (EPI == EPI_CACHE) {
+            // slot of row r: looked up by lane r % 64 in its register r / 64
+            const int sr = __shfl(sl[(i * RPI) / 64], (i * RPI) % 64 + lane / LPR, 64);
+            if (sr < 0 || sr >= g.n_slots || !col_ok) continue;
+            uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc);
+            *(u32x4*)(dst + (int64_t)z * g.cache_bstride + (int64_t)sr * nh + (isv ? col - nh : col)) = v;
+          } else {
+            const int row = m0 + r;
+            if (row >= M || !col_ok) continue;
+            *(u32x4*)((uint16_t*)g.C + (int64_t)z * g.c_bstride + (int64_t)row * g.ldc + col) = v;
+          }
+        }
+      }
+    }  // tiles
+  };
+  if constexpr (MI > 1 && !LAYER) {   // (the layer epilogue's registers leave no room for two loops)
+    if (!g.M_dev_z && M <= 32) run(std::integral_constant<int, 1>{});   // uniform
+    else run(std::integral_constant<int, MI>{});
+  } else {
+    run(std::integral_constant<int, MI>{});
+  }
 }
 
 // Launch over a batch of `batch` layers: one workgroup per CU (112 KB of
