@@ -331,9 +331,13 @@ def decode_times(key, steps):
     # the launch sequence the library takes for this workload
     if cfg.n_tokens <= 1024 and n_ck <= (16 if cfg.b else 32):
         scores = "one route launch for all checkpoints" if cfg.b else "cosines of all checkpoints"
-        if all(c.get("maps") is None for c in dw.cks):
+        plain = sum(c.get("maps") is None for c in dw.cks)
+        if plain == n_ck:
             path = (f"{scores}, one decision workgroup, gather of the exit states, one projection "
                     "over all filled blocks")
+        elif plain >= 2:
+            path = (f"{scores}, one decision workgroup, gather of the exit states and one projection "
+                    "for the checkpoints without maps, a fill per checkpoint with maps")
         else:
             path = f"{scores}, one decision workgroup, a fill per checkpoint"
     else:

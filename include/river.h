@@ -370,8 +370,10 @@ typedef struct {
  * shape rules are river_kv_fill's. With n <= 1024 and the routers off at
  * every checkpoint (at most 32), or on at every checkpoint (at most 16, bf16,
  * d % 256 == 0, d <= 8192, b <= 128), two launches decide all checkpoints
- * (instead of a route and a compaction per checkpoint); without maps and on
- * the fill's MFMA path one projection then fills every checkpoint's exits.
+ * (instead of a route and a compaction per checkpoint); on the fill's MFMA
+ * path one projection then fills the exits of every checkpoint without
+ * maps (all of them, or at least two), and each checkpoint with maps
+ * fills its own.
  */
 river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
                                const river_checkpoint* ck, int n_layers, const void* gamma,

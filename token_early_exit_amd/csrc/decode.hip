@@ -81,13 +81,15 @@ struct DecodePlan {
   int idx_stride;
   int32_t* counts;                // [n_ck][64]: {running or done before, exiting} (compact's layout)
   int32_t* exit_layer;            // [n]
-  // one fill for all checkpoints (NULL: not wanted): the exits of all
-  // checkpoints in checkpoint order, the checkpoint of each token's exit
-  // (-1: none) and, for block layer[0] + 1 + j, the number of exits at
-  // checkpoints before it (a prefix of ord)
+  // one fill for the checkpoints of single_mask (bit c: checkpoint c; NULL
+  // arrays: not wanted): their exits in checkpoint order, the checkpoint of
+  // each token's exit among them (-1: none or another checkpoint) and, for
+  // block first + j (first = 1 + the layer of the lowest checkpoint of the
+  // mask), the number of their exits before it (a prefix of ord)
   int32_t* ord;                   // [n]
   int32_t* ck_of;                 // [n]
-  int32_t* m_layer;               // [n_layers - layer[0]]
+  int32_t* m_layer;               // [n_layers + 1 - first]
+  uint32_t single_mask;
 };
 
 // One workgroup, token i in thread i: the checkpoints in order. Under the
@@ -103,8 +105,9 @@ __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
   const int n = p.n;
   bool alive = i < n;
   int el = p.n_layers, my_ck = -1;
-  int off = 0;                                // exits of the checkpoints before c
+  int off = 0;                                // exits of the single fill's checkpoints before c
   for (int c = 0; c < p.n_ck; ++c) {
+    const bool sf = (p.single_mask >> c) & 1u;
     const int64_t at = (int64_t)c * n + (i < n ? i : 0);
     // the route's decision: cos > tau, and p > theta with a router
     bool e = alive && p.cos[at] > p.tau[c] && (!p.prob || p.prob[at] > p.theta[c]);
@@ -127,15 +130,15 @@ __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
     if (e) {
       const int r = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
       p.exit_idx[(int64_t)c * p.idx_stride + r] = i;
-      if (p.ord) p.ord[off + r] = i;
-      my_ck = c;
+      if (p.ord && sf) p.ord[off + r] = i;
+      if (sf) my_ck = c;
     }
     if (i == 0) {
       p.counts[c * 64] = n - total;
       p.counts[c * 64 + 1] = total;
       tot[c] = total;
     }
-    off += total;
+    off += sf ? total : 0;
     __syncthreads();                          // wsum is rewritten next round
     alive = alive && !e;
   }
@@ -143,11 +146,12 @@ __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
     p.exit_layer[i] = el;
     if (p.ck_of) p.ck_of[i] = my_ck;
   }
-  if (p.m_layer && p.n_ck > 0) {
-    const int first = p.layer[0] + 1;         // first filled block
+  if (p.m_layer && p.single_mask) {
+    const int first = p.layer[__builtin_ctz(p.single_mask)] + 1;   // first filled block
     for (int j = i; j < p.n_layers + 1 - first; j += DC_TOKENS) {
       int m = 0;
-      for (int c = 0; c < p.n_ck; ++c) m += p.layer[c] < first + j ? tot[c] : 0;
+      for (int c = 0; c < p.n_ck; ++c)
+        m += ((p.single_mask >> c) & 1u) && p.layer[c] < first + j ? tot[c] : 0;
       p.m_layer[j] = m;
     }
   }
@@ -296,21 +300,25 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
       st = check_launch("decode_step cosines");
       if (st != RIVER_OK) return st;
     }
-    // one fill for all checkpoints when none has maps and the plain MFMA
-    // projection takes the shape: block e_0 + 1 + j projects the first
-    // m_layer[j] rows of the exit order, gathered from each token's exit
-    // checkpoint
+    // one fill for the checkpoints without maps (all of them, or at least
+    // two beside checkpoints with maps) when the plain MFMA projection
+    // takes the shape: block e_0 + 1 + j (e_0 the first such checkpoint)
+    // projects the first m_layer[j] rows of their exit order, gathered from
+    // each token's exit checkpoint; checkpoints with maps fill on their own
     river_w4 k0, v0;
-    bool single = n_ck > 0;
-    for (int c = 0; c < n_ck; ++c) single = single && !ck[c].maps;
+    uint32_t mask = 0;
+    for (int c = 0; c < n_ck; ++c)
+      if (!ck[c].maps) mask |= 1u << c;
+    bool single = mask != 0 && (__builtin_popcount(mask) >= 2 || mask == (n_ck == 32 ? ~0u : (1u << n_ck) - 1));
+    const int c0 = single ? __builtin_ctz(mask) : 0;
     if (single) {
-      decode_layer_offset(*wk, ck[0].layer, n_out, d, &k0);
-      decode_layer_offset(*wv, ck[0].layer, n_out, d, &v0);
+      decode_layer_offset(*wk, ck[c0].layer, n_out, d, &k0);
+      decode_layer_offset(*wv, ck[c0].layer, n_out, d, &v0);
       single = kv_fill_plain_mfma(n, d, dt, n, d, &k0, &v0, n_out);
     }
     DecodePlan q{};
     q.n = n; q.n_ck = n_ck; q.batch_min = rule == RIVER_RULE_BATCH_MIN; q.n_layers = n_layers;
-    if (single) { q.ord = ord; q.ck_of = ck_of; q.m_layer = m_layer; }
+    if (single) { q.ord = ord; q.ck_of = ck_of; q.m_layer = m_layer; q.single_mask = mask; }
     q.cos = (const float*)plan;
     q.prob = routers_on ? prob : nullptr;
     for (int c = 0; c < n_ck; ++c) { q.tau[c] = ck[c].tau; q.theta[c] = ck[c].theta; q.layer[c] = ck[c].layer; }
@@ -330,12 +338,14 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
       decode_gather_kernel<<<n, WAVE, 0, s>>>(gq);
       st = check_launch("decode_step gather");
       if (st != RIVER_OK) return st;
-      const int e0 = ck[0].layer;
-      return launch_kv_fill(n, nullptr, d, dt, xs, d, n, ord, slot, n_layers - e0, nullptr, &k0, &v0, nullptr,
-                            n_kv_heads, head_dim, (char*)k_cache + e0 * cache_layer,
-                            (char*)v_cache + e0 * cache_layer, n_slots, fws, fws_bytes, s, m_layer);
+      const int e0 = ck[c0].layer;
+      st = launch_kv_fill(n, nullptr, d, dt, xs, d, n, ord, slot, n_layers - e0, nullptr, &k0, &v0, nullptr,
+                          n_kv_heads, head_dim, (char*)k_cache + e0 * cache_layer,
+                          (char*)v_cache + e0 * cache_layer, n_slots, fws, fws_bytes, s, m_layer);
+      if (st != RIVER_OK) return st;
     }
     for (int c = 0; c < n_ck; ++c) {
+      if (single && ((mask >> c) & 1u)) continue;   // in the single fill
       const river_checkpoint& k = ck[c];
       const int e = k.layer;
       river_w4 k4, v4;
