@@ -613,7 +613,7 @@ def cpu_baseline(wl, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "one GPU only (no sharding across GPUs): --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     tee.load()

@@ -66,7 +66,7 @@ typedef enum {
   RIVER_ERR_ARG = 1,          /* a size, pointer or threshold is invalid     */
   RIVER_ERR_DTYPE = 2,        /* an element type is not supported here       */
   RIVER_ERR_ALIGN = 3,        /* a pointer or leading dimension is misaligned */
-  RIVER_ERR_UNSUPPORTED = 4,  /* a valid shape this build does not handle    */
+  RIVER_ERR_UNSUPPORTED = 4,  /* a valid shape the library does not handle   */
   RIVER_ERR_WORKSPACE = 5,    /* workspace missing or too small              */
   RIVER_ERR_NOT_SPD = 6,      /* X^T X + lambda I is not positive definite   */
   RIVER_ERR_HIP = 7           /* a HIP runtime call or kernel launch failed  */

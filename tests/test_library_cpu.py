@@ -44,6 +44,25 @@ def test_workspace_sizes():
     assert ws(tee.OP_KV_FILL, 4096, 768, 0, 0, 8) >= 8 * 4096 * 768 * 2
     assert ws(tee.OP_COMPACT, 100000) >= 4 * 25
     assert ws(tee.OP_RIDGE_FIT, 2048, 768, 768, 8, tee.RIVER_BF16) > 0
+    # split reductions: up to 64 rows always, 65 to 256 rows when the
+    # projection has few tiles (at most 128 of 64 rows x 256 outputs)
+    nh = 8 * 64
+    base = ws(tee.OP_KV_FILL, 200, 2048, 0, 0, 2)
+    assert ws(tee.OP_KV_FILL, 200, 2048, nh, 0, 2) >= base + 2 * 200 * 2 * nh * 4 * 2
+    assert ws(tee.OP_KV_FILL, 256, 4096, 1024, 0, 21) == ws(tee.OP_KV_FILL, 256, 4096, 0, 0, 21)
+    assert ws(tee.OP_KV_FILL, 300, 2048, nh, 0, 1) == ws(tee.OP_KV_FILL, 300, 2048, 0, 0, 1)
+    # the decode step holds the split of its smallest fill (one block)
+    assert ws(tee.OP_DECODE_STEP, 256, 4096, 1024, 0, 32) > ws(tee.OP_DECODE_STEP, 256, 4096, 0, 0, 32)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess, sys, json, os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    line = [l for l in r.stdout.splitlines() if l.startswith("{")][-1]
+    assert "--gpus must be 1" in json.loads(line)["error"]
 
 
 def _route(**kw):
