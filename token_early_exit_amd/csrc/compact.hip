@@ -345,10 +345,15 @@ river_status launch_compact(int n, int d, river_dtype dt, const uint8_t* mask, c
   if (path == 0) path = n <= FUSED_MAX ? 4 : 3;
   const int64_t es = (int64_t)esize(dt);
   if (path == 4) {
-    // 16 tokens per workgroup while the mask prefixes the workgroups read
-    // stay small (n^2 / 32 bytes in all), 64 beyond
+    // 8 tokens per workgroup up to 8192 tokens (measured at 4096 tokens of
+    // d = 768: 4.14 µs against 4.57 with 16 and 4.22 with 4), 16 while the
+    // mask prefixes the workgroups read stay small (n^2 / 32 bytes in all),
+    // 64 beyond
     const char* hh = (h_cont || out) ? (const char*)h : nullptr;
-    if (n <= 16384)
+    if (n <= 8192)
+      compact_fused_kernel<8><<<(n + 7) / 8, 256, 0, s>>>(a, hh, ld_h * es, (int)(d * es), (char*)h_cont,
+                                                          ld_cont * es, (char*)out, ld_out * es, n_out_rows);
+    else if (n <= 16384)
       compact_fused_kernel<16><<<(n + 15) / 16, 256, 0, s>>>(a, hh, ld_h * es, (int)(d * es), (char*)h_cont,
                                                              ld_cont * es, (char*)out, ld_out * es, n_out_rows);
     else
