@@ -106,6 +106,21 @@ def test_route_with_gamma_and_odd_width():
     check_route(route_gpu(*args, gamma=gamma), route_ref(*args, gamma=gamma), 0.5, 0.5, True)
 
 
+@pytest.mark.parametrize("n", [8192, 8195])
+def test_route_large_batch_gamma_narrow_router(n):
+    """32-token workgroups (from 8192 tokens) with gamma, a router of 64
+    units (half the waves own none) and a ragged last workgroup."""
+    g = torch.Generator().manual_seed(n)
+    d, b = 1024, 64
+    hp = torch.randn(n, d, generator=g).bfloat16().to(DEV)
+    hc = (hp.float().cpu() + 0.3 * torch.randn(n, d, generator=g)).bfloat16().to(DEV)
+    gamma = (0.5 + torch.rand(d, generator=g)).bfloat16().to(DEV)
+    wd = (torch.randn(b, d, generator=g) / d ** 0.5).bfloat16().to(DEV)
+    wu = (torch.randn(b, generator=g) / b ** 0.5).bfloat16().to(DEV)
+    args = (hp, hc, wd, wu, 0.5, 0.5)
+    check_route(route_gpu(*args, gamma=gamma), route_ref(*args, gamma=gamma), 0.5, 0.5, True)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_route_edges(dtype):
     g = torch.Generator().manual_seed(6)
@@ -167,7 +182,7 @@ def compact_gpu(mask, h, row_ids=None, out=None):
 
 
 @pytest.mark.parametrize("path", [0, 1, 2, 3, 4])
-@pytest.mark.parametrize("n", [0, 1, 33, 63, 64, 65, 1023, 1024, 1025, 5000, 8192, 20000])
+@pytest.mark.parametrize("n", [0, 1, 33, 63, 64, 65, 1023, 1024, 1025, 5000, 8192, 8193, 20000])
 def test_compact_all_paths(path, n):
     if path == 1 and n > 64:
         pytest.skip("the ballot path takes n <= 64")
