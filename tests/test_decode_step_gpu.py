@@ -289,7 +289,7 @@ def test_decode_step_8b_router_and_maps():
 
 
 @pytest.mark.parametrize("case", ["ragged-37", "200-split", "300-no-split", "router-off-maps",
-                                  "fp32-tiny", "mixed-routers"])
+                                  "fp32-tiny", "mixed-routers", "routers-maps"])
 def test_decode_step_paths_and_shapes(case):
     """Shapes around the step's paths, each against the oracle and against
     the per-checkpoint launches: 37 tokens (single fill, split reduction,
@@ -297,9 +297,12 @@ def test_decode_step_paths_and_shapes(case):
     differ between the paths), 300 tokens (no split), maps at two
     router-off checkpoints (two decision launches, a fill per checkpoint),
     fp32 states (the generic fill), and routers at some checkpoints only
-    (per-checkpoint launches). Exit layers agree bit for bit; so do the
-    caches wherever both paths fill with the same launches."""
-    bitwise = case not in ("ragged-37", "200-split")
+    (per-checkpoint launches), and routers at every checkpoint with maps at
+    two (the single fill of the others beside a fill per checkpoint with
+    maps; the paths split the projection differently). Exit layers agree
+    bit for bit; so do the caches wherever both paths fill with the same
+    launches."""
+    bitwise = case not in ("ragged-37", "200-split", "routers-maps")
     if case == "ragged-37":
         cfg = get_config(2, n_tokens=37)
     elif case == "200-split":
@@ -337,6 +340,25 @@ def test_decode_step_paths_and_shapes(case):
         for c in cks:
             if c["layer"] in (8, 12):
                 c["maps"] = G.near_identity_maps(cfg, cfg.L - c["layer"], tag=f"m{c['layer']}").to(DEV)
+    if case == "routers-maps":
+        # a router at every checkpoint, theta at the middle of the widest gap
+        # of the running tokens' probabilities (nobody exits where there is
+        # no clear gap); maps for the fills at the second and fifth
+        alive = np.ones(cfg.n_tokens, bool)
+        for k, c in enumerate(cks):
+            wd, wu = (t.to(DEV) for t in G.router_weights(cfg, c["layer"]))
+            c["w_down"], c["w_up"], c["tau"], c["theta"] = wd, wu, -INF, INF
+            _, prob, _, _ = O.route(np64(c["h_prev"]), np64(c["h_cur"]), None, 1e-6, np64(wd), np64(wu),
+                                    -INF, -INF)
+            v = np.sort(prob[alive])
+            if len(v) >= 8:
+                lo, hi = len(v) // 2, len(v) - len(v) // 8
+                g = lo + int(np.argmax(np.diff(v)[lo:hi]))
+                if v[g + 1] - v[g] > 2.5 * BAND:
+                    c["theta"] = 0.5 * (v[g] + v[g + 1])
+            alive &= ~(prob > f32(c["theta"]))
+            if k in (1, 4):
+                c["maps"] = G.near_identity_maps(cfg, cfg.L - c["layer"], tag=f"rm{k}").to(DEV)
     if case == "mixed-routers":
         # the 8B shape's cosines differ in the 8th digit: routers at every
         # other checkpoint decide (tau off, theta at the middle of the widest
@@ -372,6 +394,11 @@ def test_decode_step_paths_and_shapes(case):
         assert torch.equal(k0.view(iv), k1.view(iv)) and torch.equal(v0.view(iv), v1.view(iv))
     exg = check_step(cfg, cks, e0, k0, v0, slot, wk, wv)
     assert (exg < cfg.L).any()
+    if case == "routers-maps":
+        # exits both at checkpoints with maps and at checkpoints without
+        got = set(np.unique(np.asarray(exg)[np.asarray(exg) < cfg.L]).tolist())
+        with_maps = {cks[1]["layer"], cks[4]["layer"]}
+        assert got & with_maps and got - with_maps, got
 
 
 def test_decode_step_graph_replay():
