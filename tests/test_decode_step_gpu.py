@@ -449,3 +449,69 @@ def test_decode_step_graph_replay():
         assert torch.equal(kr.view(torch.int16), k2.view(torch.int16))
         assert torch.equal(vr.view(torch.int16), v2.view(torch.int16))
         assert (er < cfg.L).any()
+
+
+def test_decode_step_graph_replay_routers_and_maps():
+    """Routers at every checkpoint of the Llama-3-8B shape (64 tokens) and
+    maps at two: the route launch for all checkpoints, the decision
+    workgroup, the single fill of the six without maps and the fills of the
+    two with maps, captured once and replayed for three steps with new
+    states; each replay equals an eager call bit for bit."""
+    cfg = get_config("3D", n_tokens=64)
+    n = cfg.n_tokens
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    layers = list(cfg.route_layers)
+    need = sorted({l - 1 for l in layers} | set(layers))
+    steps = []
+    for k in range(3):
+        hs = G.hidden_states(cfg, n, need, tag=f"gstep{k}")
+        steps.append({l: t.to(DEV) for l, t in hs.items()})
+    buf = {l: torch.empty_like(t) for l, t in steps[0].items()}
+    cks = []
+    for k, l in enumerate(layers):
+        wd, wu = (t.to(DEV) for t in G.router_weights(cfg, l))
+        c = {"layer": l, "tau": -INF, "theta": INF, "w_down": wd, "w_up": wu}
+        # theta between the 8th and 9th largest probabilities of step 0
+        _, prob, _, _ = O.route(np64(steps[0][l - 1]), np64(steps[0][l]), None, 1e-6, np64(wd),
+                                np64(wu), -INF, -INF)
+        p = np.sort(prob)[::-1]
+        c["theta"] = 0.5 * (p[7] + p[8])
+        if k in (1, 4):
+            c["maps"] = G.near_identity_maps(cfg, cfg.L - l, tag=f"gm{k}").to(DEV)
+        cks.append(c)
+    gcks = [dict(c, h_prev=buf[c["layer"] - 1], h_cur=buf[c["layer"]]) for c in cks]
+    kc, vc = G.nan_cache(cfg, cfg.L, device=DEV)
+    ex = torch.full((n,), -7, dtype=torch.int32, device=DEV)
+    ws = step_workspace(cfg, n)
+    for l in buf:
+        buf[l].copy_(steps[0][l])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                 # warm-up outside the capture
+        tee.river_decode_step(gcks, wk, wv, cfg.n_kv_heads, cfg.head_dim, slot, kc, vc, ex,
+                              workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        tee.river_decode_step(gcks, wk, wv, cfg.n_kv_heads, cfg.head_dim, slot, kc, vc, ex,
+                              workspace=ws)
+    for k in range(3):
+        for l in buf:
+            buf[l].copy_(steps[k][l])
+        kc.fill_(float("nan"))
+        vc.fill_(float("nan"))
+        ex.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        kr, vr, er = kc.clone(), vc.clone(), ex.clone()
+        eck = [dict(c, h_prev=steps[k][c["layer"] - 1], h_cur=steps[k][c["layer"]]) for c in cks]
+        e2, k2, v2 = run_gpu(eck, cfg, wk, wv, slot)
+        assert torch.equal(er, e2)
+        assert torch.equal(kr.view(torch.int16), k2.view(torch.int16))
+        assert torch.equal(vr.view(torch.int16), v2.view(torch.int16))
+        ev = er.cpu().numpy()
+        assert (ev < cfg.L).any()
+        del kr, vr, e2, k2, v2
