@@ -256,7 +256,10 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
  *            256 x 256 tile per CU the weights dequantised to bf16 (the
  *            values the int4 path forms in
  *            registers), which a 256 x 256 bf16 GEMM then projects. With
- *            less, the projection dequantises in registers, unsplit.
+ *            less, the projection dequantises in registers, unsplit. With
+ *            maps and a workspace for fewer layers than n_layers, a chunk
+ *            at such row counts takes as many x_hat layers as leave room
+ *            for its dequantised weights (when one layer does).
  * Only the filled slots are written; every other byte is left unchanged.
  * Paths: bf16 with d % 256 == 0, n_out % 64 == 0, group % 64 == 0, the
  * same group and scale/zero dtype for wk and wv, an even number of groups
@@ -492,6 +495,20 @@ river_status river_debug_set_gemm_path(int path);
  * bit-identical; the caches too when both paths split the projection's
  * reduction into the same parts (otherwise they agree to rounding). */
 river_status river_debug_set_decode_path(int path);
+
+/* Test hook, host only (enqueues nothing): the plan river_kv_fill takes for
+ * a plain bf16 fill with maps on its MFMA path (d % 256 == 0, n_out =
+ * n_kv_heads * head_dim with n_out % 64 == 0) given ws_bytes of workspace:
+ * *chunk = layers per chunk (x_hat of that many layers held at once; at
+ * large row counts after the room of the chunk's dequantised weights, when
+ * at least one layer fits beside them), *path = the projection's
+ * path for the first chunk (0 = int4 dequantised in registers, 1 = split
+ * reduction over d in *parts parts, 2 = bf16 GEMM on weights dequantised
+ * into the workspace), *parts = the split's parts (1 otherwise).
+ * dev_count != 0: the row count lives on the device. The gemm-path hook
+ * applies. RIVER_ERR_WORKSPACE when not even one layer of x_hat fits. */
+river_status river_debug_kv_fill_plan(int m_max, int dev_count, int d, int n_out, int n_layers,
+                                      size_t ws_bytes, int* chunk, int* path, int* parts);
 
 #ifdef __cplusplus
 }

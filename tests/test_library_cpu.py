@@ -229,3 +229,169 @@ def test_router_fit_argument_errors():
     need = tee.river_workspace_size(tee.OP_ROUTER_FIT, 64, 128, 16, 32, 2)
     assert need >= 3 * 128 * 16 * 4
     assert call(wsn=need - 1) == 5
+
+
+# ------------------------------------------------- fill chunk and path plan
+
+def test_kv_fill_plan_keeps_room_for_dequantised_weights():
+    """A workspace sized for 6 of 12 layers at 4096 rows (d = 1024, n_out =
+    1024): the chunk leaves room for its dequantised weights, so the
+    projection takes the path the size was meant for, instead of the chunk
+    taking that room as x_hat layers and the projection falling back to
+    registers."""
+    m, d, no = 4096, 1024, 1024
+    xb = m * d * 2
+    ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, no, 0, 6)
+    chunk, path, parts = tee.river_debug_kv_fill_plan(m, d, no, 12, ws)
+    assert path == 2 and parts == 1
+    assert chunk * xb + chunk * 2 * no * d * 2 <= ws
+    assert chunk == 6
+    # sized for every layer: one chunk of all of them, dequantised weights
+    ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, no, 0, 12)
+    assert tee.river_debug_kv_fill_plan(m, d, no, 12, ws) == (12, 2, 1)
+    # x_hat only: fewer layers per chunk, the rest for the weights
+    ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, 0, 0, 6)
+    chunk, path, _ = tee.river_debug_kv_fill_plan(m, d, no, 6, ws)
+    assert path == 2 and 1 <= chunk < 6 and chunk * xb + chunk * 2 * no * d * 2 <= ws
+    # one layer of x_hat and nothing more: in registers
+    ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, 0, 0, 1)
+    assert tee.river_debug_kv_fill_plan(m, d, no, 6, ws) == (1, 0, 1)
+    # the row count on the device: never dequantised automatically
+    ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, no, 0, 12)
+    assert tee.river_debug_kv_fill_plan(m, d, no, 12, ws, dev_count=True) == (12, 0, 1)
+
+
+@pytest.mark.parametrize("m,d,nl,want", [
+    (30704, 5120, 48, (48, 2, 1)),     # long-context prefill at 32K tokens
+    (63472, 5120, 48, (48, 2, 1)),     # and at 64K
+    (7782, 4096, 1, (1, 2, 1)),        # 8B prefill, the late exits
+    (410, 4096, 21, (21, 0, 1)),       # 8B prefill, the early exits
+    (64, 4096, 8, (8, 1, 4)),          # decode-sized: split reduction
+])
+def test_kv_fill_plan_at_the_workload_shapes(m, d, nl, want):
+    ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, 1024, 0, nl)
+    assert tee.river_debug_kv_fill_plan(m, d, 1024, nl, ws) == want
+
+
+def test_kv_fill_plan_rejects_a_workspace_under_one_layer():
+    with pytest.raises(tee.RiverError) as e:
+        tee.river_debug_kv_fill_plan(4096, 1024, 1024, 4, 1024)
+    assert e.value.name == "ERR_WORKSPACE"
+
+
+# ------------------------------------------------- 31-bit operand spans
+
+def test_long_context_64k_spans_fit_31_bits():
+    """Every byte span the MFMA fill addresses with 32-bit offsets, at the
+    long-context shape with 65536 tokens (63,472 filled rows, d = 5120,
+    48 layers of 8 x 128 K/V heads), stays below 2^31: the states it
+    gathers from, one layer of x_hat, one map, the dequantised K/V weights
+    of one layer, and one layer of the cache that the epilogue indexes in
+    64-bit; the ridge fit's transposed operands at 16384 calibration
+    tokens. The whole caches and the x_hat of all layers are larger, and
+    are only ever offset in 64 bits by layer."""
+    lim = 1 << 31
+    N, m, d, nl, n_out, n_calib = 65536, 63472, 5120, 48, 1024, 16384
+    assert N * d * 2 < lim                       # h, gathered rows (map GEMM's A)
+    assert m * d * 2 < lim                       # one layer of x_hat (projection's A)
+    assert d * d * 2 < lim                       # one map (map GEMM's B)
+    assert 2 * n_out * d * 2 < lim               # one layer of dequantised K|V (B)
+    assert 4 * n_out * d < lim                   # the span check the fill applies
+    assert N * n_out * 2 < lim                   # one cache layer
+    assert nl * N * n_out * 2 >= lim             # the whole cache does not: 64-bit layer offsets
+    np_ = (n_calib + 255) // 256 * 256
+    assert d * np_ * 2 < lim and d * ((3 * d + 255) // 256 * 256) * 2 < lim
+    ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, n_out, 0, nl)
+    assert ws >= nl * m * d * 2 + nl * 2 * n_out * d * 2
+    assert tee.river_debug_kv_fill_plan(m, d, n_out, nl, ws) == (nl, 2, 1)
+
+
+def test_ridge_fit_rejects_31_bit_overflow():
+    """A bf16 fit whose transposed operand (d_in x padded n) would need byte
+    offsets of 2^31 or more is refused before anything runs."""
+    lib = tee.load()
+    a = dict(n=210048, d_in=5120, d_out=5120, T=1, X=256, xdt=tee.RIVER_BF16, Y=256,
+             ydt=tee.RIVER_BF16, lam=0.1, W=256, wdt=tee.RIVER_BF16, ws=256, wsn=1 << 62, s=None)
+    assert lib.river_ridge_fit(*a.values()) == 4
+    assert b"2^31" in lib.river_last_error()
+    a["n"] = 16384
+    a["wsn"] = 0
+    assert lib.river_ridge_fit(*a.values()) == 5      # passes the span check, stops at the workspace
+
+
+# ------------------------------------------------- binding shape checks
+
+def _fill_args(nl=3, n=16, d=256, hk=2, hd=64, slots=32, group=64):
+    import torch
+    h = torch.zeros(n, d, dtype=torch.bfloat16)
+    slot = torch.arange(n, dtype=torch.int32)
+
+    def w(layers=nl):
+        return (torch.zeros(layers, hk * hd, d // 2, dtype=torch.uint8),
+                torch.ones(layers, hk * hd, d // group, dtype=torch.bfloat16),
+                torch.zeros(layers, hk * hd, d // group, dtype=torch.bfloat16), group)
+    kc = torch.zeros(nl, slots, hk, hd, dtype=torch.bfloat16)
+    return h, slot, w, kc
+
+
+def test_binding_rejects_mismatched_fill_shapes():
+    import torch
+    h, slot, w, kc = _fill_args()
+    ok = dict(m_max=4)
+    with pytest.raises(ValueError, match="wv"):
+        tee.river_kv_fill(h, slot, w(), w(2), 2, 64, kc, kc.clone(), **ok)
+    with pytest.raises(ValueError, match="k_cache"):
+        tee.river_kv_fill(h, slot, w(), w(), 2, 64, kc[:2], kc.clone(), **ok)
+    with pytest.raises(ValueError, match="slot count"):
+        tee.river_kv_fill(h, slot, w(), w(), 2, 64, kc, kc[:, :16].clone(), **ok)
+    with pytest.raises(ValueError, match="slot"):
+        tee.river_kv_fill(h, slot[:8], w(), w(), 2, 64, kc, kc.clone(), **ok)
+    with pytest.raises(ValueError, match="row_idx"):
+        tee.river_kv_fill(h, slot, w(), w(), 2, 64, kc, kc.clone(), m_max=8,
+                          row_idx=torch.zeros(4, dtype=torch.int32))
+    with pytest.raises(ValueError, match="maps"):
+        tee.river_kv_fill(h, slot, w(), w(), 2, 64, kc, kc.clone(), m_max=4,
+                          maps=torch.zeros(2, 256, 256, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="k_cache"):
+        tee.river_kv_fill(h, slot, w(), w(), 4, 32, kc, kc.clone(), **ok)   # heads x dim differ
+    with pytest.raises(ValueError, match="k_bias"):
+        tee.river_kv_fill_layer(h, slot, w(), w(), 2, 64, kc, kc.clone(), m_max=4,
+                                k_bias=torch.zeros(2, 128, dtype=torch.bfloat16))
+
+
+def test_binding_rejects_mismatched_decode_and_ridge_shapes():
+    import torch
+    h, slot, w, kc = _fill_args(nl=4)
+    ck = [{"layer": 1, "h_prev": h, "h_cur": h, "tau": 0.5, "theta": -math.inf}]
+    ex = torch.zeros(16, dtype=torch.int32)
+    with pytest.raises(ValueError, match="wk"):
+        tee.river_decode_step(ck, w(3), w(4), 2, 64, slot, kc, kc.clone(), ex)
+    with pytest.raises(ValueError, match="v_cache"):
+        tee.river_decode_step(ck, w(4), w(4), 2, 64, slot, kc, kc[:3].clone(), ex)
+    with pytest.raises(ValueError, match="maps"):
+        ck2 = [dict(ck[0], maps=torch.zeros(4, 256, 256, dtype=torch.bfloat16))]
+        tee.river_decode_step(ck2, w(4), w(4), 2, 64, slot, kc, kc.clone(), ex)
+    X = torch.zeros(64, 128, dtype=torch.bfloat16)
+    Y = torch.zeros(2, 32, 64, dtype=torch.bfloat16)
+    W = torch.zeros(2, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="calibration token"):
+        tee.river_ridge_fit(X, Y, 0.1, W)
+    with pytest.raises(ValueError, match="W must be"):
+        tee.river_ridge_fit(X, torch.zeros(2, 64, 64, dtype=torch.bfloat16), 0.1, W[:1])
+
+
+def test_binding_rejects_mismatched_route_and_compact_shapes():
+    import torch
+    h = torch.zeros(16, 256, dtype=torch.bfloat16)
+    mask = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="h_prev"):
+        tee.river_route(h[:8], h, mask)
+    with pytest.raises(ValueError, match="w_up"):
+        tee.river_route(h, h, mask, w_down=torch.zeros(8, 256, dtype=torch.bfloat16),
+                        w_up=torch.zeros(4, dtype=torch.bfloat16))
+    i32 = lambda k: torch.zeros(k, dtype=torch.int32)
+    with pytest.raises(ValueError, match="exit_idx"):
+        tee.river_compact(mask, h, i32(16), i32(8), i32(2))
+    with pytest.raises(ValueError, match="out must have"):
+        tee.river_compact(mask, h, i32(16), i32(16), i32(2),
+                          out=torch.zeros(16, 128, dtype=torch.bfloat16))

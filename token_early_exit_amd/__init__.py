@@ -29,7 +29,7 @@ EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fi
            "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
            "river_debug_set_compact_path", "river_debug_set_gemm_path",
-           "river_debug_set_decode_path"]
+           "river_debug_set_decode_path", "river_debug_kv_fill_plan"]
 
 
 class RiverError(RuntimeError):
@@ -99,6 +99,8 @@ def load():
     lib.river_debug_set_compact_path.argtypes = [_I]
     lib.river_debug_set_gemm_path.argtypes = [_I]
     lib.river_debug_set_decode_path.argtypes = [_I]
+    lib.river_debug_kv_fill_plan.argtypes = [_I, _I, _I, _I, _I, _S, _P, _P, _P]
+    lib.river_debug_kv_fill_plan.restype = _I
     lib.river_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.river_workspace_size.restype = _S
     lib.river_last_error.restype = ctypes.c_char_p
@@ -160,11 +162,73 @@ def river_debug_set_decode_path(path):
     _check(load().river_debug_set_decode_path(path))
 
 
+def river_debug_kv_fill_plan(m_max, d, n_out, n_layers, ws_bytes, dev_count=False):
+    """(layers per chunk, projection path, parts) of a plain bf16 fill with
+    maps; path 0 = int4 in registers, 1 = split reduction, 2 = dequantised
+    weights."""
+    c, p, k = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check(load().river_debug_kv_fill_plan(m_max, int(bool(dev_count)), d, n_out, n_layers, ws_bytes,
+                                           ctypes.byref(c), ctypes.byref(p), ctypes.byref(k)))
+    return c.value, p.value, k.value
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_w4(w, n_layers, n_out, d, name):
+    q, s, z, group = w
+    _need(q.dim() == 3 and tuple(q.shape) == (n_layers, n_out, d // 2),
+          f"{name}: q must be [{n_layers}][{n_out}][{d // 2}], got {tuple(q.shape)}")
+    _need(group > 0 and d % group == 0, f"{name}: group {group} must divide d = {d}")
+    for t, nm in ((s, "scale"), (z, "zero")):
+        _need(tuple(t.shape) == (n_layers, n_out, d // group),
+              f"{name}: {nm} must be [{n_layers}][{n_out}][{d // group}], got {tuple(t.shape)}")
+
+
+def _check_fill(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, m_max, m_dev, row_idx,
+                maps, n_layers):
+    """Shapes a fill reads and writes, checked against each other (the C
+    interface takes bare pointers and cannot): a mismatch raises here
+    instead of becoming an out-of-bounds device access."""
+    n_rows, d = h.shape
+    n_out = n_kv_heads * head_dim
+    _check_w4(wk, n_layers, n_out, d, "wk")
+    _check_w4(wv, n_layers, n_out, d, "wv")
+    for c, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(c.dim() == 4 and c.shape[0] == n_layers and tuple(c.shape[2:]) == (n_kv_heads, head_dim),
+              f"{nm} must be [{n_layers}][n_slots][{n_kv_heads}][{head_dim}], got {tuple(c.shape)}")
+        _need(c.is_contiguous(), f"{nm} must be contiguous")
+    _need(k_cache.shape[1] == v_cache.shape[1], "k_cache and v_cache must have the same slot count")
+    _need(slot.dim() == 1 and slot.shape[0] >= n_rows,
+          f"slot must hold one entry per row of h ({n_rows}), got {tuple(slot.shape)}")
+    if row_idx is not None:
+        _need(row_idx.dim() == 1 and row_idx.shape[0] >= m_max,
+              f"row_idx must hold m_max = {m_max} entries, got {tuple(row_idx.shape)}")
+    if m_dev is not None:
+        _need(m_dev.numel() >= 1, "m_dev must hold one count")
+    if maps is not None:
+        _need(tuple(maps.shape) == (n_layers, d, d) and maps.is_contiguous(),
+              f"maps must be contiguous [{n_layers}][{d}][{d}], got {tuple(maps.shape)}")
+
+
 def river_route(h_prev, h_cur, mask_out, *, gamma=None, eps=1e-6, w_down=None, w_up=None,
                 tau=-math.inf, theta=-math.inf, rule=RULE_TOKEN, cos_out=None, prob_out=None,
                 all_exit_out=None, stream=None):
     n, d = h_cur.shape
     b = 0 if w_down is None else w_down.shape[0]
+    _need(tuple(h_prev.shape) == (n, d), f"h_prev must be [{n}][{d}] like h_cur, got {tuple(h_prev.shape)}")
+    _need(mask_out.numel() >= n, f"mask_out must hold {n} entries")
+    for t, nm in ((cos_out, "cos_out"), (prob_out, "prob_out")):
+        if t is not None:
+            _need(t.numel() >= n, f"{nm} must hold {n} entries")
+    if gamma is not None:
+        _need(gamma.numel() == d, f"gamma must hold d = {d} entries")
+    if w_down is not None:
+        _need(w_down.dim() == 2 and w_down.shape[1] == d and w_down.is_contiguous(),
+              f"w_down must be contiguous [b][{d}]")
+        _need(w_up is not None and w_up.numel() == b, f"w_up must hold b = {b} entries")
     _check(load().river_route(n, d, _dt(h_cur), _ptr(h_prev), _ld(h_prev), _ptr(h_cur), _ld(h_cur),
                               _ptr(gamma), eps, _ptr(w_down), _ptr(w_up), b, tau, theta, rule,
                               _ptr(cos_out), _ptr(prob_out), _ptr(mask_out), _ptr(all_exit_out),
@@ -181,6 +245,19 @@ def river_compact(mask, h, cont_idx, exit_idx, counts, *, row_ids=None, h_cont=N
         ld_h = 0
         d = d or 8
         dt = RIVER_BF16 if dt is None else dt
+    for t, nm in ((cont_idx, "cont_idx"), (exit_idx, "exit_idx")):
+        _need(t.numel() >= n, f"{nm} must hold {n} entries")
+    _need(counts.numel() >= 2, "counts must hold 2 entries")
+    if h is not None:
+        _need(h.shape[0] >= n, f"h must hold {n} rows")
+    if row_ids is not None:
+        _need(row_ids.numel() >= n, f"row_ids must hold {n} entries")
+    if h_cont is not None:
+        _need(h_cont.shape[0] >= n and h_cont.shape[1] == d, f"h_cont must be [{n}][{d}]")
+    if row_ids_cont is not None:
+        _need(row_ids_cont.numel() >= n, f"row_ids_cont must hold {n} entries")
+    if out is not None:
+        _need(out.shape[1] == d, f"out must have d = {d} columns")
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().river_compact(n, d, dt, _ptr(mask), _ptr(h), ld_h, _ptr(row_ids), _ptr(cont_idx),
                                 _ptr(exit_idx), _ptr(counts), _ptr(h_cont),
@@ -195,6 +272,13 @@ def river_exit_projection(h, out, *, m_max=None, m_dev=None, row_idx=None, row_i
     n_rows, d = h.shape
     if m_max is None:
         m_max = row_idx.shape[0] if row_idx is not None else n_rows
+    _need(out.dim() == 2 and out.shape[1] == d, f"out must have d = {d} columns")
+    if row_idx is not None:
+        _need(row_idx.numel() >= m_max, f"row_idx must hold m_max = {m_max} entries")
+    if row_ids is not None:
+        _need(row_ids.numel() >= n_rows, f"row_ids must hold one entry per row of h ({n_rows})")
+    if gamma is not None:
+        _need(gamma.numel() == d, f"gamma must hold d = {d} entries")
     _check(load().river_exit_projection(m_max, _ptr(m_dev), d, _dt(h), _ptr(h), _ld(h), n_rows,
                                         _ptr(row_idx), _ptr(row_ids), _ptr(gamma), eps, _ptr(out),
                                         _ld(out), out.shape[0], _stream(stream)))
@@ -212,6 +296,8 @@ def river_kv_fill(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, *, m_
     n_layers = wk[0].shape[0]
     if m_max is None:
         m_max = row_idx.shape[0] if row_idx is not None else n_rows
+    _check_fill(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, m_max, m_dev, row_idx,
+                maps, n_layers)
     dk = w4(*wk)
     dv = w4(*wv)
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -232,6 +318,19 @@ def river_kv_fill_layer(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache,
     n_layers = wk[0].shape[0]
     if m_max is None:
         m_max = row_idx.shape[0] if row_idx is not None else n_rows
+    _check_fill(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, m_max, m_dev, row_idx,
+                maps, n_layers)
+    n_out = n_kv_heads * head_dim
+    if norm_gamma is not None:
+        _need(tuple(norm_gamma.shape) == (n_layers, d), f"norm_gamma must be [{n_layers}][{d}]")
+    for b_, nm in ((k_bias, "k_bias"), (v_bias, "v_bias")):
+        if b_ is not None:
+            _need(tuple(b_.shape) == (n_layers, n_out), f"{nm} must be [{n_layers}][{n_out}]")
+    if pos is not None:
+        _need(pos.dim() == 1 and pos.shape[0] >= n_rows, "pos must hold one position per row of h")
+        _need(rope_cos is not None and rope_sin is not None and
+              tuple(rope_cos.shape) == tuple(rope_sin.shape) and rope_cos.shape[1] == head_dim // 2,
+              f"rope_cos and rope_sin must both be [n_pos][{head_dim // 2}]")
     dk = w4(*wk)
     dv = w4(*wv)
     lay = RiverLayer(_ptr(norm_gamma), norm_eps, _ptr(k_bias), _ptr(v_bias), _ptr(pos),
@@ -255,10 +354,27 @@ def river_decode_step(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, 
     n, d = h0.shape
     ld = _ld(h0)
     b = 0
+    n_layers = k_cache.shape[0]
+    n_out = n_kv_heads * head_dim
+    _check_w4(wk, n_layers, n_out, d, "wk")
+    _check_w4(wv, n_layers, n_out, d, "wv")
+    for cch, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(cch.dim() == 4 and tuple(cch.shape[2:]) == (n_kv_heads, head_dim) and cch.is_contiguous(),
+              f"{nm} must be contiguous [n_layers][n_slots][{n_kv_heads}][{head_dim}]")
+    _need(tuple(k_cache.shape) == tuple(v_cache.shape), "k_cache and v_cache must have the same shape")
+    _need(slot.dim() == 1 and slot.shape[0] >= n, f"slot must hold one entry per token ({n})")
+    _need(exit_layer.numel() >= n, f"exit_layer must hold one entry per token ({n})")
     arr = (RiverCheckpoint * len(checkpoints))()
     for i, c in enumerate(checkpoints):
         if _ld(c["h_prev"]) != ld or _ld(c["h_cur"]) != ld:
             raise ValueError("every state must have the same leading dimension")
+        _need(c["h_prev"].shape[0] >= n and c["h_cur"].shape[0] >= n,
+              f"checkpoint {i}: states must hold {n} rows")
+        mp = c.get("maps")
+        if mp is not None:
+            e = int(c["layer"])
+            _need(tuple(mp.shape) == (n_layers - e, d, d) and mp.is_contiguous(),
+                  f"checkpoint {i}: maps must be contiguous [{n_layers - e}][{d}][{d}]")
         wd = c.get("w_down")
         if wd is not None:
             b = wd.shape[0]
@@ -281,6 +397,13 @@ def river_router_fit(h, labels, w_down, w_up, *, epochs=100, batch=256, order=No
     """w_down (fp32 [b][d]) and w_up (fp32 [b]) are trained in place."""
     n, d = h.shape
     b = w_down.shape[0]
+    _need(tuple(w_down.shape) == (b, d) and w_down.is_contiguous(), f"w_down must be contiguous [b][{d}]")
+    _need(w_up.numel() == b, f"w_up must hold b = {b} entries")
+    _need(labels.numel() >= n, f"labels must hold {n} entries")
+    if order is not None:
+        _need(order.numel() >= epochs * n, f"order must hold epochs x n = {epochs * n} entries")
+    if loss_out is not None:
+        _need(loss_out.numel() >= epochs, f"loss_out must hold {epochs} entries")
     if workspace is None:
         raise ValueError("river_router_fit needs a workspace (river_workspace_size(OP_ROUTER_FIT, ...))")
     ws_n = workspace.numel() * workspace.element_size()
@@ -292,7 +415,11 @@ def river_router_fit(h, labels, w_down, w_up, *, epochs=100, batch=256, order=No
 
 def river_ridge_fit(X, Y, lam, W, *, workspace=None, stream=None):
     n, d_in = X.shape
-    n_targets, _, d_out = Y.shape
+    n_targets, n_y, d_out = Y.shape
+    _need(n_y == n, f"Y must be [n_targets][{n}][d_out] (one row per calibration token), got {tuple(Y.shape)}")
+    _need(tuple(W.shape) == (n_targets, d_out, d_in),
+          f"W must be [{n_targets}][{d_out}][{d_in}], got {tuple(W.shape)}")
+    _need(X.is_contiguous() and Y.is_contiguous() and W.is_contiguous(), "X, Y and W must be contiguous")
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().river_ridge_fit(n, d_in, d_out, n_targets, _ptr(X), _dt(X), _ptr(Y), _dt(Y),
                                   lam, _ptr(W), _dt(W), _ptr(workspace), ws_n, _stream(stream)))

@@ -78,6 +78,17 @@ river_status river_debug_set_decode_path(int path) {
   return RIVER_OK;
 }
 
+river_status river_debug_kv_fill_plan(int m_max, int dev_count, int d, int n_out, int n_layers,
+                                      size_t ws_bytes, int* chunk, int* path, int* parts) {
+  g_err[0] = 0;
+  if (m_max < 1 || d < 256 || d % 256 || n_out < 64 || n_out % 64 || n_layers < 1 || !chunk || !path || !parts)
+    return fail(RIVER_ERR_ARG, "kv_fill_plan: the plain MFMA fill's shape is needed");
+  if (ws_bytes < kv_fill_workspace(m_max, d, 1, RIVER_BF16))
+    return fail(RIVER_ERR_WORKSPACE, "kv_fill_plan: less than one layer of x_hat");
+  kv_fill_plan(m_max, dev_count != 0, d, n_out, n_layers, ws_bytes, chunk, path, parts);
+  return RIVER_OK;
+}
+
 size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int n_layers) {
   (void)n_targets;
   switch (op) {
@@ -373,6 +384,16 @@ river_status river_ridge_fit(int n, int d_in, int d_out, int n_targets, const vo
   if (xdt == RIVER_BF16 && (d_in % 64 || d_out % 64 || n % 64))
     return fail(RIVER_ERR_UNSUPPORTED, "ridge_fit: bf16 path needs n, d_in, d_out multiples of 64");
   if (xdt == RIVER_F32 && (d_in % 4 || d_out % 4)) return fail(RIVER_ERR_UNSUPPORTED, "ridge_fit: fp32 path needs d_in, d_out multiples of 4");
+  if (xdt == RIVER_BF16) {
+    // the MFMA GEMMs address each operand (X^T and Y_t^T over the padded
+    // calibration count, and the split factors over 3 d_in) with 31-bit
+    // byte offsets
+    const int64_t np = ((int64_t)n + 255) / 256 * 256, k3 = (3 * (int64_t)d_in + 255) / 256 * 256;
+    const int64_t lim = (int64_t)1 << 31, dmax = d_in > d_out ? d_in : d_out;
+    if (dmax * np * 2 >= lim || dmax * k3 * 2 >= lim)
+      return fail(RIVER_ERR_UNSUPPORTED, "ridge_fit: an operand of %lld x %lld bf16 exceeds 2^31 bytes",
+                  (long long)dmax, (long long)(np > k3 ? np : k3));
+  }
   size_t need = ridge_workspace(n, d_in, d_out, xdt);
   if (!workspace || ws_bytes < need)
     return fail(RIVER_ERR_WORKSPACE, "ridge_fit: workspace of %zu bytes needed, %zu given", need, ws_bytes);

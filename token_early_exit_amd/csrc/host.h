@@ -53,6 +53,8 @@ size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt);
 size_t kv_fill_layer_workspace(int m_max, int d, int n_layers);
 size_t kv_fill_proj_workspace(int m_max, int d, int n_out, int n_layers);
 size_t decode_proj_workspace(int n, int d, int n_out, int n_layers);
+void kv_fill_plan(int m_max, bool dev_count, int d, int nh, int n_layers, size_t ws_bytes, int* chunk,
+                  int* path, int* ks);
 river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
                             int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
                             int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,

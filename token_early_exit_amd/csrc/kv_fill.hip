@@ -240,7 +240,7 @@ static bool fill_mfma_ok(int d, river_dtype dt, int nh, const river_w4* wk, cons
   const int64_t lim = (int64_t)1 << 31;
   return dt == RIVER_BF16 && d % 256 == 0 && nh % 64 == 0 && wk->group % 64 == 0 &&
          wk->group == wv->group && wk->sz_dtype == wv->sz_dtype && even &&
-         a_span < lim && ws_span < lim && (int64_t)nh * d < lim && (int64_t)d * d * 2 < lim;
+         a_span < lim && ws_span < lim && (int64_t)4 * nh * d < lim && (int64_t)d * d * 2 < lim;
 }
 
 bool kv_fill_plain_mfma(int m_max, int d, river_dtype dt, int n_rows, int64_t ld_h, const river_w4* wk,
@@ -312,6 +312,51 @@ size_t kv_fill_proj_workspace(int m_max, int d, int n_out, int n_layers) {
   }
   if (dequant_wanted(m_max, 2 * n_out, n_layers)) return align_up((size_t)n_layers * 2 * n_out * d * 2, 256);
   return 0;
+}
+
+// The plain projection's path for nl layers with avail workspace bytes
+// (the automatic choice, or the one the gemm-path hook forces):
+// PROJ_DEQUANT, the 256 x 256 bf16 GEMM on weights dequantised into the
+// workspace; PROJ_SPLIT, the reduction over d in *ks parts whose fp32 sums
+// a second kernel adds; PROJ_REGS, the int4 kernel dequantising in
+// registers. dev_count: the row count lives on the device (m_max may bound
+// far fewer rows, so no automatic dequantisation); per_layer_rows: a row
+// count per layer (the decode step's single fill).
+enum { PROJ_REGS = 0, PROJ_SPLIT = 1, PROJ_DEQUANT = 2 };
+static int proj_path(int m_max, bool dev_count, bool per_layer_rows, int d, int N, int nl, size_t avail,
+                     int* ks) {
+  const int path = gemm_path_override();
+  *ks = 1;
+  if (path != 1 && m_max > 64 && !per_layer_rows &&
+      (path == 2 || (!dev_count && dequant_wanted(m_max, N, nl))) && avail >= (size_t)nl * N * d * 2)
+    return PROJ_DEQUANT;
+  *ks = choose_ksplit(m_max, N, d, nl, avail);
+  return *ks > 1 ? PROJ_SPLIT : PROJ_REGS;
+}
+
+// the workspace bytes of the dequantised weights of nl layers when the
+// automatic path projects on them (large row counts), else 0
+static size_t dequant_room(int m_max, bool dev_count, int d, int nh, int nl) {
+  int ks;
+  const int p = proj_path(m_max, dev_count, false, d, 2 * nh, nl, SIZE_MAX, &ks);
+  return p == PROJ_DEQUANT ? align_up((size_t)nl * 2 * nh * d * 2, 256) : 0;
+}
+
+// Layers per chunk of a fill that keeps x_hat (and, with an input norm, the
+// row sums) in the workspace, per_layer bytes per layer. At large row
+// counts, as many as fit after the chunk's dequantised weights, so that a
+// workspace sized for fewer layers than the call has still projects on
+// them; when not even one layer leaves that room, as many layers as fit
+// (the projection then dequantises in registers). Otherwise as many as fit;
+// what is left holds the partial sums of a split reduction, if any.
+static int fill_chunk(int m_max, bool dev_count, int d, int nh, int n_layers, size_t per_layer,
+                      size_t ws_bytes, bool plain) {
+  const size_t fit = ws_bytes / per_layer;
+  const int chunk = fit < (size_t)n_layers ? (int)fit : n_layers;
+  if (!plain) return chunk;
+  for (int c = chunk; c >= 1; --c)
+    if ((size_t)c * per_layer + dequant_room(m_max, dev_count, d, nh, c) <= ws_bytes) return c;
+  return chunk;
 }
 
 // the split space any fill of a decode step may use: blocks e + 1 .. L for a
@@ -407,11 +452,9 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
     if (!layer) {
-      const int path = gemm_path_override();
-      // (with the row count on the device, 2048 may bound a few hundred rows:
-      // no automatic dequantisation there)
-      if (path != 1 && m_max > 64 && !q.M_dev_z && (path == 2 || (!m_dev && dequant_wanted(m_max, q.N, nl))) &&
-          part_bytes >= (size_t)nl * q.N * d * 2) {
+      int ks;
+      const int pp = proj_path(m_max, m_dev != nullptr, q.M_dev_z != nullptr, d, q.N, nl, part_bytes, &ks);
+      if (pp == PROJ_DEQUANT) {
         uint16_t* dq = (uint16_t*)part_ws;
         const int64_t threads = (int64_t)nl * q.N * (d / 8);
         w4_dequant_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(q, nl, dq);
@@ -422,8 +465,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
         gemm_big_launch<EPI_CACHE>(p, nl, s);
         return check_launch("kv_fill projection (bf16)");
       }
-      const int ks = choose_ksplit(m_max, q.N, d, nl, part_bytes);
-      if (ks > 1) {
+      if (pp == PROJ_SPLIT) {
         q.ksplit = ks;
         q.part = (float*)part_ws;
         w4_gemm_launch<64, EPI_PART, false>(q, nl, s);
@@ -451,8 +493,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
   }
 
   const size_t xb = layer_xhat_bytes(m_max, d), sb = gamma ? layer_ss_bytes(m_max, d) : 0;
-  int chunk = (int)(ws_bytes / (xb + sb));
-  if (chunk > n_layers) chunk = n_layers;
+  const int chunk = fill_chunk(m_max, m_dev != nullptr, d, nh, n_layers, xb + sb, ws_bytes, !layer);
   uint16_t* xh = (uint16_t*)workspace;
   float* ss = (float*)((char*)workspace + (size_t)chunk * xb);
   part_ws = (char*)workspace + (size_t)chunk * (xb + sb);
@@ -502,6 +543,18 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     if (st != RIVER_OK) return st;
   }
   return RIVER_OK;
+}
+
+// the plan of a plain bf16 fill with maps (the test hook
+// river_debug_kv_fill_plan): layers per chunk, and the projection's path
+// and parts for the first chunk
+void kv_fill_plan(int m_max, bool dev_count, int d, int nh, int n_layers, size_t ws_bytes, int* chunk,
+                  int* path, int* ks) {
+  const size_t xb = layer_xhat_bytes(m_max, d);
+  *chunk = fill_chunk(m_max, dev_count, d, nh, n_layers, xb, ws_bytes, true);
+  const size_t used = (size_t)*chunk * xb;
+  *path = *chunk > 0 ? proj_path(m_max, dev_count, false, d, 2 * nh, *chunk, ws_bytes - used, ks) : PROJ_REGS;
+  if (*chunk == 0) *ks = 1;
 }
 
 }  // namespace river_host
