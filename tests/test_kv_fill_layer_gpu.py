@@ -105,11 +105,13 @@ def test_layer_fill_llama1b_decode_identity():
     pos = slot.clone()                         # a decode token's position is its slot
     wk, wv = _kv(cfg, layers)
     parts = _parts(cfg, layers, bias=False)
-    rows = torch.arange(0, 64, 3, dtype=torch.int32, device=DEV)
-    m_dev = torch.tensor([rows.numel()], dtype=torch.int32, device=DEV)
-    kc, vc = fill_layer_gpu(cfg, h, slot, wk, wv, len(layers), parts, pos=pos, row_idx=rows,
+    sel = torch.arange(0, 64, 3, dtype=torch.int32)
+    rows = torch.full((64,), -1, dtype=torch.int32)        # row_idx holds m_max entries
+    rows[: sel.numel()] = sel
+    m_dev = torch.tensor([sel.numel()], dtype=torch.int32, device=DEV)
+    kc, vc = fill_layer_gpu(cfg, h, slot, wk, wv, len(layers), parts, pos=pos, row_idx=rows.to(DEV),
                             m_dev=m_dev, m_max=64)
-    check_layer(cfg, kc, vc, h, rows.cpu().numpy(), slot, None, wk, wv, parts, pos)
+    check_layer(cfg, kc, vc, h, sel.numpy(), slot, None, wk, wv, parts, pos)
 
 
 @pytest.mark.parametrize("norm,bias,rope", [(True, True, True), (False, False, True),
