@@ -388,6 +388,35 @@ river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_c
                                hipStream_t s);
 
 /*
+ * river_decode_step_static -- river_decode_step with no workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). It
+ * allocates nothing: its scratch is a static device array of 64 MiB
+ * (67,108,864 bytes) that the library holds on each GPU it runs on until
+ * the process ends; the array's device address is looked up once per
+ * device, on the first call with that device current.
+ *
+ * Arguments, results and the rest of the contract are river_decode_step's.
+ * The call uses min(64 MiB, river_workspace_size(RIVER_OP_DECODE_STEP, n,
+ * d, n_kv_heads * head_dim, 0, n_layers)) bytes of the scratch, so its
+ * result equals river_decode_step's with a workspace of that size. It
+ * returns RIVER_ERR_WORKSPACE, with the sizes in river_last_error, when
+ * even the least workspace river_decode_step takes (the fixed part, plus
+ * one layer of x_hat with maps) exceeds 64 MiB.
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (the step writes every byte it reads before reading it):
+ * calls that overlap on one GPU, on any streams or threads, race; the
+ * caller orders them (one stream, or events).
+ */
+river_status river_decode_step_static(int n, int d, river_dtype dt, int64_t ld, int n_ck,
+                                      const river_checkpoint* ck, int n_layers, const void* gamma,
+                                      float eps, int b, river_rule rule, const river_w4* wk,
+                                      const river_w4* wv, int n_kv_heads, int head_dim,
+                                      const int32_t* slot, void* k_cache, void* v_cache,
+                                      int64_t n_slots, int32_t* exit_layer, hipStream_t s);
+
+/*
  * river_ridge_fit -- closed-form ridge maps (RidgeFill, ridge box):
  *
  *   W_t = (X^T X + lambda I)^-1 X^T Y_t     for t = 0..n_targets-1

@@ -7,8 +7,8 @@ CPU fallback: if the library is not built, ``load()`` raises.
 
 The calls keep the C names: ``river_route``, ``river_compact``,
 ``river_exit_projection``, ``river_kv_fill``, ``river_kv_fill_layer``,
-``river_decode_step``, ``river_router_fit``, ``river_ridge_fit``; plus
-``river_workspace_size``.
+``river_decode_step``, ``river_decode_step_static``, ``river_router_fit``,
+``river_ridge_fit``; plus ``river_workspace_size``.
 """
 
 import ctypes
@@ -29,7 +29,7 @@ EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fi
            "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
            "river_debug_set_compact_path", "river_debug_set_gemm_path",
-           "river_debug_set_decode_path", "river_debug_kv_fill_plan"]
+           "river_debug_set_decode_path", "river_debug_kv_fill_plan", "river_decode_step_static"]
 
 
 class RiverError(RuntimeError):
@@ -89,11 +89,15 @@ def load():
     lib.river_decode_step.argtypes = [_I, _I, _I, _L, _I, ctypes.POINTER(RiverCheckpoint), _I, _P, _F,
                                       _I, _I, ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4), _I,
                                       _I, _P, _P, _P, _L, _P, _P, _S, _P]
+    lib.river_decode_step_static.argtypes = [_I, _I, _I, _L, _I, ctypes.POINTER(RiverCheckpoint), _I, _P,
+                                             _F, _I, _I, ctypes.POINTER(RiverW4),
+                                             ctypes.POINTER(RiverW4), _I, _I, _P, _P, _P, _L, _P, _P]
     lib.river_router_fit.argtypes = [_I, _I, _I, _P, _L, _P, _P, _F, _I, _P, _P, _I, _I, _P, _F, _F,
                                      _F, _F, _P, _P, _S, _P]
     lib.river_ridge_fit.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _S, _P]
     for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill",
-              "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
+              "river_kv_fill_layer", "river_decode_step", "river_decode_step_static",
+              "river_router_fit", "river_ridge_fit",
               "river_debug_set_compact_path", "river_debug_set_gemm_path", "river_debug_set_decode_path"):
         getattr(lib, f).restype = _I
     lib.river_debug_set_compact_path.argtypes = [_I]
@@ -344,12 +348,10 @@ def river_kv_fill_layer(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache,
                                       k_cache.shape[1], _ptr(workspace), ws_n, _stream(stream)))
 
 
-def river_decode_step(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, v_cache,
-                      exit_layer, *, gamma=None, eps=1e-6, rule=RULE_TOKEN, workspace=None,
-                      stream=None):
-    """checkpoints: list of dicts with layer, h_prev, h_cur, tau, theta and
-    optionally w_down, w_up, maps; wk, wv: (q, scale, zero, group) of every
-    block; caches [n_layers][n_slots][Hkv][Dh]."""
+def _decode_args(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, v_cache, exit_layer, gamma,
+                 eps, rule):
+    """The C arguments of a decode step up to exit_layer (checked), and the
+    descriptors they point to (kept alive by the caller)."""
     h0 = checkpoints[0]["h_cur"]
     n, d = h0.shape
     ld = _ld(h0)
@@ -383,12 +385,33 @@ def river_decode_step(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, 
                                  _ptr(c.get("maps")))
     dk = w4(*wk)
     dv = w4(*wv)
+    args = (n, d, _dt(h0), ld, len(checkpoints), arr, n_layers, _ptr(gamma), eps, b, rule,
+            ctypes.byref(dk), ctypes.byref(dv), n_kv_heads, head_dim, _ptr(slot), _ptr(k_cache),
+            _ptr(v_cache), k_cache.shape[1], _ptr(exit_layer))
+    return args, (arr, dk, dv)
+
+
+def river_decode_step(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, v_cache,
+                      exit_layer, *, gamma=None, eps=1e-6, rule=RULE_TOKEN, workspace=None,
+                      stream=None):
+    """checkpoints: list of dicts with layer, h_prev, h_cur, tau, theta and
+    optionally w_down, w_up, maps; wk, wv: (q, scale, zero, group) of every
+    block; caches [n_layers][n_slots][Hkv][Dh]."""
+    args, keep = _decode_args(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, v_cache,
+                              exit_layer, gamma, eps, rule)
     ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().river_decode_step(n, d, _dt(h0), ld, len(checkpoints), arr, k_cache.shape[0],
-                                    _ptr(gamma), eps, b, rule, ctypes.byref(dk), ctypes.byref(dv),
-                                    n_kv_heads, head_dim, _ptr(slot), _ptr(k_cache), _ptr(v_cache),
-                                    k_cache.shape[1], _ptr(exit_layer), _ptr(workspace), ws_n,
-                                    _stream(stream)))
+    _check(load().river_decode_step(*args, _ptr(workspace), ws_n, _stream(stream)))
+    del keep
+
+
+def river_decode_step_static(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, v_cache,
+                             exit_layer, *, gamma=None, eps=1e-6, rule=RULE_TOKEN, stream=None):
+    """river_decode_step on the library's static device scratch (no
+    workspace, nothing allocated)."""
+    args, keep = _decode_args(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, v_cache,
+                              exit_layer, gamma, eps, rule)
+    _check(load().river_decode_step_static(*args, _stream(stream)))
+    del keep
 
 
 def river_router_fit(h, labels, w_down, w_up, *, epochs=100, batch=256, order=None, gamma=None,

@@ -340,6 +340,35 @@ river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_c
                             head_dim, slot, k_cache, v_cache, n_slots, exit_layer, workspace, ws_bytes, s);
 }
 
+river_status river_decode_step_static(int n, int d, river_dtype dt, int64_t ld, int n_ck,
+                                      const river_checkpoint* ck, int n_layers, const void* gamma,
+                                      float eps, int b, river_rule rule, const river_w4* wk,
+                                      const river_w4* wv, int n_kv_heads, int head_dim,
+                                      const int32_t* slot, void* k_cache, void* v_cache,
+                                      int64_t n_slots, int32_t* exit_layer, hipStream_t s) {
+  g_err[0] = 0;
+  if (n <= 0 || d < 8 || n_layers < 2 || n_ck < 0 || n_kv_heads < 1 || head_dim < 1 || (n_ck > 0 && !ck))
+    return river_decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads,
+                             head_dim, slot, k_cache, v_cache, n_slots, exit_layer, nullptr, 0, s);
+  void* p = nullptr;
+  size_t cap = 0;
+  river_status st = decode_static_scratch(&p, &cap);
+  if (st != RIVER_OK) return st;
+  bool any_maps = false;
+  for (int c = 0; c < n_ck; ++c) any_maps |= ck[c].maps != nullptr;
+  // the least river_decode_step takes, and the size that fills every
+  // checkpoint in one pass with room for the split reductions
+  const size_t need = decode_fixed_workspace(n, d, dt, n_layers) + (any_maps ? kv_fill_workspace(n, d, 1, dt) : 0);
+  if (need > cap)
+    return fail(RIVER_ERR_WORKSPACE,
+                "decode_step_static: %zu bytes of scratch needed (n = %d, d = %d, %d blocks), the static "
+                "scratch holds %zu", need, n, d, n_layers, cap);
+  const size_t want = decode_fixed_workspace(n, d, dt, n_layers) + kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) +
+                      decode_proj_workspace(n, d, n_kv_heads * head_dim, n_layers);
+  return river_decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads, head_dim,
+                           slot, k_cache, v_cache, n_slots, exit_layer, p, want < cap ? want : cap, s);
+}
+
 river_status river_router_fit(int n, int d, river_dtype dt, const void* h, int64_t ld_h,
                               const uint8_t* labels, const void* gamma, float eps, int b,
                               float* w_down, float* w_up, int epochs, int batch,

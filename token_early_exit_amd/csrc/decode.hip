@@ -29,10 +29,20 @@
 // Nothing waits on the host, allocates or sets memory through the runtime,
 // so the whole step can be captured once into a HIP graph and replayed for
 // every generated token.
+#include <mutex>
+
 #include "common.h"
 #include "cosine.h"
 
 namespace river {
+
+// The scratch of river_decode_step_static: a file-scope device array that
+// each GPU the library runs on holds from the code object's load until the
+// process ends. Host code never passes the array's name to a kernel (on
+// the host it only stands for the symbol); it passes the device address
+// hipGetSymbolAddress returned for the current device.
+constexpr size_t DECODE_STATIC_SCRATCH = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[DECODE_STATIC_SCRATCH];
 
 // every token running, no exit yet
 __global__ __launch_bounds__(256) void decode_init_kernel(int n, uint8_t* alive, int32_t* exit_layer,
@@ -207,6 +217,28 @@ static size_t a256(size_t x) { return align_up(x, 256); }
 static size_t plan_ck_bytes(int n) { return 3 * a256(4 * (size_t)n) + a256((size_t)n) + 256; }
 static size_t plan_fill_bytes(int n, int d, int n_layers) {
   return a256((size_t)n * d * 4) + 2 * a256(4 * (size_t)n) + a256(4 * (size_t)n_layers);
+}
+
+// Device address of the static scratch on the current device (looked up
+// once per device, on its first use, with that device current).
+river_status decode_static_scratch(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static void* addr[256] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RIVER_ERR_HIP, "decode_step_static: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 256) return fail(RIVER_ERR_UNSUPPORTED, "decode_step_static: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(RIVER_ERR_HIP, "decode_step_static: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  *bytes = DECODE_STATIC_SCRATCH;
+  return RIVER_OK;
 }
 
 size_t decode_fixed_workspace(int n, int d, river_dtype dt, int n_layers) {

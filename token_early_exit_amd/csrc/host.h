@@ -74,6 +74,7 @@ river_status launch_route_scores(int n, int d, river_dtype dt, int64_t ld, int n
                                  uint8_t* mask_scratch, hipStream_t s);
 
 size_t decode_fixed_workspace(int n, int d, river_dtype dt, int n_layers);
+river_status decode_static_scratch(void** ptr, size_t* bytes);
 void decode_layer_offset(const river_w4& w, int e, int n_out, int d, river_w4* out);
 river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
                                 const river_checkpoint* ck, int n_layers, const void* gamma,
