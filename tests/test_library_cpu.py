@@ -116,7 +116,7 @@ def test_kv_fill_and_ridge_argument_errors():
                             tee.RIVER_F32, 16, 10, None)
     assert r == 5                                                  # workspace too small
     assert lib.river_debug_set_compact_path(9) == 1
-    assert lib.river_debug_set_gemm_path(3) == 1
+    assert lib.river_debug_set_gemm_path(4) == 1
     assert lib.river_debug_set_decode_path(2) == 1
 
 

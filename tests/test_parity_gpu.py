@@ -419,6 +419,50 @@ def test_kv_fill_dequantised_projection(maps):
         assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-2 * b.abs().amax(dim=-1, keepdim=True))
 
 
+@pytest.mark.parametrize("count_on_device", [True, False])
+def test_kv_fill_quad_tiles_equal_eight_wave_tiles(count_on_device):
+    """d = 1280 (a multiple of 160): the 256 x 256 tiles of the map GEMM and
+    of the projection on dequantised weights run on the 4-wave kernel
+    (gemm path 2) and on the 8-wave kernel (path 3). Both run the same MFMAs
+    in the same order, so the caches agree bit for bit; the 4-wave result is
+    within the K/V bar of the oracle. 300 of 640 rows (a ragged last tile),
+    three layers, the count on the device or on the host."""
+    cfg = get_config(1, d=1280, n_tokens=640, n_slots=700)
+    layers = [5, 6, 7]
+    nl = len(layers)
+    h = G.hidden_states(cfg, cfg.n_tokens, [4])[4].to(DEV)
+    g = torch.Generator().manual_seed(160)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    maps = G.near_identity_maps(cfg, nl, scale=0.5).to(DEV)
+    sel = torch.sort(torch.randperm(cfg.n_tokens, generator=g)[:300]).values.to(torch.int32)
+    if count_on_device:
+        rows = torch.full((cfg.n_tokens,), -1, dtype=torch.int32)
+        rows[:300] = sel
+        m_max, m_dev = cfg.n_tokens, torch.tensor([300], dtype=torch.int32, device=DEV)
+    else:
+        rows, m_max, m_dev = sel, 300, None
+    rows = rows.to(DEV)
+    nh = cfg.n_kv_heads * cfg.head_dim
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, m_max, cfg.d, nh, 0, nl)
+                     + nl * 2 * nh * cfg.d * 2, dtype=torch.uint8, device=DEV)
+    out = {}
+    try:
+        for p in (2, 3):
+            tee.river_debug_set_gemm_path(p)
+            kc, vc = G.nan_cache(cfg, nl, device=DEV)
+            tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=m_max,
+                              m_dev=m_dev, row_idx=rows, maps=maps, workspace=ws)
+            torch.cuda.synchronize()
+            out[p] = (kc, vc)
+    finally:
+        tee.river_debug_set_gemm_path(0)
+    for a, b in zip(out[2], out[3]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    kc, vc = out[2]
+    check_fill(cfg, kc, vc, h, sel.numpy(), slot, maps, wk, wv)
+
+
 def test_kv_fill_identity_null_equals_explicit_eye():
     cfg = get_config(2)
     layers = list(range(9, 17))

@@ -67,7 +67,7 @@ river_status river_debug_set_compact_path(int path) {
 }
 
 river_status river_debug_set_gemm_path(int path) {
-  if (path < 0 || path > 2) return fail(RIVER_ERR_ARG, "gemm path must be 0..2, got %d", path);
+  if (path < 0 || path > 3) return fail(RIVER_ERR_ARG, "gemm path must be 0..3, got %d", path);
   g_gemm_path.store(path, std::memory_order_relaxed);
   return RIVER_OK;
 }

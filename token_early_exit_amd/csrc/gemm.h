@@ -110,6 +110,26 @@ __device__ __forceinline__ void interleave() {
   }
 }
 
+// Scheduling hint that spreads a sub-step's memory instructions over its
+// MFMAs: after MFMA k an LDS read while k % RSTEP == 0 and reads remain,
+// otherwise one of N_VMEM global loads, so neither a burst of reads nor of
+// loads stalls the in-order issue of the next MFMA.
+template <int N_MFMA, int N_READ, int N_VMEM, int RSTEP>
+__device__ __forceinline__ void interleave_spread() {
+  int r = 0, v = 0;
+#pragma unroll
+  for (int k = 0; k < N_MFMA; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+    if (k % RSTEP == 0 && r < N_READ) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  // LDS read
+      ++r;
+    } else if (v < N_VMEM) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                  // global load
+      ++v;
+    }
+  }
+}
+
 constexpr int N_CU = 256;
 
 template <int BM, int EPI>

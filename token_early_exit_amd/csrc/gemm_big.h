@@ -308,20 +308,4 @@ inline void gemm_big_launch(const GemmArgs& g, int batch, hipStream_t s) {
   gemm_big_kernel<EPI><<<dim3(grid, 1), 512, 0, s>>>(g, tn, batch);
 }
 
-// bf16-output GEMM: 256 x 256 tiles from 1024 rows on when they give at
-// least one tile per CU (measured: 7782 rows of one 4096-wide layer, 496
-// tiles, run 15% faster than on 128 x 128 tiles), the 128-row kernel
-// otherwise. With the row count on the device the bound may be far above
-// it (546 of 4096 rows in the GPT-2-shape step: 72 busy 256 x 256 tiles
-// against 240 of 128 x 128; the whole fill measured 43 µs instead of 30),
-// so there the big tiles need two per CU at the bound.
-template <int EPI>
-inline void gemm_bf16_auto(const GemmArgs& g, int batch, hipStream_t s) {
-  const int64_t big = (int64_t)((g.N + 255) / 256) * ((g.M_max + 255) / 256) * batch;
-  const int path = river_host::gemm_path_override();
-  const bool auto_big = g.M_dev ? big >= 2 * N_CU : (g.M_max >= 1024 && big >= N_CU);
-  if (path == 2 || (path == 0 && auto_big)) gemm_big_launch<EPI>(g, batch, s);
-  else gemm_auto<EPI>(g, batch, s);
-}
-
 }  // namespace river

@@ -1,0 +1,316 @@
+// bf16 GEMM for large row counts with the reduction a multiple of 160:
+// C[z] = A[z] . B[z]^T (both operands K-contiguous), fp32 accumulation,
+// bf16 output (EPI_BF16), or EPI_CACHE (columns [0, nh) to the K cache and
+// [nh, 2 nh) to the V cache at the slot of each row).
+//
+// Workgroup tile 256 x 256 as in gemm_big.h, but 4 waves, one per SIMD,
+// each owning a 128 x 128 quadrant: 4 x 4 accumulators of 32x32 (256
+// accumulator registers, held in the AGPRs), fed by
+// v_mfma_f32_32x32x16_bf16, so each 16-byte fragment read from LDS feeds 4
+// MFMAs (0.5 KB of LDS reads per MFMA against 0.75 KB for 128 x 64 wave
+// blocks). The K-slab is 32 wide; a ring of 5 stages of 32 KB fills the
+// 160 KB of LDS and keeps four slabs in flight. Inside a sub-step the LDS
+// reads of the next fragments go one after every other MFMA and the global
+// loads after the others, so no burst of reads or loads holds back the
+// in-order issue of the MFMAs. On the long-context shapes (d = 5120) this
+// measured 2-5% faster than the 8-wave kernel and draws less power per
+// flop (the same MFMA busy fraction at a higher sustained clock).
+//
+// The MFMAs run in the same order on the same fragments as gemm_big.h
+// (slab by slab, sub-step 0 then 1, chunk 2 h + s), so the results are
+// bit-identical to it.
+#pragma once
+
+#include "gemm_big.h"
+
+namespace river {
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_quad_kernel(GemmArgs g, int tiles_n, int batch) {
+  static_assert(EPI == EPI_BF16 || EPI == EPI_CACHE, "bf16 output");
+  constexpr int BM = 256, BN = 256;
+  constexpr int MI = 4, NI = 4;          // 32x32 fragments per wave
+  constexpr int AD = BM * 4 / 256;       // A loads per thread per slab (4)
+  constexpr int BD = BN * 4 / 256;       // B loads per thread per slab (4)
+  constexpr int PER_SLAB = AD + BD;
+  constexpr int SSZ = (BM + BN) * 4;
+  __shared__ u32x4 S0[SSZ], S1[SSZ], S2[SSZ], S3[SSZ], S4[SSZ];
+
+  const int M_max = g.M_max, N = g.N, K = g.K, a_nrows = g.a_nrows;
+  int M = M_max;
+  if (g.M_dev) {
+    const int md = *g.M_dev;
+    M = md < 0 ? 0 : (md < M_max ? md : M_max);
+  }
+  constexpr int GM = 4;
+  const int tiles_m_act = (M + BM - 1) / BM;
+  const int total = tiles_n * tiles_m_act * batch;
+  const int xcd = blockIdx.x & 7, wg_in_xcd = blockIdx.x >> 3;
+  const int per_xcd = (gridDim.x + 7 - xcd) >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int t_end = (xcd + 1) * chunk < total ? (xcd + 1) * chunk : total;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5;
+  const int KT = K / 32;
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  auto stage = [&](auto st) -> u32x4* {
+    constexpr int S = decltype(st)::value;
+    if constexpr (S == 0) return S0; else if constexpr (S == 1) return S1;
+    else if constexpr (S == 2) return S2; else if constexpr (S == 3) return S3; else return S4;
+  };
+
+  // persistent, XCD-aware tile walk with groups of GM row tiles (gemm.h)
+  for (int tile = xcd * chunk + wg_in_xcd; tile < t_end; tile += per_xcd) {
+    const int z = tile / (tiles_n * tiles_m_act);
+    const int tz = tile - z * tiles_n * tiles_m_act;
+    const int g0 = tz / (GM * tiles_n) * GM;
+    const int gsz = tiles_m_act - g0 < GM ? tiles_m_act - g0 : GM;
+    const int tg = tz - g0 * tiles_n;
+    const int mt = g0 + tg % gsz;
+    const int nt = tg / gsz;
+    const int m0 = mt * BM, n0 = nt * BN;
+
+    // EPI_CACHE: the row ids of this lane's four output rows go out now, the
+    // slots once the first slab has landed (its wait covers these loads)
+    [[maybe_unused]] int er[MI], sl[MI];
+    if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = m0 + wm * 128 + mi * 32 + (lane & 31);
+        const int rc = row < M ? row : M - 1;
+        er[mi] = g.e_rows ? g.e_rows[rc] : rc;
+      }
+    }
+    // load i of this thread fills LDS chunk p = (i * 4 + wave) * 64 + lane
+    // of the A (or B) rows: row p / 4, physical chunk p % 4, which holds
+    // logical chunk (p % 4) ^ swz4(row)
+    int a_src_row[AD];
+#pragma unroll
+    for (int i = 0; i < AD; ++i) {
+      const int t = m0 + (((i * 4 + wave) * 64 + lane) >> 2);
+      a_src_row[i] = g.a_rows ? g.a_rows[t < M ? t : M - 1] : t;
+    }
+    const void* a_buf = g.A + (int64_t)z * g.a_bstride;
+    const int a_bytes = (int)(a_nrows * g.lda * 2);
+    uint32_t a_off[AD];
+#pragma unroll
+    for (int i = 0; i < AD; ++i) {
+      const int p = (i * 4 + wave) * 64 + lane;
+      const int r = p >> 2, c = (p & 3) ^ swz4(r);
+      int src = a_src_row[i];
+      if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
+      a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
+    }
+    const void* b_buf = g.B + (int64_t)z * g.b_bstride;
+    const int b_bytes = (int)(N * g.ldb * 2);                   // rows past N read zeros
+    uint32_t b_off[BD];
+#pragma unroll
+    for (int i = 0; i < BD; ++i) {
+      const int p = (i * 4 + wave) * 64 + lane;
+      const int r = p >> 2, c = (p & 3) ^ swz4(r);
+      b_off[i] = (uint32_t)(((int64_t)(n0 + r) * g.ldb + c * 8) * 2);
+    }
+    auto issue = [&](auto st, int j) {
+      u32x4* l = stage(st);
+#pragma unroll
+      for (int i = 0; i < AD; ++i) buf_lds<16>(a_buf, a_bytes, a_off[i], j * 64, l + (i * 4 + wave) * 64);
+#pragma unroll
+      for (int i = 0; i < BD; ++i) buf_lds<16>(b_buf, b_bytes, b_off[i], j * 64, l + BM * 4 + (i * 4 + wave) * 64);
+    };
+
+    struct Frag { bf16x8 a[MI], b[NI]; };
+    auto frag = [&](const u32x4* l, int s, Frag& f) {
+      const int ch = 2 * h + s;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int r = wm * 128 + mi * 32 + (lane & 31);
+        f.a[mi] = __builtin_bit_cast(bf16x8, l[r * 4 + (ch ^ swz4(r))]);
+      }
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int r = wn * 128 + ni * 32 + (lane & 31);
+        f.b[ni] = __builtin_bit_cast(bf16x8, l[BM * 4 + r * 4 + (ch ^ swz4(r))]);
+      }
+    };
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
+    // B first: lane l holds output row l % 32 and, per group of four
+    // registers, four consecutive columns
+    auto mfma = [&](const Frag& f) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
+    };
+
+    if (tile != xcd * chunk + wg_in_xcd) {
+      // every wave is done with the previous tile's stages
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    issue(I0{}, 0);
+    issue(I1{}, 1);
+    issue(I2{}, 2);
+    issue(I3{}, 3);
+    wait_barrier<3 * PER_SLAB, true>();   // slab 0 landed
+    if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = m0 + wm * 128 + mi * 32 + (lane & 31);
+        const bool ok = row < M && er[mi] >= 0 && er[mi] < g.e_nrows;
+        sl[mi] = ok ? g.slot[er[mi]] : -1;
+      }
+    }
+    Frag f0, f1;
+    frag(S0, 0, f0);
+
+    // slab kt in stage kt % 5: issue slab kt + 4 into the stage of slab
+    // kt - 1 (free since the previous barrier), sub-step 0 with the reads of
+    // sub-step 1 spread over it, the barrier for slab kt + 1, then sub-step 1
+    // with the reads of slab kt + 1's first fragments
+    auto iter = [&](auto st, int kt, auto w, auto issue_next) {
+      constexpr int ST = decltype(st)::value;
+      using NX = std::integral_constant<int, (ST + 1) % 5>;
+      using PV = std::integral_constant<int, (ST + 4) % 5>;
+      constexpr bool ISS = decltype(issue_next)::value;
+      if constexpr (ISS) issue(PV{}, kt + 4);
+      frag(stage(st), 1, f1);
+      mfma(f0);
+      interleave_spread<MI * NI, MI + NI, ISS ? PER_SLAB : 0, 2>();
+      wait_barrier<decltype(w)::value, true>();   // slab kt + 1 landed
+      frag(stage(NX{}), 0, f0);                   // (a spare read after the last slab)
+      mfma(f1);
+      interleave_spread<MI * NI, MI + NI, 0, 2>();
+    };
+    using W3 = std::integral_constant<int, 3 * PER_SLAB>;
+    using W2 = std::integral_constant<int, 2 * PER_SLAB>;
+    using W1 = std::integral_constant<int, PER_SLAB>;
+    using W0 = std::integral_constant<int, 0>;
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    int kt = 0;                            // KT a multiple of 5
+    for (; kt + 5 < KT; kt += 5) {
+      iter(I0{}, kt, W3{}, T_{});
+      iter(I1{}, kt + 1, W3{}, T_{});
+      iter(I2{}, kt + 2, W3{}, T_{});
+      iter(I3{}, kt + 3, W3{}, T_{});
+      iter(I4{}, kt + 4, W3{}, T_{});
+    }
+    iter(I0{}, kt, W3{}, T_{});
+    iter(I1{}, kt + 1, W2{}, F_{});
+    iter(I2{}, kt + 2, W1{}, F_{});
+    iter(I3{}, kt + 3, W0{}, F_{});
+    iter(I4{}, kt + 4, W0{}, F_{});
+
+    // ---- epilogue, straight from the accumulators: lane l holds row
+    // mi * 32 + l % 32 of the wave block and, per group gq, the four
+    // consecutive columns ni * 32 + 8 gq + 4 (l / 32) + 0..3
+    {
+      const int rb = m0 + wm * 128, cb = n0 + wn * 128;
+      if constexpr (EPI == EPI_CACHE) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const int row = rb + mi * 32 + (lane & 31);
+          const int slot = sl[mi];
+          if (row >= M || slot < 0 || slot >= g.n_slots) continue;
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = cb + ni * 32 + 8 * gq + 4 * h;
+              if (col >= N) continue;
+              const bool isv = col >= g.nh;
+              uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc) + (int64_t)z * g.cache_bstride +
+                              (int64_t)slot * g.nh + (isv ? col - g.nh : col);
+              *(uint2*)dst = uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
+                                   pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
+            }
+        }
+        continue;                                  // next tile
+      }
+      uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.c_bstride;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = rb + mi * 32 + (lane & 31);
+        if (row >= M) continue;
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = cb + ni * 32 + 8 * gq + 4 * h;
+            if (col >= N) continue;
+            *(uint2*)(C + (int64_t)row * g.ldc + col) =
+                uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
+                      pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
+          }
+      }
+    }
+  }  // tiles
+}
+
+// Launch: one workgroup of 4 waves per CU (160 KB of LDS), capped by the
+// tile count and rounded up to whole XCDs. K % 160 == 0, N % 4 == 0, the
+// other requirements as gemm_launch's.
+template <int EPI>
+inline void gemm_quad_launch(const GemmArgs& g, int batch, hipStream_t s) {
+  const int tn = (g.N + 255) / 256;
+  const int tm = (g.M_max + 255) / 256;
+  const int64_t tiles = (int64_t)tn * tm * batch;
+  int grid = (int)(tiles < N_CU ? tiles : N_CU);
+  grid = (grid + 7) / 8 * 8;
+  gemm_quad_kernel<EPI><<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);
+}
+
+// bf16-output GEMM: 256 x 256 tiles from 1024 rows on when they give at
+// least one tile per CU (measured: 7782 rows of one 4096-wide layer, 496
+// tiles, run 15% faster than on 128 x 128 tiles), the 128-row kernel
+// otherwise. With the row count on the device the bound may be far above
+// it (546 of 4096 rows in the GPT-2-shape step: 72 busy 256 x 256 tiles
+// against 240 of 128 x 128; the whole fill measured 43 µs instead of 30),
+// so there the big tiles need two per CU at the bound.
+// The 256 x 256 tiles run on the 4-wave kernel of this file when K is a
+// multiple of 160 (and the output has no norm epilogue), on gemm_big.h's
+// 8-wave kernel otherwise (and always under gemm path 3).
+template <int EPI>
+inline void gemm_bf16_auto(const GemmArgs& g, int batch, hipStream_t s) {
+  const int64_t big = (int64_t)((g.N + 255) / 256) * ((g.M_max + 255) / 256) * batch;
+  const int path = river_host::gemm_path_override();
+  const bool auto_big = g.M_dev ? big >= 2 * N_CU : (g.M_max >= 1024 && big >= N_CU);
+  if (path == 2 || path == 3 || (path == 0 && auto_big)) {
+    if constexpr (EPI == EPI_BF16) {
+      if (path != 3 && g.K % 160 == 0) {
+        gemm_quad_launch<EPI>(g, batch, s);
+        return;
+      }
+    }
+    gemm_big_launch<EPI>(g, batch, s);
+  } else {
+    gemm_auto<EPI>(g, batch, s);
+  }
+}
+
+// The projection on dequantised weights (EPI_CACHE), on the same choice of
+// kernel by K and gemm path 3.
+inline void gemm_cache_launch(const GemmArgs& g, int batch, hipStream_t s) {
+  if (river_host::gemm_path_override() != 3 && g.K % 160 == 0) gemm_quad_launch<EPI_CACHE>(g, batch, s);
+  else gemm_big_launch<EPI_CACHE>(g, batch, s);
+}
+
+
+
+}  // namespace river

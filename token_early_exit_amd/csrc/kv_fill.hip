@@ -28,6 +28,7 @@
 #include "common.h"
 #include "gemm.h"
 #include "gemm_big.h"
+#include "gemm_quad.h"
 #include "w4gemm.h"
 
 namespace river {
@@ -328,7 +329,7 @@ static int proj_path(int m_max, bool dev_count, bool per_layer_rows, int d, int 
   const int path = gemm_path_override();
   *ks = 1;
   if (path != 1 && m_max > 64 && !per_layer_rows &&
-      (path == 2 || (!dev_count && dequant_wanted(m_max, N, nl))) && avail >= (size_t)nl * N * d * 2)
+      (path >= 2 || (!dev_count && dequant_wanted(m_max, N, nl))) && avail >= (size_t)nl * N * d * 2)
     return PROJ_DEQUANT;
   *ks = choose_ksplit(m_max, N, d, nl, avail);
   return *ks > 1 ? PROJ_SPLIT : PROJ_REGS;
@@ -462,7 +463,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
         if (st != RIVER_OK) return st;
         GemmArgs p = q;
         p.B = dq; p.ldb = d; p.b_bstride = (int64_t)q.N * d;
-        gemm_big_launch<EPI_CACHE>(p, nl, s);
+        gemm_cache_launch(p, nl, s);
         return check_launch("kv_fill projection (bf16)");
       }
       if (pp == PROJ_SPLIT) {
