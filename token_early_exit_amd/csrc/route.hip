@@ -610,6 +610,13 @@ using namespace river;
 // same at 8192 tokens)
 constexpr int ROUTE_WAVES = 8;
 
+// 32 tokens per workgroup (RT = 2) once 16-token workgroups would exceed
+// one per CU: every workgroup reads the whole router (1 MB at b = 128,
+// d = 4096) besides its tokens' states, so at 7782 tokens 487 workgroups of
+// 16 (two per CU on most CUs) read 2.5 MB per CU where 244 of 32 read 1.5;
+// up to 4096 tokens 16-token workgroups keep every CU busy with 1.25 MB.
+static bool route_two(int n) { return n > 16 * 256; }   // 256 CUs
+
 // the streaming path's conditions (launch_route takes it whenever they hold)
 static bool stream_ok(int n, int d, river_dtype dt, int b, int64_t ld_prev, int64_t ld_cur) {
   return dt == RIVER_BF16 && d % 256 == 0 && b <= 128 && (int64_t)n * ld_cur * 2 < ((int64_t)1 << 31) &&
@@ -632,7 +639,7 @@ river_status launch_route_scores(int n, int d, river_dtype dt, int64_t ld, int n
                        __builtin_inff(), __builtin_inff(), cos_out + (int64_t)c * n, prob_out + (int64_t)c * n,
                        mask_scratch + (int64_t)c * n, nullptr, nullptr, nullptr, 0, 0};
   // the same tile as launch_route at this n, so the same values
-  const bool two = n >= 8192;
+  const bool two = route_two(n);
   const int T = two ? 32 : 16;
   const dim3 grid((unsigned)((n + T - 1) / T), (unsigned)n_ck);
   const dim3 blk(64 * ROUTE_WAVES);
@@ -662,7 +669,7 @@ river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int6
     // W_down within 31 bits, gamma (if any) within its LDS copy
     const bool stream = w_down && stream_ok(n, d, dt, b, ld_prev, ld_cur);
     if (stream) {
-      const bool two = n >= 8192;
+      const bool two = route_two(n);
       const int T = two ? 32 : 16;
       const dim3 grid((n + T - 1) / T);
       const dim3 blk(64 * ROUTE_WAVES);
