@@ -665,11 +665,12 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-# the map GEMM's own code: the 256 x 256 kernel and its launch (gemm_big.h),
-# the scheduling helpers and argument block (gemm.h), the device helpers
+# the map GEMM's own code: the 4-wave 256 x 256 kernel and its launch
+# (gemm_quad.h), the 8-wave kernel it shares helpers with (gemm_big.h), the
+# scheduling helpers and argument block (gemm.h), the device helpers
 # (common.h)
-MAP_GEMM_SOURCES = ["token_early_exit_amd/csrc/gemm_big.h", "token_early_exit_amd/csrc/gemm.h",
-                    "token_early_exit_amd/csrc/common.h"]
+MAP_GEMM_SOURCES = ["token_early_exit_amd/csrc/gemm_quad.h", "token_early_exit_amd/csrc/gemm_big.h",
+                    "token_early_exit_amd/csrc/gemm.h", "token_early_exit_amd/csrc/common.h"]
 
 
 def measured_traffic(name, sources):
@@ -991,7 +992,7 @@ def main():
         return
     value = wl.m / (ms_step * 1e-3)
     ach = lc["map_flops_per_launch"] / (lc["map_gemm_ms"] * 1e-3) / 1e12
-    roof = {"kernel": "gemm_big_kernel<0> (the map GEMM: x_hat = X M^T for all 48 layers in one launch)",
+    roof = {"kernel": "gemm_quad_kernel<0> (the map GEMM: x_hat = X M^T for all 48 layers in one launch)",
             "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": ach / MFMA_BF16_PEAK_TFLOPS,
             "traffic": measured_traffic(f"map_gemm_long_context_{args.tokens}_traffic.json",
