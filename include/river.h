@@ -511,11 +511,11 @@ river_status river_debug_set_compact_path(int path);
  * for the map GEMM and, with room in the workspace and more than 64 rows,
  * the projection on dequantised weights; 1 and 2 also keep the map GEMM
  * from splitting its reduction at small row counts; 3 = as 2, with the
- * 256 x 256 tiles on the 8-wave kernel even where d % 160 == 0 would take
+ * 256 x 256 tiles on the 8-wave kernel even where d % 128 == 0 would take
  * the 4-wave one). Process-wide. The 128 and 256 tiles group the reduction
  * over d into MFMA steps differently, so their results agree to fp32
  * rounding, not bit for bit; the two 256 x 256 kernels (paths 2 and 3 at
- * d % 160 == 0) run the same MFMAs in the same order and agree bit for
+ * d % 128 == 0) run the same MFMAs in the same order and agree bit for
  * bit. */
 river_status river_debug_set_gemm_path(int path);
 

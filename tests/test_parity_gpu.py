@@ -419,15 +419,17 @@ def test_kv_fill_dequantised_projection(maps):
         assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-2 * b.abs().amax(dim=-1, keepdim=True))
 
 
+@pytest.mark.parametrize("d", [1280, 1024])
 @pytest.mark.parametrize("count_on_device", [True, False])
-def test_kv_fill_quad_tiles_equal_eight_wave_tiles(count_on_device):
-    """d = 1280 (a multiple of 160): the 256 x 256 tiles of the map GEMM and
-    of the projection on dequantised weights run on the 4-wave kernel
-    (gemm path 2) and on the 8-wave kernel (path 3). Both run the same MFMAs
-    in the same order, so the caches agree bit for bit; the 4-wave result is
-    within the K/V bar of the oracle. 300 of 640 rows (a ragged last tile),
-    three layers, the count on the device or on the host."""
-    cfg = get_config(1, d=1280, n_tokens=640, n_slots=700)
+def test_kv_fill_quad_tiles_equal_eight_wave_tiles(count_on_device, d):
+    """The 256 x 256 tiles of the map GEMM and of the projection on
+    dequantised weights run on the 4-wave kernels (gemm path 2: the ring of
+    five 32 KB units at d = 1280, a multiple of 320; two 64 KB stages at d =
+    1024) and on the 8-wave kernel (path 3). Both run the same MFMAs in the
+    same order, so the caches agree bit for bit; the 4-wave result is within
+    the K/V bar of the oracle. 300 of 640 rows (a ragged last tile), three
+    layers, the count on the device or on the host."""
+    cfg = get_config(1, d=d, n_tokens=640, n_slots=700)
     layers = [5, 6, 7]
     nl = len(layers)
     h = G.hidden_states(cfg, cfg.n_tokens, [4])[4].to(DEV)
