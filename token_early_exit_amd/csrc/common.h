@@ -119,6 +119,10 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // ------------------------------------------------------- buffer loads
+// a buffer offset past every resource here (they span under 2^31 bytes):
+// the load returns zeros and fetches nothing
+constexpr uint32_t BUF_OOB = 0x80000000u;
+
 // dword 3 of a raw (untyped) buffer resource on gfx9-family GPUs: 32-bit
 // data format, no swizzle, no index stride
 constexpr int RSRC_WORD3 = 0x00020000;

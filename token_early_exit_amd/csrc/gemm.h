@@ -215,8 +215,9 @@ __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, i
       const int p = (i * 4 + wave) * 64 + lane;
       const int r = p >> 3, c = (p & 7) ^ swz(r);
       int src = a_src_row[i];
-      if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
-      a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2) + k_off;
+      if (src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
+      // rows past the count read zeros without a fetch (not stored either)
+      a_off[i] = m0 + r >= M ? BUF_OOB : (uint32_t)(((int64_t)src * g.lda + c * 8) * 2) + k_off;
     }
     const void* b_buf = g.B + (int64_t)z * g.b_bstride;
     const int b_bytes = (int)(N * g.ldb * 2);                   // rows past N read zeros

@@ -113,8 +113,9 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(GemmArgs g, int tiles_n, 
       const int p = (i * 8 + wave) * 64 + lane;
       const int r = p >> 2, c = (p & 3) ^ swz4(r);
       int src = a_src_row[i];
-      if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
-      a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
+      if (src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
+      // rows past the count read zeros without a fetch (not stored either)
+      a_off[i] = m0 + r >= M ? BUF_OOB : (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
     }
     const void* b_buf = g.B + (int64_t)z * g.b_bstride;
     const int b_bytes = (int)(N * g.ldb * 2);                   // rows past N read zeros

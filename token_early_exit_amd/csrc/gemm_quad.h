@@ -103,8 +103,9 @@ struct QuadTile {
       const int c = (lane & 7) ^ swz(r);
       const int t = m0 + r;
       int src = g.a_rows ? g.a_rows[t < M ? t : M - 1] : t;
-      if (t >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
-      a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
+      if (src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
+      // rows past the count read zeros without a fetch (not stored either)
+      a_off[i] = t >= M ? BUF_OOB : (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
     }
     b_buf = g.B + (int64_t)z * g.b_bstride;
     b_bytes = (int)(N * g.ldb * 2);                           // rows past N read zeros

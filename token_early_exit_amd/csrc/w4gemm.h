@@ -263,8 +263,9 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
         const int p = (i * NW + wave) * 64 + lane;
         const int r = p >> 3, c = (p & 7) ^ swz(r);
         int src = a_src_row[i];
-        if (m0 + r >= M || src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
-        a_off[i] = (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
+        if (src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
+        // rows past the count read zeros without a fetch (not stored either)
+        a_off[i] = m0 + r >= M ? BUF_OOB : (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
       }
       // B: this wave's CW columns n0 + CW wave .. lie wholly in the K or the V
       // half (nh % 64 == 0): one resource per operand for the layer's
