@@ -375,6 +375,43 @@ def test_kv_fill_map_gemm_tiles(gemm_path):
         assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-2 * b.abs().amax(dim=-1, keepdim=True))
 
 
+@pytest.mark.parametrize("count", ["device", "host"])
+def test_kv_fill_map_narrow_tiles_equal_128_tiles(count):
+    """A row bound of at most 256 (a decode step's exits) runs the map GEMM
+    on 32-row tiles with an 8-slab ring (automatic); it takes the reduction
+    in the same order as the 128-row tiles (gemm path 1), so the caches agree
+    bit for bit, and every filled row is within the K/V bar. d = 2048, six
+    layers; 13 rows under a bound of 256 with the count on the device, or 200
+    rows (ragged 32-row tiles) with the count on the host."""
+    cfg = get_config(1, d=2048, n_tokens=256, n_slots=300)
+    layers = [3, 4, 5, 6, 7, 8]
+    h = G.hidden_states(cfg, cfg.n_tokens, [2])[2].to(DEV)
+    g = torch.Generator().manual_seed(2048)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    maps = G.near_identity_maps(cfg, len(layers), scale=0.5).to(DEV)
+    if count == "device":
+        sel = torch.sort(torch.randperm(cfg.n_tokens, generator=g)[:13]).values.to(torch.int32)
+        rows = torch.full((cfg.n_tokens,), -1, dtype=torch.int32)
+        rows[:13] = sel
+        m_max, m_dev = cfg.n_tokens, torch.tensor([13], dtype=torch.int32, device=DEV)
+    else:
+        sel = torch.sort(torch.randperm(cfg.n_tokens, generator=g)[:200]).values.to(torch.int32)
+        rows, m_max, m_dev = sel, 200, None
+    out = {}
+    try:
+        for p in (0, 1):
+            tee.river_debug_set_gemm_path(p)
+            out[p] = fill_gpu(cfg, h, slot, wk, wv, len(layers), row_idx=rows.to(DEV), m_dev=m_dev,
+                              m_max=m_max, maps=maps)
+    finally:
+        tee.river_debug_set_gemm_path(0)
+    for a, b in zip(out[0], out[1]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    kc, vc = out[0]
+    check_fill(cfg, kc, vc, h, sel.numpy(), slot, maps, wk, wv)
+
+
 @pytest.mark.parametrize("maps", [False, True])
 def test_kv_fill_dequantised_projection(maps):
     """The projection as a 256 x 256 bf16 GEMM on weights dequantised into

@@ -29,6 +29,7 @@
 #include "gemm.h"
 #include "gemm_big.h"
 #include "gemm_quad.h"
+#include "gemm_narrow.h"
 #include "w4gemm.h"
 
 namespace river {
@@ -528,6 +529,10 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
           gemm_part_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(p, nl);
           st = check_launch("kv_fill map sum");
         }
+      } else if (gemm_path_override() == 0 && m_max <= 256 && gemm_narrow_ok(p)) {
+        // decode-sized row bound: 32-row tiles with eight slabs of maps in flight
+        gemm_narrow_launch(p, nl, s);
+        st = check_launch("kv_fill map narrow");
       } else {
         gemm_bf16_auto<EPI_BF16>(p, nl, s);
         st = check_launch("kv_fill map");

@@ -8,12 +8,17 @@
 // Workgroup tile BM x 256, NW waves (8 by default: two per SIMD, which hide
 // each other's latencies). Wave w owns the CW = 256 / NW output columns
 // [CW w, CW w + CW) for all BM rows: BM/32 x CW/32 accumulators of 32x32 fed
-// by v_mfma_f32_32x32x16_bf16. Only A goes through LDS (buffer loads straight
-// into LDS, a 4-stage ring, three K-slabs ahead); every wave reads the same
-// A fragments. Each lane fetches the 16 bytes of int4 weights it needs per
-// slab (staged through LDS with the A tile, three slabs ahead) and
-// dequantizes them in registers into the MFMA's B operand: no dequantized
-// tile goes through LDS, and each weight is dequantized once per workgroup.
+// by v_mfma_f32_32x32x16_bf16. Only A goes through LDS as a tile (buffer
+// loads straight into LDS, a 4-stage ring, three K-slabs ahead); every wave
+// reads the same A fragments. The int4 weights of four slabs at a time
+// (128 contiguous bytes of each column, so every wave load covers 8 columns
+// x 128 bytes, whole lines) go into one of two LDS buffers, three slabs
+// ahead of their first use; each lane takes from there the 16 bytes it needs
+// per slab and dequantizes them in registers into the MFMA's B operand: no
+// dequantized tile goes through LDS, and each weight is dequantized once per
+// workgroup. (Loading each slab's 32 bytes per column separately touched 32
+// lines per wave load; the L1 then stalled the address unit on 35 of its 52
+// cycles per load.)
 //
 // The reduction index inside a 64-wide slab is permuted so that one 16-byte
 // load per lane and column fragment covers the whole slab: in sub-step s
@@ -166,19 +171,19 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
   constexpr int CW = 32 * NI;            // columns per wave
   constexpr int AD = BM * 8 / (64 * NW); // A DMA instructions per thread per slab
   constexpr int SZB = SZ_BF16 ? 2 : 4;
-  // vector-memory instructions per thread per slab: A DMAs, NI weight loads,
-  // one scale and one zero load
-  constexpr int PER_SLAB = AD + NI + 2;
+  // vector-memory instructions per thread per slab: A DMAs, one scale and
+  // one zero load; per four slabs WQD weight loads (8 columns x 128 bytes)
+  constexpr int PER_SLAB = AD + 2;
+  constexpr int WQD = CW / 8;
   // one LDS array per pipeline stage: the A tile (BM x 64 bf16, swizzled),
-  // then per wave and column fragment the lanes' 16 weight bytes (64 x 16 B)
-  // and per wave the scale and zero words of 64 columns from its first one
-  // (2 x 64 x 4 B).
-  // The weights pass through LDS only so that their loads are waited for
-  // like the A tile's.
-  constexpr int QOFF = BM * 8;                    // in 16-byte units
-  constexpr int ZOFF = QOFF + NW * NI * 64;
+  // then per wave the scale and zero words of 64 columns from its first one
+  // (2 x 64 x 4 B)
+  constexpr int ZOFF = BM * 8;                    // in 16-byte units
   constexpr int SSZ = ZOFF + NW * 32;
   __shared__ u32x4 S0[SSZ], S1[SSZ], S2[SSZ], S3[SSZ];
+  // the weights of four slabs: column c (0..255 of the tile) holds its 128
+  // bytes at chunks 8 c + (q ^ swz(c)), q = 2 (slab % 4) + half; two buffers
+  __shared__ u32x4 WQ[2 * BN * 8];
   // LAYER: per-row sums of squares of the tile's input rows, reduced by the
   // whole workgroup in the epilogue (RG threads per row, RCH 16-byte chunks
   // of partial sums per thread and round)
@@ -282,9 +287,9 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
       const void* s_buf = (const char*)(which ? g.s[1] : g.s[0]) + z * szs * SZB;
       const void* z_buf = (const char*)(which ? g.zp[1] : g.zp[0]) + z * szs * SZB;
       const int sz_bytes = nh * gpr * SZB;
-      uint32_t q_off[NI];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni) q_off[ni] = (uint32_t)((hc0 + 32 * ni + (lane & 31)) * (K / 2) + h * 16);
+      // weight load m of this wave (per four slabs): wave columns 8 m + l / 8,
+      // 16-byte chunk (l % 8) ^ swz(column) of their 128-byte run
+      uint32_t wq_off[WQD];
       [[maybe_unused]] const uint32_t sz_off_plain = (uint32_t)((hc0 + lane) * gpr * SZB);
       // LAYER with rotary embedding: output channel of wave column j (0..31)
       // is hb + o0 + j for j < 16 and hb + hd/2 + o0 + j - 16 otherwise
@@ -304,17 +309,27 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
         }
         return hc0 + j;
       };
-      if constexpr (LAYER) q_off[0] = (uint32_t)(chan(lane & 31) * (K / 2) + h * 16);
+#pragma unroll
+      for (int m = 0; m < WQD; ++m) {
+        const int jc = 8 * m + (lane >> 3);                   // wave column
+        const int cl = CW * wave + jc;                        // tile column
+        wq_off[m] = (uint32_t)(chan(jc) * (K / 2) + ((lane & 7) ^ swz(cl)) * 16);
+      }
       const uint32_t sz_off = LAYER ? (uint32_t)(chan(lane & 31) * gpr * SZB) : sz_off_plain;
 
-      // every load of K-slab j into LDS stage ST
+      // the weights of slabs j .. j + 3 (j - j0 a multiple of 4) into buffer
+      // ((j - j0) / 4) % 2
+      auto issue_w = [&](int j) {
+        u32x4* lw = WQ + (((j - j0) >> 2) & 1) * (BN * 8);
+#pragma unroll
+        for (int m = 0; m < WQD; ++m) buf_lds<16>(q_buf, q_bytes, wq_off[m], j * 32, lw + (wave * WQD + m) * 64);
+      };
+      // every load of K-slab j into LDS stage ST (and, for the first slab of
+      // four, their weights after them)
       auto issue = [&](auto st, int j) {
         u32x4* la = stage(st);
 #pragma unroll
         for (int i = 0; i < AD; ++i) buf_lds<16>(a_buf, a_bytes, a_off[i], j * 128, la + (i * NW + wave) * 64);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          buf_lds<16>(q_buf, q_bytes, q_off[ni], j * 32, la + QOFF + (wave * NI + ni) * 64);
         const int gi = j / slabs_per_group;   // uniform
         // bf16 scale / zero: the aligned word holding group gi (rows hold an
         // even number of groups, so the word stays inside the row)
@@ -322,6 +337,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
         uint32_t* lz = (uint32_t*)(la + ZOFF) + wave * 128;
         buf_lds<4>(s_buf, sz_bytes, sz_off, go, lz);
         buf_lds<4>(z_buf, sz_bytes, sz_off, go, lz + 64);
+        if (((j - j0) & 3) == 0) issue_w(j);   // uniform
       };
       // this lane's weights of slab j (held in stage la) from LDS
       struct BRegs { u32x4 q[NI]; uint32_t s[NI], zz[NI]; };
@@ -330,7 +346,9 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
         const int sh = SZ_BF16 ? ((j / slabs_per_group) & 1) * 16 : 0;
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          b.q[ni] = la[QOFF + (wave * NI + ni) * 64 + lane];
+          const int cl = CW * wave + 32 * ni + (lane & 31);
+          const int q = 2 * ((j - j0) & 3) + h;
+          b.q[ni] = WQ[(((j - j0) >> 2) & 1) * (BN * 8) + cl * 8 + (q ^ swz(cl))];
           const uint32_t sw = lz[ni * 32 + (lane & 31)];
           const uint32_t zw = lz[64 + ni * 32 + (lane & 31)];
           b.s[ni] = SZ_BF16 ? (sw >> sh) & 0xFFFFu : sw;
@@ -452,7 +470,10 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
         mfma(f1);
         interleave<1, MA * NI, MA + 3 * NI, 0>();
       };
+      // at the barrier of slab kt + 1 the loads of slabs kt + 2 and kt + 3
+      // may be outstanding, with the weights issued after slab kt + 4 m's
       using W2 = std::integral_constant<int, 2 * PER_SLAB>;
+      using W2Q = std::integral_constant<int, 2 * PER_SLAB + WQD>;
       using W1 = std::integral_constant<int, PER_SLAB>;
       using W0 = std::integral_constant<int, 0>;
       using T_ = std::true_type;
@@ -460,8 +481,8 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
       int kt = 0;
       for (; kt + 4 < KT; kt += 4) {       // every slab here issues slab kt + 3
         iter(I0{}, bA, bB, kt, W2{}, T_{});
-        iter(I1{}, bB, bA, kt + 1, W2{}, T_{});
-        iter(I2{}, bA, bB, kt + 2, W2{}, T_{});
+        iter(I1{}, bB, bA, kt + 1, W2Q{}, T_{});
+        iter(I2{}, bA, bB, kt + 2, W2Q{}, T_{});
         iter(I3{}, bB, bA, kt + 3, W2{}, T_{});
       }
       // last four slabs: only the first still has a slab to issue
@@ -548,7 +569,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
   }
 }
 
-// Launch over a batch of `batch` layers: one workgroup per CU (112 KB of
+// Launch over a batch of `batch` layers: one workgroup per CU (144 KB of
 // LDS for BM = 128), capped by the tile count and rounded to whole XCDs.
 // W4_WAVES: 4 waves (64 columns each, one per SIMD) or 8 (32 columns each,
 // two per SIMD, which hide each other's latencies).
