@@ -378,11 +378,13 @@ def test_kv_fill_map_gemm_tiles(gemm_path):
 @pytest.mark.parametrize("count", ["device", "host"])
 def test_kv_fill_map_narrow_tiles_equal_128_tiles(count):
     """A row bound of at most 256 (a decode step's exits) runs the map GEMM
-    on 32-row tiles with an 8-slab ring (automatic); it takes the reduction
-    in the same order as the 128-row tiles (gemm path 1), so the caches agree
-    bit for bit, and every filled row is within the K/V bar. d = 2048, six
-    layers; 13 rows under a bound of 256 with the count on the device, or 200
-    rows (ragged 32-row tiles) with the count on the host."""
+    on 32-row tiles with an 8-slab ring (automatic). Each tile starts its
+    reduction at its own slab (tiles that run at the same time then read
+    different parts of the maps' rows), so its sums run in another order than
+    the 128-row tiles' (gemm path 1): the caches agree to a few bf16 ulps,
+    and every filled row is within the K/V bar. d = 2048, six layers; 13 rows
+    under a bound of 256 with the count on the device, or 200 rows (ragged
+    32-row tiles) with the count on the host."""
     cfg = get_config(1, d=2048, n_tokens=256, n_slots=300)
     layers = [3, 4, 5, 6, 7, 8]
     h = G.hidden_states(cfg, cfg.n_tokens, [2])[2].to(DEV)
@@ -406,8 +408,10 @@ def test_kv_fill_map_narrow_tiles_equal_128_tiles(count):
                               m_max=m_max, maps=maps)
     finally:
         tee.river_debug_set_gemm_path(0)
+    s = slot[sel.long().to(DEV)].long()
     for a, b in zip(out[0], out[1]):
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        a, b = a[:, s].float(), b[:, s].float()
+        assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-3 * b.abs().amax(dim=-1, keepdim=True))
     kc, vc = out[0]
     check_fill(cfg, kc, vc, h, sel.numpy(), slot, maps, wk, wv)
 

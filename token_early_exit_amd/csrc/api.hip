@@ -286,13 +286,15 @@ river_status river_kv_fill_layer(int m_max, const int32_t* m_dev, int d, river_d
                          n_slots, workspace, ws_bytes, s);
 }
 
-river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
-                               const river_checkpoint* ck, int n_layers, const void* gamma,
-                               float eps, int b, river_rule rule, const river_w4* wk,
-                               const river_w4* wv, int n_kv_heads, int head_dim,
-                               const int32_t* slot, void* k_cache, void* v_cache, int64_t n_slots,
-                               int32_t* exit_layer, void* workspace, size_t ws_bytes,
-                               hipStream_t s) {
+// fork_ok: the step may run one checkpoint's fill on a second stream (made
+// on first use); the allocation-free entry point never does
+static river_status decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
+                                const river_checkpoint* ck, int n_layers, const void* gamma,
+                                float eps, int b, river_rule rule, const river_w4* wk,
+                                const river_w4* wv, int n_kv_heads, int head_dim,
+                                const int32_t* slot, void* k_cache, void* v_cache, int64_t n_slots,
+                                int32_t* exit_layer, void* workspace, size_t ws_bytes,
+                                hipStream_t s, bool fork_ok) {
   g_err[0] = 0;
   if (!dt_ok(dt)) return fail(RIVER_ERR_DTYPE, "decode_step: dtype %d is not RIVER_F32 or RIVER_BF16", (int)dt);
   if (n < 0 || n_ck < 0) return fail(RIVER_ERR_ARG, "decode_step: negative size");
@@ -337,7 +339,19 @@ river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_c
     if (st != RIVER_OK) return st;
   }
   return launch_decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads,
-                            head_dim, slot, k_cache, v_cache, n_slots, exit_layer, workspace, ws_bytes, s);
+                            head_dim, slot, k_cache, v_cache, n_slots, exit_layer, workspace, ws_bytes, s,
+                            fork_ok);
+}
+
+river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
+                               const river_checkpoint* ck, int n_layers, const void* gamma,
+                               float eps, int b, river_rule rule, const river_w4* wk,
+                               const river_w4* wv, int n_kv_heads, int head_dim,
+                               const int32_t* slot, void* k_cache, void* v_cache, int64_t n_slots,
+                               int32_t* exit_layer, void* workspace, size_t ws_bytes,
+                               hipStream_t s) {
+  return decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads, head_dim, slot,
+                     k_cache, v_cache, n_slots, exit_layer, workspace, ws_bytes, s, true);
 }
 
 river_status river_decode_step_static(int n, int d, river_dtype dt, int64_t ld, int n_ck,
@@ -348,8 +362,8 @@ river_status river_decode_step_static(int n, int d, river_dtype dt, int64_t ld, 
                                       int64_t n_slots, int32_t* exit_layer, hipStream_t s) {
   g_err[0] = 0;
   if (n <= 0 || d < 8 || n_layers < 2 || n_ck < 0 || n_kv_heads < 1 || head_dim < 1 || (n_ck > 0 && !ck))
-    return river_decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads,
-                             head_dim, slot, k_cache, v_cache, n_slots, exit_layer, nullptr, 0, s);
+    return decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads, head_dim,
+                       slot, k_cache, v_cache, n_slots, exit_layer, nullptr, 0, s, false);
   void* p = nullptr;
   size_t cap = 0;
   river_status st = decode_static_scratch(&p, &cap);
@@ -365,8 +379,8 @@ river_status river_decode_step_static(int n, int d, river_dtype dt, int64_t ld, 
                 "scratch holds %zu", need, n, d, n_layers, cap);
   const size_t want = decode_fixed_workspace(n, d, dt, n_layers) + kv_fill_workspace(n, d, n_layers - 1, RIVER_BF16) +
                       decode_proj_workspace(n, d, n_kv_heads * head_dim, n_layers);
-  return river_decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads, head_dim,
-                           slot, k_cache, v_cache, n_slots, exit_layer, p, want < cap ? want : cap, s);
+  return decode_step(n, d, dt, ld, n_ck, ck, n_layers, gamma, eps, b, rule, wk, wv, n_kv_heads, head_dim, slot,
+                     k_cache, v_cache, n_slots, exit_layer, p, want < cap ? want : cap, s, false);
 }
 
 river_status river_router_fit(int n, int d, river_dtype dt, const void* h, int64_t ld_h,

@@ -33,6 +33,7 @@
 
 #include "common.h"
 #include "cosine.h"
+#include "gemm.h"
 
 namespace river {
 
@@ -241,6 +242,41 @@ river_status decode_static_scratch(void** ptr, size_t* bytes) {
   return RIVER_OK;
 }
 
+// The second stream of a decode step on each device, with the events of
+// its fork and join, made on the device's first step that forks (default
+// priority, non-blocking) and kept until the process ends. The mutex keeps
+// the fork-to-join launches of two host threads from interleaving.
+constexpr int DECODE_SIDE_CUS = 192;
+struct DecodeSide {
+  std::mutex mu;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+static river_status decode_side(DecodeSide** out) {
+  static std::mutex mu;
+  static DecodeSide sides[256];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RIVER_ERR_HIP, "decode_step: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 256) return fail(RIVER_ERR_UNSUPPORTED, "decode_step: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  DecodeSide& sd = sides[dev];
+  if (!sd.stream) {
+    hipStream_t st = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) return fail(RIVER_ERR_HIP, "decode_step: second stream: %s", hipGetErrorString(e));
+    sd.fork = f;
+    sd.join = j;
+    sd.stream = st;
+  }
+  *out = &sd;
+  return RIVER_OK;
+}
+
 size_t decode_fixed_workspace(int n, int d, river_dtype dt, int n_layers) {
   (void)dt;
   return a256(2 * (size_t)n) + a256((size_t)n) + 2 * a256(4 * (size_t)n) + 256 + compact_workspace(n) +
@@ -262,7 +298,7 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
                                 const river_w4* wv, int n_kv_heads, int head_dim,
                                 const int32_t* slot, void* k_cache, void* v_cache, int64_t n_slots,
                                 int32_t* exit_layer, void* workspace, size_t ws_bytes,
-                                hipStream_t s) {
+                                hipStream_t s, bool fork_ok) {
   char* w = (char*)workspace;
   uint8_t* alive = (uint8_t*)w;
   w += a256(2 * (size_t)n);
@@ -362,34 +398,87 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     decode_plan_kernel<<<1, DC_TOKENS, 0, s>>>(q);
     st = check_launch("decode_step plan");
     if (st != RIVER_OK) return st;
-    if (single) {
-      DecodeGather gq{};
-      gq.n = n; gq.row_bytes = (int)(d * esize(dt)); gq.ld_bytes = ld * (int64_t)esize(dt);
-      for (int c = 0; c < n_ck; ++c) gq.hc[c] = ck[c].h_cur;
-      gq.ck_of = ck_of; gq.x = xs;
-      decode_gather_kernel<<<n, WAVE, 0, s>>>(gq);
-      st = check_launch("decode_step gather");
-      if (st != RIVER_OK) return st;
-      const int e0 = ck[c0].layer;
-      st = launch_kv_fill(n, nullptr, d, dt, xs, d, n, ord, slot, n_layers - e0, nullptr, &k0, &v0, nullptr,
-                          n_kv_heads, head_dim, (char*)k_cache + e0 * cache_layer,
-                          (char*)v_cache + e0 * cache_layer, n_slots, fws, fws_bytes, s, m_layer);
-      if (st != RIVER_OK) return st;
-    }
+    // The fills left: the single fill, and one per other checkpoint. When
+    // there are at least two and the workspace holds, besides what the
+    // others take, everything the first checkpoint's fill (the most blocks,
+    // with maps its GEMM streams the most maps) would take with unlimited
+    // room, that fill runs on a second stream on DECODE_SIDE_CUS of the
+    // CUs while the rest run on s on the others: the two share no data
+    // (each token exits once) and their kernels make the same choices as
+    // in sequence, so the results are the same.
+    int side_c = -1, n_fills = single ? 1 : 0;
     for (int c = 0; c < n_ck; ++c) {
-      if (single && ((mask >> c) & 1u)) continue;   // in the single fill
+      if (single && ((mask >> c) & 1u)) continue;
+      if (side_c < 0) side_c = c;
+      ++n_fills;
+    }
+    size_t side_bytes = 0;
+    if (fork_ok && side_c >= 0 && n_fills >= 2 && decode_path_override() == 0) {
+      const size_t need_side =
+          kv_fill_full_workspace(n, d, n_out, n_layers - ck[side_c].layer, ck[side_c].maps != nullptr);
+      size_t need_rest = single ? kv_fill_full_workspace(n, d, n_out, n_layers - ck[c0].layer, false) : 0;
+      for (int c = side_c + 1; c < n_ck; ++c) {
+        if (single && ((mask >> c) & 1u)) continue;
+        const size_t b = kv_fill_full_workspace(n, d, n_out, n_layers - ck[c].layer, ck[c].maps != nullptr);
+        need_rest = b > need_rest ? b : need_rest;
+      }
+      if (need_side + need_rest <= fws_bytes) side_bytes = align_up(need_side, 256);
+    }
+    DecodeSide* side = nullptr;
+    std::unique_lock<std::mutex> side_lock;
+    if (side_bytes) {
+      st = decode_side(&side);
+      if (st != RIVER_OK) return st;
+      side_lock = std::unique_lock<std::mutex>(side->mu);
+      hipError_t e = hipEventRecord(side->fork, s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+      if (e != hipSuccess) return fail(RIVER_ERR_HIP, "decode_step: fork: %s", hipGetErrorString(e));
+    }
+    auto fill_ck = [&](int c, void* ws, size_t wsb, hipStream_t on) -> river_status {
       const river_checkpoint& k = ck[c];
       const int e = k.layer;
       river_w4 k4, v4;
       decode_layer_offset(*wk, e, n_out, d, &k4);
       decode_layer_offset(*wv, e, n_out, d, &v4);
-      st = launch_kv_fill(n, q.counts + c * 64 + 1, d, dt, k.h_cur, ld, n, q.exit_idx + (size_t)c * q.idx_stride,
-                          slot, n_layers - e, k.maps, &k4, &v4, nullptr, n_kv_heads, head_dim,
-                          (char*)k_cache + e * cache_layer, (char*)v_cache + e * cache_layer, n_slots, fws,
-                          fws_bytes, s);
-      if (st != RIVER_OK) return st;
+      return launch_kv_fill(n, q.counts + c * 64 + 1, d, dt, k.h_cur, ld, n, q.exit_idx + (size_t)c * q.idx_stride,
+                            slot, n_layers - e, k.maps, &k4, &v4, nullptr, n_kv_heads, head_dim,
+                            (char*)k_cache + e * cache_layer, (char*)v_cache + e * cache_layer, n_slots, ws,
+                            wsb, on);
+    };
+    if (side_bytes) {
+      CuBudget budget(DECODE_SIDE_CUS);
+      st = fill_ck(side_c, fws, side_bytes, side->stream);
     }
-    return RIVER_OK;
+    void* rws = (char*)fws + side_bytes;
+    const size_t rws_bytes = fws_bytes - side_bytes;
+    if (st == RIVER_OK) {
+      CuBudget budget(side_bytes ? N_CU - DECODE_SIDE_CUS : N_CU);
+      if (single) {
+        DecodeGather gq{};
+        gq.n = n; gq.row_bytes = (int)(d * esize(dt)); gq.ld_bytes = ld * (int64_t)esize(dt);
+        for (int c = 0; c < n_ck; ++c) gq.hc[c] = ck[c].h_cur;
+        gq.ck_of = ck_of; gq.x = xs;
+        decode_gather_kernel<<<n, WAVE, 0, s>>>(gq);
+        st = check_launch("decode_step gather");
+        if (st == RIVER_OK) {
+          const int e0 = ck[c0].layer;
+          st = launch_kv_fill(n, nullptr, d, dt, xs, d, n, ord, slot, n_layers - e0, nullptr, &k0, &v0, nullptr,
+                              n_kv_heads, head_dim, (char*)k_cache + e0 * cache_layer,
+                              (char*)v_cache + e0 * cache_layer, n_slots, rws, rws_bytes, s, m_layer);
+        }
+      }
+      for (int c = 0; c < n_ck && st == RIVER_OK; ++c) {
+        if ((single && ((mask >> c) & 1u)) || (side_bytes && c == side_c)) continue;
+        st = fill_ck(c, rws, rws_bytes, s);
+      }
+    }
+    if (side_bytes) {
+      // join, also after a failed launch, so that a capture of s stays whole
+      hipError_t e = hipEventRecord(side->join, side->stream);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+      if (e != hipSuccess && st == RIVER_OK) st = fail(RIVER_ERR_HIP, "decode_step: join: %s", hipGetErrorString(e));
+    }
+    return st;
   }
 
   decode_init_kernel<<<(n + 255) / 256, 256, 0, s>>>(n, alive, exit_layer, n_layers);

@@ -132,6 +132,27 @@ __device__ __forceinline__ void interleave_spread() {
 
 constexpr int N_CU = 256;
 
+// CUs that one persistent launch may occupy: all of them, unless a caller
+// that runs two launch sequences side by side on two streams narrows it for
+// one of them (CuBudget, host side), so that neither waits for the other's
+// workgroups to leave a CU. A multiple of 8 (whole XCDs).
+inline int& launch_cu_budget() {
+  static thread_local int n = N_CU;
+  return n;
+}
+struct CuBudget {
+  int prev;
+  explicit CuBudget(int n) : prev(launch_cu_budget()) { launch_cu_budget() = n; }
+  ~CuBudget() { launch_cu_budget() = prev; }
+};
+// workgroups of a persistent launch over `tiles` tiles: one per CU of the
+// budget at most, rounded up to whole XCDs
+inline int persistent_grid(int64_t tiles) {
+  const int cus = launch_cu_budget();
+  const int grid = (int)(tiles < cus ? tiles : cus);
+  return (grid + 7) / 8 * 8;
+}
+
 template <int BM, int EPI>
 __global__ __launch_bounds__(256) void gemm_nt_kernel(GemmArgs g, int tiles_n, int batch) {
   static_assert(EPI == EPI_BF16 || EPI == EPI_F32 || EPI == EPI_BF16N || EPI == EPI_PART,
@@ -407,8 +428,7 @@ inline void gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 127) / 128;
   const int tm = (g.M_max + BM - 1) / BM;
   const int64_t tiles = (int64_t)tn * tm * batch * (EPI == EPI_PART ? g.ksplit : 1);
-  int grid = (int)(tiles < N_CU ? tiles : N_CU);
-  grid = (grid + 7) / 8 * 8;
+  const int grid = persistent_grid(tiles);
   gemm_nt_kernel<BM, EPI><<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);
 }
 

@@ -304,8 +304,7 @@ inline void gemm_big_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 255) / 256;
   const int tm = (g.M_max + 255) / 256;
   const int64_t tiles = (int64_t)tn * tm * batch;
-  int grid = (int)(tiles < N_CU ? tiles : N_CU);
-  grid = (grid + 7) / 8 * 8;
+  const int grid = persistent_grid(tiles);
   gemm_big_kernel<EPI><<<dim3(grid, 1), 512, 0, s>>>(g, tn, batch);
 }
 

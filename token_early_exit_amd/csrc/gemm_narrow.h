@@ -14,8 +14,15 @@
 // accumulator on v_mfma_f32_32x32x16_bf16, B first (lane l holds output
 // row l % 32 and, per group of four registers, four consecutive columns).
 // Sub-step s of a slab takes logical 16-byte chunk 4 h + s of each row, as
-// gemm.h does, so the sums run in the same order and the results are
-// bit-identical to gemm_nt_kernel's.
+// gemm.h does.
+//
+// Each tile starts its walk over K at its own slab, (37 tile) mod K/64, and
+// wraps around. All CUs start together and advance at about the same pace,
+// so with a common start every load in flight on the chip would sit at the
+// same 128-byte offset of an 8 KB map row; measured on a pure read of this
+// pattern (21 maps of 4096^2) that reaches 4.1-4.8 TB/s, with staggered
+// starts 5.7-6.1 (the GEMM: 129-135 -> 121-126 us). The sums then run in
+// another order than gemm_nt_kernel's: the results agree to rounding.
 //
 // Loads: every wave load covers 8 rows x 128 contiguous bytes (8 lanes per
 // row); chunk p of an operand block holds logical chunk (p % 8) ^ swz(row)
@@ -84,8 +91,11 @@ __global__ __launch_bounds__(256, 1) void gemm_narrow_kernel(GemmArgs g, int til
       const int r = p >> 3, c = (p & 7) ^ swz(r);
       b_off[i] = (uint32_t)(((int64_t)(n0 + r) * g.ldb + c * 8) * 2);
     }
-    auto issue = [&](int st, int j) {
+    // the tile's k-th slab is slab (k + j0) mod KT of the operands
+    const int j0 = (tile * 37) % KT;
+    auto issue = [&](int st, int k) {
       u32x4* l = L + st * SSZ;
+      const int j = k + j0 < KT ? k + j0 : k + j0 - KT;
       buf_lds<16>(a_buf, a_bytes, a_off, j * 128, l + wave * 64);
 #pragma unroll
       for (int i = 0; i < BD; ++i) buf_lds<16>(b_buf, b_bytes, b_off[i], j * 128, l + BM * 8 + (i * 4 + wave) * 64);
@@ -177,8 +187,7 @@ inline void gemm_narrow_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + NARROW_BN - 1) / NARROW_BN;
   const int tm = (g.M_max + NARROW_BM - 1) / NARROW_BM;
   const int64_t tiles = (int64_t)tn * tm * batch;
-  int grid = (int)(tiles < N_CU ? tiles : N_CU);
-  grid = (grid + 7) / 8 * 8;
+  const int grid = persistent_grid(tiles);
   gemm_narrow_kernel<<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);
 }
 

@@ -494,8 +494,7 @@ inline void gemm_quad_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 255) / 256;
   const int tm = (g.M_max + 255) / 256;
   const int64_t tiles = (int64_t)tn * tm * batch;
-  int grid = (int)(tiles < N_CU ? tiles : N_CU);
-  grid = (grid + 7) / 8 * 8;
+  const int grid = persistent_grid(tiles);
   if (g.K % 320 == 0) gemm_quad_kernel<EPI><<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);
   else gemm_quad2_kernel<EPI><<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);
 }

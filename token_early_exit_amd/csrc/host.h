@@ -53,6 +53,7 @@ size_t kv_fill_workspace(int m_max, int d, int n_layers, river_dtype dt);
 size_t kv_fill_layer_workspace(int m_max, int d, int n_layers);
 size_t kv_fill_proj_workspace(int m_max, int d, int n_out, int n_layers);
 size_t decode_proj_workspace(int n, int d, int n_out, int n_layers);
+size_t kv_fill_full_workspace(int m_max, int d, int n_out, int nl, bool maps);
 void kv_fill_plan(int m_max, bool dev_count, int d, int nh, int n_layers, size_t ws_bytes, int* chunk,
                   int* path, int* ks);
 river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
@@ -82,7 +83,7 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
                                 const river_w4* wv, int n_kv_heads, int head_dim,
                                 const int32_t* slot, void* k_cache, void* v_cache, int64_t n_slots,
                                 int32_t* exit_layer, void* workspace, size_t ws_bytes,
-                                hipStream_t s);
+                                hipStream_t s, bool fork_ok);
 
 size_t calib_workspace(int n, int d, int b, int batch, int epochs);
 river_status launch_router_fit(int n, int d, river_dtype dt, const void* h, int64_t ld_h,

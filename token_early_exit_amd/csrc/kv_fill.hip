@@ -361,6 +361,20 @@ static int fill_chunk(int m_max, bool dev_count, int d, int nh, int n_layers, si
   return chunk;
 }
 
+// The workspace from which a fill whose row count lives on the device (a
+// decode step's) makes the choices it would make with unlimited room: the
+// maps' outputs of all nl layers in one chunk, and the largest split
+// reduction its map GEMM or projection would take.
+size_t kv_fill_full_workspace(int m_max, int d, int n_out, int nl, bool maps) {
+  if (m_max <= 0 || nl <= 0) return 0;
+  const int kp = choose_ksplit(m_max, 2 * n_out, d, nl, SIZE_MAX);
+  size_t split = kp > 1 ? (size_t)kp * nl * m_max * 2 * n_out * 4 : 0;
+  if (!maps) return align_up(split, 256);
+  const int km = choose_map_ksplit(m_max, d, nl, SIZE_MAX);
+  const size_t ms = km > 1 ? (size_t)km * nl * m_max * d * 4 : 0;
+  return (size_t)nl * layer_xhat_bytes(m_max, d) + align_up(ms > split ? ms : split, 256);
+}
+
 // the split space any fill of a decode step may use: blocks e + 1 .. L for a
 // checkpoint e, 1 to n_layers - 1 layers of at most n rows each
 size_t decode_proj_workspace(int n, int d, int n_out, int n_layers) {

@@ -620,8 +620,7 @@ inline void w4_gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 255) / 256;
   const int tm = (g.M_max + BM - 1) / BM;
   const int64_t tiles = (int64_t)tn * tm * batch * (EPI == EPI_PART ? g.ksplit : 1);
-  int grid = (int)(tiles < N_CU ? tiles : N_CU);
-  grid = (grid + 7) / 8 * 8;
+  const int grid = persistent_grid(tiles);
   if (g.sz_bf16[0]) w4_gemm_kernel<BM, EPI, true, W4_WAVES, LAYER><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
   else w4_gemm_kernel<BM, EPI, false, W4_WAVES, LAYER><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
 }
