@@ -460,6 +460,61 @@ def test_kv_fill_dequantised_projection(maps):
         assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-2 * b.abs().amax(dim=-1, keepdim=True))
 
 
+@pytest.mark.parametrize("rows,nl,split", [(13, 3, False), (13, 3, True), (0, 3, True), (32, 17, True),
+                                           (243, 1, True), (100, 12, True), (256, 2, False)])
+def test_kv_fill_deep_projection(rows, nl, split):
+    """Decode-sized projections (count on the device, bound 256, d = 4096,
+    2 x 1024 outputs, group 128, bf16 scales) take the deep pipeline when its
+    32-row tiles fit one round on the CUs, with a split over d chosen on the
+    device when the workspace has room; more rows take the 128-row int4
+    kernel (100 rows x 12 blocks: 384 tiles), each launch idle for the
+    other's counts. Without a split (no workspace, or 136 tiles at 32 rows x
+    17 blocks) the caches equal the 128-row kernel's (gemm path 1) bit for
+    bit; with one they agree to bf16 rounding. Every filled row is within the
+    K/V bar, the other slots keep their sentinel; 0 rows write nothing."""
+    cfg = get_config("3D")
+    layers = list(range(5, 5 + nl))
+    g = torch.Generator().manual_seed(4096 + rows)
+    h = G.hidden_states(cfg, cfg.n_tokens, [4])[4].to(DEV)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    sel = torch.sort(torch.randperm(cfg.n_tokens, generator=g)[:rows]).values.to(torch.int32)
+    idx = torch.full((cfg.n_tokens,), -1, dtype=torch.int32)
+    idx[:rows] = sel
+    idx = idx.to(DEV)
+    m_dev = torch.tensor([rows], dtype=torch.int32, device=DEV)
+    nh = cfg.n_kv_heads * cfg.head_dim
+    ws = None
+    if split:
+        ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, cfg.n_tokens, cfg.d, nh, 0, nl) + (16 << 20),
+                         dtype=torch.uint8, device=DEV)
+    out = {}
+    try:
+        for p in (0, 1):
+            tee.river_debug_set_gemm_path(p)
+            kc, vc = G.nan_cache(cfg, nl, device=DEV)
+            tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=cfg.n_tokens,
+                              m_dev=m_dev, row_idx=idx, workspace=ws if p == 0 else None)
+            torch.cuda.synchronize()
+            out[p] = (kc, vc)
+    finally:
+        tee.river_debug_set_gemm_path(0)
+    kc, vc = out[0]
+    if rows == 0:
+        assert torch.isnan(kc.float()).all() and torch.isnan(vc.float()).all()
+        return
+    pick = np.linspace(0, rows - 1, min(rows, 24)).astype(np.int64)
+    check_fill(cfg, kc, vc, h, sel.numpy(), slot, None, wk, wv, sample=pick)
+    s_ = slot[sel.long().to(DEV)].long()
+    bitwise = not split or (rows, nl) in ((32, 17), (100, 12))
+    for a, b in zip(out[0], out[1]):
+        if bitwise:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        else:
+            a, b = a[:, s_].float(), b[:, s_].float()
+            assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-3 * b.abs().amax(dim=-1, keepdim=True))
+
+
 @pytest.mark.parametrize("d", [1280, 1024])
 @pytest.mark.parametrize("count_on_device", [True, False])
 def test_kv_fill_quad_tiles_equal_eight_wave_tiles(count_on_device, d):

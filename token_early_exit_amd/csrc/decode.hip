@@ -117,41 +117,55 @@ __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
   bool alive = i < n;
   int el = p.n_layers, my_ck = -1;
   int off = 0;                                // exits of the single fill's checkpoints before c
-  for (int c = 0; c < p.n_ck; ++c) {
-    const bool sf = (p.single_mask >> c) & 1u;
-    const int64_t at = (int64_t)c * n + (i < n ? i : 0);
-    // the route's decision: cos > tau, and p > theta with a router
-    bool e = alive && p.cos[at] > p.tau[c] && (!p.prob || p.prob[at] > p.theta[c]);
-    if (p.batch_min) {
-      const int all = __syncthreads_and(!alive || e);
-      const int any = __syncthreads_or(alive);
-      e = alive && all && any;
-    }
-    if (e) el = p.layer[c];
-    const uint64_t b = __ballot(e);
-    if (lane == 0) wsum[wave] = __popcll(b);
-    __syncthreads();
-    int before = 0, total = 0;
+  // the scores of PF checkpoints are loaded together, so their latencies
+  // overlap instead of adding up checkpoint by checkpoint
+  constexpr int PF = 8;
+  for (int c0 = 0; c0 < p.n_ck; c0 += PF) {
+    float cv[PF], pv[PF];
 #pragma unroll
-    for (int w = 0; w < DC_TOKENS / WAVE; ++w) {
-      const int v = wsum[w];
-      before += w < wave ? v : 0;
-      total += v;
+    for (int k = 0; k < PF; ++k) {
+      const int64_t at = (int64_t)(c0 + k < p.n_ck ? c0 + k : 0) * n + (i < n ? i : 0);
+      cv[k] = p.cos[at];
+      pv[k] = p.prob ? p.prob[at] : 0.f;
     }
-    if (e) {
-      const int r = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
-      p.exit_idx[(int64_t)c * p.idx_stride + r] = i;
-      if (p.ord && sf) p.ord[off + r] = i;
-      if (sf) my_ck = c;
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+      const int c = c0 + k;
+      if (c >= p.n_ck) break;                   // uniform
+      const bool sf = (p.single_mask >> c) & 1u;
+      // the route's decision: cos > tau, and p > theta with a router
+      bool e = alive && cv[k] > p.tau[c] && (!p.prob || pv[k] > p.theta[c]);
+      if (p.batch_min) {
+        const int all = __syncthreads_and(!alive || e);
+        const int any = __syncthreads_or(alive);
+        e = alive && all && any;
+      }
+      if (e) el = p.layer[c];
+      const uint64_t b = __ballot(e);
+      if (lane == 0) wsum[wave] = __popcll(b);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < DC_TOKENS / WAVE; ++w) {
+        const int v = wsum[w];
+        before += w < wave ? v : 0;
+        total += v;
+      }
+      if (e) {
+        const int r = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        p.exit_idx[(int64_t)c * p.idx_stride + r] = i;
+        if (p.ord && sf) p.ord[off + r] = i;
+        if (sf) my_ck = c;
+      }
+      if (i == 0) {
+        p.counts[c * 64] = n - total;
+        p.counts[c * 64 + 1] = total;
+        tot[c] = total;
+      }
+      off += sf ? total : 0;
+      __syncthreads();                          // wsum is rewritten next round
+      alive = alive && !e;
     }
-    if (i == 0) {
-      p.counts[c * 64] = n - total;
-      p.counts[c * 64 + 1] = total;
-      tot[c] = total;
-    }
-    off += sf ? total : 0;
-    __syncthreads();                          // wsum is rewritten next round
-    alive = alive && !e;
   }
   if (i < n) {
     p.exit_layer[i] = el;

@@ -72,7 +72,22 @@ struct GemmArgs {
   const int32_t* pos; const float* rcos; const float* rsin; int64_t n_pos; int head_dim;
   // split reduction (EPI_PART): K is cut into ksplit parts of K / ksplit
   int ksplit; float* part;
+  // w4deep.h: bytes at part for partial sums whose parts the kernel
+  // chooses from the row count on the device (0: no split)
+  int64_t part_cap;
+  // two launches of the int4 projection that split the row counts on the
+  // device between them (w4deep.h): with gate = +1 a kernel runs only when
+  // ceil(rows / 32) * gate_units <= gate_cus (the deep pipeline's tiles fit
+  // one round), with gate = -1 only when not; gate = 0: always
+  int gate, gate_units, gate_cus;
 };
+
+// whether the kernel of a gated projection launch runs for `rows` rows
+__device__ __forceinline__ bool gate_open(const GemmArgs& g, int rows) {
+  if (!g.gate) return true;
+  const bool deep = (int64_t)((rows + 31) / 32) * g.gate_units <= g.gate_cus;
+  return g.gate > 0 ? deep : !deep;
+}
 
 __device__ __forceinline__ float load_sz(const void* p, int64_t i, int bf16) {
   return bf16 ? bf16_to_f32(((const uint16_t*)p)[i]) : ((const float*)p)[i];

@@ -31,6 +31,7 @@
 #include "gemm_quad.h"
 #include "gemm_narrow.h"
 #include "w4gemm.h"
+#include "w4deep.h"
 
 namespace river {
 
@@ -336,6 +337,17 @@ static int proj_path(int m_max, bool dev_count, bool per_layer_rows, int d, int 
   return *ks > 1 ? PROJ_SPLIT : PROJ_REGS;
 }
 
+// Decode-sized projections (a row bound of at most 256 with one count on
+// the device) take the deep pipeline (w4deep.h) when it takes the shape and
+// its tiles for the count fit one round on the CUs. At the 8B decode shape
+// (d = 4096, 2 x 1024 outputs) it measured 41 us against 50 for 13 rows x
+// 21 blocks and 24 against 57 (28 split) for 243 rows x 1 block, but 80
+// against 65 for 64 rows x 21 blocks (336 tiles): every 32-row tile
+// dequantises its weights again.
+static bool deep_wanted(int m_max, bool dev_count, const GemmArgs& q) {
+  return gemm_path_override() == 0 && dev_count && m_max <= 256 && w4_deep_ok(q);
+}
+
 // the workspace bytes of the dequantised weights of nl layers when the
 // automatic path projects on them (large row counts), else 0
 static size_t dequant_room(int m_max, bool dev_count, int d, int nh, int nl) {
@@ -369,8 +381,12 @@ size_t kv_fill_full_workspace(int m_max, int d, int n_out, int nl, bool maps) {
   if (m_max <= 0 || nl <= 0) return 0;
   const int kp = choose_ksplit(m_max, 2 * n_out, d, nl, SIZE_MAX);
   size_t split = kp > 1 ? (size_t)kp * nl * m_max * 2 * n_out * 4 : 0;
+  // the deep projection's split keeps every part's 32-row tile on a CU of
+  // its own: at most N_CU x 32 x 256 partial sums
+  if (m_max <= 256 && split < (size_t)N_CU * 32 * 256 * 4) split = (size_t)N_CU * 32 * 256 * 4;
   if (!maps) return align_up(split, 256);
-  const int km = choose_map_ksplit(m_max, d, nl, SIZE_MAX);
+  // (the map GEMM splits only where the 32-row tiles do not take it)
+  const int km = m_max <= 256 && d % 512 == 0 ? 1 : choose_map_ksplit(m_max, d, nl, SIZE_MAX);
   const size_t ms = km > 1 ? (size_t)km * nl * m_max * d * 4 : 0;
   return (size_t)nl * layer_xhat_bytes(m_max, d) + align_up(ms > split ? ms : split, 256);
 }
@@ -468,6 +484,29 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     q.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
     q.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
     if (!layer) {
+      if (deep_wanted(m_max, m_dev != nullptr && q.M_dev_z == nullptr, q)) {
+        // the deep pipeline when its 32-row tiles for the count on the
+        // device fit one round on the CUs, with the workspace left for the
+        // partial sums of a split it chooses on the device; otherwise the
+        // path below (each launch does nothing for the other's counts).
+        // Both choices take the whole chip's CUs, whatever the launch's
+        // budget, so that the results do not depend on it.
+        const int cus = N_CU;
+        GemmArgs qd = q;
+        qd.gate = 1;
+        qd.gate_units = ((q.N + 255) / 256) * nl;
+        qd.gate_cus = cus;
+        if (part_bytes >= (size_t)256 * q.N * 4) {
+          qd.part = (float*)part_ws;
+          qd.part_cap = (int64_t)part_bytes;
+        }
+        w4_deep_launch(qd, nl, s);
+        river_status st = check_launch("kv_fill projection (deep)");
+        if (st != RIVER_OK || (int64_t)((m_max + 31) / 32) * qd.gate_units <= cus) return st;
+        q.gate = -1;
+        q.gate_units = qd.gate_units;
+        q.gate_cus = cus;
+      }
       int ks;
       const int pp = proj_path(m_max, m_dev != nullptr, q.M_dev_z != nullptr, d, q.N, nl, part_bytes, &ks);
       if (pp == PROJ_DEQUANT) {
@@ -524,7 +563,11 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
       p.A = (const uint16_t*)h; p.lda = ld_h; p.a_bstride = 0; p.a_rows = row_idx; p.a_nrows = n_rows;
       p.B = (const uint16_t*)maps + (int64_t)l0 * d * d; p.ldb = d; p.b_bstride = (int64_t)d * d;
       p.C = xh; p.ldc = d; p.c_bstride = xb / 2;
-      const int mks = gamma || gemm_path_override() != 0 ? 1 : choose_map_ksplit(m_max, d, nl, part_bytes);
+      // a decode-sized row bound with the count on the device: 32-row tiles
+      // with eight slabs of maps in flight (at 243 rows x one block of
+      // 4096^2: 19 us, against 23 + 5.5 for the split below)
+      const bool narrow = !gamma && gemm_path_override() == 0 && m_dev && m_max <= 256 && gemm_narrow_ok(p);
+      const int mks = gamma || narrow || gemm_path_override() != 0 ? 1 : choose_map_ksplit(m_max, d, nl, part_bytes);
       if (gamma) {
         p.gamma = (const uint16_t*)gamma + (int64_t)l0 * d; p.gamma_bstride = d;
         p.ss = ss; p.ss_bstride = sb / 4;
@@ -543,7 +586,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
           gemm_part_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(p, nl);
           st = check_launch("kv_fill map sum");
         }
-      } else if (gemm_path_override() == 0 && m_max <= 256 && gemm_narrow_ok(p)) {
+      } else if (narrow || (gemm_path_override() == 0 && m_max <= 256 && gemm_narrow_ok(p))) {
         // decode-sized row bound: 32-row tiles with eight slabs of maps in flight
         gemm_narrow_launch(p, nl, s);
         st = check_launch("kv_fill map narrow");
