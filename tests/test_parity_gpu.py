@@ -461,17 +461,19 @@ def test_kv_fill_dequantised_projection(maps):
 
 
 @pytest.mark.parametrize("rows,nl,split", [(13, 3, False), (13, 3, True), (0, 3, True), (32, 17, True),
-                                           (243, 1, True), (100, 12, True), (256, 2, False)])
+                                           (243, 1, True), (100, 12, True), (256, 2, False), (13, 21, True)])
 def test_kv_fill_deep_projection(rows, nl, split):
     """Decode-sized projections (count on the device, bound 256, d = 4096,
     2 x 1024 outputs, group 128, bf16 scales) take the deep pipeline when its
     32-row tiles fit one round on the CUs, with a split over d chosen on the
     device when the workspace has room; more rows take the 128-row int4
-    kernel (100 rows x 12 blocks: 384 tiles), each launch idle for the
-    other's counts. Without a split (no workspace, or 136 tiles at 32 rows x
-    17 blocks) the caches equal the 128-row kernel's (gemm path 1) bit for
-    bit; with one they agree to bf16 rounding. Every filled row is within the
-    K/V bar, the other slots keep their sentinel; 0 rows write nothing."""
+    kernel (100 rows x 12 blocks: 384 tiles), in one launch that picks its
+    side from the count when the 128-row side takes no split (21 or 12
+    blocks here), else in two launches each idle for the other's counts.
+    Without a split (no workspace, or 136 or 168 tiles at 32 rows) the caches
+    equal the 128-row kernel's (gemm path 1) bit for bit; with one they agree
+    to bf16 rounding. Every filled row is within the K/V bar, the other
+    slots keep their sentinel; 0 rows write nothing."""
     cfg = get_config("3D")
     layers = list(range(5, 5 + nl))
     g = torch.Generator().manual_seed(4096 + rows)
@@ -506,7 +508,7 @@ def test_kv_fill_deep_projection(rows, nl, split):
     pick = np.linspace(0, rows - 1, min(rows, 24)).astype(np.int64)
     check_fill(cfg, kc, vc, h, sel.numpy(), slot, None, wk, wv, sample=pick)
     s_ = slot[sel.long().to(DEV)].long()
-    bitwise = not split or (rows, nl) in ((32, 17), (100, 12))
+    bitwise = not split or (rows, nl) in ((32, 17), (100, 12), (13, 21))
     for a, b in zip(out[0], out[1]):
         if bitwise:
             assert torch.equal(a.view(torch.int16), b.view(torch.int16))

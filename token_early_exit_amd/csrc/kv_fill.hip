@@ -500,9 +500,18 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
           qd.part = (float*)part_ws;
           qd.part_cap = (int64_t)part_bytes;
         }
+        const bool all_deep = (int64_t)((m_max + 31) / 32) * qd.gate_units <= cus;
+        int ks;
+        if (!all_deep && m_max > 64 &&
+            proj_path(m_max, true, false, d, q.N, nl, part_bytes, &ks) == PROJ_REGS) {
+          // the other counts on the 128-row kernel without a split: one
+          // launch takes both
+          w4_either_launch(qd, nl, s);
+          return check_launch("kv_fill projection (deep or 128-row)");
+        }
         w4_deep_launch(qd, nl, s);
         river_status st = check_launch("kv_fill projection (deep)");
-        if (st != RIVER_OK || (int64_t)((m_max + 31) / 32) * qd.gate_units <= cus) return st;
+        if (st != RIVER_OK || all_deep) return st;
         q.gate = -1;
         q.gate_units = qd.gate_units;
         q.gate_cus = cus;

@@ -59,8 +59,12 @@ __device__ __forceinline__ int w4_deep_parts(const GemmArgs& g, int units, int r
   return p > 1 ? p : 1;
 }
 
+constexpr int W4_DEEP_LDS = 3 * (32 * 32 + 256 * 8 + 8 * 2 * 64 / 4);   // 16-byte units
+
+// The deep projection's work on LDS (W4_DEEP_LDS of it) given by the
+// caller; gated: honour the gate of a split launch.
 template <bool SZ_BF16>
-__global__ __launch_bounds__(512, 1) void w4_deep_kernel(GemmArgs g, int tiles_n, int batch) {
+__device__ __forceinline__ void w4_deep_body(const GemmArgs& g, int tiles_n, int batch, u32x4* L, bool gated) {
   constexpr int BM = 32, BN = 256, NW = 8, CW = 32;
   constexpr int SZB = SZ_BF16 ? 2 : 4;
   // stage layout in 16-byte units: A [32 rows][32 chunks] (physical chunk
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(512, 1) void w4_deep_kernel(GemmArgs g, int tiles_n
   constexpr int NS = 3;
   // loads per thread and super-slab: 2 A, 4 weights, scale, zero
   constexpr int PER = 2 + 4 + 2;
-  __shared__ u32x4 L[NS * SSZ];
+  static_assert(NS * SSZ == W4_DEEP_LDS, "the LDS layout");
 
   const int M_max = g.M_max, N = g.N, K = g.K, nh = g.nh, a_nrows = g.a_nrows;
   const int grp = g.group[0];
@@ -83,7 +87,7 @@ __global__ __launch_bounds__(512, 1) void w4_deep_kernel(GemmArgs g, int tiles_n
     const int md = *g.M_dev;
     M = md < 0 ? 0 : (md < M_max ? md : M_max);
   }
-  if (!gate_open(g, M)) return;          // the other launch's counts
+  if (gated && !gate_open(g, M)) return;   // the other launch's counts
   const int tiles_m_act = ((g.M_dev_z ? M_max : M) + BM - 1) / BM;
   const int tiles = tiles_n * tiles_m_act * batch;
   // parts for the whole chip whatever the launch's CU budget, so that the
@@ -270,6 +274,29 @@ __global__ __launch_bounds__(512, 1) void w4_deep_kernel(GemmArgs g, int tiles_n
   }
 }
 
+template <bool SZ_BF16>
+__global__ __launch_bounds__(512, 1) void w4_deep_kernel(GemmArgs g, int tiles_n, int batch) {
+  __shared__ u32x4 L[W4_DEEP_LDS];
+  w4_deep_body<SZ_BF16>(g, tiles_n, batch, L, true);
+}
+
+// One launch for both ranges of counts: the deep pipeline when its tiles
+// fit one round (g.gate_units, g.gate_cus), else the 128-row int4 kernel
+// (tn_deep, tn_big: their column tiles), on one LDS array, so that the
+// count the launch does not take costs no launch of its own.
+template <bool SZ_BF16, bool SZT>
+__global__ __launch_bounds__(512, 1) void w4_either_kernel(GemmArgs g, int tn_deep, int tn_big, int batch) {
+  constexpr int BIG = w4_lds_units<128, 8, false, SZT>();
+  __shared__ u32x4 L[W4_DEEP_LDS > BIG ? W4_DEEP_LDS : BIG];
+  int M = g.M_max;
+  if (g.M_dev) {
+    const int md = *g.M_dev;
+    M = md < 0 ? 0 : (md < g.M_max ? md : g.M_max);
+  }
+  if ((int64_t)((M + 31) / 32) * g.gate_units <= g.gate_cus) w4_deep_body<SZ_BF16>(g, tn_deep, batch, L, false);
+  else w4_gemm_body<128, EPI_CACHE, SZ_BF16, 8, false, SZT>(g, tn_big, batch, L, false);
+}
+
 // The deep pipeline's shape conditions (the caller has checked those of
 // the MFMA fill: d % 256 == 0, nh % 64 == 0, equal groups and scale types
 // for K and V, spans below 2^31 bytes).
@@ -320,6 +347,26 @@ __global__ __launch_bounds__(256) void w4_deep_finish_kernel(GemmArgs g, int bat
   const bool isv = col >= nh;
   uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc);
   *(u32x4*)(dst + (int64_t)z * g.cache_bstride + (int64_t)sl * nh + (isv ? col - nh : col)) = o;
+}
+
+// The projection over `batch` layers for every count, one launch (the
+// 128-row kernel's side without a split, M_max > 64), and with g.part set
+// the finish kernel of the deep side's split.
+inline void w4_either_launch(const GemmArgs& g, int batch, hipStream_t s) {
+  const int tn = (g.N + 255) / 256;
+  const int grid = persistent_grid(launch_cu_budget());
+  const bool szt = w4_tile_scales_ok(g);
+  if (g.sz_bf16[0]) {
+    if (szt) w4_either_kernel<true, true><<<grid, 512, 0, s>>>(g, tn, tn, batch);
+    else w4_either_kernel<true, false><<<grid, 512, 0, s>>>(g, tn, tn, batch);
+  } else {
+    if (szt) w4_either_kernel<false, true><<<grid, 512, 0, s>>>(g, tn, tn, batch);
+    else w4_either_kernel<false, false><<<grid, 512, 0, s>>>(g, tn, tn, batch);
+  }
+  if (g.part) {
+    const int64_t threads = (int64_t)batch * g.M_max * (g.N / 8);
+    w4_deep_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(g, batch, tn, N_CU);
+  }
 }
 
 // The projection over `batch` layers, and (with g.part set) the finish

@@ -161,8 +161,17 @@ __device__ __forceinline__ void layer_epilogue(const GemmArgs& g, f32x16 (&acc)[
   }
 }
 
+// LDS of the int4 projection, in 16-byte units (the layout is described in
+// w4_gemm_body)
+template <int BM, int NW, bool LAYER, bool SZT>
+constexpr int w4_lds_units() {
+  return 4 * (BM * 8 + (SZT ? 0 : NW * 32)) + 2 * 256 * 8 + (SZT ? NW * 256 : 0) + (LAYER ? (64 * NW / BM) * BM / 4 : 0);
+}
+
+// The projection's work on LDS (w4_lds_units of it) given by the caller.
+// gated: honour the gate of a split launch (w4deep.h).
 template <int BM, int EPI, bool SZ_BF16, int NW, bool LAYER, bool SZT>
-__global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_n, int batch) {
+__device__ __forceinline__ void w4_gemm_body(const GemmArgs& g, int tiles_n, int batch, u32x4* LDS, bool gated) {
   static_assert(!LAYER || (NW == 8 && EPI == EPI_CACHE), "the layer epilogue takes 32-column waves");
   static_assert(!SZT || (NW == 8 && !LAYER), "tile-wide scales: 32-column waves, plain channels");
   static_assert(EPI == EPI_CACHE || EPI == EPI_PART, "cache or partial-sum output");
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
   constexpr int RG = 64 * NW / BM;
   constexpr int RCH = 4;
   constexpr int RSO = SZO + (SZT ? NW * SZW : 0);
-  __shared__ u32x4 LDS[RSO + (LAYER ? RG * BM / 4 : 0)];
+  static_assert(RSO + (LAYER ? RG * BM / 4 : 0) == w4_lds_units<BM, NW, LAYER, SZT>(), "the LDS layout");
   u32x4* const WQ = LDS + WQO;
   [[maybe_unused]] float* const RSUM = (float*)(LDS + RSO);
 
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
     const int md = *g.M_dev;
     M = md < 0 ? 0 : (md < M_max ? md : M_max);
   }
-  if (!gate_open(g, M)) return;          // the other launch's counts
+  if (gated && !gate_open(g, M)) return;   // the other launch's counts
   // with per-entry row counts every entry walks the row tiles of M_max and
   // skips those past its own count
   const int tiles_m_act = ((g.M_dev_z ? M_max : M) + BM - 1) / BM;
@@ -609,6 +618,12 @@ __global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_
   }
 }
 
+template <int BM, int EPI, bool SZ_BF16, int NW, bool LAYER, bool SZT>
+__global__ __launch_bounds__(64 * NW) void w4_gemm_kernel(GemmArgs g, int tiles_n, int batch) {
+  __shared__ u32x4 LDS[w4_lds_units<BM, NW, LAYER, SZT>()];
+  w4_gemm_body<BM, EPI, SZ_BF16, NW, LAYER, SZT>(g, tiles_n, batch, LDS, true);
+}
+
 // Launch over a batch of `batch` layers: one workgroup per CU (144 KB of
 // LDS for BM = 128), capped by the tile count and rounded to whole XCDs.
 // W4_WAVES: 4 waves (64 columns each, one per SIMD) or 8 (32 columns each,
@@ -677,7 +692,8 @@ inline void w4_gemm_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tm = (g.M_max + BM - 1) / BM;
   const int64_t tiles = (int64_t)tn * tm * batch * (EPI == EPI_PART ? g.ksplit : 1);
   const int grid = persistent_grid(tiles);
-  if constexpr (!LAYER) {
+  // (not for the parts of a split: a part uses only its share of the rows)
+  if constexpr (!LAYER && EPI != EPI_PART) {
     if (w4_tile_scales_ok(g)) {
       if (g.sz_bf16[0]) w4_gemm_kernel<BM, EPI, true, W4_WAVES, false, true><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
       else w4_gemm_kernel<BM, EPI, false, W4_WAVES, false, true><<<grid, 64 * W4_WAVES, 0, s>>>(g, tn, batch);
