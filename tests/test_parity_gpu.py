@@ -375,18 +375,20 @@ def test_kv_fill_map_gemm_tiles(gemm_path):
         assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-2 * b.abs().amax(dim=-1, keepdim=True))
 
 
+@pytest.mark.parametrize("nl", [6, 1])
 @pytest.mark.parametrize("count", ["device", "host"])
-def test_kv_fill_map_narrow_tiles_equal_128_tiles(count):
+def test_kv_fill_map_narrow_tiles_equal_128_tiles(count, nl):
     """A row bound of at most 256 (a decode step's exits) runs the map GEMM
-    on 32-row tiles with an 8-slab ring (automatic). Each tile starts its
-    reduction at its own slab (tiles that run at the same time then read
-    different parts of the maps' rows), so its sums run in another order than
-    the 128-row tiles' (gemm path 1): the caches agree to a few bf16 ulps,
-    and every filled row is within the K/V bar. d = 2048, six layers; 13 rows
-    under a bound of 256 with the count on the device, or 200 rows (ragged
-    32-row tiles) with the count on the host."""
+    on 32-row tiles with an 8-slab ring (automatic). Over several maps each
+    tile starts its reduction at its own slab (tiles that run at the same
+    time then read different parts of the maps' rows), so its sums run in
+    another order than the 128-row tiles' (gemm path 1): the caches agree to
+    a few bf16 ulps; over one map they agree bit for bit. Every filled row is
+    within the K/V bar. d = 2048, six layers or one; 13 rows under a bound of
+    256 with the count on the device, or 200 rows (ragged 32-row tiles) with
+    the count on the host."""
     cfg = get_config(1, d=2048, n_tokens=256, n_slots=300)
-    layers = [3, 4, 5, 6, 7, 8]
+    layers = [3, 4, 5, 6, 7, 8][:nl]
     h = G.hidden_states(cfg, cfg.n_tokens, [2])[2].to(DEV)
     g = torch.Generator().manual_seed(2048)
     slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
@@ -410,6 +412,8 @@ def test_kv_fill_map_narrow_tiles_equal_128_tiles(count):
         tee.river_debug_set_gemm_path(0)
     s = slot[sel.long().to(DEV)].long()
     for a, b in zip(out[0], out[1]):
+        if nl == 1:
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
         a, b = a[:, s].float(), b[:, s].float()
         assert torch.all((a - b).abs() <= 2 ** -6 * b.abs() + 1e-3 * b.abs().amax(dim=-1, keepdim=True))
     kc, vc = out[0]

@@ -260,7 +260,11 @@ river_status decode_static_scratch(void** ptr, size_t* bytes) {
 // its fork and join, made on the device's first step that forks (default
 // priority, non-blocking) and kept until the process ends. The mutex keeps
 // the fork-to-join launches of two host threads from interleaving.
-constexpr int DECODE_SIDE_CUS = 192;
+// DECODE_SIDE_CUS: the second stream's CU budget; at the 8B decode shape
+// (the first fill streams 21 maps of 4096^2, the others need one map and
+// one block) 176 and 192 measured 241 and 243 us per graph-replayed step,
+// 208 and 224 (the others then take longer than the first) 279 and 297.
+constexpr int DECODE_SIDE_CUS = 176;
 struct DecodeSide {
   std::mutex mu;
   hipStream_t stream = nullptr;

@@ -16,13 +16,16 @@
 // Sub-step s of a slab takes logical 16-byte chunk 4 h + s of each row, as
 // gemm.h does.
 //
-// Each tile starts its walk over K at its own slab, (37 tile) mod K/64, and
-// wraps around. All CUs start together and advance at about the same pace,
-// so with a common start every load in flight on the chip would sit at the
-// same 128-byte offset of an 8 KB map row; measured on a pure read of this
-// pattern (21 maps of 4096^2) that reaches 4.1-4.8 TB/s, with staggered
-// starts 5.7-6.1 (the GEMM: 129-135 -> 121-126 us). The sums then run in
-// another order than gemm_nt_kernel's: the results agree to rounding.
+// Over several maps each tile starts its walk over K at its own slab,
+// (37 tile) mod K/64, and wraps around. All CUs start together and advance
+// at about the same pace, so with a common start every load in flight on
+// the chip would sit at the same 128-byte offset of an 8 KB map row;
+// measured on a pure read of this pattern (21 maps of 4096^2) that reaches
+// 4.1-4.8 TB/s, with staggered starts 5.7-6.1 (the GEMM: 129-135 -> 121-126
+// us). The sums then run in another order than gemm_nt_kernel's: the
+// results agree to rounding. Over one map (read from L2 by every row tile)
+// there is no rotation, and the results are bit-identical to
+// gemm_nt_kernel<128>'s.
 //
 // Loads: every wave load covers 8 rows x 128 contiguous bytes (8 lanes per
 // row); chunk p of an operand block holds logical chunk (p % 8) ^ swz(row)
@@ -91,8 +94,9 @@ __global__ __launch_bounds__(256, 1) void gemm_narrow_kernel(GemmArgs g, int til
       const int r = p >> 3, c = (p & 7) ^ swz(r);
       b_off[i] = (uint32_t)(((int64_t)(n0 + r) * g.ldb + c * 8) * 2);
     }
-    // the tile's k-th slab is slab (k + j0) mod KT of the operands
-    const int j0 = (tile * 37) % KT;
+    // the tile's k-th slab is slab (k + j0) mod KT of the operands (one
+    // matrix, re-read from L2 by every row tile: no rotation)
+    const int j0 = batch > 1 ? (tile * 37) % KT : 0;
     auto issue = [&](int st, int k) {
       u32x4* l = L + st * SSZ;
       const int j = k + j0 < KT ? k + j0 : k + j0 - KT;

@@ -496,7 +496,9 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
         qd.gate = 1;
         qd.gate_units = ((q.N + 255) / 256) * nl;
         qd.gate_cus = cus;
-        if (part_bytes >= (size_t)256 * q.N * 4) {
+        // (a split needs fewer tiles than half the CUs: with more column
+        // tiles than that none is possible, and no finish kernel runs)
+        if (part_bytes >= (size_t)256 * q.N * 4 && 2 * qd.gate_units <= cus) {
           qd.part = (float*)part_ws;
           qd.part_cap = (int64_t)part_bytes;
         }
@@ -595,6 +597,13 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
           gemm_part_finish_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(p, nl);
           st = check_launch("kv_fill map sum");
         }
+      } else if (narrow && nl == 1 && launch_cu_budget() < 128) {
+        // one map on few CUs (a decode step's later fill beside the first
+        // one): the 128-row tiles, a quarter of the tiles with four times
+        // the MFMA work per byte; bit-identical to the 32-row tiles over one
+        // map
+        gemm_launch<128, EPI_BF16>(p, nl, s);
+        st = check_launch("kv_fill map");
       } else if (narrow || (gemm_path_override() == 0 && m_max <= 256 && gemm_narrow_ok(p))) {
         // decode-sized row bound: 32-row tiles with eight slabs of maps in flight
         gemm_narrow_launch(p, nl, s);
