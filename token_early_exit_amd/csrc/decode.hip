@@ -109,8 +109,11 @@ struct DecodePlan {
 // batch rule every running token exits where all of them pass (and at
 // least one runs). Each checkpoint's exits are listed in token order from
 // a ballot per wave and the wave totals.
+// The workgroup has as many waves as the tokens need (its barriers and the
+// wave totals' reads scale with them).
 __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
   __shared__ int wsum[DC_TOKENS / WAVE];
+  const int nw = blockDim.x / WAVE;
   __shared__ int tot[DC_MAX];
   const int i = threadIdx.x, lane = i % WAVE, wave = i / WAVE;
   const int n = p.n;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
       __syncthreads();
       int before = 0, total = 0;
 #pragma unroll
-      for (int w = 0; w < DC_TOKENS / WAVE; ++w) {
+      for (int w = 0; w < nw; ++w) {
         const int v = wsum[w];
         before += w < wave ? v : 0;
         total += v;
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(DC_TOKENS) void decode_plan_kernel(DecodePlan p) {
   }
   if (p.m_layer && p.single_mask) {
     const int first = p.layer[__builtin_ctz(p.single_mask)] + 1;   // first filled block
-    for (int j = i; j < p.n_layers + 1 - first; j += DC_TOKENS) {
+    for (int j = i; j < p.n_layers + 1 - first; j += blockDim.x) {
       int m = 0;
       for (int c = 0; c < p.n_ck; ++c)
         m += ((p.single_mask >> c) & 1u) && p.layer[c] < first + j ? tot[c] : 0;
@@ -413,7 +416,7 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     q.idx_stride = (int)(CO / 4);
     q.counts = (int32_t*)(rec + (size_t)n_ck * CO);
     q.exit_layer = exit_layer;
-    decode_plan_kernel<<<1, DC_TOKENS, 0, s>>>(q);
+    decode_plan_kernel<<<1, (n + WAVE - 1) / WAVE * WAVE, 0, s>>>(q);
     st = check_launch("decode_step plan");
     if (st != RIVER_OK) return st;
     // The fills left: the single fill, and one per other checkpoint. When
