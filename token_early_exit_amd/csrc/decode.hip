@@ -57,6 +57,7 @@ __global__ __launch_bounds__(256) void decode_init_kernel(int n, uint8_t* alive,
 
 // ------------------------------------------------- all checkpoints at once
 constexpr int DC_MAX = 32;       // checkpoints of the two-launch path
+constexpr int RM_HALVES = 16;    // checkpoints whose route halves the workspace holds
 constexpr int DC_TOKENS = 1024;  // tokens of the two-launch path (one workgroup)
 
 struct DecodeCos {
@@ -301,7 +302,8 @@ static river_status decode_side(DecodeSide** out) {
 size_t decode_fixed_workspace(int n, int d, river_dtype dt, int n_layers) {
   (void)dt;
   return a256(2 * (size_t)n) + a256((size_t)n) + 2 * a256(4 * (size_t)n) + 256 + compact_workspace(n) +
-         (size_t)(n_layers > 1 ? n_layers - 1 : 0) * plan_ck_bytes(n) + plan_fill_bytes(n, d, n_layers);
+         (size_t)(n_layers > 1 ? n_layers - 1 : 0) * plan_ck_bytes(n) + plan_fill_bytes(n, d, n_layers) +
+         (n <= DC_TOKENS ? route_halves_bytes(n, n_layers - 1 < RM_HALVES ? n_layers - 1 : RM_HALVES) : 0);
 }
 
 // descriptor of blocks e+1..L inside one that covers blocks 1..L
@@ -344,6 +346,9 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
   w += a256(4 * (size_t)n);
   int32_t* m_layer = (int32_t*)w;
   w += a256(4 * (size_t)n_layers);
+  // the route's halves (two-launch path with routers)
+  void* halves = n <= DC_TOKENS ? (void*)w : nullptr;
+  w += n <= DC_TOKENS ? route_halves_bytes(n, n_layers - 1 < RM_HALVES ? n_layers - 1 : RM_HALVES) : 0;
   void* fws = w;
   const size_t fixed = (size_t)(w - (char*)workspace);
   const size_t fws_bytes = ws_bytes - fixed;
@@ -367,7 +372,8 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     uint8_t* masks = (uint8_t*)(plan + (size_t)n_ck * (3 * CO + 256));
     river_status st = RIVER_OK;
     if (routers_on) {
-      st = launch_route_scores(n, d, dt, ld, n_ck, ck, gamma, eps, b, (float*)plan, prob, masks, s);
+      st = launch_route_scores(n, d, dt, ld, n_ck, ck, gamma, eps, b, (float*)plan, prob, masks,
+                               n_ck <= RM_HALVES ? halves : nullptr, s);
       if (st != RIVER_OK) return st;
     } else if (n_ck > 0) {
       DecodeCos a{};

@@ -70,9 +70,12 @@ bool kv_fill_plain_mfma(int m_max, int d, river_dtype dt, int n_rows, int64_t ld
 // cosine and router probability of every token at every checkpoint (all
 // with a router) in one launch, [n_ck][n] each; mask_scratch [n_ck][n]
 bool route_scores_ok(int n, int d, river_dtype dt, int b, int64_t ld, int n_ck);
+// halves: room for route_halves_bytes(n, n_ck) (the reduction over d in two
+// workgroups per token group where d % 512 == 0), or NULL
 river_status launch_route_scores(int n, int d, river_dtype dt, int64_t ld, int n_ck, const river_checkpoint* ck,
                                  const void* gamma, float eps, int b, float* cos_out, float* prob_out,
-                                 uint8_t* mask_scratch, hipStream_t s);
+                                 uint8_t* mask_scratch, void* halves, hipStream_t s);
+size_t route_halves_bytes(int n, int n_ck);
 
 size_t decode_fixed_workspace(int n, int d, river_dtype dt, int n_layers);
 river_status decode_static_scratch(void** ptr, size_t* bytes);

@@ -318,6 +318,57 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
   if (part == 0 && gi < n) write_decision(a, gi, cosine_from(sd, sa, sb), sigmoidf_(z), true);
 }
 
+// The router epilogue of the streaming route, on the pre-activations of
+// T = 16 RT tokens in the 16x16 MFMA layout (lane l of wave w holds unit
+// UW w + 16 uf + l % 16 of tokens 16 rt + 4 (l / 16) + i) and the tokens'
+// norms in nrm: RMSNorm scale, SiLU, w_up, the per-wave logits added in
+// wave order, sigmoid, the decision. Every thread calls it.
+template <int RT, int NW>
+__device__ __forceinline__ void route_stream_epilogue(const RouteArgs& a, const f32x4 (&acc)[RT][8 / NW],
+                                                      const float (&wup)[8 / NW], float (*red)[16 * RT],
+                                                      float (*nrm)[3], int row0) {
+  constexpr int T = 16 * RT, UF = 8 / NW, UW = 16 * UF;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int d = a.d, b = a.b, n = a.n;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float zp[4] = {0.f, 0.f, 0.f, 0.f}, r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = 1.0f / sqrtf(nrm[rt * 16 + 4 * (lane >> 4) + i][2] / (float)d + a.eps);
+#pragma unroll
+    for (int uf = 0; uf < UF; ++uf) {
+      const bool uok = wave * UW + uf * 16 + (lane & 15) < b;   // units past b do not exist
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float c = silu_hw(acc[rt][uf][i] * r[i]) * wup[uf];
+        zp[i] += uok ? c : 0.f;   // a select: a missing unit adds nothing, whatever c is
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = row_sum<16>(zp[i]);
+      if ((lane & 15) == 0) red[wave][rt * 16 + 4 * (lane >> 4) + i] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < T) {
+    const int gi = row0 + tid;
+    float z = red[0][tid];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) z += red[w][tid];   // fixed order
+    if (gi < n) write_decision(a, gi, cosine_from(nrm[tid][0], nrm[tid][1], nrm[tid][2]), sigmoidf_(z), true);
+  }
+}
+
+// The two halves of a route whose reduction over d is split (HALVES):
+// per checkpoint and half, the pre-activations [half][token][128 units]
+// and the norms [half][token][4] (dot, |h_prev|^2, |h_cur|^2, unused).
+struct RouteHalves {
+  float* u;                  // [n_ck][2][n][128]
+  float* nrm;                // [n_ck][2][n][4]
+};
+
 // ------------------------------------------------------ streaming path
 // d % 256 == 0, bf16, b <= 128: one workgroup = NW waves, T = 16 RT tokens.
 // The feature dimension is walked in 64-wide slabs. Each slab of W_down
@@ -330,8 +381,19 @@ __global__ __launch_bounds__(512) void route_mfma_kernel(RouteArgs a) {
 // pre-activations need no cross-wave sum; meanwhile 8 threads per token
 // accumulate, in fp32, the three dot products over 8 features of each slab.
 // The per-wave logits are added in wave order.
-template <int RT, bool HAS_GAMMA, int NW>
-__device__ __forceinline__ void route_stream_body(const RouteArgs& a) {
+//
+// HALVES (d % 512 == 0): the reduction over d in two halves of KT / 2
+// slabs, each in an accumulator set of its own, added at the end (the
+// pre-activations and the three norms). HALF < 0: one workgroup walks both
+// and adds them; HALF = 0 or 1: the workgroup walks its half and writes the
+// half's sums (hv) for route_halves_kernel, which adds them in the same
+// order and runs the same epilogue. A decode step's route takes 16-token
+// workgroups, 128 for 8 checkpoints of 256 tokens: each walks 64 slabs one
+// barrier at a time, half the CUs idle; in halves, 256 workgroups walk 32.
+// The results are the same bits either way.
+template <int RT, bool HAS_GAMMA, int NW, bool HALVES = false>
+__device__ __forceinline__ void route_stream_body(const RouteArgs& a, int half = -1,
+                                                  RouteHalves hv = RouteHalves{}) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int T = 16 * RT;
   constexpr int UF = 8 / NW;             // 16-unit MFMA fragments per wave
@@ -411,15 +473,27 @@ __device__ __forceinline__ void route_stream_body(const RouteArgs& a) {
                   h_off[i], j * 128, l + WB + (i * NW + wave) * 64);
   };
 
-  f32x4 acc[RT][UF];
+  struct Sums {
+    f32x4 acc[RT][UF];
+    float dot, na, nb;
+  };
+  auto zero = [&](Sums& s) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int uf = 0; uf < UF; ++uf) acc[rt][uf] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dot = 0.f, na = 0.f, nb = 0.f;
+      for (int uf = 0; uf < UF; ++uf) s.acc[rt][uf] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s.dot = s.na = s.nb = 0.f;
+  };
+  Sums S0s, S1s;                                  // the halves' sums (the first only without HALVES)
+  zero(S0s);
+  if constexpr (HALVES) zero(S1s);
   const int my_t = tid >> 3, my_q = tid & 7;      // dot-product share: token, chunk
 
-  auto compute = [&](const u32x4* l, int j) {
+  auto compute = [&](const u32x4* l, int j, Sums& sm) {
+    auto& acc = sm.acc;
+    auto& dot = sm.dot;
+    auto& na = sm.na;
+    auto& nb = sm.nb;
     const u32x4* lw = l;
     const u32x4* lc = l + WB;
     const u32x4* lp = l + WB + HB;
@@ -482,76 +556,93 @@ __device__ __forceinline__ void route_stream_body(const RouteArgs& a) {
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   // slab j in stage j % 4; slab j + 3 is issued after the barrier of slab
-  // j (its stage held slab j - 1, which every wave has finished with). KT is
-  // a multiple of 4: the loop body has static stages and no branches, and
-  // the last four slabs wait for exactly what is still in flight.
-  issue(I0{}, 0);
-  issue(I1{}, 1);
-  issue(I2{}, 2);
-  auto iter = [&](auto st, int j, auto w, auto iss) {
+  // j (its stage held slab j - 1, which every wave has finished with). The
+  // slabs walked, [j0, j1), are a multiple of 4: the loop body has static
+  // stages and no branches, and the last four slabs wait for exactly what
+  // is still in flight. With HALVES and both halves in this workgroup the
+  // sums switch sets at KT / 2 (a multiple of 4).
+  const int j0 = HALVES && half == 1 ? KT / 2 : 0;
+  const int j1 = HALVES && half == 0 ? KT / 2 : KT;
+  issue(I0{}, j0);
+  issue(I1{}, j0 + 1);
+  issue(I2{}, j0 + 2);
+  auto iter = [&](auto st, int j, auto w, auto iss, Sums& sm) {
     using NX = std::integral_constant<int, (decltype(st)::value + 3) & 3>;
     wait_barrier<decltype(w)::value, true>();   // slab j landed; its loads and older ones done
     if constexpr (decltype(iss)::value) issue(NX{}, j + 3);
-    compute(stage(st), j);
+    compute(stage(st), j, sm);
   };
   using W2 = std::integral_constant<int, 2 * PER_SLAB>;
   using W1 = std::integral_constant<int, PER_SLAB>;
   using W0 = std::integral_constant<int, 0>;
   using T_ = std::true_type;
   using F_ = std::false_type;
-  int j = 0;
-  for (; j + 4 < KT; j += 4) {
-    iter(I0{}, j, W2{}, T_{});
-    iter(I1{}, j + 1, W2{}, T_{});
-    iter(I2{}, j + 2, W2{}, T_{});
-    iter(I3{}, j + 3, W2{}, T_{});
+  auto group = [&](int j, Sums& sm) {
+    iter(I0{}, j, W2{}, T_{}, sm);
+    iter(I1{}, j + 1, W2{}, T_{}, sm);
+    iter(I2{}, j + 2, W2{}, T_{}, sm);
+    iter(I3{}, j + 3, W2{}, T_{}, sm);
+  };
+  // the sums of slab j: the second set from KT / 2 on when one workgroup
+  // walks both halves
+  auto sums_of = [&](int j) -> Sums& {
+    if constexpr (HALVES) {
+      if (half < 0 && j >= KT / 2) return S1s;   // uniform
+    }
+    return S0s;
+  };
+  int j = j0;
+  for (; j + 4 < j1; j += 4) group(j, sums_of(j));
+  {
+    Sums& sm = sums_of(j);
+    iter(I0{}, j, W2{}, T_{}, sm);
+    iter(I1{}, j + 1, W1{}, F_{}, sm);
+    iter(I2{}, j + 2, W0{}, F_{}, sm);
+    iter(I3{}, j + 3, W0{}, F_{}, sm);
   }
-  iter(I0{}, j, W2{}, T_{});
-  iter(I1{}, j + 1, W1{}, F_{});
-  iter(I2{}, j + 2, W0{}, F_{});
-  iter(I3{}, j + 3, W0{}, F_{});
 
-  // dot products: sum over the 8 threads of each token (fixed order)
-  dot = row_sum<8>(dot);
-  na = row_sum<8>(na);
-  nb = row_sum<8>(nb);
+  // dot products: sum over the 8 threads of each token (fixed order); the
+  // halves' sums added in order
+  float dot = row_sum<8>(S0s.dot), na = row_sum<8>(S0s.na), nb = row_sum<8>(S0s.nb);
+  f32x4 acc[RT][UF];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int uf = 0; uf < UF; ++uf) acc[rt][uf] = S0s.acc[rt][uf];
+  if constexpr (HALVES) {
+    if (half >= 0) {
+      // this half's sums for route_halves_kernel: lane l of wave w holds
+      // unit UW w + 16 uf + l % 16 of tokens 16 rt + 4 (l / 16) + i
+      const int64_t base = (int64_t)half * n;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int uf = 0; uf < UF; ++uf)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = row0 + rt * 16 + 4 * (lane >> 4) + i;
+            if (t < n) hv.u[(base + t) * 128 + wave * UW + uf * 16 + (lane & 15)] = acc[rt][uf][i];
+          }
+      if (my_q == 0 && tid < DT && row0 + my_t < n)
+        *(f32x4*)(hv.nrm + (base + row0 + my_t) * 4) = f32x4{dot, na, nb, 0.f};
+      return;
+    }
+    dot += row_sum<8>(S1s.dot);
+    na += row_sum<8>(S1s.na);
+    nb += row_sum<8>(S1s.nb);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int uf = 0; uf < UF; ++uf) acc[rt][uf] += S1s.acc[rt][uf];
+  }
   if (my_q == 0 && tid < DT) { nrm[my_t][0] = dot; nrm[my_t][1] = na; nrm[my_t][2] = nb; }
   __syncthreads();
-  // router epilogue of this wave's units: 16x16 accumulator layout, lane l
-  // holds unit 16 uf + l % 16 of rows (tokens) 4 (l / 16) + i
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    float zp[4] = {0.f, 0.f, 0.f, 0.f}, r[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = 1.0f / sqrtf(nrm[rt * 16 + 4 * (lane >> 4) + i][2] / (float)d + a.eps);
-#pragma unroll
-    for (int uf = 0; uf < UF; ++uf) {
-      const bool uok = wave * UW + uf * 16 + (lane & 15) < b;   // units past b do not exist
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float c = silu_hw(acc[rt][uf][i] * r[i]) * wup[uf];
-        zp[i] += uok ? c : 0.f;   // a select: a missing unit adds nothing, whatever c is
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float v = row_sum<16>(zp[i]);
-      if ((lane & 15) == 0) red[wave][rt * 16 + 4 * (lane >> 4) + i] = v;
-    }
-  }
-  __syncthreads();
-  if (tid < T) {
-    const int gi = row0 + tid;
-    float z = red[0][tid];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) z += red[w][tid];   // fixed order
-    if (gi < n) write_decision(a, gi, cosine_from(nrm[tid][0], nrm[tid][1], nrm[tid][2]), sigmoidf_(z), true);
-  }
+  route_stream_epilogue<RT, NW>(a, acc, wup, red, nrm, row0);
 }
 
-template <int RT, bool HAS_GAMMA, int NW>
+template <int RT, bool HAS_GAMMA, int NW, bool HALVES>
 __global__ __launch_bounds__(64 * NW) void route_stream_kernel(RouteArgs a) {
-  route_stream_body<RT, HAS_GAMMA, NW>(a);
+  route_stream_body<RT, HAS_GAMMA, NW, HALVES>(a);
 }
 
 // The router checkpoints of a decode step in one launch: blockIdx.y picks
@@ -561,9 +652,61 @@ constexpr int RM_MAX = 16;
 struct RouteMulti { RouteArgs a[RM_MAX]; };
 static_assert(sizeof(RouteMulti) <= 4000, "kernel arguments are limited to 4 KB");
 
-template <int RT, bool HAS_GAMMA, int NW>
+template <int RT, bool HAS_GAMMA, int NW, bool HALVES>
 __global__ __launch_bounds__(64 * NW) void route_stream_multi_kernel(RouteMulti m) {
-  route_stream_body<RT, HAS_GAMMA, NW>(m.a[blockIdx.y]);
+  route_stream_body<RT, HAS_GAMMA, NW, HALVES>(m.a[blockIdx.y]);
+}
+
+// The checkpoints' routes in halves: blockIdx.z picks the half, each
+// writes its sums to hv (checkpoint blockIdx.y at its stride).
+template <int RT, bool HAS_GAMMA, int NW>
+__global__ __launch_bounds__(64 * NW) void route_stream_halves_kernel(RouteMulti m, RouteHalves hv) {
+  const RouteArgs& a = m.a[blockIdx.y];
+  RouteHalves h{hv.u + (int64_t)blockIdx.y * 2 * a.n * 128, hv.nrm + (int64_t)blockIdx.y * 2 * a.n * 4};
+  route_stream_body<RT, HAS_GAMMA, NW, true>(a, blockIdx.z, h);
+}
+
+// The halves added (in the order of the one-workgroup route) and the
+// streaming route's epilogue: the same cosines, probabilities and masks.
+template <int RT, int NW>
+__global__ __launch_bounds__(64 * NW) void route_halves_kernel(RouteMulti m, RouteHalves hv) {
+  constexpr int T = 16 * RT, UF = 8 / NW, UW = 16 * UF;
+  __shared__ float red[NW][T];
+  __shared__ float nrm[T][3];
+  const RouteArgs& a = m.a[blockIdx.y];
+  const int n = a.n, b = a.b;
+  const float* u = hv.u + (int64_t)blockIdx.y * 2 * n * 128;
+  const float* nr = hv.nrm + (int64_t)blockIdx.y * 2 * n * 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row0 = blockIdx.x * T;
+  float wup[UF];
+#pragma unroll
+  for (int uf = 0; uf < UF; ++uf) {
+    const int un = wave * UW + uf * 16 + (lane & 15);
+    wup[uf] = un < b ? load_elem<true>(a.wu, un) : 0.f;
+  }
+  f32x4 acc[RT][UF];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int uf = 0; uf < UF; ++uf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        int t = row0 + rt * 16 + 4 * (lane >> 4) + i;
+        t = t < n ? t : n - 1;                    // rows past n: any values, not written
+        const int64_t o = (int64_t)t * 128 + wave * UW + uf * 16 + (lane & 15);
+        acc[rt][uf][i] = u[o] + u[(int64_t)n * 128 + o];
+      }
+  if (tid < T) {
+    const int t = row0 + tid < n ? row0 + tid : n - 1;
+    const f32x4 x = *(const f32x4*)(nr + (int64_t)t * 4), y = *(const f32x4*)(nr + ((int64_t)n + t) * 4);
+    nrm[tid][0] = x[0] + y[0];
+    nrm[tid][1] = x[1] + y[1];
+    nrm[tid][2] = x[2] + y[2];
+  }
+  __syncthreads();
+  route_stream_epilogue<RT, NW>(a, acc, wup, red, nrm, row0);
 }
 
 // ------------------------------------------------------------ batch rule
@@ -617,6 +760,14 @@ constexpr int ROUTE_WAVES = 8;
 // up to 4096 tokens 16-token workgroups keep every CU busy with 1.25 MB.
 static bool route_two(int n) { return n > 16 * 256; }   // 256 CUs
 
+// the reduction over d in two halves (summed in a fixed order) where the
+// slabs split into whole groups of four: d % 512 == 0
+static bool route_halves(int d) { return d % 512 == 0; }
+
+size_t route_halves_bytes(int n, int n_ck) {
+  return align_up((size_t)n_ck * 2 * n * (128 + 4) * 4, 256);
+}
+
 // the streaming path's conditions (launch_route takes it whenever they hold)
 static bool stream_ok(int n, int d, river_dtype dt, int b, int64_t ld_prev, int64_t ld_cur) {
   return dt == RIVER_BF16 && d % 256 == 0 && b <= 128 && (int64_t)n * ld_cur * 2 < ((int64_t)1 << 31) &&
@@ -629,7 +780,7 @@ bool route_scores_ok(int n, int d, river_dtype dt, int b, int64_t ld, int n_ck) 
 
 river_status launch_route_scores(int n, int d, river_dtype dt, int64_t ld, int n_ck, const river_checkpoint* ck,
                                  const void* gamma, float eps, int b, float* cos_out, float* prob_out,
-                                 uint8_t* mask_scratch, hipStream_t s) {
+                                 uint8_t* mask_scratch, void* halves, hipStream_t s) {
   if (n <= 0 || n_ck <= 0) return RIVER_OK;
   if (!route_scores_ok(n, d, dt, b, ld, n_ck))
     return fail(RIVER_ERR_UNSUPPORTED, "route scores: shape outside the streaming path");
@@ -641,15 +792,40 @@ river_status launch_route_scores(int n, int d, river_dtype dt, int64_t ld, int n
   // the same tile as launch_route at this n, so the same values
   const bool two = route_two(n);
   const int T = two ? 32 : 16;
-  const dim3 grid((unsigned)((n + T - 1) / T), (unsigned)n_ck);
   const dim3 blk(64 * ROUTE_WAVES);
-  if (gamma) {
-    if (two) route_stream_multi_kernel<2, true, ROUTE_WAVES><<<grid, blk, 0, s>>>(m);
-    else route_stream_multi_kernel<1, true, ROUTE_WAVES><<<grid, blk, 0, s>>>(m);
-  } else {
-    if (two) route_stream_multi_kernel<2, false, ROUTE_WAVES><<<grid, blk, 0, s>>>(m);
-    else route_stream_multi_kernel<1, false, ROUTE_WAVES><<<grid, blk, 0, s>>>(m);
+  if (halves && route_halves(d)) {
+    // the reduction over d in two workgroups per token group, then their
+    // sums added and the epilogue run (the same bits as launch_route's
+    // one-workgroup halves)
+    RouteHalves hv{(float*)halves, (float*)halves + (size_t)n_ck * 2 * n * 128};
+    const dim3 grid((unsigned)((n + T - 1) / T), (unsigned)n_ck, 2);
+    auto go = [&](auto rt, auto g) {
+      constexpr int RT = decltype(rt)::value;
+      route_stream_halves_kernel<RT, decltype(g)::value, ROUTE_WAVES><<<grid, blk, 0, s>>>(m, hv);
+    };
+    if (gamma) { if (two) go(std::integral_constant<int, 2>{}, std::true_type{}); else go(std::integral_constant<int, 1>{}, std::true_type{}); }
+    else { if (two) go(std::integral_constant<int, 2>{}, std::false_type{}); else go(std::integral_constant<int, 1>{}, std::false_type{}); }
+    river_status st = check_launch("route scores (halves)");
+    if (st != RIVER_OK) return st;
+    const dim3 g2((unsigned)((n + T - 1) / T), (unsigned)n_ck);
+    if (two) route_halves_kernel<2, ROUTE_WAVES><<<g2, blk, 0, s>>>(m, hv);
+    else route_halves_kernel<1, ROUTE_WAVES><<<g2, blk, 0, s>>>(m, hv);
+    return check_launch("route scores (sum of halves)");
   }
+  // (both halves in one workgroup where launch_route sums them so)
+  const dim3 grid((unsigned)((n + T - 1) / T), (unsigned)n_ck);
+  auto go = [&](auto rt, auto g, auto hl) {
+    route_stream_multi_kernel<decltype(rt)::value, decltype(g)::value, ROUTE_WAVES, decltype(hl)::value>
+        <<<grid, blk, 0, s>>>(m);
+  };
+  using R1 = std::integral_constant<int, 1>;
+  using R2 = std::integral_constant<int, 2>;
+  auto pick = [&](auto g) {
+    if (route_halves(d)) { if (two) go(R2{}, g, std::true_type{}); else go(R1{}, g, std::true_type{}); }
+    else { if (two) go(R2{}, g, std::false_type{}); else go(R1{}, g, std::false_type{}); }
+  };
+  if (gamma) pick(std::true_type{});
+  else pick(std::false_type{});
   return check_launch("route scores");
 }
 
@@ -674,11 +850,21 @@ river_status launch_route(int n, int d, river_dtype dt, const void* h_prev, int6
       const dim3 grid((n + T - 1) / T);
       const dim3 blk(64 * ROUTE_WAVES);
       if (gamma) {
-        if (two) route_stream_kernel<2, true, ROUTE_WAVES><<<grid, blk, 0, s>>>(a);
-        else route_stream_kernel<1, true, ROUTE_WAVES><<<grid, blk, 0, s>>>(a);
+        if (route_halves(d)) {
+          if (two) route_stream_kernel<2, true, ROUTE_WAVES, true><<<grid, blk, 0, s>>>(a);
+          else route_stream_kernel<1, true, ROUTE_WAVES, true><<<grid, blk, 0, s>>>(a);
+        } else {
+          if (two) route_stream_kernel<2, true, ROUTE_WAVES, false><<<grid, blk, 0, s>>>(a);
+          else route_stream_kernel<1, true, ROUTE_WAVES, false><<<grid, blk, 0, s>>>(a);
+        }
       } else {
-        if (two) route_stream_kernel<2, false, ROUTE_WAVES><<<grid, blk, 0, s>>>(a);
-        else route_stream_kernel<1, false, ROUTE_WAVES><<<grid, blk, 0, s>>>(a);
+        if (route_halves(d)) {
+          if (two) route_stream_kernel<2, false, ROUTE_WAVES, true><<<grid, blk, 0, s>>>(a);
+          else route_stream_kernel<1, false, ROUTE_WAVES, true><<<grid, blk, 0, s>>>(a);
+        } else {
+          if (two) route_stream_kernel<2, false, ROUTE_WAVES, false><<<grid, blk, 0, s>>>(a);
+          else route_stream_kernel<1, false, ROUTE_WAVES, false><<<grid, blk, 0, s>>>(a);
+        }
       }
     } else if (mfma) {
       const bool two = n >= 8192;   // 32 tokens per workgroup once the grid is large
