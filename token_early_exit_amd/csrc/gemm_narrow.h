@@ -73,7 +73,10 @@ __global__ __launch_bounds__(256, 1) void gemm_narrow_kernel(GemmArgs g, int til
     const int tg = tz - g0 * tiles_n;
     const int m0 = (g0 + tg % gsz) * BM, n0 = (tg / gsz) * BN;
 
-    // A load: chunk tid of the 32-row block (row tid / 8)
+    // A load: chunk tid of the 32-row block (row tid / 8); a wave whose 8
+    // rows all lie past the count loads nothing (uniform: its rows' results
+    // are never stored, whatever LDS holds for them)
+    const bool a_on = m0 + 8 * wave < M;
     const void* a_buf = g.A + (int64_t)z * g.a_bstride;
     const int a_bytes = (int)(a_nrows * g.lda * 2);
     uint32_t a_off;
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256, 1) void gemm_narrow_kernel(GemmArgs g, int til
     auto issue = [&](int st, int k) {
       u32x4* l = L + st * SSZ;
       const int j = k + j0 < KT ? k + j0 : k + j0 - KT;
-      buf_lds<16>(a_buf, a_bytes, a_off, j * 128, l + wave * 64);
+      if (a_on) buf_lds<16>(a_buf, a_bytes, a_off, j * 128, l + wave * 64);
 #pragma unroll
       for (int i = 0; i < BD; ++i) buf_lds<16>(b_buf, b_bytes, b_off[i], j * 128, l + BM * 8 + (i * 4 + wave) * 64);
     };
@@ -138,7 +141,9 @@ __global__ __launch_bounds__(256, 1) void gemm_narrow_kernel(GemmArgs g, int til
     // stage, the MFMAs of slab kt
     auto iter = [&](auto st, int kt, auto w, auto iss) {
       constexpr int ST = decltype(st)::value;
-      wait_barrier<decltype(w)::value * PER, true>();
+      // the loads of this wave per slab: PER, or PER - 1 without its A rows
+      if (a_on) wait_barrier<decltype(w)::value * PER, true>();
+      else wait_barrier<decltype(w)::value * (PER - 1), true>();
       if constexpr (decltype(iss)::value) issue((ST + NARROW_NS - 1) % NARROW_NS, kt + NARROW_NS - 1);
       compute(ST);
     };
