@@ -539,16 +539,25 @@ def decode_times(key, steps):
     cfg = dw.cfg
     n_ck = len(dw.cks)
     if cfg.n_tokens <= 1024 and n_ck <= (16 if cfg.b else 32):
-        scores = "one route launch for all checkpoints" if cfg.b else "cosines of all checkpoints"
+        if cfg.b:
+            scores = ("the routes of all checkpoints in two halves of d per token group, their sum"
+                      if cfg.d % 512 == 0 else "one route launch for all checkpoints")
+        else:
+            scores = "cosines of all checkpoints"
         plain = sum(c.get("maps") is None for c in dw.cks)
+        # the fills: one for the checkpoints without maps when there are two
+        # or more of them, one per other checkpoint; from two on the first
+        # of the others runs on a second stream
+        fills = (1 if plain >= 2 else plain) + (n_ck - plain)
+        two = " (the first of them on a second stream)" if fills >= 2 else ""
         if plain == n_ck:
             path = (f"{scores}, one decision workgroup, gather of the exit states, one projection "
                     "over all filled blocks")
         elif plain >= 2:
             path = (f"{scores}, one decision workgroup, gather of the exit states and one projection "
-                    "for the checkpoints without maps, a fill per checkpoint with maps")
+                    f"for the checkpoints without maps, a fill per checkpoint with maps{two}")
         else:
-            path = f"{scores}, one decision workgroup, a fill per checkpoint"
+            path = f"{scores}, one decision workgroup, a fill per checkpoint{two}"
     else:
         path = "per checkpoint: route, compact, fill"
     del g
