@@ -37,6 +37,16 @@
 // all reads of this one are done, so the rest of the sub-step reads the next
 // stage's first fragments and starts loads into the freed space.
 //
+// A tile starts with the B rows of its first stage: their offsets need no
+// row ids, so they go out while the row ids of the A rows (a gather) land.
+// It ends through LDS: each wave writes its 128 x 128 block as bf16 into
+// 32 KB of LDS and reads it back a row piece at a time, so that every store
+// covers 4 rows x 256 contiguous bytes (where storing straight from the
+// accumulators wrote 16-byte pieces of 32 rows per store). Measured on the
+// same box, bit-identical: 30704 x 5120 x 5120 x 8 at 1288-1335 TFLOP/s
+// against 1224-1290; on 63472 x 5120 x K x 8 the cost of a tile beyond its
+// stages fell from about 13 to 10 µs (K from 320 to 5120).
+//
 // The MFMAs run in the same order on the same fragments as gemm_big.h
 // (slab by slab, sub-step 0 then 1, K-chunk 2 h + s of the slab), so the
 // results are bit-identical to it.
@@ -45,6 +55,16 @@
 #include "gemm_big.h"
 
 namespace river {
+
+// waits for this wave's LDS reads, then the workgroup barrier (no wait on
+// the global loads)
+__device__ __forceinline__ void quad_lds_barrier_() {
+  constexpr int imm = 15 | (3 << 14) | (7 << 4) | (0 << 8);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(imm);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Per-tile state of the 4-wave kernels: the tile walk, the load offsets,
 // the fragment reads and the epilogue, shared by both pipelines.
@@ -60,6 +80,7 @@ struct QuadTile {
   const void* b_buf;
   int a_bytes, b_bytes, b_rowstep;
   uint32_t a_off[AD], b_off[2];
+  int src[AD];                           // source rows of the A loads (row ids, then offsets())
   int pa[2][2], pb[2][2];                // read byte offsets within an operand block
   int er[MI], sl[MI];                    // EPI_CACHE: row ids, then slots
 
@@ -94,27 +115,25 @@ struct QuadTile {
     // an operand block: row p / 8 = 32 i + 8 wave + lane / 8, physical chunk
     // lane % 8 holding logical chunk (lane % 8) ^ swz(row); swz(row) depends
     // on i only through i % 2, so the B loads i and i + 2 differ by 64 rows
-    const int a_nrows = g.a_nrows;
+    // the row ids go out now; offsets() turns them into the A offsets
     a_buf = g.A + (int64_t)z * g.a_bstride;
-    a_bytes = (int)(a_nrows * g.lda * 2);
+    a_bytes = (int)(g.a_nrows * g.lda * 2);
 #pragma unroll
     for (int i = 0; i < AD; ++i) {
-      const int r = i * 32 + wave * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(r);
-      const int t = m0 + r;
-      int src = g.a_rows ? g.a_rows[t < M ? t : M - 1] : t;
-      if (src < 0 || src >= a_nrows) src = 0;   // row 0 stands in; dropped
-      // rows past the count read zeros without a fetch (not stored either)
-      a_off[i] = t >= M ? BUF_OOB : (uint32_t)(((int64_t)src * g.lda + c * 8) * 2);
+      const int t = m0 + i * 32 + wave * 8 + (lane >> 3);
+      src[i] = g.a_rows ? g.a_rows[t < M ? t : M - 1] : t;
     }
     b_buf = g.B + (int64_t)z * g.b_bstride;
-    b_bytes = (int)(N * g.ldb * 2);                           // rows past N read zeros
+    b_bytes = (int)(N * g.ldb * 2);
     b_rowstep = 64 * g.ldb * 2;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = i * 32 + wave * 8 + (lane >> 3);
       const int c = (lane & 7) ^ swz(r);
-      b_off[i] = (uint32_t)(((int64_t)(n0 + r) * g.ldb + c * 8) * 2);
+      // rows past N read zeros without a fetch; below N the offset lies
+      // under b_bytes < 2^31 (32-bit arithmetic: a 64-bit form here made
+      // the compiler wait for the row ids before the B loads)
+      b_off[i] = n0 + r >= N ? BUF_OOB : (uint32_t)(n0 + r) * (uint32_t)(g.ldb * 2) + (uint32_t)(c * 16);
     }
     // read offsets: rows 32 apart differ in swz by 4, so row r + 32 m of
     // logical chunk ch sits at (r + 32 m) * 8 + (ch ^ swz(r) ^ 4 (m & 1));
@@ -127,6 +146,21 @@ struct QuadTile {
         pa[s][jx] = (rowa * 8 + ((4 * jx + 2 * h + s) ^ swz(rowa))) * 16;
         pb[s][jx] = (rowb * 8 + ((4 * jx + 2 * h + s) ^ swz(rowb))) * 16;
       }
+  }
+
+  // the A offsets from the row ids (waits for them)
+  __device__ __forceinline__ void offsets() {
+#pragma unroll
+    for (int i = 0; i < AD; ++i) {
+      const int r = i * 32 + wave * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(r);
+      const int t = m0 + r;
+      int s = src[i];
+      if (s < 0 || s >= g.a_nrows) s = 0;   // row 0 stands in; dropped
+      // rows past the count read zeros without a fetch (not stored either);
+      // s < a_nrows and a_nrows * lda * 2 < 2^31: exact in 32 bits
+      a_off[i] = t >= M ? BUF_OOB : (uint32_t)s * (uint32_t)(g.lda * 2) + (uint32_t)(c * 16);
+    }
   }
 
   // load x (0-7) of stage j's A rows, or of its B rows, into the 32 KB
@@ -161,46 +195,62 @@ struct QuadTile {
     else f.b[e - MI] = *(const bf16x8*)(base + bb[s][j ^ (e & 1)] + (e - MI) * 4096);
   }
 
-  // ---- epilogue, straight from the accumulators: lane l holds row
-  // mi * 32 + l % 32 of the wave block and, per group gq, the four
-  // consecutive columns ni * 32 + 8 gq + 4 (l / 32) + 0..3
-  __device__ __forceinline__ void store(const f32x16 (&acc)[MI][NI]) const {
-    const int rb = m0 + wm * 128, cb = n0 + wn * 128;
+  // ---- epilogue through LDS. Lane l holds row mi * 32 + l % 32 of the
+  // wave block and, per group gq, the four consecutive columns
+  // ni * 32 + 8 gq + 4 (l / 32) + 0..3. The block goes as bf16 into the
+  // wave's 32 KB of LDS (units 0-3; row r, 16-byte chunk c at
+  // r * 16 + (c ^ (r & 15)): conflict-free both ways) and comes back as 4
+  // rows x 16 chunks per read, each lane storing 16 bytes. EPI_CACHE: the
+  // slots of the block's rows go to LDS as well (after the units, 512 bytes
+  // per wave), since a lane stores other rows than it holds. Every wave
+  // reads back only its own block, so one barrier (the last stage's reads
+  // done) suffices; the next tile's first loads wait at its own barrier.
+  __device__ __forceinline__ void store(const f32x16 (&acc)[MI][NI], u32x4* L) const {
+    quad_lds_barrier_();
+    // the lane's byte offset in its row through a move the compiler cannot
+    // hoist: otherwise it keeps the 16 chunk offsets of every lane live
+    // across the tiles (and spills them)
+    int lo;
+    asm volatile("v_lshlrev_b32 %0, 3, %1" : "=v"(lo) : "v"(lane >> 5));
+    const int x = lane & 15, r0 = lane & 31;
+    char* W = (char*)(L + wave * 2048);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int r = mi * 32 + r0;                 // r & 15 == x
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int c = ni * 4 + gq;
+          *(uint2*)(W + r * 256 + ((c ^ x) << 4) + lo) =
+              uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
+                    pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
+        }
+    }
+    int* S = (int*)(L + 4 * 2048) + wave * 128;
     if constexpr (EPI == EPI_CACHE) {
+      if (lane < 32) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = rb + mi * 32 + (lane & 31);
-        const int slot = sl[mi];
-        if (row >= M || slot < 0 || slot >= g.n_slots) continue;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int col = cb + ni * 32 + 8 * gq + 4 * h;
-            if (col >= N) continue;
-            const bool isv = col >= g.nh;
-            uint16_t* dst = (uint16_t*)(isv ? g.vc : g.kc) + (int64_t)z * g.cache_bstride +
-                            (int64_t)slot * g.nh + (isv ? col - g.nh : col);
-            *(uint2*)dst = uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
-                                 pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
-          }
+        for (int mi = 0; mi < MI; ++mi) S[mi * 32 + lane] = sl[mi];
       }
-    } else {
-      uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.c_bstride;
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi) {
-        const int row = rb + mi * 32 + (lane & 31);
-        if (row >= M) continue;
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int col = cb + ni * 32 + 8 * gq + 4 * h;
-            if (col >= N) continue;
-            *(uint2*)(C + (int64_t)row * g.ldc + col) =
-                uint2{pack_bf16x2(acc[mi][ni][4 * gq], acc[mi][ni][4 * gq + 1]),
-                      pack_bf16x2(acc[mi][ni][4 * gq + 2], acc[mi][ni][4 * gq + 3])};
-          }
+    }
+    const u32x4* R = L + wave * 2048;
+    const int rb = m0 + wm * 128, cb = n0 + wn * 128;
+    uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.c_bstride;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) {
+      const int r = i * 4 + (lane >> 4), c = lane & 15;
+      const u32x4 v = R[r * 16 + (c ^ (r & 15))];
+      const int row = rb + r, col = cb + c * 8;
+      if (row >= M || col >= N) continue;
+      if constexpr (EPI == EPI_CACHE) {
+        const int slot = S[r];
+        if (slot < 0 || slot >= g.n_slots) continue;
+        const bool isv = col >= g.nh;
+        *(u32x4*)((uint16_t*)(isv ? g.vc : g.kc) + (int64_t)z * g.cache_bstride + (int64_t)slot * g.nh +
+                  (isv ? col - g.nh : col)) = v;
+      } else {
+        *(u32x4*)(C + (int64_t)row * g.ldc + col) = v;
       }
     }
   }
@@ -214,15 +264,7 @@ __device__ __forceinline__ void quad_mfma(f32x16 (&acc)[4][4], const Frag& f, in
   acc[k >> 2][k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[k & 3], f.a[k >> 2], acc[k >> 2][k & 3], 0, 0, 0);
 }
 
-// waits for this wave's LDS reads, then the workgroup barrier (no wait on
-// the global loads)
-__device__ __forceinline__ void quad_lds_barrier() {
-  constexpr int imm = 15 | (3 << 14) | (7 << 4) | (0 << 8);   // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(imm);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
+__device__ __forceinline__ void quad_lds_barrier() { quad_lds_barrier_(); }
 
 // byte offsets plus a block base, through a register move the compiler
 // cannot hoist (otherwise it keeps one set per block live across the loop)
@@ -277,12 +319,14 @@ __global__ __launch_bounds__(256, 1) void gemm_quad_kernel(GemmArgs g, int tiles
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[mi][ni][e] = 0.f;
 
-    // prologue: A(0) in unit 0, B(0) in 1, A(1) in 2, B(1) loads 0-3 in 3;
-    // A(0) and B(0) landed
-#pragma unroll
-    for (int x = 0; x < 8; ++x) q.load_a(L, 0, x);
+    // prologue: B(0) in unit 1 (while the row ids land), A(0) in 0, A(1)
+    // in 2, B(1) loads 0-3 in 3; A(0) and B(0) landed
 #pragma unroll
     for (int x = 0; x < 8; ++x) q.load_b(L + 2048, 0, x);
+    __builtin_amdgcn_sched_barrier(0);
+    q.offsets();
+#pragma unroll
+    for (int x = 0; x < 8; ++x) q.load_a(L, 0, x);
 #pragma unroll
     for (int x = 0; x < 8; ++x) q.load_a(L + 2 * 2048, 1, x);
 #pragma unroll
@@ -365,7 +409,7 @@ __global__ __launch_bounds__(256, 1) void gemm_quad_kernel(GemmArgs g, int tiles
     iter(I2{}, t + 2, T_{}, T_{});
     iter(I3{}, t + 3, T_{}, F_{});
     iter(I4{}, t + 4, F_{}, F_{});
-    q.store(acc);
+    q.store(acc, L);
   }
 }
 
@@ -375,7 +419,7 @@ __global__ __launch_bounds__(256, 1) void gemm_quad2_kernel(GemmArgs g, int tile
   static_assert(EPI == EPI_BF16 || EPI == EPI_CACHE, "bf16 output");
   using T = QuadTile<EPI>;
   using Frag = typename T::Frag;
-  __shared__ u32x4 L[4 * 2048];          // [A 0][A 1][B 0][B 1]
+  __shared__ u32x4 L[4 * 2048 + 128];    // [A 0][A 1][B 0][B 1], then the epilogue's slots
 
   int M = g.M_max;
   if (g.M_dev) {
@@ -411,8 +455,13 @@ __global__ __launch_bounds__(256, 1) void gemm_quad2_kernel(GemmArgs g, int tile
       else q.load_b(L + 4096 + S * 2048, j, x - 8);
     };
 
+    // B(0) first (while the row ids land), then A(0) and stage 1's loads 0-5
 #pragma unroll
-    for (int x = 0; x < 16; ++x) load(0, 0, x);
+    for (int x = 8; x < 16; ++x) load(0, 0, x);
+    __builtin_amdgcn_sched_barrier(0);
+    q.offsets();
+#pragma unroll
+    for (int x = 0; x < 8; ++x) load(0, 0, x);
 #pragma unroll
     for (int x = 0; x < 6; ++x) load(1, 1, x);
     wait_barrier<6, true>();               // stage 0 landed
@@ -482,13 +531,13 @@ __global__ __launch_bounds__(256, 1) void gemm_quad2_kernel(GemmArgs g, int tile
     }
     iter(I0{}, t, T_{}, F_{});
     iter(I1{}, t + 1, F_{}, F_{});
-    q.store(acc);
+    q.store(acc, L);
   }
 }
 
 // Launch: one workgroup of 4 waves per CU, capped by the tile count and
-// rounded up to whole XCDs. K % 128 == 0 (the ring at K % 320 == 0), N % 4
-// == 0, the other requirements as gemm_launch's.
+// rounded up to whole XCDs. quad_ok (the ring at K % 320 == 0), the other
+// requirements as gemm_launch's.
 template <int EPI>
 inline void gemm_quad_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + 255) / 256;
@@ -499,6 +548,18 @@ inline void gemm_quad_launch(const GemmArgs& g, int batch, hipStream_t s) {
   else gemm_quad2_kernel<EPI><<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);
 }
 
+// The 4-wave kernels' conditions besides the launch's: K % 128 == 0, and
+// the epilogue's 16-byte stores of 8 columns: N and the output row pitch (ldc,
+// or nh for the cache) multiples of 8, the output 16-byte aligned.
+template <int EPI>
+inline bool quad_ok(const GemmArgs& g) {
+  if (g.K % 128 || g.N % 8) return false;
+  if constexpr (EPI == EPI_CACHE)
+    return g.nh % 8 == 0 && g.cache_bstride % 8 == 0 && ((uintptr_t)g.kc | (uintptr_t)g.vc) % 16 == 0;
+  else
+    return g.ldc % 8 == 0 && g.c_bstride % 8 == 0 && (uintptr_t)g.C % 16 == 0;
+}
+
 // bf16-output GEMM: 256 x 256 tiles from 1024 rows on when they give at
 // least one tile per CU (measured: 7782 rows of one 4096-wide layer, 496
 // tiles, run 15% faster than on 128 x 128 tiles), the 128-row kernel
@@ -507,8 +568,9 @@ inline void gemm_quad_launch(const GemmArgs& g, int batch, hipStream_t s) {
 // against 240 of 128 x 128; the whole fill measured 43 µs instead of 30),
 // so there the big tiles need two per CU at the bound.
 // The 256 x 256 tiles run on the 4-wave kernels of this file when K is a
-// multiple of 128 (and the output has no norm epilogue), on gemm_big.h's
-// 8-wave kernel otherwise (and always under gemm path 3).
+// multiple of 128 and the output allows 16-byte stores (quad_ok; and the
+// output has no norm epilogue), on gemm_big.h's 8-wave kernel otherwise (and
+// always under gemm path 3).
 template <int EPI>
 inline void gemm_bf16_auto(const GemmArgs& g, int batch, hipStream_t s) {
   const int64_t big = (int64_t)((g.N + 255) / 256) * ((g.M_max + 255) / 256) * batch;
@@ -516,7 +578,7 @@ inline void gemm_bf16_auto(const GemmArgs& g, int batch, hipStream_t s) {
   const bool auto_big = g.M_dev ? big >= 2 * N_CU : (g.M_max >= 1024 && big >= N_CU);
   if (path == 2 || path == 3 || (path == 0 && auto_big)) {
     if constexpr (EPI == EPI_BF16) {
-      if (path != 3 && g.K % 128 == 0) {
+      if (path != 3 && quad_ok<EPI>(g)) {
         gemm_quad_launch<EPI>(g, batch, s);
         return;
       }
@@ -530,7 +592,7 @@ inline void gemm_bf16_auto(const GemmArgs& g, int batch, hipStream_t s) {
 // The projection on dequantised weights (EPI_CACHE), on the same choice of
 // kernel by K and gemm path 3.
 inline void gemm_cache_launch(const GemmArgs& g, int batch, hipStream_t s) {
-  if (river_host::gemm_path_override() != 3 && g.K % 128 == 0) gemm_quad_launch<EPI_CACHE>(g, batch, s);
+  if (river_host::gemm_path_override() != 3 && quad_ok<EPI_CACHE>(g)) gemm_quad_launch<EPI_CACHE>(g, batch, s);
   else gemm_big_launch<EPI_CACHE>(g, batch, s);
 }
 
