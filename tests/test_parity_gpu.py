@@ -567,6 +567,44 @@ def test_kv_fill_quad_tiles_equal_eight_wave_tiles(count_on_device, d):
     check_fill(cfg, kc, vc, h, sel.numpy(), slot, maps, wk, wv)
 
 
+@pytest.mark.parametrize("d", [1280, 1152])
+def test_kv_fill_quad_tiles_ragged_columns(d):
+    """Column tiles that run past the output: 5 K/V heads of 64 (640
+    projection columns, 2.5 tiles of 256) and, at d = 1152, 4.5 tiles of map
+    columns (the two-stage 4-wave kernel; d = 1280 takes the ring). The
+    4-wave kernels stage each tile's output in LDS and store only columns
+    below N and rows below the count; they agree bit for bit with the 8-wave
+    kernel and stay within the K/V bar of the oracle."""
+    cfg = get_config(1, d=d, n_kv_heads=5, n_tokens=640, n_slots=700)
+    layers = [5, 6]
+    nl = len(layers)
+    h = G.hidden_states(cfg, cfg.n_tokens, [4])[4].to(DEV)
+    g = torch.Generator().manual_seed(161)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    maps = G.near_identity_maps(cfg, nl, scale=0.5).to(DEV)
+    sel = torch.sort(torch.randperm(cfg.n_tokens, generator=g)[:333]).values.to(torch.int32)
+    rows = sel.to(DEV)
+    nh = cfg.n_kv_heads * cfg.head_dim
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, 333, cfg.d, nh, 0, nl)
+                     + nl * 2 * nh * cfg.d * 2, dtype=torch.uint8, device=DEV)
+    out = {}
+    try:
+        for p in (2, 3):
+            tee.river_debug_set_gemm_path(p)
+            kc, vc = G.nan_cache(cfg, nl, device=DEV)
+            tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=333,
+                              row_idx=rows, maps=maps, workspace=ws)
+            torch.cuda.synchronize()
+            out[p] = (kc, vc)
+    finally:
+        tee.river_debug_set_gemm_path(0)
+    for a, b in zip(out[2], out[3]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    kc, vc = out[2]
+    check_fill(cfg, kc, vc, h, sel.numpy(), slot, maps, wk, wv)
+
+
 def test_kv_fill_identity_null_equals_explicit_eye():
     cfg = get_config(2)
     layers = list(range(9, 17))
