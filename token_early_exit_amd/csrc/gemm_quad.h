@@ -58,7 +58,7 @@ namespace river {
 
 // waits for this wave's LDS reads, then the workgroup barrier (no wait on
 // the global loads)
-__device__ __forceinline__ void quad_lds_barrier_() {
+__device__ __forceinline__ void quad_lds_barrier() {
   constexpr int imm = 15 | (3 << 14) | (7 << 4) | (0 << 8);   // lgkmcnt(0)
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(imm);
@@ -206,7 +206,7 @@ struct QuadTile {
   // reads back only its own block, so one barrier (the last stage's reads
   // done) suffices; the next tile's first loads wait at its own barrier.
   __device__ __forceinline__ void store(const f32x16 (&acc)[MI][NI], u32x4* L) const {
-    quad_lds_barrier_();
+    quad_lds_barrier();
     // the lane's byte offset in its row through a move the compiler cannot
     // hoist: otherwise it keeps the 16 chunk offsets of every lane live
     // across the tiles (and spills them)
@@ -263,8 +263,6 @@ template <class Frag>
 __device__ __forceinline__ void quad_mfma(f32x16 (&acc)[4][4], const Frag& f, int k) {
   acc[k >> 2][k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[k & 3], f.a[k >> 2], acc[k >> 2][k & 3], 0, 0, 0);
 }
-
-__device__ __forceinline__ void quad_lds_barrier() { quad_lds_barrier_(); }
 
 // byte offsets plus a block base, through a register move the compiler
 // cannot hoist (otherwise it keeps one set per block live across the loop)
