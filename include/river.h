@@ -260,6 +260,14 @@ river_status river_exit_projection(int m_max, const int32_t* m_dev, int d, river
  *            maps and a workspace for fewer layers than n_layers, a chunk
  *            at such row counts takes as many x_hat layers as leave room
  *            for its dequantised weights (when one layer does).
+ *            With maps, bf16, d % 128 == 0 and m_max >= 4 * n_out rows
+ *            given on the host (m_dev NULL), the fill instead forms per
+ *            layer F = deq([Wk; Wv]) . maps[l] (2 n_out x d, bf16) and
+ *            projects the rows through it, K|V = F . h[r]: the same values
+ *            up to rounding, in 2 n_out d^2 instead of 2 m d^2 flops for
+ *            the maps; it needs 2 x (2 n_out d) + d^2 bf16 per layer of the
+ *            chunk (the dequantised weights, the transposed map and F),
+ *            which the size above holds at such row counts.
  * Only the filled slots are written; every other byte is left unchanged.
  * Paths: bf16 with d % 256 == 0, n_out % 64 == 0, group % 64 == 0, the
  * same group and scale/zero dtype for wk and wv, an even number of groups
@@ -529,13 +537,45 @@ river_status river_debug_set_gemm_path(int path);
  * reduction into the same parts (otherwise they agree to rounding). */
 river_status river_debug_set_decode_path(int path);
 
+/* Test hook: how river_kv_fill runs a plain fill with maps on its MFMA path
+ * (bf16, d % 128 == 0, the row count given on the host): 0 = automatic
+ * (through the product F = deq([Wk; Wv]) . maps per layer from m_max >=
+ * 4 n_out rows on, when the workspace holds one layer of dequantised
+ * weights, transposed map and F), 1 = never, 2 = whenever the workspace
+ * holds it. Process-wide; the two ways agree to rounding. */
+river_status river_debug_set_fill_fuse(int mode);
+
+/* Launches river_kv_fill can time (river_debug_time_kernels). */
+typedef enum {
+  RIVER_TIMED_FILL_PROJECTION = 0, /* the bf16 projection into the cache: through the
+                                      product F, or on dequantised weights           */
+  RIVER_TIMED_FILL_PRODUCT = 1     /* the GEMM F = deq([Wk; Wv]) . maps               */
+} river_timed_kernel;
+
+/* Measurement hook: with on != 0, river_kv_fill records a pair of HIP events
+ * on its stream right before and after each launch named in
+ * river_timed_kernel (of the current device, up to 1024 pairs not yet read;
+ * none on a stream under graph capture). Process-wide; on = 0 stops new
+ * records. Timing adds an event record before and after the launch and no
+ * other work. */
+river_status river_debug_time_kernels(int on);
+
+/* Reads and clears the records of one river_timed_kernel: waits for each
+ * record's end event, then *total_ms = the sum of the elapsed times and
+ * *launches = their number (0 and 0.0 when none). Records whose end was
+ * never recorded (a launch that failed) are dropped uncounted.
+ * RIVER_ERR_ARG for an unknown kind or a null pointer, RIVER_ERR_HIP when
+ * waiting for an event fails. */
+river_status river_debug_kernel_times(int kind, double* total_ms, int* launches);
+
 /* Test hook, host only (enqueues nothing): the plan river_kv_fill takes for
  * a plain bf16 fill with maps on its MFMA path (d % 256 == 0, n_out =
  * n_kv_heads * head_dim with n_out % 64 == 0) given ws_bytes of workspace:
  * *chunk = layers per chunk (x_hat of that many layers held at once; at
  * large row counts after the room of the chunk's dequantised weights, when
  * at least one layer fits beside them), *path = the projection's
- * path for the first chunk (0 = int4 dequantised in registers, 1 = split
+ * path for the first chunk (3 = through the product F = deq(W) . maps,
+ * *chunk then its layers per chunk; 0 = int4 dequantised in registers, 1 = split
  * reduction over d in *parts parts, 2 = bf16 GEMM on weights dequantised
  * into the workspace), *parts = the split's parts (1 otherwise).
  * dev_count != 0: the row count lives on the device. The gemm-path hook

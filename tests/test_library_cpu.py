@@ -37,6 +37,15 @@ def test_version_and_error_string():
     assert tee.load().river_last_error() is not None
 
 
+def test_kernel_timing_hook_rejects_unknown_kinds():
+    """The timing switch only sets a flag (no device call); reading an
+    unknown launch kind is an argument error before any device call."""
+    tee.river_debug_time_kernels(False)
+    for kind in (-1, 2, 99):
+        with pytest.raises(RuntimeError, match="ERR_ARG"):
+            tee.river_debug_kernel_times(kind)
+
+
 def test_workspace_sizes():
     ws = tee.river_workspace_size
     assert ws(tee.OP_ROUTE, 4096, 768) == 0
@@ -241,6 +250,14 @@ def test_kv_fill_plan_keeps_room_for_dequantised_weights():
     registers."""
     m, d, no = 4096, 1024, 1024
     xb = m * d * 2
+    tee.river_debug_set_fill_fuse(1)             # the x_hat path (not through the product)
+    try:
+        _plan_keeps_room(m, d, no, xb)
+    finally:
+        tee.river_debug_set_fill_fuse(0)
+
+
+def _plan_keeps_room(m, d, no, xb):
     ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, no, 0, 6)
     chunk, path, parts = tee.river_debug_kv_fill_plan(m, d, no, 12, ws)
     assert path == 2 and parts == 1
@@ -261,16 +278,42 @@ def test_kv_fill_plan_keeps_room_for_dequantised_weights():
     assert tee.river_debug_kv_fill_plan(m, d, no, 12, ws, dev_count=True) == (12, 0, 1)
 
 
-@pytest.mark.parametrize("m,d,nl,want", [
-    (30704, 5120, 48, (48, 2, 1)),     # long-context prefill at 32K tokens
-    (63472, 5120, 48, (48, 2, 1)),     # and at 64K
-    (7782, 4096, 1, (1, 2, 1)),        # 8B prefill, the late exits
-    (410, 4096, 21, (21, 0, 1)),       # 8B prefill, the early exits
-    (64, 4096, 8, (8, 1, 4)),          # decode-sized: split reduction
+@pytest.mark.parametrize("m,d,nl,want,want_xhat", [
+    (30704, 5120, 48, (48, 3, 1), (48, 2, 1)),     # long-context prefill at 32K tokens
+    (63472, 5120, 48, (48, 3, 1), (48, 2, 1)),     # and at 64K
+    (7782, 4096, 1, (1, 3, 1), (1, 2, 1)),         # 8B prefill, the late exits
+    (410, 4096, 21, (21, 0, 1), (21, 0, 1)),       # 8B prefill, the early exits
+    (64, 4096, 8, (8, 1, 4), (8, 1, 4)),           # decode-sized: split reduction
 ])
-def test_kv_fill_plan_at_the_workload_shapes(m, d, nl, want):
+def test_kv_fill_plan_at_the_workload_shapes(m, d, nl, want, want_xhat):
+    """From 4 n_out rows given on the host the fill runs through the product
+    of weights and maps (path 3); below, and with the row count on the
+    device, through x_hat; the fill-fuse hook can switch the product off."""
     ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, 1024, 0, nl)
     assert tee.river_debug_kv_fill_plan(m, d, 1024, nl, ws) == want
+    assert tee.river_debug_kv_fill_plan(m, d, 1024, nl, ws, dev_count=True)[1] != 3
+    tee.river_debug_set_fill_fuse(1)
+    try:
+        assert tee.river_debug_kv_fill_plan(m, d, 1024, nl, ws) == want_xhat
+    finally:
+        tee.river_debug_set_fill_fuse(0)
+
+
+def test_kv_fill_plan_product_chunks_by_its_own_layer_size():
+    """Through the product a layer needs its dequantised K|V weights, its
+    transposed map and the product (2 x 2 n_out d + d^2 bf16), so a
+    workspace for fewer layers splits the call into chunks of that many."""
+    m, d, no, nl = 63472, 5120, 1024, 48
+    per = 2 * (2 * no * d * 2) + d * d * 2
+    assert tee.river_debug_kv_fill_plan(m, d, no, nl, 10 * per + 100) == (10, 3, 1)
+    tee.river_debug_set_fill_fuse(2)
+    try:
+        # forced: from one row on, whatever the count, when a layer's room fits
+        per = 2 * (2 * 1024 * 1024 * 2) + 1024 * 1024 * 2
+        assert tee.river_debug_kv_fill_plan(300, 1024, 1024, 4, 4 * per) == (4, 3, 1)
+        assert tee.river_debug_kv_fill_plan(300, 1024, 1024, 4, per - 1)[1] != 3
+    finally:
+        tee.river_debug_set_fill_fuse(0)
 
 
 def test_kv_fill_plan_rejects_a_workspace_under_one_layer():
@@ -303,7 +346,14 @@ def test_long_context_64k_spans_fit_31_bits():
     assert d * np_ * 2 < lim and d * ((3 * d + 255) // 256 * 256) * 2 < lim
     ws = tee.river_workspace_size(tee.OP_KV_FILL, m, d, n_out, 0, nl)
     assert ws >= nl * m * d * 2 + nl * 2 * n_out * d * 2
-    assert tee.river_debug_kv_fill_plan(m, d, n_out, nl, ws) == (nl, 2, 1)
+    # through the product: one layer of F (2 n_out x d, the projection's B)
+    # and one transposed map (its B) are the spans above
+    assert tee.river_debug_kv_fill_plan(m, d, n_out, nl, ws) == (nl, 3, 1)
+    tee.river_debug_set_fill_fuse(1)
+    try:
+        assert tee.river_debug_kv_fill_plan(m, d, n_out, nl, ws) == (nl, 2, 1)
+    finally:
+        tee.river_debug_set_fill_fuse(0)
 
 
 def test_ridge_fit_rejects_31_bit_overflow():

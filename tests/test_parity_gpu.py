@@ -605,6 +605,94 @@ def test_kv_fill_quad_tiles_ragged_columns(d):
     check_fill(cfg, kc, vc, h, sel.numpy(), slot, maps, wk, wv)
 
 
+@pytest.mark.parametrize("d,heads,m,nl", [(768, 12, 3100, 3), (1280, 5, 1300, 2)])
+def test_kv_fill_through_the_product_of_weights_and_maps(d, heads, m, nl):
+    """From 4 n_out rows given on the host the plain fill with maps forms F =
+    deq([Wk; Wv]) . maps per layer and projects the rows through it (the
+    fill and the projection are both linear, so K and V are the same up to
+    rounding). Both ways, through F and through x_hat (the fill-fuse hook),
+    stay within the K/V bar of the oracle on every row, and agree with each
+    other to it. d = 768 takes the two-stage 4-wave kernels; d = 1280 the
+    ring, with 640 projection columns and F's 640 rows both ragged tiles of
+    256. Ridge-fitted maps from the calibration states, rows in random
+    order, slots a permutation."""
+    cfg = get_config(1, d=d, n_kv_heads=heads, n_tokens=m + 200, n_slots=m + 300)
+    e = 4
+    layers = list(range(e + 1, e + 1 + nl))
+    X, Y = G.calibration(cfg, e)
+    maps = torch.from_numpy(O.ridge_fit(np64(X), np64(Y[:nl]), cfg.ridge_lambda)).to(torch.bfloat16).to(DEV)
+    h = G.hidden_states(cfg, cfg.n_tokens, [e])[e].to(DEV)
+    g = torch.Generator().manual_seed(162)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    rows = torch.randperm(cfg.n_tokens, generator=g)[:m].to(torch.int32)
+    nh = cfg.n_kv_heads * cfg.head_dim
+    assert m >= 4 * nh
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, m, d, nh, 0, nl), dtype=torch.uint8, device=DEV)
+    assert tee.river_debug_kv_fill_plan(m, d, nh, nl, ws.numel())[1] == 3
+    out = {}
+    try:
+        for mode in (0, 1):
+            tee.river_debug_set_fill_fuse(mode)
+            kc, vc = G.nan_cache(cfg, nl, device=DEV)
+            tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=m,
+                              row_idx=rows.to(DEV), maps=maps, workspace=ws)
+            torch.cuda.synchronize()
+            out[mode] = (kc, vc)
+    finally:
+        tee.river_debug_set_fill_fuse(0)
+    for mode in (0, 1):
+        check_fill(cfg, *out[mode], h, rows.numpy(), slot, maps, wk, wv)
+    s = slot[rows.to(DEV).long()].long()
+    for a, b in zip(out[0], out[1]):
+        x, y = a[:, s].float().reshape(nl, m, -1), b[:, s].float().reshape(nl, m, -1)
+        err = (x - y).norm(dim=-1) / y.norm(dim=-1).clamp_min(1e-30)
+        assert err.max().item() <= KV_TOL, err.max().item()
+
+
+def test_kv_fill_times_its_gemm_launches_when_asked():
+    """The measurement hook: with timing on, every chunk of a fill through
+    the product leaves one timed product launch and one timed projection
+    launch, each with a positive elapsed time; reading clears the records;
+    with timing off the fill records nothing. The timed fill's K and V equal
+    the untimed fill's bit for bit."""
+    cfg = get_config(1, d=768, n_kv_heads=12, n_tokens=3300, n_slots=3400)
+    m, nl, e = 3100, 3, 4
+    layers = list(range(e + 1, e + 1 + nl))
+    g = torch.Generator().manual_seed(163)
+    maps = (torch.eye(cfg.d) + 0.02 * torch.randn(nl, cfg.d, cfg.d, generator=g)).to(torch.bfloat16).to(DEV)
+    h = G.hidden_states(cfg, cfg.n_tokens, [e])[e].to(DEV)
+    slot = torch.randperm(cfg.n_slots, generator=g)[: cfg.n_tokens].to(torch.int32).to(DEV)
+    wk, wv = _kv(cfg, layers)
+    rows = torch.randperm(cfg.n_tokens, generator=g)[:m].to(torch.int32).to(DEV)
+    nh = cfg.n_kv_heads * cfg.head_dim
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FILL, m, cfg.d, nh, 0, nl), dtype=torch.uint8,
+                     device=DEV)
+    chunk, path, _ = tee.river_debug_kv_fill_plan(m, cfg.d, nh, nl, ws.numel())
+    assert path == 3
+    chunks = -(-nl // chunk)
+    for kind in (tee.TIMED_FILL_PROJECTION, tee.TIMED_FILL_PRODUCT):
+        tee.river_debug_kernel_times(kind)
+    out = []
+    for on in (True, False):
+        kc, vc = G.nan_cache(cfg, nl, device=DEV)
+        tee.river_debug_time_kernels(on)
+        try:
+            tee.river_kv_fill(h, slot, wk, wv, cfg.n_kv_heads, cfg.head_dim, kc, vc, m_max=m, row_idx=rows,
+                              maps=maps, workspace=ws)
+        finally:
+            tee.river_debug_time_kernels(False)
+        torch.cuda.synchronize()
+        out.append((kc, vc))
+        for kind in (tee.TIMED_FILL_PROJECTION, tee.TIMED_FILL_PRODUCT):
+            ms, n = tee.river_debug_kernel_times(kind)
+            assert n == (chunks if on else 0), (on, kind, n)
+            assert (ms > 0.0) if on else ms == 0.0, (on, kind, ms)
+            assert tee.river_debug_kernel_times(kind) == (0.0, 0)
+    for a, b in zip(out[0], out[1]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_kv_fill_identity_null_equals_explicit_eye():
     cfg = get_config(2)
     layers = list(range(9, 17))

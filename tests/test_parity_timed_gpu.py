@@ -5,7 +5,8 @@ calls, the same workspace sizes and so the same launch paths), runs one
 step on NaN-filled caches and checks it against the float64 oracle:
 
 * the long-context prefill at 32,768 and 65,536 tokens (d = 5120, 48
-  filled layers, the projection on dequantised weights);
+  filled layers, through the product of the dequantised weights and the
+  maps);
 * the Llama-3-8B prefill step over all eight checkpoints (route, compaction
   with the gather and the exit scatter, the fills at blocks 11 and 31);
 * the GPT-2-shape step (route, compaction with the gather and the exit
@@ -149,15 +150,15 @@ def test_ridge_fit_long_context_full(long_calibration):
 def test_long_context_step(long_calibration, N):
     """One step of the benchmark's long-context workload: the positional
     compaction, then the fill of every row between the first 16 and the
-    last 2048 through 48 layers on the path the benchmark times (x_hat of
-    all layers in the workspace, the projection on dequantised weights)."""
+    last 2048 through 48 layers on the path the benchmark times (per layer
+    the product F = deq([Wk; Wv]) . maps, then the rows through F)."""
     cfg0, _, _, mb, mf = long_calibration
     nl = 48
     wl = B.LongContextWorkload(N, maps=Cycle(mb, nl))
     cfg = wl.cfg
     m, d = wl.m, cfg.d
     assert m == N - cfg.fill_lo - cfg.fill_tail
-    assert tee.river_debug_kv_fill_plan(m, d, wl.n_out, nl, wl.ws.numel()) == (nl, 2, 1)
+    assert tee.river_debug_kv_fill_plan(m, d, wl.n_out, nl, wl.ws.numel()) == (nl, 3, 1)
     wl.kc.fill_(float("nan"))
     wl.vc.fill_(float("nan"))
     wl.step()

@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(HERE, "libriver.so")
 
 RIVER_F32, RIVER_BF16 = 0, 1
 RULE_TOKEN, RULE_BATCH_MIN = 0, 1
+TIMED_FILL_PROJECTION, TIMED_FILL_PRODUCT = 0, 1
 (OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT, OP_KV_FILL_LAYER, OP_DECODE_STEP,
  OP_ROUTER_FIT) = 0, 1, 2, 3, 4, 5, 6
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_DTYPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED",
@@ -29,7 +30,8 @@ EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fi
            "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
            "river_debug_set_compact_path", "river_debug_set_gemm_path",
-           "river_debug_set_decode_path", "river_debug_kv_fill_plan", "river_decode_step_static"]
+           "river_debug_set_decode_path", "river_debug_set_fill_fuse", "river_debug_kv_fill_plan", "river_decode_step_static",
+           "river_debug_time_kernels", "river_debug_kernel_times"]
 
 
 class RiverError(RuntimeError):
@@ -98,11 +100,15 @@ def load():
     for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill",
               "river_kv_fill_layer", "river_decode_step", "river_decode_step_static",
               "river_router_fit", "river_ridge_fit",
-              "river_debug_set_compact_path", "river_debug_set_gemm_path", "river_debug_set_decode_path"):
+              "river_debug_set_compact_path", "river_debug_set_gemm_path", "river_debug_set_decode_path",
+              "river_debug_set_fill_fuse", "river_debug_time_kernels", "river_debug_kernel_times"):
         getattr(lib, f).restype = _I
     lib.river_debug_set_compact_path.argtypes = [_I]
     lib.river_debug_set_gemm_path.argtypes = [_I]
     lib.river_debug_set_decode_path.argtypes = [_I]
+    lib.river_debug_set_fill_fuse.argtypes = [_I]
+    lib.river_debug_time_kernels.argtypes = [_I]
+    lib.river_debug_kernel_times.argtypes = [_I, _P, _P]
     lib.river_debug_kv_fill_plan.argtypes = [_I, _I, _I, _I, _I, _S, _P, _P, _P]
     lib.river_debug_kv_fill_plan.restype = _I
     lib.river_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
@@ -166,10 +172,26 @@ def river_debug_set_decode_path(path):
     _check(load().river_debug_set_decode_path(path))
 
 
+def river_debug_set_fill_fuse(mode):
+    _check(load().river_debug_set_fill_fuse(mode))
+
+
+def river_debug_time_kernels(on):
+    _check(load().river_debug_time_kernels(int(bool(on))))
+
+
+def river_debug_kernel_times(kind):
+    """(total ms, launches) of the recorded launches of one kind
+    (TIMED_FILL_PROJECTION or TIMED_FILL_PRODUCT); clears them."""
+    ms, n = ctypes.c_double(), ctypes.c_int()
+    _check(load().river_debug_kernel_times(kind, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
 def river_debug_kv_fill_plan(m_max, d, n_out, n_layers, ws_bytes, dev_count=False):
     """(layers per chunk, projection path, parts) of a plain bf16 fill with
     maps; path 0 = int4 in registers, 1 = split reduction, 2 = dequantised
-    weights."""
+    weights, 3 = through the product of the weights and the maps."""
     c, p, k = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     _check(load().river_debug_kv_fill_plan(m_max, int(bool(dev_count)), d, n_out, n_layers, ws_bytes,
                                            ctypes.byref(c), ctypes.byref(p), ctypes.byref(k)))

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 
@@ -17,6 +18,7 @@ static thread_local char g_err[512] = "";
 static std::atomic<int> g_compact_path{0};
 static std::atomic<int> g_gemm_path{0};
 static std::atomic<int> g_decode_path{0};
+static std::atomic<int> g_fill_fuse{0};
 
 void set_error(const char* fmt, ...) {
   va_list ap;
@@ -42,6 +44,65 @@ river_status check_launch(const char* what) {
 int compact_path_override() { return g_compact_path.load(std::memory_order_relaxed); }
 int gemm_path_override() { return g_gemm_path.load(std::memory_order_relaxed); }
 int decode_path_override() { return g_decode_path.load(std::memory_order_relaxed); }
+int fill_fuse_override() { return g_fill_fuse.load(std::memory_order_relaxed); }
+
+// event records of river_debug_time_kernels: a fixed table (nothing here
+// allocates beyond the events themselves, created on first use and reused)
+namespace {
+struct TimedLaunch {
+  hipEvent_t a = nullptr, b = nullptr;
+  int dev = -1, kind = 0;
+  bool used = false, ended = false;
+};
+constexpr int TIMED_MAX = 1024;
+std::atomic<int> g_time_on{0};
+std::mutex g_time_mu;
+TimedLaunch g_timed[TIMED_MAX];
+}  // namespace
+
+int debug_timer_begin(hipStream_t s, int kind) {
+  if (!g_time_on.load(std::memory_order_relaxed)) return -1;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  int dev = -1;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone ||
+      hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();   // leave no error behind for the launch checks
+    return -1;
+  }
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  int idx = -1;
+  for (int i = 0; i < TIMED_MAX && idx < 0; ++i)
+    if (!g_timed[i].used && g_timed[i].dev == dev) idx = i;
+  for (int i = 0; i < TIMED_MAX && idx < 0; ++i)
+    if (g_timed[i].dev < 0) idx = i;
+  if (idx < 0) return -1;
+  TimedLaunch& t = g_timed[idx];
+  if (t.dev < 0) {
+    if (hipEventCreate(&t.a) != hipSuccess || hipEventCreate(&t.b) != hipSuccess) {
+      if (t.a) (void)hipEventDestroy(t.a);
+      t.a = nullptr;
+      (void)hipGetLastError();
+      return -1;
+    }
+    t.dev = dev;
+  }
+  if (hipEventRecord(t.a, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  t.kind = kind;
+  t.used = true;
+  t.ended = false;
+  return idx;
+}
+
+void debug_timer_end(hipStream_t s, int rec) {
+  if (rec < 0 || rec >= TIMED_MAX) return;
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  TimedLaunch& t = g_timed[rec];
+  if (hipEventRecord(t.b, s) == hipSuccess) t.ended = true;
+  else (void)hipGetLastError();
+}
 
 static bool dt_ok(river_dtype dt) { return dt == RIVER_F32 || dt == RIVER_BF16; }
 
@@ -76,6 +137,51 @@ river_status river_debug_set_decode_path(int path) {
   if (path < 0 || path > 1) return fail(RIVER_ERR_ARG, "decode path must be 0..1, got %d", path);
   g_decode_path.store(path, std::memory_order_relaxed);
   return RIVER_OK;
+}
+
+river_status river_debug_set_fill_fuse(int mode) {
+  if (mode < 0 || mode > 2) return fail(RIVER_ERR_ARG, "fill fuse mode must be 0..2, got %d", mode);
+  g_fill_fuse.store(mode, std::memory_order_relaxed);
+  return RIVER_OK;
+}
+
+river_status river_debug_time_kernels(int on) {
+  g_time_on.store(on != 0, std::memory_order_relaxed);
+  return RIVER_OK;
+}
+
+river_status river_debug_kernel_times(int kind, double* total_ms, int* launches) {
+  g_err[0] = 0;
+  if (kind != RIVER_TIMED_FILL_PROJECTION && kind != RIVER_TIMED_FILL_PRODUCT)
+    return fail(RIVER_ERR_ARG, "kernel_times: unknown launch kind %d", kind);
+  if (!total_ms || !launches) return fail(RIVER_ERR_ARG, "kernel_times: null output");
+  std::lock_guard<std::mutex> lk(g_time_mu);
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(RIVER_ERR_HIP, "kernel_times: hipGetDevice failed");
+  double sum = 0.0;
+  int n = 0;
+  river_status st = RIVER_OK;
+  for (int i = 0; i < TIMED_MAX; ++i) {
+    TimedLaunch& t = g_timed[i];
+    if (!t.used || t.kind != kind) continue;
+    t.used = false;
+    if (!t.ended || st != RIVER_OK) continue;
+    float ms = 0.f;
+    hipError_t e = t.dev == cur ? hipSuccess : hipSetDevice(t.dev);
+    if (e == hipSuccess) e = hipEventSynchronize(t.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.a, t.b);
+    if (e != hipSuccess) {
+      st = fail(RIVER_ERR_HIP, "kernel_times: %s", hipGetErrorString(e));
+      continue;
+    }
+    sum += ms;
+    ++n;
+  }
+  if (hipSetDevice(cur) != hipSuccess && st == RIVER_OK)
+    st = fail(RIVER_ERR_HIP, "kernel_times: restoring the device failed");
+  *total_ms = sum;
+  *launches = n;
+  return st;
 }
 
 river_status river_debug_kv_fill_plan(int m_max, int dev_count, int d, int n_out, int n_layers,

@@ -22,6 +22,12 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 int compact_path_override();
 int gemm_path_override();
 int decode_path_override();
+int fill_fuse_override();
+// event marks around a launch (river_debug_time_kernels): the begin mark
+// returns a record, or -1 when timing is off, the stream is capturing or
+// the records are full; the end mark closes that record
+int debug_timer_begin(hipStream_t s, int kind);
+void debug_timer_end(hipStream_t s, int rec);
 
 // launchers implemented by the kernel files; argument checks are done by
 // the caller (api.hip)

@@ -16,6 +16,13 @@
 //                                      scatter as the epilogue
 // Layers are the grid's z dimension, so one launch covers a whole chunk.
 //
+// Both phases are linear in the exit state, so at row counts well above the
+// projection's outputs (given on the host) the fill instead forms, per
+// chunk of layers, F[l] = deq([Wk[l]; Wv[l]]) . maps[l] (2 n_out x d, bf16:
+// 2 n_out d^2 flops per layer instead of 2 m d^2) and projects the exit
+// states through it: [K|V][l] = X . F[l]^T. The same K and V up to
+// rounding (one bf16 rounding of F instead of one of x_hat).
+//
 // Generic path (fp32, or shapes the MFMA tiles do not take): one workgroup
 // per (token, layer), fp32 throughout.
 //
@@ -227,6 +234,28 @@ __global__ __launch_bounds__(256) void w4_dequant_kernel(GemmArgs g, int nl, uin
   *(u32x4*)(out + ((int64_t)z * N + col) * K + k8 * 8) = u32x4{o[0], o[1], o[2], o[3]};
 }
 
+// out[z] = in[z]^T for d x d bf16 matrices (d % 64 == 0): 64 x 64 tiles,
+// 16-byte loads along the rows of in and 16-byte stores along the rows of
+// out, the tile transposed through LDS (rows padded by 16 bytes)
+__global__ __launch_bounds__(256) void transpose_maps_kernel(const uint16_t* in, uint16_t* out, int d) {
+  __shared__ uint16_t t[64][72];
+  const int64_t zo = (int64_t)blockIdx.z * d * d;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, ch = i & 7;
+    *(u32x4*)&t[r][ch * 8] = *(const u32x4*)(in + zo + (int64_t)(r0 + r) * d + c0 + ch * 8);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int c = i >> 3, ch = i & 7;          // row c of out, its rows ch * 8 .. + 7 of in
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = (uint32_t)t[ch * 8 + 2 * e][c] | ((uint32_t)t[ch * 8 + 2 * e + 1][c] << 16);
+    *(u32x4*)(out + zo + (int64_t)(c0 + c) * d + r0 + ch * 8) = v;
+  }
+}
+
 }  // namespace river
 
 namespace river_host {
@@ -354,6 +383,23 @@ static size_t dequant_room(int m_max, bool dev_count, int d, int nh, int nl) {
   int ks;
   const int p = proj_path(m_max, dev_count, false, d, 2 * nh, nl, SIZE_MAX, &ks);
   return p == PROJ_DEQUANT ? align_up((size_t)nl * 2 * nh * d * 2, 256) : 0;
+}
+
+// The product path (F[l] = deq(W[l]) . maps[l], then X . F[l]^T): for a
+// plain fill with maps and the row count on the host, from 2 (2 n_out) rows
+// on (F's 2 (2 n_out) d^2 flops at most half the map GEMM's 2 m d^2, which
+// leaves room for the maps' transposition), when the 256 x 256 tiles take
+// both GEMMs (d % 128 == 0). Per layer the workspace holds the dequantised
+// weights, the transposed map and F. The fill-fuse hook: 1 never, 2 from
+// one row on.
+static size_t fused_layer_bytes(int d, int nh) {
+  return 2 * align_up((size_t)2 * nh * d * 2, 256) + align_up((size_t)d * d * 2, 256);
+}
+static bool fused_wanted(int m_max, bool dev_count, int d, int nh, size_t ws_bytes) {
+  const int mode = fill_fuse_override();
+  if (mode == 1 || dev_count || d % 128 || gemm_path_override() == 1 || gemm_path_override() == 3) return false;
+  if (ws_bytes < fused_layer_bytes(d, nh)) return false;
+  return mode == 2 || m_max >= 4 * nh;
 }
 
 // Layers per chunk of a fill that keeps x_hat (and, with an input norm, the
@@ -528,7 +574,9 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
         if (st != RIVER_OK) return st;
         GemmArgs p = q;
         p.B = dq; p.ldb = d; p.b_bstride = (int64_t)q.N * d;
+        const int tp = debug_timer_begin(s, RIVER_TIMED_FILL_PROJECTION);
         gemm_cache_launch(p, nl, s);
+        debug_timer_end(s, tp);
         return check_launch("kv_fill projection (bf16)");
       }
       if (pp == PROJ_SPLIT) {
@@ -556,6 +604,58 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     part_ws = (char*)workspace;
     part_bytes = workspace ? ws_bytes : 0;
     return stage2(0, n_layers, (const uint16_t*)h, ld_h, 0, row_idx, n_rows, nullptr, 0, 0);
+  }
+
+  if (maps && !layer && fused_wanted(m_max, m_dev != nullptr, d, nh, ws_bytes)) {
+    // per chunk: the weights dequantised (as the int4 path forms them), the
+    // maps transposed, F = deq(W) . maps, then the exit states through F
+    const size_t wb = align_up((size_t)2 * nh * d * 2, 256), tb = align_up((size_t)d * d * 2, 256);
+    const size_t per = 2 * wb + tb;
+    const int fchunk = ws_bytes / per < (size_t)n_layers ? (int)(ws_bytes / per) : n_layers;
+    uint16_t* dq = (uint16_t*)workspace;
+    uint16_t* tr = (uint16_t*)((char*)workspace + (size_t)fchunk * wb);
+    uint16_t* fw = (uint16_t*)((char*)workspace + (size_t)fchunk * (wb + tb));
+    for (int l0 = 0; l0 < n_layers; l0 += fchunk) {
+      const int nl = n_layers - l0 < fchunk ? n_layers - l0 : fchunk;
+      GemmArgs q = g;
+      q.N = 2 * nh;
+      q.q[0] = wk->q + (int64_t)l0 * q.q_bstride;
+      q.q[1] = wv->q + (int64_t)l0 * q.q_bstride;
+      q.s[0] = (const char*)wk->scale + (int64_t)l0 * q.sz_bstride[0] * esize(wk->sz_dtype);
+      q.zp[0] = (const char*)wk->zero + (int64_t)l0 * q.sz_bstride[0] * esize(wk->sz_dtype);
+      q.s[1] = (const char*)wv->scale + (int64_t)l0 * q.sz_bstride[1] * esize(wv->sz_dtype);
+      q.zp[1] = (const char*)wv->zero + (int64_t)l0 * q.sz_bstride[1] * esize(wv->sz_dtype);
+      const int64_t threads = (int64_t)nl * q.N * (d / 8);
+      w4_dequant_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(q, nl, dq);
+      river_status st = check_launch("kv_fill weight dequantisation");
+      if (st != RIVER_OK) return st;
+      transpose_maps_kernel<<<dim3((unsigned)(d / 64), (unsigned)(d / 64), (unsigned)nl), 256, 0, s>>>(
+          (const uint16_t*)maps + (int64_t)l0 * d * d, tr, d);
+      if ((st = check_launch("kv_fill map transposition")) != RIVER_OK) return st;
+      // F[l] = deq(W[l]) . maps[l]: rows = the 2 n_out outputs, reduction
+      // over the map's output index (a row of the transposed map)
+      GemmArgs f{};
+      f.M_max = q.N; f.N = d; f.K = d;
+      f.A = dq; f.lda = d; f.a_bstride = (int64_t)q.N * d; f.a_nrows = q.N;
+      f.B = tr; f.ldb = d; f.b_bstride = (int64_t)d * d;
+      f.C = fw; f.ldc = d; f.c_bstride = (int64_t)wb / 2;
+      const int tf = debug_timer_begin(s, RIVER_TIMED_FILL_PRODUCT);
+      gemm_bf16_auto<EPI_BF16>(f, nl, s);
+      debug_timer_end(s, tf);
+      if ((st = check_launch("kv_fill map-weight product")) != RIVER_OK) return st;
+      // [K|V][l] = X . F[l]^T into the cache
+      GemmArgs pr = q;
+      pr.A = (const uint16_t*)h; pr.lda = ld_h; pr.a_bstride = 0; pr.a_rows = row_idx; pr.a_nrows = n_rows;
+      pr.B = fw; pr.ldb = d; pr.b_bstride = (int64_t)wb / 2;
+      pr.e_rows = row_idx;
+      pr.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
+      pr.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
+      const int tp = debug_timer_begin(s, RIVER_TIMED_FILL_PROJECTION);
+      gemm_cache_launch(pr, nl, s);
+      debug_timer_end(s, tp);
+      if ((st = check_launch("kv_fill projection through the product")) != RIVER_OK) return st;
+    }
+    return RIVER_OK;
   }
 
   const size_t xb = layer_xhat_bytes(m_max, d), sb = gamma ? layer_ss_bytes(m_max, d) : 0;
@@ -631,6 +731,13 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
 // and parts for the first chunk
 void kv_fill_plan(int m_max, bool dev_count, int d, int nh, int n_layers, size_t ws_bytes, int* chunk,
                   int* path, int* ks) {
+  if (fused_wanted(m_max, dev_count, d, nh, ws_bytes)) {
+    const size_t per = fused_layer_bytes(d, nh);
+    *chunk = ws_bytes / per < (size_t)n_layers ? (int)(ws_bytes / per) : n_layers;
+    *path = 3;
+    *ks = 1;
+    return;
+  }
   const size_t xb = layer_xhat_bytes(m_max, d);
   *chunk = fill_chunk(m_max, dev_count, d, nh, n_layers, xb, ws_bytes, true);
   const size_t used = (size_t)*chunk * xb;
