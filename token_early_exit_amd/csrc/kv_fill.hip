@@ -214,24 +214,29 @@ __global__ __launch_bounds__(256) void gemm_part_finish_kernel(GemmArgs g, int b
 
 // bf16 copies of a chunk's int4 K/V weights, [nl][2 nh][K]: the values the
 // W4 kernel forms in registers (dequant8, the same scale and -zero * scale),
-// one thread per 8 weights
+// one thread per 32 weights (16 bytes in, 64 bytes out; K % 32 == 0 and the
+// group a multiple of 32, so one scale and zero per thread); 32-bit indices
+// (nl * 2 nh * K / 32 < 2^31, checked by the launcher)
 __global__ __launch_bounds__(256) void w4_dequant_kernel(GemmArgs g, int nl, uint16_t* out) {
   const int K = g.K, nh = g.nh, N = 2 * nh;
-  const int per_row = K / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)nl * N * per_row) return;
-  const int k8 = (int)(idx % per_row);
-  const int col = (int)((idx / per_row) % N);
-  const int z = (int)(idx / ((int64_t)per_row * N));
+  const int per_row = K / 32;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nl * N * per_row) return;
+  const int row = idx / per_row, k32 = idx - row * per_row;
+  const int z = row / N, col = row - z * N;
   const int which = col >= nh ? 1 : 0, hc = col - which * nh;
-  const uint32_t w = *(const uint32_t*)(g.q[which] + z * g.q_bstride + (int64_t)hc * (K / 2) + k8 * 4);
+  const u32x4 w = *(const u32x4*)(g.q[which] + z * g.q_bstride + (int64_t)hc * (K / 2) + k32 * 16);
   const int gpr = K / g.group[which];
-  const int64_t si = z * g.sz_bstride[which] + (int64_t)hc * gpr + (k8 * 8) / g.group[which];
+  const int64_t si = z * g.sz_bstride[which] + (int64_t)hc * gpr + (k32 * 32) / g.group[which];
   const float sc = load_sz(g.s[which], si, g.sz_bf16[which]);
   const float ze = load_sz(g.zp[which], si, g.sz_bf16[which]);
-  uint32_t o[4];
-  dequant8(w, sc, -ze * sc, o);
-  *(u32x4*)(out + ((int64_t)z * N + col) * K + k8 * 8) = u32x4{o[0], o[1], o[2], o[3]};
+  u32x4* o = (u32x4*)(out + (int64_t)row * K + k32 * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t v[4];
+    dequant8(w[i], sc, -ze * sc, v);
+    o[i] = u32x4{v[0], v[1], v[2], v[3]};
+  }
 }
 
 // out[z] = in[z]^T for d x d bf16 matrices (d % 64 == 0): 64 x 64 tiles,
@@ -259,7 +264,17 @@ __global__ __launch_bounds__(256) void transpose_maps_kernel(const uint16_t* in,
 }  // namespace river
 
 namespace river_host {
+
 using namespace river;
+
+// launch of w4_dequant_kernel over nl layers of 2 nh rows of K weights
+static river_status w4_dequant_launch(const GemmArgs& q, int nl, uint16_t* out, hipStream_t s) {
+  const int64_t threads = (int64_t)nl * 2 * q.nh * (q.K / 32);
+  if (q.K % 32 || q.group[0] % 32 || q.group[1] % 32 || threads >= ((int64_t)1 << 31))
+    return fail(RIVER_ERR_UNSUPPORTED, "kv_fill: weight dequantisation needs K and the groups in multiples of 32");
+  w4_dequant_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(q, nl, out);
+  return check_launch("kv_fill weight dequantisation");
+}
 
 // The MFMA path: K-slabs in groups of four (d % 256), 64-column blocks inside
 // the K or the V half (nh % 64), one quantization group per slab or more
@@ -568,9 +583,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
       const int pp = proj_path(m_max, m_dev != nullptr, q.M_dev_z != nullptr, d, q.N, nl, part_bytes, &ks);
       if (pp == PROJ_DEQUANT) {
         uint16_t* dq = (uint16_t*)part_ws;
-        const int64_t threads = (int64_t)nl * q.N * (d / 8);
-        w4_dequant_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(q, nl, dq);
-        river_status st = check_launch("kv_fill weight dequantisation");
+        river_status st = w4_dequant_launch(q, nl, dq, s);
         if (st != RIVER_OK) return st;
         GemmArgs p = q;
         p.B = dq; p.ldb = d; p.b_bstride = (int64_t)q.N * d;
@@ -625,9 +638,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
       q.zp[0] = (const char*)wk->zero + (int64_t)l0 * q.sz_bstride[0] * esize(wk->sz_dtype);
       q.s[1] = (const char*)wv->scale + (int64_t)l0 * q.sz_bstride[1] * esize(wv->sz_dtype);
       q.zp[1] = (const char*)wv->zero + (int64_t)l0 * q.sz_bstride[1] * esize(wv->sz_dtype);
-      const int64_t threads = (int64_t)nl * q.N * (d / 8);
-      w4_dequant_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(q, nl, dq);
-      river_status st = check_launch("kv_fill weight dequantisation");
+      river_status st = w4_dequant_launch(q, nl, dq, s);
       if (st != RIVER_OK) return st;
       transpose_maps_kernel<<<dim3((unsigned)(d / 64), (unsigned)(d / 64), (unsigned)nl), 256, 0, s>>>(
           (const uint16_t*)maps + (int64_t)l0 * d * d, tr, d);
