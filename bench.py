@@ -315,11 +315,25 @@ class Prefill8BWorkload:
                           h_cont=s["h_cont"], row_ids_cont=s["ids_cont"], out=self.out,
                           workspace=s["cws"])
 
+    def fold(self):
+        """From now on the fills run through the folded products F =
+        deq([Wk; Wv]) M of each exit block's maps (formed here, once)."""
+        self.F, self.fold_ms = {}, 0.0
+        for c in self.maps:
+            wk, wv = (self.wk1, self.wv1) if c == self.e1 else (self.wk2, self.wv2)
+            self.F[c], ms = fold_maps(self.cfg, self.maps[c], wk, wv)
+            self.fold_ms += ms
+
     def fill(self, c):
         s = self.ck[c]
         cfg = self.cfg
         wk, wv = (self.wk1, self.wv1) if c == self.e1 else (self.wk2, self.wv2)
         nl = self.maps[c].shape[0]
+        if getattr(self, "F", None) is not None:
+            tee.river_kv_fill_folded(s["hc"], s["slot"], self.F[c], cfg.n_kv_heads, cfg.head_dim,
+                                     self.kc[cfg.L - nl:], self.vc[cfg.L - nl:], m_max=s["n"],
+                                     m_dev=s["counts"][1:], row_idx=s["ext"])
+            return
         tee.river_kv_fill(s["hc"], s["slot"], wk, wv, cfg.n_kv_heads, cfg.head_dim, self.kc[cfg.L - nl:],
                           self.vc[cfg.L - nl:], m_max=s["n"], m_dev=s["counts"][1:], row_idx=s["ext"],
                           maps=self.maps[c], workspace=s["fws"])
@@ -344,9 +358,16 @@ class Prefill8BWorkload:
             cb += 2 * (nc - ne) * d * 2 + 4 * (nc - ne)          # continuing rows gathered, their ids
             cb += 2 * ne * d * 2                                  # exited rows scattered
             if c in self.maps:
-                nl = self.maps[c].shape[0]
-                ff += 2.0 * ne * nl * (d * d + d * 2 * self.n_out)
+                ff += self.fill_flops(c)
         return rb, cb, ff
+
+    def fill_flops(self, c):
+        """Flops of the fill at c as it runs: the map and the projection, or
+        the projection through F once folded."""
+        ne, nl, d = self.exits[c], self.maps[c].shape[0], self.d
+        if getattr(self, "F", None) is not None:
+            return 2.0 * ne * nl * d * 2 * self.n_out
+        return 2.0 * ne * nl * (d * d + d * 2 * self.n_out)
 
 
 class Gpt2Workload:
@@ -458,6 +479,35 @@ class Gpt2Workload:
         return route_bytes, compact_bytes, fill_flops
 
 
+def fold_maps(cfg, maps, wk, wv, dev="cuda"):
+    """F = deq([Wk; Wv]) . M for each layer of maps (river_kv_fold), and the
+    milliseconds it took (once per fitted map, off the step)."""
+    nl, d = maps.shape[0], maps.shape[1]
+    n_out = cfg.n_kv_heads * cfg.head_dim
+    F = torch.empty((nl, 2 * n_out, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(tee.river_workspace_size(tee.OP_KV_FOLD, 0, d, n_out, 0, nl), dtype=torch.uint8,
+                     device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    tee.river_kv_fold(wk, wv, cfg.n_kv_heads, cfg.head_dim, F, maps=maps, workspace=ws)
+    torch.cuda.synchronize()
+    return F, (time.perf_counter() - t0) * 1e3
+
+
+def fold_checkpoints(cfg, cks, wk, wv, dev="cuda"):
+    """Folded products for every decode checkpoint with maps (blocks e+1..L
+    of the weights), set as the checkpoint's "folded"; total milliseconds."""
+    t = 0.0
+    for c in cks:
+        if c.get("maps") is None:
+            continue
+        e = c["layer"]
+        sub = lambda w: tuple(x[e:] for x in w[:3]) + (w[3],)
+        c["folded"], ms = fold_maps(cfg, c["maps"], sub(wk), sub(wv), dev)
+        t += ms
+    return t
+
+
 class DecodeWorkload:
     """One generation step of the token-level exit loop on a decode shape:
     Llama-3.2-1B (64 tokens, checks after blocks 8..15, router off, tau_l at
@@ -467,10 +517,11 @@ class DecodeWorkload:
     theta_31 = -inf and +inf elsewhere, near-identity maps). The thresholds
     come from the library's own cosines and probabilities."""
 
-    def __init__(self, key, dev="cuda"):
+    def __init__(self, key, folded=False, dev="cuda"):
         cfg = self.cfg = get_config(key)
         n = cfg.n_tokens
         layers = list(cfg.route_layers)
+        self.fold_ms = None
         need = sorted({l - 1 for l in layers} | set(layers))
         self.hs = G.hidden_states(cfg, n, need, device=dev)
         self.slot = G.slots(cfg, device=dev)
@@ -516,6 +567,8 @@ class DecodeWorkload:
                 c["theta"] = -math.inf
                 alive &= ~(cv > np.float32(c["tau"]))
             self.cks.append(c)
+        if folded:
+            self.fold_ms = fold_checkpoints(cfg, self.cks, self.wk, self.wv, dev)
         torch.cuda.synchronize()
 
     def step(self, i=0):
@@ -526,10 +579,11 @@ class DecodeWorkload:
 
 # ------------------------------------------------------------ measurements
 
-def decode_times(key, steps):
+def decode_times(key, steps, folded=False):
     """µs per decode step: eager (each call enqueues the step's kernels from
-    the host) and replayed from one captured graph."""
-    dw = DecodeWorkload(key)
+    the host) and replayed from one captured graph. folded: the checkpoints
+    with maps fill through river_kv_fold's products, formed beforehand."""
+    dw = DecodeWorkload(key, folded=folded)
     for _ in range(3):
         dw.step()
     torch.cuda.synchronize()
@@ -563,13 +617,16 @@ def decode_times(key, steps):
                     f"for the checkpoints without maps, a fill per checkpoint with maps{two}")
         else:
             path = f"{scores}, one decision workgroup, a fill per checkpoint{two}"
+        if folded:
+            path += "; the fills with maps through the folded products deq([Wk; Wv]) M"
     else:
         path = "per checkpoint: route, compact, fill"
     del g
+    extra = {"fold_ms_once": dw.fold_ms} if folded else {}
     return {"tokens": cfg.n_tokens, "d": cfg.d, "blocks": cfg.L, "checkpoints": n_ck,
             "exits_per_checkpoint": [int((ex == c["layer"]).sum()) for c in dw.cks],
             "filled_token_layers": int(sum(cfg.L - e for e in ex)),
-            "path": path, "eager_us": eager * 1e3, "graph_us": graph * 1e3}
+            "path": path, "eager_us": eager * 1e3, "graph_us": graph * 1e3, **extra}
 
 
 def router_fit_times(key, n, epochs=100, batch=256):
@@ -915,8 +972,10 @@ def long_context_figures(wl, steps, warmup):
                              "other_fill_ms is the weights' dequantisation and the maps' transposition"}
 
 
-def prefill_8b_figures(steps=10, warmup=2):
-    wl = Prefill8BWorkload()
+def prefill_8b_figures(steps=10, warmup=2, wl=None):
+    """The 8B prefill step's figures; wl: an existing workload (e.g. one
+    whose fills were folded)."""
+    wl = wl or Prefill8BWorkload()
     for i in range(warmup):
         wl.step(i)
     ms = time_region(wl.step, steps) / steps
@@ -932,7 +991,7 @@ def prefill_8b_figures(steps=10, warmup=2):
     for c in (wl.e1, wl.e2):
         fms = time_region(lambda i: wl.fill(c), steps) / steps
         ne, nl = wl.exits[c], wl.maps[c].shape[0]
-        f = 2.0 * ne * nl * (wl.d * wl.d + wl.d * 2 * wl.n_out)
+        f = wl.fill_flops(c)
         fills[f"exit_at_{c}"] = {"rows": ne, "layers": nl, "ms": fms, "tflops": f / (fms * 1e-3) / 1e12,
                                  "frac_of_bf16_peak": f / (fms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
     out = {"workload": "llama3-8b-shape prefill: 8192 tokens, d=4096, 32 blocks, routers (b=128) at "
@@ -945,6 +1004,10 @@ def prefill_8b_figures(steps=10, warmup=2):
            "route_compact_gbs": (rb + cb) / (rc_ms * 1e-3) / 1e9,
            "route_compact_frac_hbm": (rb + cb) / (rc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "fill_flops": ff, "fills": fills, "ridge_fit_ms_22_maps": wl.ridge_ms}
+    if getattr(wl, "F", None) is not None:
+        out["workload"] += ("; the fills through the folded products F = deq([Wk; Wv]) M of each block's "
+                            "map, formed once beforehand")
+        out["fold_ms_once"] = wl.fold_ms
     return wl, out
 
 
@@ -1001,14 +1064,20 @@ def main():
         print(json.dumps({"router_fit": router_fit_all()}))
         return
     if only in ("decode2", "decode3D"):
-        print(json.dumps({"decode_step": decode_times(2 if only == "decode2" else "3D", 20)}))
+        key = 2 if only == "decode2" else "3D"
+        out = {"decode_step": decode_times(key, 20)}
+        if key == "3D":
+            out["decode_step_folded"] = decode_times(key, 20, folded=True)
+        print(json.dumps(out))
         return
     if only == "route-compact":
         print(json.dumps({"route_compact_8b_cold": route_compact_8b_cold()}))
         return
     if only == "8b":
-        _, f = prefill_8b_figures(args.steps, args.warmup)
-        print(json.dumps({"prefill_8b": f}))
+        wl8, f = prefill_8b_figures(args.steps, args.warmup)
+        wl8.fold()
+        _, ff = prefill_8b_figures(args.steps, args.warmup, wl=wl8)
+        print(json.dumps({"prefill_8b": f, "prefill_8b_folded": ff}))
         return
     if only == "gpt2":
         _, f = gpt2_figures(args.rotate, max(args.steps, 50), args.warmup)
@@ -1072,6 +1141,8 @@ def main():
     torch.cuda.empty_cache()
 
     wl8, line["prefill_8b"] = prefill_8b_figures()
+    wl8.fold()
+    _, line["prefill_8b_folded"] = prefill_8b_figures(wl=wl8)
     progress("8B prefill step done")
     line["route_compact_8b_cold"] = route_compact_8b_cold()
     progress("8B route and compaction (cold) done")
@@ -1082,6 +1153,8 @@ def main():
             decode_times(2, 50),
         "llama3-8b decode: 256 tokens, d=4096, 8 router checkpoints, maps for the exits at 11 and 31":
             decode_times("3D", 20),
+        "llama3-8b decode, maps folded into the K/V weights beforehand":
+            decode_times("3D", 20, folded=True),
     }
     progress("decode steps done")
     line["router_fit"] = router_fit_all()

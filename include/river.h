@@ -82,7 +82,8 @@ typedef enum { RIVER_RULE_TOKEN = 0, RIVER_RULE_BATCH_MIN = 1 } river_rule;
 /* Operation ids for river_workspace_size. */
 typedef enum {
   RIVER_OP_ROUTE = 0, RIVER_OP_COMPACT = 1, RIVER_OP_KV_FILL = 2, RIVER_OP_RIDGE_FIT = 3,
-  RIVER_OP_KV_FILL_LAYER = 4, RIVER_OP_DECODE_STEP = 5, RIVER_OP_ROUTER_FIT = 6
+  RIVER_OP_KV_FILL_LAYER = 4, RIVER_OP_DECODE_STEP = 5, RIVER_OP_ROUTER_FIT = 6,
+  RIVER_OP_KV_FOLD = 7
 } river_op;
 
 /*
@@ -286,6 +287,59 @@ river_status river_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype d
                            void* workspace, size_t ws_bytes, hipStream_t s);
 
 /*
+ * river_kv_fold -- the skipped layers' maps folded into their K/V weights.
+ *
+ * RidgeFill 思路源头: a skipped layer's K and V come from its own
+ * projection applied to the input the fitted map predicts. Both steps are
+ * linear in the exit state, so per layer they compose into one matrix,
+ * formed once per fitted map (off the per-step path, like the fit):
+ *   F[l] = deq([Wk[l]; Wv[l]]) . maps[l]     (2 n_out x d, n_out =
+ *                                             n_kv_heads * head_dim)
+ *   F[l][o][k] = sum_j deq(W[l])[o][j] maps[l][j][k], rows 0..n_out-1 from
+ *   Wk, n_out..2 n_out-1 from Wv; fp32 accumulation, rounded to bf16.
+ * Without maps (NULL) F[l] is the dequantised weights themselves.
+ *
+ * maps     : bf16 [n_layers][d][d] (output-major, as river_kv_fill takes
+ *            them), or NULL.
+ * wk, wv   : host pointers to int4 descriptors of n_layers layers.
+ * F        : bf16 [n_layers][2 n_out][d], written; caller-owned.
+ * workspace: with maps, river_workspace_size(RIVER_OP_KV_FOLD, 0, d, n_out,
+ *            0, L) bytes process L layers per pass (at least one);
+ *            without maps none is needed.
+ * Shapes: d % 256 == 0, n_out % 64 == 0, group % 64 == 0 and the same for
+ * wk and wv (RIVER_ERR_UNSUPPORTED otherwise). Asynchronous on s.
+ */
+river_status river_kv_fold(int d, int n_layers, const void* maps,
+                           const river_w4* wk, const river_w4* wv,
+                           int n_kv_heads, int head_dim, void* F,
+                           void* workspace, size_t ws_bytes, hipStream_t s);
+
+/*
+ * river_kv_fill_folded -- river_kv_fill through folded products.
+ *
+ * River-LLM 方法步骤详情 step 1 and 技术新颖性 (the skipped layers' K/V at
+ * each exited token's own slot), RidgeFill 思路源头 (the map, then the
+ * layer's projection), with the two composed by river_kv_fold:
+ *   [K | V] = F[l] . h[r]  ->  k_cache[l][slot[r]], v_cache[l][slot[r]]
+ * for l = 0..n_layers-1 and t = 0..m-1, r = row_idx[t] (or t). The same
+ * K and V as river_kv_fill with the maps and weights F was folded from, up
+ * to rounding (one bf16 rounding of F in place of one of x_hat).
+ *
+ * Arguments as river_kv_fill's, bf16 only (h, F, caches); F: bf16
+ * [n_layers][2 n_out][d] from river_kv_fold. No workspace. Needs d % 256
+ * == 0 and n_out % 64 == 0, with h's and F's byte spans under 2^31
+ * (RIVER_ERR_UNSUPPORTED otherwise). Rows and slots outside their ranges
+ * are skipped; only the filled slots are written.
+ */
+river_status river_kv_fill_folded(int m_max, const int32_t* m_dev, int d,
+                                  const void* h, int64_t ld_h, int n_rows,
+                                  const int32_t* row_idx, const int32_t* slot,
+                                  int n_layers, const void* F,
+                                  int n_kv_heads, int head_dim,
+                                  void* k_cache, void* v_cache, int64_t n_slots,
+                                  hipStream_t s);
+
+/*
  * The rest of a skipped layer's K/V path, for river_kv_fill_layer. Each
  * part is switched off by a NULL pointer.
  *
@@ -345,6 +399,9 @@ typedef struct {
   const void* w_down;     /* dt [b][d] router, or NULL (cosine test only)        */
   const void* w_up;       /* dt [b]                                              */
   const void* maps;       /* dt [n_layers - e][d][d] (blocks e+1..L), or NULL    */
+  const void* folded;     /* bf16 [n_layers - e][2 n_out][d]: river_kv_fold of   */
+                          /* the maps of blocks e+1..L (used in place of maps),  */
+                          /* or NULL                                             */
 } river_checkpoint;
 
 /*
@@ -384,7 +441,8 @@ typedef struct {
  * (instead of a route and a compaction per checkpoint); on the fill's MFMA
  * path one projection then fills the exits of every checkpoint without
  * maps (all of them, or at least two), and each checkpoint with maps
- * fills its own.
+ * fills its own. A checkpoint with folded products (river_checkpoint.folded,
+ * bf16 only) fills as river_kv_fill_folded does, with no workspace for it.
  */
 river_status river_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
                                const river_checkpoint* ck, int n_layers, const void* gamma,

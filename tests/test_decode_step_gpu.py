@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import bench as B
 import oracle as O
 import token_early_exit_amd as tee
 from synth import get_config
@@ -256,7 +257,8 @@ def test_decode_step_8b_two_launch_equals_per_checkpoint():
     assert np.sum(e0.cpu().numpy() == 11) == 13
 
 
-def test_decode_step_8b_router_and_maps():
+@pytest.mark.parametrize("folded", [False, True])
+def test_decode_step_8b_router_and_maps(folded):
     """Llama-3-8B-shape decode (256 tokens, d = 4096, checkpoints every four
     blocks with a router each): tau off, theta_11 between the 13th and 14th
     largest probabilities, theta_31 = -inf, +inf elsewhere; near-identity
@@ -283,6 +285,9 @@ def test_decode_step_8b_router_and_maps():
             c["theta"] = -INF
             c["maps"] = G.near_identity_maps(cfg, cfg.L - l, tag="maps31", device=DEV)
         cks.append(c)
+    if folded:
+        # the checkpoints with maps fill through deq([Wk; Wv]) M (river_kv_fold)
+        B.fold_checkpoints(cfg, cks, wk, wv, DEV)
     ex, kc, vc = run_gpu(cks, cfg, wk, wv, slot)
     exg = check_step(cfg, cks, ex, kc, vc, slot, wk, wv, sample_per_ck=12)
     assert np.sum(exg == 11) == 13 and np.sum(exg == 31) == n - 13

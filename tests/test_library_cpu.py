@@ -53,6 +53,9 @@ def test_workspace_sizes():
     assert ws(tee.OP_KV_FILL, 4096, 768, 0, 0, 8) >= 8 * 4096 * 768 * 2
     assert ws(tee.OP_COMPACT, 100000) >= 4 * 25
     assert ws(tee.OP_RIDGE_FIT, 2048, 768, 768, 8, tee.RIVER_BF16) > 0
+    # folding: the dequantised weights (2 n_out x d) and the transposed map (d x d) per layer
+    assert ws(tee.OP_KV_FOLD, 0, 4096, 1024, 0, 3) == 3 * (2 * 1024 * 4096 * 2 + 4096 * 4096 * 2)
+    assert ws(tee.OP_KV_FOLD, 0, 4096, 1024, 0, 0) == 0
     # split reductions: up to 64 rows always, 65 to 256 rows when the
     # projection has few tiles (at most 128 of 64 rows x 256 outputs)
     nh = 8 * 64
@@ -127,6 +130,35 @@ def test_kv_fill_and_ridge_argument_errors():
     assert lib.river_debug_set_compact_path(9) == 1
     assert lib.river_debug_set_gemm_path(4) == 1
     assert lib.river_debug_set_decode_path(2) == 1
+
+
+def test_kv_fold_and_folded_fill_argument_errors():
+    lib = tee.load()
+    w = tee.RiverW4(16, 16, 16, tee.RIVER_BF16, 64)
+    bad = tee.RiverW4(16, 16, 16, tee.RIVER_BF16, 48)
+    fold = lambda **k: lib.river_kv_fold(*dict(dict(d=256, nl=2, maps=None, wk=ctypes.byref(w),
+                                                    wv=ctypes.byref(w), hk=2, hd=64, F=16, ws=None,
+                                                    wsn=0, s=None), **k).values())
+    assert fold(nl=0) == 0                                         # empty call
+    assert fold(wk=None) == 1
+    assert fold(wk=ctypes.byref(bad)) == 1                         # group does not divide d
+    assert fold(d=128) == 4                                        # d % 256
+    assert fold(hd=48) == 4                                        # n_out % 64
+    assert fold(maps=16) == 5                                      # maps need a workspace
+    assert fold(maps=16, ws=16, wsn=tee.river_workspace_size(tee.OP_KV_FOLD, 0, 256, 128, 0, 1) - 1) == 5
+    assert fold(F=8) == 3
+    fill = lambda **k: lib.river_kv_fill_folded(*dict(dict(m=8, mdev=None, d=256, h=16, ld=256, nrows=8,
+                                                           ri=None, slot=16, nl=2, F=16, hk=2, hd=64,
+                                                           kc=16, vc=16, ns=8, s=None), **k).values())
+    assert fill(m=0) == 0                                          # empty call
+    assert fill(d=128, ld=128) == 4                                # d % 256
+    assert fill(F=None) == 1
+    assert fill(m=9) == 1                                          # more rows than h has
+    assert fill(ld=252) == 3                                       # ld below d
+    assert fill(kc=8) == 3
+    assert fill(nl=70000) == 4                                     # layers past the grid limit
+    assert fill(nrows=1 << 20, m=8, ld=1024, d=1024) == 4          # h spans 2^31 bytes
+    assert len(lib.river_last_error()) > 0
 
 
 def _exit_projection(**kw):

@@ -206,18 +206,21 @@ def prefill_8b_inputs():
     return cfg, theta11, (mb1, mf1), (mb2, mf2)
 
 
-def test_prefill_8b_step(prefill_8b_inputs):
+@pytest.mark.parametrize("folded", [False, True])
+def test_prefill_8b_step(prefill_8b_inputs, folded):
     """One step of the benchmark's 8B prefill workload: every checkpoint's
     decision against the oracle's (outside the band), the compaction of the
     GPU's own masks (indices, counts, gathered rows and ids, exit scatter)
     bit-exact, the fills at 11 (every exited row, 21 layers) and 31 (sampled
     rows of 7782, one layer) within the K/V bar, and every other cache slot
-    untouched."""
+    untouched; folded: the fills through river_kv_fold's products."""
     cfg, theta11, (mb1, mf1), (mb2, mf2) = prefill_8b_inputs
     wl = B.Prefill8BWorkload(theta11=theta11, maps11=torch.stack([Cycle(mb1, 21)[l] for l in range(21)]),
                              maps31=mb2)
     n, L = wl.n, cfg.L
     assert wl.theta[wl.e1] == theta11
+    if folded:
+        wl.fold()               # the fills through deq([Wk; Wv]) M, as the benchmark's folded step
     wl.kc.fill_(float("nan"))
     wl.vc.fill_(float("nan"))
     wl.out.fill_(float("nan"))

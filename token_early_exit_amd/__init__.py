@@ -22,12 +22,12 @@ RIVER_F32, RIVER_BF16 = 0, 1
 RULE_TOKEN, RULE_BATCH_MIN = 0, 1
 TIMED_FILL_PROJECTION, TIMED_FILL_PRODUCT = 0, 1
 (OP_ROUTE, OP_COMPACT, OP_KV_FILL, OP_RIDGE_FIT, OP_KV_FILL_LAYER, OP_DECODE_STEP,
- OP_ROUTER_FIT) = 0, 1, 2, 3, 4, 5, 6
+ OP_ROUTER_FIT, OP_KV_FOLD) = 0, 1, 2, 3, 4, 5, 6, 7
 STATUS = {0: "OK", 1: "ERR_ARG", 2: "ERR_DTYPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED",
           5: "ERR_WORKSPACE", 6: "ERR_NOT_SPD", 7: "ERR_HIP"}
 
 EXPORTS = ["river_route", "river_compact", "river_exit_projection", "river_kv_fill",
-           "river_kv_fill_layer", "river_decode_step", "river_router_fit", "river_ridge_fit",
+           "river_kv_fill_layer", "river_kv_fold", "river_kv_fill_folded", "river_decode_step", "river_router_fit", "river_ridge_fit",
            "river_workspace_size", "river_last_error", "river_version",
            "river_debug_set_compact_path", "river_debug_set_gemm_path",
            "river_debug_set_decode_path", "river_debug_set_fill_fuse", "river_debug_kv_fill_plan", "river_decode_step_static",
@@ -56,7 +56,7 @@ class RiverLayer(ctypes.Structure):
 class RiverCheckpoint(ctypes.Structure):
     _fields_ = [("layer", ctypes.c_int), ("h_prev", ctypes.c_void_p), ("h_cur", ctypes.c_void_p),
                 ("tau", ctypes.c_float), ("theta", ctypes.c_float), ("w_down", ctypes.c_void_p),
-                ("w_up", ctypes.c_void_p), ("maps", ctypes.c_void_p)]
+                ("w_up", ctypes.c_void_p), ("maps", ctypes.c_void_p), ("folded", ctypes.c_void_p)]
 
 
 _lib = None
@@ -94,11 +94,15 @@ def load():
     lib.river_decode_step_static.argtypes = [_I, _I, _I, _L, _I, ctypes.POINTER(RiverCheckpoint), _I, _P,
                                              _F, _I, _I, ctypes.POINTER(RiverW4),
                                              ctypes.POINTER(RiverW4), _I, _I, _P, _P, _P, _L, _P, _P]
+    lib.river_kv_fold.argtypes = [_I, _I, _P, ctypes.POINTER(RiverW4), ctypes.POINTER(RiverW4), _I, _I, _P,
+                                  _P, _S, _P]
+    lib.river_kv_fill_folded.argtypes = [_I, _P, _I, _P, _L, _I, _P, _P, _I, _P, _I, _I, _P, _P, _L, _P]
     lib.river_router_fit.argtypes = [_I, _I, _I, _P, _L, _P, _P, _F, _I, _P, _P, _I, _I, _P, _F, _F,
                                      _F, _F, _P, _P, _S, _P]
     lib.river_ridge_fit.argtypes = [_I, _I, _I, _I, _P, _I, _P, _I, _F, _P, _I, _P, _S, _P]
     for f in ("river_route", "river_compact", "river_exit_projection", "river_kv_fill",
-              "river_kv_fill_layer", "river_decode_step", "river_decode_step_static",
+              "river_kv_fill_layer", "river_kv_fold", "river_kv_fill_folded",
+              "river_decode_step", "river_decode_step_static",
               "river_router_fit", "river_ridge_fit",
               "river_debug_set_compact_path", "river_debug_set_gemm_path", "river_debug_set_decode_path",
               "river_debug_set_fill_fuse", "river_debug_time_kernels", "river_debug_kernel_times"):
@@ -334,6 +338,53 @@ def river_kv_fill(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, *, m_
                                 ws_n, _stream(stream)))
 
 
+def river_kv_fold(wk, wv, n_kv_heads, head_dim, F, *, maps=None, workspace=None, stream=None):
+    """F[l] = deq([Wk[l]; Wv[l]]) . maps[l] (bf16 [n_layers][2 n_out][d]);
+    wk, wv: (q, scale, zero, group) tuples; maps None folds the identity."""
+    n_layers, n_out, half = wk[0].shape
+    d = 2 * half
+    _check_w4(wk, n_layers, n_out, d, "wk")
+    _check_w4(wv, n_layers, n_out, d, "wv")
+    _need(n_out == n_kv_heads * head_dim, f"wk holds {n_out} outputs, not n_kv_heads * head_dim")
+    _need(tuple(F.shape) == (n_layers, 2 * n_out, d) and F.is_contiguous() and _dt(F) == RIVER_BF16,
+          f"F must be contiguous bf16 [{n_layers}][{2 * n_out}][{d}], got {tuple(F.shape)}")
+    if maps is not None:
+        _need(tuple(maps.shape) == (n_layers, d, d) and maps.is_contiguous() and _dt(maps) == RIVER_BF16,
+              f"maps must be contiguous bf16 [{n_layers}][{d}][{d}], got {tuple(maps.shape)}")
+    dk = w4(*wk)
+    dv = w4(*wv)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().river_kv_fold(d, n_layers, _ptr(maps), ctypes.byref(dk), ctypes.byref(dv), n_kv_heads,
+                                head_dim, _ptr(F), _ptr(workspace), ws_n, _stream(stream)))
+
+
+def river_kv_fill_folded(h, slot, F, n_kv_heads, head_dim, k_cache, v_cache, *, m_max=None, m_dev=None,
+                         row_idx=None, stream=None):
+    """river_kv_fill through F from river_kv_fold (bf16 throughout)."""
+    n_rows, d = h.shape
+    n_layers = F.shape[0]
+    n_out = n_kv_heads * head_dim
+    if m_max is None:
+        m_max = row_idx.shape[0] if row_idx is not None else n_rows
+    _need(tuple(F.shape) == (n_layers, 2 * n_out, d) and F.is_contiguous() and _dt(F) == RIVER_BF16,
+          f"F must be contiguous bf16 [{n_layers}][{2 * n_out}][{d}], got {tuple(F.shape)}")
+    for c, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(c.dim() == 4 and c.shape[0] == n_layers and tuple(c.shape[2:]) == (n_kv_heads, head_dim),
+              f"{nm} must be [{n_layers}][n_slots][{n_kv_heads}][{head_dim}], got {tuple(c.shape)}")
+        _need(c.is_contiguous(), f"{nm} must be contiguous")
+    _need(k_cache.shape[1] == v_cache.shape[1], "k_cache and v_cache must have the same slot count")
+    _need(slot.dim() == 1 and slot.shape[0] >= n_rows,
+          f"slot must hold one entry per row of h ({n_rows}), got {tuple(slot.shape)}")
+    if row_idx is not None:
+        _need(row_idx.dim() == 1 and row_idx.shape[0] >= m_max,
+              f"row_idx must hold m_max = {m_max} entries, got {tuple(row_idx.shape)}")
+    if m_dev is not None:
+        _need(m_dev.numel() >= 1, "m_dev must hold one count")
+    _check(load().river_kv_fill_folded(m_max, _ptr(m_dev), d, _ptr(h), _ld(h), n_rows, _ptr(row_idx),
+                                       _ptr(slot), n_layers, _ptr(F), n_kv_heads, head_dim, _ptr(k_cache),
+                                       _ptr(v_cache), k_cache.shape[1], _stream(stream)))
+
+
 def river_kv_fill_layer(h, slot, wk, wv, n_kv_heads, head_dim, k_cache, v_cache, *, m_max=None,
                         m_dev=None, row_idx=None, maps=None, norm_gamma=None, norm_eps=1e-6,
                         k_bias=None, v_bias=None, pos=None, rope_cos=None, rope_sin=None,
@@ -399,12 +450,18 @@ def _decode_args(checkpoints, wk, wv, n_kv_heads, head_dim, slot, k_cache, v_cac
             e = int(c["layer"])
             _need(tuple(mp.shape) == (n_layers - e, d, d) and mp.is_contiguous(),
                   f"checkpoint {i}: maps must be contiguous [{n_layers - e}][{d}][{d}]")
+        fo = c.get("folded")
+        if fo is not None:
+            e = int(c["layer"])
+            _need(tuple(fo.shape) == (n_layers - e, 2 * n_out, d) and fo.is_contiguous() and
+                  _dt(fo) == RIVER_BF16,
+                  f"checkpoint {i}: folded must be contiguous bf16 [{n_layers - e}][{2 * n_out}][{d}]")
         wd = c.get("w_down")
         if wd is not None:
             b = wd.shape[0]
         arr[i] = RiverCheckpoint(int(c["layer"]), _ptr(c["h_prev"]), _ptr(c["h_cur"]),
                                  float(c["tau"]), float(c["theta"]), _ptr(wd), _ptr(c.get("w_up")),
-                                 _ptr(c.get("maps")))
+                                 _ptr(c.get("maps")), _ptr(c.get("folded")))
     dk = w4(*wk)
     dv = w4(*wv)
     args = (n, d, _dt(h0), ld, len(checkpoints), arr, n_layers, _ptr(gamma), eps, b, rule,

@@ -213,6 +213,9 @@ size_t river_workspace_size(int op, int n, int d, int d_out, int n_targets, int 
     case RIVER_OP_ROUTER_FIT:
       if (n <= 0 || d <= 0 || d_out <= 0 || n_targets <= 0 || n_layers <= 0) return 0;
       return calib_workspace(n, d, d_out, n_targets, n_layers);
+    case RIVER_OP_KV_FOLD:
+      if (d <= 0 || d_out <= 0 || n_layers <= 0) return 0;
+      return kv_fold_workspace(d, d_out, n_layers, true);
     case RIVER_OP_RIDGE_FIT:
       if (n <= 0 || d <= 0 || d_out <= 0) return 0;
       return ridge_workspace(n, d, d_out, n_layers == RIVER_F32 ? RIVER_F32 : RIVER_BF16);
@@ -392,6 +395,61 @@ river_status river_kv_fill_layer(int m_max, const int32_t* m_dev, int d, river_d
                          n_slots, workspace, ws_bytes, s);
 }
 
+river_status river_kv_fold(int d, int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
+                           int n_kv_heads, int head_dim, void* F, void* workspace, size_t ws_bytes,
+                           hipStream_t s) {
+  g_err[0] = 0;
+  if (d < 0 || n_layers < 0) return fail(RIVER_ERR_ARG, "kv_fold: negative size");
+  if (d == 0 || n_layers == 0) return RIVER_OK;
+  if (n_kv_heads < 1 || head_dim < 1) return fail(RIVER_ERR_ARG, "kv_fold: n_kv_heads and head_dim must be >= 1");
+  if (!wk || !wv || !F) return fail(RIVER_ERR_ARG, "kv_fold: a required pointer is NULL");
+  for (const river_w4* w : {wk, wv}) {
+    if (!w->q || !w->scale || !w->zero) return fail(RIVER_ERR_ARG, "kv_fold: int4 descriptor has a NULL pointer");
+    if (!dt_ok(w->sz_dtype)) return fail(RIVER_ERR_DTYPE, "kv_fold: scale/zero dtype %d unsupported", (int)w->sz_dtype);
+    if (w->group < 2 || d % w->group || w->group % 2) return fail(RIVER_ERR_ARG, "kv_fold: group %d must be even and divide d", w->group);
+    if (!aligned16(w->q)) return fail(RIVER_ERR_ALIGN, "kv_fold: int4 weights must be 16-byte aligned");
+  }
+  if ((int64_t)n_kv_heads * head_dim > (1 << 24)) return fail(RIVER_ERR_ARG, "kv_fold: n_kv_heads * head_dim too large");
+  const int nh = n_kv_heads * head_dim;
+  if (!kv_fold_ok(d, nh, wk, wv))
+    return fail(RIVER_ERR_UNSUPPORTED, "kv_fold: needs d %% 256 == 0, n_out %% 64 == 0 and groups of 64k (d = %d, n_out = %d)", d, nh);
+  if (n_layers > 65535) return fail(RIVER_ERR_UNSUPPORTED, "kv_fold: at most 65535 layers per call");
+  if (!aligned16(F) || (maps && !aligned16(maps))) return fail(RIVER_ERR_ALIGN, "kv_fold: F and maps must be 16-byte aligned");
+  if (maps) {
+    const size_t need = kv_fold_workspace(d, nh, 1, true);
+    if (!workspace || ws_bytes < need)
+      return fail(RIVER_ERR_WORKSPACE, "kv_fold: at least %zu workspace bytes needed, %zu given", need, ws_bytes);
+    if (!aligned16(workspace)) return fail(RIVER_ERR_ALIGN, "kv_fold: workspace must be 16-byte aligned");
+  }
+  return launch_kv_fold(d, n_layers, maps, wk, wv, nh, F, workspace, ws_bytes, s);
+}
+
+river_status river_kv_fill_folded(int m_max, const int32_t* m_dev, int d, const void* h, int64_t ld_h,
+                                  int n_rows, const int32_t* row_idx, const int32_t* slot, int n_layers,
+                                  const void* F, int n_kv_heads, int head_dim, void* k_cache,
+                                  void* v_cache, int64_t n_slots, hipStream_t s) {
+  g_err[0] = 0;
+  if (m_max < 0 || n_layers < 0 || n_rows < 0) return fail(RIVER_ERR_ARG, "kv_fill_folded: negative size");
+  if (m_max == 0 || n_layers == 0) return RIVER_OK;
+  if (d < 8 || d % 8) return fail(RIVER_ERR_ARG, "kv_fill_folded: d = %d must be a positive multiple of 8", d);
+  if (n_kv_heads < 1 || head_dim < 1) return fail(RIVER_ERR_ARG, "kv_fill_folded: n_kv_heads and head_dim must be >= 1");
+  if (!h || !slot || !F || !k_cache || !v_cache) return fail(RIVER_ERR_ARG, "kv_fill_folded: a required pointer is NULL");
+  if (!row_idx && m_max > n_rows) return fail(RIVER_ERR_ARG, "kv_fill_folded: m_max = %d > n_rows = %d without row_idx", m_max, n_rows);
+  if (n_slots < 1) return fail(RIVER_ERR_ARG, "kv_fill_folded: n_slots must be >= 1");
+  if (!ld_ok(ld_h, d, RIVER_BF16) || !aligned16(h)) return fail(RIVER_ERR_ALIGN, "kv_fill_folded: h misaligned or ld_h invalid");
+  if ((int64_t)n_kv_heads * head_dim > (1 << 24)) return fail(RIVER_ERR_ARG, "kv_fill_folded: n_kv_heads * head_dim too large");
+  const int64_t nh = (int64_t)n_kv_heads * head_dim;
+  if (d % 256 || nh % 64) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill_folded: needs d %% 256 == 0 and n_out %% 64 == 0");
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)n_rows * ld_h * 2 >= lim || 4 * nh * d >= lim)
+    return fail(RIVER_ERR_UNSUPPORTED, "kv_fill_folded: an operand spans 2^31 bytes or more");
+  if (n_layers > 65535) return fail(RIVER_ERR_UNSUPPORTED, "kv_fill_folded: at most 65535 layers per call");
+  if (!aligned16(F) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(RIVER_ERR_ALIGN, "kv_fill_folded: F and the caches must be 16-byte aligned");
+  return launch_kv_fill_folded(m_max, m_dev, d, h, ld_h, n_rows, row_idx, slot, n_layers, F, (int)nh,
+                               k_cache, v_cache, n_slots, s);
+}
+
 // fork_ok: the step may run one checkpoint's fill on a second stream (made
 // on first use); the allocation-free entry point never does
 static river_status decode_step(int n, int d, river_dtype dt, int64_t ld, int n_ck,
@@ -425,7 +483,13 @@ static river_status decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
       if (!k.w_up) return fail(RIVER_ERR_ARG, "decode_step: checkpoint %d: w_up is NULL while w_down is set", c);
       if (!aligned16(k.w_down) || !aligned16(k.w_up)) return fail(RIVER_ERR_ALIGN, "decode_step: router weights must be 16-byte aligned");
     }
-    any_maps |= k.maps != nullptr;
+    if (k.folded) {
+      if (dt != RIVER_BF16) return fail(RIVER_ERR_DTYPE, "decode_step: checkpoint %d: folded products need bf16", c);
+      if (!aligned16(k.folded)) return fail(RIVER_ERR_ALIGN, "decode_step: checkpoint %d: folded products must be 16-byte aligned", c);
+      if (d % 256 || ((int64_t)n_kv_heads * head_dim) % 64 || (int64_t)4 * n_kv_heads * head_dim * d >= ((int64_t)1 << 31))
+        return fail(RIVER_ERR_UNSUPPORTED, "decode_step: checkpoint %d: folded products need d %% 256 == 0 and n_out %% 64 == 0", c);
+    }
+    any_maps |= k.maps != nullptr && !k.folded;
   }
   const size_t fixed = decode_fixed_workspace(n, d, dt, n_layers);
   const size_t need = fixed + (any_maps ? kv_fill_workspace(n, d, 1, dt) : 0);
@@ -439,7 +503,7 @@ static river_status decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     decode_layer_offset(*wk, e, n_kv_heads * head_dim, d, &k4);
     decode_layer_offset(*wv, e, n_kv_heads * head_dim, d, &v4);
     river_status st = kv_fill_validate("decode_step", n, d, dt, ck[c].h_cur, ld, n, nullptr, slot,
-                                       n_layers - e, ck[c].maps, &k4, &v4, nullptr, n_kv_heads,
+                                       n_layers - e, ck[c].folded ? nullptr : ck[c].maps, &k4, &v4, nullptr, n_kv_heads,
                                        head_dim, k_cache, v_cache, n_slots,
                                        (char*)workspace + fixed, ws_bytes - fixed);
     if (st != RIVER_OK) return st;
@@ -475,7 +539,7 @@ river_status river_decode_step_static(int n, int d, river_dtype dt, int64_t ld, 
   river_status st = decode_static_scratch(&p, &cap);
   if (st != RIVER_OK) return st;
   bool any_maps = false;
-  for (int c = 0; c < n_ck; ++c) any_maps |= ck[c].maps != nullptr;
+  for (int c = 0; c < n_ck; ++c) any_maps |= ck[c].maps != nullptr && !ck[c].folded;
   // the least river_decode_step takes, and the size that fills every
   // checkpoint in one pass with room for the split reductions
   const size_t need = decode_fixed_workspace(n, d, dt, n_layers) + (any_maps ? kv_fill_workspace(n, d, 1, dt) : 0);

@@ -403,7 +403,7 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     river_w4 k0, v0;
     uint32_t mask = 0;
     for (int c = 0; c < n_ck; ++c)
-      if (!ck[c].maps) mask |= 1u << c;
+      if (!ck[c].maps && !ck[c].folded) mask |= 1u << c;
     bool single = mask != 0 && (__builtin_popcount(mask) >= 2 || mask == (n_ck == 32 ? ~0u : (1u << n_ck) - 1));
     const int c0 = single ? __builtin_ctz(mask) : 0;
     if (single) {
@@ -440,20 +440,26 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
       ++n_fills;
     }
     size_t side_bytes = 0;
+    bool use_side = false;
+    // a checkpoint with folded products fills without workspace
+    auto ck_maps = [&](int c) { return ck[c].maps != nullptr && !ck[c].folded; };
     if (fork_ok && side_c >= 0 && n_fills >= 2 && decode_path_override() == 0) {
       const size_t need_side =
-          kv_fill_full_workspace(n, d, n_out, n_layers - ck[side_c].layer, ck[side_c].maps != nullptr);
+          ck[side_c].folded ? 0 : kv_fill_full_workspace(n, d, n_out, n_layers - ck[side_c].layer, ck_maps(side_c));
       size_t need_rest = single ? kv_fill_full_workspace(n, d, n_out, n_layers - ck[c0].layer, false) : 0;
       for (int c = side_c + 1; c < n_ck; ++c) {
         if (single && ((mask >> c) & 1u)) continue;
-        const size_t b = kv_fill_full_workspace(n, d, n_out, n_layers - ck[c].layer, ck[c].maps != nullptr);
+        const size_t b = ck[c].folded ? 0 : kv_fill_full_workspace(n, d, n_out, n_layers - ck[c].layer, ck_maps(c));
         need_rest = b > need_rest ? b : need_rest;
       }
-      if (need_side + need_rest <= fws_bytes) side_bytes = align_up(need_side, 256);
+      if (need_side + need_rest <= fws_bytes) {
+        side_bytes = align_up(need_side, 256);
+        use_side = true;
+      }
     }
     DecodeSide* side = nullptr;
     std::unique_lock<std::mutex> side_lock;
-    if (side_bytes) {
+    if (use_side) {
       st = decode_side(&side);
       if (st != RIVER_OK) return st;
       side_lock = std::unique_lock<std::mutex>(side->mu);
@@ -464,6 +470,11 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     auto fill_ck = [&](int c, void* ws, size_t wsb, hipStream_t on) -> river_status {
       const river_checkpoint& k = ck[c];
       const int e = k.layer;
+      if (k.folded)
+        return launch_kv_fill_folded(n, q.counts + c * 64 + 1, d, k.h_cur, ld, n,
+                                     q.exit_idx + (size_t)c * q.idx_stride, slot, n_layers - e, k.folded, n_out,
+                                     (char*)k_cache + e * cache_layer, (char*)v_cache + e * cache_layer,
+                                     n_slots, on);
       river_w4 k4, v4;
       decode_layer_offset(*wk, e, n_out, d, &k4);
       decode_layer_offset(*wv, e, n_out, d, &v4);
@@ -472,14 +483,14 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
                             (char*)k_cache + e * cache_layer, (char*)v_cache + e * cache_layer, n_slots, ws,
                             wsb, on);
     };
-    if (side_bytes) {
+    if (use_side) {
       CuBudget budget(DECODE_SIDE_CUS);
       st = fill_ck(side_c, fws, side_bytes, side->stream);
     }
     void* rws = (char*)fws + side_bytes;
     const size_t rws_bytes = fws_bytes - side_bytes;
     if (st == RIVER_OK) {
-      CuBudget budget(side_bytes ? N_CU - DECODE_SIDE_CUS : N_CU);
+      CuBudget budget(use_side ? N_CU - DECODE_SIDE_CUS : N_CU);
       if (single) {
         DecodeGather gq{};
         gq.n = n; gq.row_bytes = (int)(d * esize(dt)); gq.ld_bytes = ld * (int64_t)esize(dt);
@@ -495,11 +506,11 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
         }
       }
       for (int c = 0; c < n_ck && st == RIVER_OK; ++c) {
-        if ((single && ((mask >> c) & 1u)) || (side_bytes && c == side_c)) continue;
+        if ((single && ((mask >> c) & 1u)) || (use_side && c == side_c)) continue;
         st = fill_ck(c, rws, rws_bytes, s);
       }
     }
-    if (side_bytes) {
+    if (use_side) {
       // join, also after a failed launch, so that a capture of s stays whole
       hipError_t e = hipEventRecord(side->join, side->stream);
       if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
@@ -521,6 +532,12 @@ river_status launch_decode_step(int n, int d, river_dtype dt, int64_t ld, int n_
     st = launch_compact(n, d, dt, mask, nullptr, 0, nullptr, cont_idx, exit_idx, counts, nullptr, 0,
                         nullptr, nullptr, 0, 0, cws, cws_bytes, s);
     if (st != RIVER_OK) return st;
+    if (k.folded) {
+      st = launch_kv_fill_folded(n, counts + 1, d, k.h_cur, ld, n, exit_idx, slot, n_layers - e, k.folded, n_out,
+                                 (char*)k_cache + e * cache_layer, (char*)v_cache + e * cache_layer, n_slots, s);
+      if (st != RIVER_OK) return st;
+      continue;
+    }
     river_w4 k4, v4;
     decode_layer_offset(*wk, e, n_out, d, &k4);
     decode_layer_offset(*wv, e, n_out, d, &v4);

@@ -1,6 +1,9 @@
 // bf16 GEMM for decode-sized row counts: C[z] = A[z] . B[z]^T (both operands
-// K-contiguous), fp32 accumulation, bf16 output; the map GEMM of a fill whose
-// row bound is at most 256 (a decode step's exits at one checkpoint).
+// K-contiguous), fp32 accumulation, bf16 output (EPI_BF16), or EPI_CACHE:
+// columns [0, nh) to the K cache and [nh, 2 nh) to the V cache at the slot
+// of each row. The map GEMM of a fill whose row bound is at most 256 (a
+// decode step's exits at one checkpoint), and the projection of such rows
+// through folded products F = deq([Wk; Wv]) . M (EPI_CACHE).
 //
 // There the time goes into streaming the maps (B), d x d per layer, from
 // HBM: 21 maps of 4096 x 4096 are 705 MB for 13 rows. The 128-row tiles of
@@ -39,7 +42,9 @@ namespace river {
 
 constexpr int NARROW_BM = 32, NARROW_BN = 128, NARROW_NS = 8;
 
+template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_narrow_kernel(GemmArgs g, int tiles_n, int batch) {
+  static_assert(EPI == EPI_BF16 || EPI == EPI_CACHE, "bf16 output");
   constexpr int BM = NARROW_BM, BN = NARROW_BN;
   constexpr int SSZ = (BM + BN) * 8;     // one stage in 16-byte chunks (20 KB)
   constexpr int BD = BN * 8 / 256;       // B loads per thread per slab (A: one)
@@ -173,9 +178,24 @@ __global__ __launch_bounds__(256, 1) void gemm_narrow_kernel(GemmArgs g, int til
     iter(std::integral_constant<int, 7>{}, kt + 7, std::integral_constant<int, 0>{}, F_{});
 
     // epilogue straight from the accumulator: row m0 + l % 32, columns
-    // n0 + 32 wave + 8 gq + 4 h + 0..3
+    // n0 + 32 wave + 8 gq + 4 h + 0..3 (EPI_CACHE: nh % 4 == 0, so the four
+    // lie in one half; a row whose id or slot is out of range is dropped)
     const int row = m0 + (lane & 31);
-    if (row < M) {
+    if constexpr (EPI == EPI_CACHE) {
+      const int er = row < M ? (g.e_rows ? g.e_rows[row] : row) : -1;
+      const int slot = er >= 0 && er < g.e_nrows ? g.slot[er] : -1;
+      if (slot >= 0 && slot < g.n_slots) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = n0 + wave * 32 + 8 * gq + 4 * h;
+          if (col >= N) continue;
+          const bool isv = col >= g.nh;
+          *(uint2*)((uint16_t*)(isv ? g.vc : g.kc) + (int64_t)z * g.cache_bstride + (int64_t)slot * g.nh +
+                    (isv ? col - g.nh : col)) =
+              uint2{pack_bf16x2(acc[4 * gq], acc[4 * gq + 1]), pack_bf16x2(acc[4 * gq + 2], acc[4 * gq + 3])};
+        }
+      }
+    } else if (row < M) {
       uint16_t* C = (uint16_t*)g.C + (int64_t)z * g.c_bstride + (int64_t)row * g.ldc;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
@@ -192,12 +212,13 @@ __global__ __launch_bounds__(256, 1) void gemm_narrow_kernel(GemmArgs g, int til
 // gemm_launch; at most one workgroup per CU (160 KB of LDS).
 inline bool gemm_narrow_ok(const GemmArgs& g) { return g.K % 512 == 0 && g.N % 4 == 0; }
 
+template <int EPI = EPI_BF16>
 inline void gemm_narrow_launch(const GemmArgs& g, int batch, hipStream_t s) {
   const int tn = (g.N + NARROW_BN - 1) / NARROW_BN;
   const int tm = (g.M_max + NARROW_BM - 1) / NARROW_BM;
   const int64_t tiles = (int64_t)tn * tm * batch;
   const int grid = persistent_grid(tiles);
-  gemm_narrow_kernel<<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);
+  gemm_narrow_kernel<EPI><<<dim3(grid, 1), 256, 0, s>>>(g, tn, batch);
 }
 
 }  // namespace river

@@ -72,6 +72,15 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
 // one count (the plain MFMA path only: no maps, no layer parts)
 bool kv_fill_plain_mfma(int m_max, int d, river_dtype dt, int n_rows, int64_t ld_h, const river_w4* wk,
                         const river_w4* wv, int nh);
+// folded products F[l] = deq([Wk[l]; Wv[l]]) . maps[l] and the fill through them
+size_t kv_fold_workspace(int d, int n_out, int chunk, bool maps);
+bool kv_fold_ok(int d, int nh, const river_w4* wk, const river_w4* wv);
+river_status launch_kv_fold(int d, int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
+                            int nh, void* F, void* workspace, size_t ws_bytes, hipStream_t s);
+river_status launch_kv_fill_folded(int m_max, const int32_t* m_dev, int d, const void* h, int64_t ld_h,
+                                   int n_rows, const int32_t* row_idx, const int32_t* slot, int n_layers,
+                                   const void* F, int nh, void* k_cache, void* v_cache, int64_t n_slots,
+                                   hipStream_t s);
 
 // cosine and router probability of every token at every checkpoint (all
 // with a router) in one launch, [n_ck][n] each; mask_scratch [n_ck][n]

@@ -468,6 +468,61 @@ size_t kv_fill_layer_workspace(int m_max, int d, int n_layers) {
   return (size_t)n_layers * (layer_xhat_bytes(m_max, d) + layer_ss_bytes(m_max, d));
 }
 
+// The int4 fields of GemmArgs for the K/V weights of a fill (layer 0 of the
+// descriptors at q[0], s[0], zp[0] for K and [1] for V).
+static void set_w4(GemmArgs& g, int d, int nh, const river_w4* wk, const river_w4* wv) {
+  g.q[0] = wk->q; g.q[1] = wv->q;
+  g.s[0] = wk->scale; g.s[1] = wv->scale;
+  g.zp[0] = wk->zero; g.zp[1] = wv->zero;
+  g.group[0] = wk->group; g.group[1] = wv->group;
+  g.sz_bf16[0] = wk->sz_dtype == RIVER_BF16; g.sz_bf16[1] = wv->sz_dtype == RIVER_BF16;
+  g.nh = nh;
+  g.q_bstride = (int64_t)nh * d / 2;
+  g.sz_bstride[0] = (int64_t)nh * (d / wk->group);
+  g.sz_bstride[1] = (int64_t)nh * (d / wv->group);
+}
+
+// F[l] = deq([Wk[l]; Wv[l]]) . maps[l] for layers l0 .. l0 + nl - 1 of the
+// weights in g (set_w4): the weights dequantised as the int4 kernels form
+// them, the maps transposed, then the product (rows: the 2 n_out outputs,
+// reduction over the map's output index, a row of the transposed map),
+// rounded to bf16 into F (layer stride f_bs elements). Without maps F is the
+// dequantised weights. ws holds chunk layers of dequantised weights followed
+// by chunk layers of transposed maps (nl <= chunk).
+static river_status form_products(const GemmArgs& g, int d, int l0, int nl, const void* maps, uint16_t* F,
+                                  int64_t f_bs, void* ws, int chunk, hipStream_t s) {
+  const int nh = g.nh;
+  const size_t wb = align_up((size_t)2 * nh * d * 2, 256);
+  GemmArgs q = g;
+  q.N = 2 * nh;
+  q.q[0] = g.q[0] + (int64_t)l0 * q.q_bstride;
+  q.q[1] = g.q[1] + (int64_t)l0 * q.q_bstride;
+  q.s[0] = (const char*)g.s[0] + (int64_t)l0 * q.sz_bstride[0] * (g.sz_bf16[0] ? 2 : 4);
+  q.zp[0] = (const char*)g.zp[0] + (int64_t)l0 * q.sz_bstride[0] * (g.sz_bf16[0] ? 2 : 4);
+  q.s[1] = (const char*)g.s[1] + (int64_t)l0 * q.sz_bstride[1] * (g.sz_bf16[1] ? 2 : 4);
+  q.zp[1] = (const char*)g.zp[1] + (int64_t)l0 * q.sz_bstride[1] * (g.sz_bf16[1] ? 2 : 4);
+  if (!maps) {
+    if (f_bs != (int64_t)q.N * d) return fail(RIVER_ERR_ARG, "kv_fold: identity needs a packed F");
+    return w4_dequant_launch(q, nl, F, s);
+  }
+  uint16_t* dq = (uint16_t*)ws;
+  uint16_t* tr = (uint16_t*)((char*)ws + (size_t)chunk * wb);
+  river_status st = w4_dequant_launch(q, nl, dq, s);
+  if (st != RIVER_OK) return st;
+  transpose_maps_kernel<<<dim3((unsigned)(d / 64), (unsigned)(d / 64), (unsigned)nl), 256, 0, s>>>(
+      (const uint16_t*)maps + (int64_t)l0 * d * d, tr, d);
+  if ((st = check_launch("kv_fill map transposition")) != RIVER_OK) return st;
+  GemmArgs f{};
+  f.M_max = q.N; f.N = d; f.K = d;
+  f.A = dq; f.lda = d; f.a_bstride = (int64_t)q.N * d; f.a_nrows = q.N;
+  f.B = tr; f.ldb = d; f.b_bstride = (int64_t)d * d;
+  f.C = F; f.ldc = d; f.c_bstride = f_bs;
+  const int tf = debug_timer_begin(s, RIVER_TIMED_FILL_PRODUCT);
+  gemm_bf16_auto<EPI_BF16>(f, nl, s);
+  debug_timer_end(s, tf);
+  return check_launch("kv_fill map-weight product");
+}
+
 river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype dt, const void* h,
                             int64_t ld_h, int n_rows, const int32_t* row_idx, const int32_t* slot,
                             int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
@@ -506,15 +561,7 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
   g.M_max = m_max;
   g.M_dev = m_dev;
   g.M_dev_z = m_dev_layer;
-  g.q[0] = wk->q; g.q[1] = wv->q;
-  g.s[0] = wk->scale; g.s[1] = wv->scale;
-  g.zp[0] = wk->zero; g.zp[1] = wv->zero;
-  g.group[0] = wk->group; g.group[1] = wv->group;
-  g.sz_bf16[0] = wk->sz_dtype == RIVER_BF16; g.sz_bf16[1] = wv->sz_dtype == RIVER_BF16;
-  g.nh = nh;
-  g.q_bstride = (int64_t)nh * d / 2;
-  g.sz_bstride[0] = (int64_t)nh * (d / wk->group);
-  g.sz_bstride[1] = (int64_t)nh * (d / wv->group);
+  set_w4(g, d, nh, wk, wv);
   g.slot = slot;
   g.n_slots = n_slots;
   g.e_nrows = n_rows;
@@ -620,47 +667,24 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
   }
 
   if (maps && !layer && fused_wanted(m_max, m_dev != nullptr, d, nh, ws_bytes)) {
-    // per chunk: the weights dequantised (as the int4 path forms them), the
-    // maps transposed, F = deq(W) . maps, then the exit states through F
-    const size_t wb = align_up((size_t)2 * nh * d * 2, 256), tb = align_up((size_t)d * d * 2, 256);
-    const size_t per = 2 * wb + tb;
-    const int fchunk = ws_bytes / per < (size_t)n_layers ? (int)(ws_bytes / per) : n_layers;
-    uint16_t* dq = (uint16_t*)workspace;
-    uint16_t* tr = (uint16_t*)((char*)workspace + (size_t)fchunk * wb);
-    uint16_t* fw = (uint16_t*)((char*)workspace + (size_t)fchunk * (wb + tb));
+    // per chunk: F = deq(W) . maps in the workspace, then the exit states
+    // through F
+    const size_t wb = align_up((size_t)2 * nh * d * 2, 256);
+    const int fchunk = ws_bytes / fused_layer_bytes(d, nh) < (size_t)n_layers
+                           ? (int)(ws_bytes / fused_layer_bytes(d, nh)) : n_layers;
+    uint16_t* fw = (uint16_t*)((char*)workspace + (size_t)fchunk * (fused_layer_bytes(d, nh) - wb));
     for (int l0 = 0; l0 < n_layers; l0 += fchunk) {
       const int nl = n_layers - l0 < fchunk ? n_layers - l0 : fchunk;
-      GemmArgs q = g;
-      q.N = 2 * nh;
-      q.q[0] = wk->q + (int64_t)l0 * q.q_bstride;
-      q.q[1] = wv->q + (int64_t)l0 * q.q_bstride;
-      q.s[0] = (const char*)wk->scale + (int64_t)l0 * q.sz_bstride[0] * esize(wk->sz_dtype);
-      q.zp[0] = (const char*)wk->zero + (int64_t)l0 * q.sz_bstride[0] * esize(wk->sz_dtype);
-      q.s[1] = (const char*)wv->scale + (int64_t)l0 * q.sz_bstride[1] * esize(wv->sz_dtype);
-      q.zp[1] = (const char*)wv->zero + (int64_t)l0 * q.sz_bstride[1] * esize(wv->sz_dtype);
-      river_status st = w4_dequant_launch(q, nl, dq, s);
+      river_status st = form_products(g, d, l0, nl, maps, fw, (int64_t)wb / 2, workspace, fchunk, s);
       if (st != RIVER_OK) return st;
-      transpose_maps_kernel<<<dim3((unsigned)(d / 64), (unsigned)(d / 64), (unsigned)nl), 256, 0, s>>>(
-          (const uint16_t*)maps + (int64_t)l0 * d * d, tr, d);
-      if ((st = check_launch("kv_fill map transposition")) != RIVER_OK) return st;
-      // F[l] = deq(W[l]) . maps[l]: rows = the 2 n_out outputs, reduction
-      // over the map's output index (a row of the transposed map)
-      GemmArgs f{};
-      f.M_max = q.N; f.N = d; f.K = d;
-      f.A = dq; f.lda = d; f.a_bstride = (int64_t)q.N * d; f.a_nrows = q.N;
-      f.B = tr; f.ldb = d; f.b_bstride = (int64_t)d * d;
-      f.C = fw; f.ldc = d; f.c_bstride = (int64_t)wb / 2;
-      const int tf = debug_timer_begin(s, RIVER_TIMED_FILL_PRODUCT);
-      gemm_bf16_auto<EPI_BF16>(f, nl, s);
-      debug_timer_end(s, tf);
-      if ((st = check_launch("kv_fill map-weight product")) != RIVER_OK) return st;
       // [K|V][l] = X . F[l]^T into the cache
-      GemmArgs pr = q;
+      GemmArgs pr = g;
+      pr.N = 2 * nh;
       pr.A = (const uint16_t*)h; pr.lda = ld_h; pr.a_bstride = 0; pr.a_rows = row_idx; pr.a_nrows = n_rows;
       pr.B = fw; pr.ldb = d; pr.b_bstride = (int64_t)wb / 2;
       pr.e_rows = row_idx;
-      pr.kc = (uint16_t*)k_cache + (int64_t)l0 * q.cache_bstride;
-      pr.vc = (uint16_t*)v_cache + (int64_t)l0 * q.cache_bstride;
+      pr.kc = (uint16_t*)k_cache + (int64_t)l0 * g.cache_bstride;
+      pr.vc = (uint16_t*)v_cache + (int64_t)l0 * g.cache_bstride;
       const int tp = debug_timer_begin(s, RIVER_TIMED_FILL_PROJECTION);
       gemm_cache_launch(pr, nl, s);
       debug_timer_end(s, tp);
@@ -735,6 +759,62 @@ river_status launch_kv_fill(int m_max, const int32_t* m_dev, int d, river_dtype 
     if (st != RIVER_OK) return st;
   }
   return RIVER_OK;
+}
+
+// workspace of river_kv_fold for chunk layers per pass: the dequantised
+// weights and the transposed map of each (nothing without maps)
+size_t kv_fold_workspace(int d, int n_out, int chunk, bool maps) {
+  if (!maps || chunk <= 0) return 0;
+  return (size_t)chunk * (fused_layer_bytes(d, n_out) - align_up((size_t)2 * n_out * d * 2, 256));
+}
+
+// the shapes the folded products take: bf16, d % 128 == 0 (the 256 x 256
+// product and projection tiles), 2 n_out outputs in 64-column blocks
+bool kv_fold_ok(int d, int nh, const river_w4* wk, const river_w4* wv) {
+  return fill_mfma_ok(d, RIVER_BF16, nh, wk, wv, 0, 0) && d % 128 == 0 && nh % 8 == 0;
+}
+
+river_status launch_kv_fold(int d, int n_layers, const void* maps, const river_w4* wk, const river_w4* wv,
+                            int nh, void* F, void* workspace, size_t ws_bytes, hipStream_t s) {
+  GemmArgs g{};
+  g.K = d;
+  set_w4(g, d, nh, wk, wv);
+  const int64_t f_bs = (int64_t)2 * nh * d;
+  const size_t per = kv_fold_workspace(d, nh, 1, maps != nullptr);
+  const int chunk = !maps ? n_layers : (ws_bytes / per < (size_t)n_layers ? (int)(ws_bytes / per) : n_layers);
+  for (int l0 = 0; l0 < n_layers; l0 += chunk) {
+    const int nl = n_layers - l0 < chunk ? n_layers - l0 : chunk;
+    river_status st = form_products(g, d, l0, nl, maps, (uint16_t*)F + l0 * f_bs, f_bs, workspace, chunk, s);
+    if (st != RIVER_OK) return st;
+  }
+  return RIVER_OK;
+}
+
+// [K|V][l] = X . F[l]^T into the cache: the 32 x 128 tiles with eight slabs
+// of F in flight for a decode-sized row bound (at most 256 rows, d % 512),
+// the 256 x 256 tiles otherwise; the row count on the host (m_max) or on the
+// device (m_dev, at most m_max). No workspace.
+river_status launch_kv_fill_folded(int m_max, const int32_t* m_dev, int d, const void* h, int64_t ld_h,
+                                   int n_rows, const int32_t* row_idx, const int32_t* slot, int n_layers,
+                                   const void* F, int nh, void* k_cache, void* v_cache, int64_t n_slots,
+                                   hipStream_t s) {
+  GemmArgs g{};
+  g.M_max = m_max; g.M_dev = m_dev;
+  g.N = 2 * nh; g.K = d; g.nh = nh;
+  g.A = (const uint16_t*)h; g.lda = ld_h; g.a_bstride = 0; g.a_rows = row_idx; g.a_nrows = n_rows;
+  g.B = (const uint16_t*)F; g.ldb = d; g.b_bstride = (int64_t)2 * nh * d;
+  g.e_rows = row_idx; g.e_nrows = n_rows;
+  g.slot = slot; g.n_slots = n_slots;
+  g.cache_bstride = n_slots * nh;
+  g.kc = k_cache; g.vc = v_cache;
+  if (m_max <= 256 && gemm_narrow_ok(g) && gemm_path_override() == 0) {
+    gemm_narrow_launch<EPI_CACHE>(g, n_layers, s);
+    return check_launch("kv_fill folded (32-row tiles)");
+  }
+  const int tp = debug_timer_begin(s, RIVER_TIMED_FILL_PROJECTION);
+  gemm_cache_launch(g, n_layers, s);
+  debug_timer_end(s, tp);
+  return check_launch("kv_fill folded");
 }
 
 // the plan of a plain bf16 fill with maps (the test hook
