@@ -63,8 +63,8 @@ def parse():
                     help="context length of the long-context prefill (the headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default=None,
-                    choices=["long", "8b", "gpt2", "route-compact", "decode2", "decode3D", "router-fit",
-                             "copy"],
+                    choices=["long", "8b", "8b-folded", "gpt2", "route-compact", "decode2", "decode3D",
+                             "decode3D-folded", "router-fit", "copy"],
                     help="run one workload only and print its figures (profiling runs)")
     ap.add_argument("--copy-probe-mb", type=int, default=256,
                     help="with --only copy: a plain device copy of this many MiB (counter calibration)")
@@ -182,6 +182,19 @@ class LongContextWorkload:
     def step(self, i=0):
         self.compact()
         self.fill()
+
+    def fold(self):
+        """F = deq([Wk; Wv]) M of the 48 maps, formed once (river_kv_fold)."""
+        self.F, self.fold_ms = fold_maps(self.cfg, self.maps, self.wk, self.wv)
+
+    def fill_folded(self, i=0):
+        cfg = self.cfg
+        tee.river_kv_fill_folded(self.h, self.slot, self.F, cfg.n_kv_heads, cfg.head_dim, self.kc, self.vc,
+                                 m_max=self.m, row_idx=self.ext)
+
+    def step_folded(self, i=0):
+        self.compact()
+        self.fill_folded()
 
     def flops(self):
         """(the maps over every row, the projection of every row, the
@@ -468,6 +481,21 @@ class Gpt2Workload:
         self.route(s)
         self.compact(s)
         self.fill(s)
+
+    def fold(self):
+        """F = deq([Wk; Wv]) M of the 8 maps, formed once (river_kv_fold)."""
+        self.F, self.fold_ms = fold_maps(self.cfg, self.maps, self.wk, self.wv)
+
+    def fill_folded(self, s):
+        cfg = self.cfg
+        tee.river_kv_fill_folded(s["hc"], self.slot, self.F, cfg.n_kv_heads, cfg.head_dim, s["kc"], s["vc"],
+                                 m_max=cfg.n_tokens, m_dev=s["counts"][1:], row_idx=s["ext"])
+
+    def step_folded(self, i):
+        s = self.sets[i % len(self.sets)]
+        self.route(s)
+        self.compact(s)
+        self.fill_folded(s)
 
     def work(self, n_exit):
         cfg = self.cfg
@@ -972,6 +1000,26 @@ def long_context_figures(wl, steps, warmup):
                              "other_fill_ms is the weights' dequantisation and the maps' transposition"}
 
 
+def long_context_folded_figures(wl, steps, warmup):
+    """The long-context step with the 48 maps folded into the K/V weights
+    once beforehand (river_kv_fold): compaction, then the rows through F."""
+    wl.fold()
+    for i in range(warmup):
+        wl.step_folded(i)
+    ms = time_region(wl.step_folded, steps) / steps
+    fill_ms = time_region(wl.fill_folded, max(2, steps // 2)) / max(2, steps // 2)
+    _, proj_f, _ = wl.flops()
+    out = {"ms_per_step": ms, "exited_tokens_per_s": wl.m / (ms * 1e-3), "fill_ms": fill_ms,
+           "fill_tflops": proj_f / (fill_ms * 1e-3) / 1e12,
+           "fill_frac_of_bf16_peak": proj_f / (fill_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+           "fold_ms_once": wl.fold_ms,
+           "note": "the fill through the folded products F = deq([Wk; Wv]) M of the 48 maps, formed once "
+                   "(like the fit) instead of in every step"}
+    del wl.F
+    torch.cuda.empty_cache()
+    return out
+
+
 def prefill_8b_figures(steps=10, warmup=2, wl=None):
     """The 8B prefill step's figures; wl: an existing workload (e.g. one
     whose fills were folded)."""
@@ -1026,6 +1074,16 @@ def gpt2_figures(R, steps=200, warmup=20):
     rb, cb, ff = wl.work(n_exit)
     cfg = wl.cfg
     ep_bytes = n_exit * (2 * cfg.d * 2 + 4)
+    wl.fold()
+    for i in range(warmup):
+        wl.step_folded(i)
+    ms_folded = time_region(wl.step_folded, steps) / steps
+    fill_folded = graph_time(lambda i: wl.fill_folded(wl.sets[i % sets]), max(50, steps // 2), sets)
+    ff_folded = 2.0 * n_exit * wl.nl * cfg.d * 2 * cfg.n_kv_heads * cfg.head_dim
+    folded = {"ms_per_step": ms_folded, "exited_tokens_per_s": n_exit / (ms_folded * 1e-3),
+              "fill_us": fill_folded * 1e3, "fill_tflops": ff_folded / (fill_folded * 1e-3) / 1e12,
+              "fold_ms_once": wl.fold_ms,
+              "note": "the fill through the folded products F = deq([Wk; Wv]) M of the 8 maps, formed once"}
     return wl, {
         "workload": "gpt2-small-shape prefill: 4096 tokens, d=768, L=12, exit check at layer 4 (tau=0.9, "
                     "theta=0.5, router b=128), fill of layers 5-12 through ridge maps and int4 (group 64) "
@@ -1038,7 +1096,8 @@ def gpt2_figures(R, steps=200, warmup=20):
         "fill_tflops": ff / (k["fill"] * 1e-3) / 1e12,
         "exit_projection_gbs": ep_bytes / (k["exit_projection"] * 1e-3) / 1e9,
         "fill_layer_overhead_us": (k["fill_layer"] - k["fill"]) * 1e3,
-        "ridge_fit_ms_8_maps": wl.ridge_ms}
+        "ridge_fit_ms_8_maps": wl.ridge_ms,
+        "folded": folded}
 
 
 def main():
@@ -1062,6 +1121,15 @@ def main():
         return
     if only == "router-fit":
         print(json.dumps({"router_fit": router_fit_all()}))
+        return
+    if only == "decode3D-folded":
+        print(json.dumps({"decode_step_folded": decode_times("3D", 20, folded=True)}))
+        return
+    if only == "8b-folded":
+        wl8 = Prefill8BWorkload()
+        wl8.fold()
+        _, ff = prefill_8b_figures(args.steps, args.warmup, wl=wl8)
+        print(json.dumps({"prefill_8b_folded": ff}))
         return
     if only in ("decode2", "decode3D"):
         key = 2 if only == "decode2" else "3D"
@@ -1089,8 +1157,9 @@ def main():
     progress(f"long context N={args.tokens}: {wl.m} rows x {wl.nl} layers, maps fitted in "
              f"{wl.ridge_ms:.0f} ms")
     ms_step, lc = long_context_figures(wl, args.steps, args.warmup)
+    lcf = long_context_folded_figures(wl, args.steps, args.warmup)
     if only == "long":
-        print(json.dumps({"long_context": lc, "ms_per_step": ms_step}))
+        print(json.dumps({"long_context": lc, "ms_per_step": ms_step, "long_context_folded": lcf}))
         return
     value = wl.m / (ms_step * 1e-3)
     ach = lc["projection_flops_per_launch"] / (lc["projection_ms"] * 1e-3) / 1e12
@@ -1128,6 +1197,7 @@ def main():
         "fill_tflops": lc["fill_tflops"],
         "fill_frac_of_bf16_peak": lc["fill_frac_of_bf16_peak"],
         "long_context": lc,
+        "long_context_folded": lcf,
         "ridge_fit_ms_48_maps": wl.ridge_ms,
         "roofline": roof,
     }

@@ -146,12 +146,14 @@ def test_ridge_fit_long_context_full(long_calibration):
         assert rel <= 5e-3, (t, rel)
 
 
-@pytest.mark.parametrize("N", [32768, 65536])
-def test_long_context_step(long_calibration, N):
+@pytest.mark.parametrize("N,folded", [(32768, False), (65536, False), (65536, True)])
+def test_long_context_step(long_calibration, N, folded):
     """One step of the benchmark's long-context workload: the positional
     compaction, then the fill of every row between the first 16 and the
     last 2048 through 48 layers on the path the benchmark times (per layer
-    the product F = deq([Wk; Wv]) . maps, then the rows through F)."""
+    the product F = deq([Wk; Wv]) . maps, then the rows through F); folded:
+    the step with F formed once beforehand (river_kv_fold, then
+    river_kv_fill_folded)."""
     cfg0, _, _, mb, mf = long_calibration
     nl = 48
     wl = B.LongContextWorkload(N, maps=Cycle(mb, nl))
@@ -161,7 +163,11 @@ def test_long_context_step(long_calibration, N):
     assert tee.river_debug_kv_fill_plan(m, d, wl.n_out, nl, wl.ws.numel()) == (nl, 3, 1)
     wl.kc.fill_(float("nan"))
     wl.vc.fill_(float("nan"))
-    wl.step()
+    if folded:
+        wl.fold()
+        wl.step_folded()
+    else:
+        wl.step()
     torch.cuda.synchronize()
     # compaction of the positional mask: bit-exact
     assert wl.counts.cpu().tolist() == [N - m, m]
