@@ -441,6 +441,33 @@ def test_binding_rejects_mismatched_fill_shapes():
                                 k_bias=torch.zeros(2, 128, dtype=torch.bfloat16))
 
 
+def test_binding_rejects_mismatched_folded_shapes():
+    """The folded fill's wrappers check F, the caches and the dtypes
+    against each other before any call (CPU tensors: nothing runs)."""
+    import torch
+    d, hk, hd, nl = 256, 2, 64, 3
+    n_out = hk * hd
+    q = torch.zeros((nl, n_out, d // 2), dtype=torch.uint8)
+    sz = torch.ones((nl, n_out, d // 64), dtype=torch.bfloat16)
+    w = (q, sz, sz, 64)
+    F = torch.zeros((nl, 2 * n_out, d), dtype=torch.bfloat16)
+    h = torch.zeros((8, d), dtype=torch.bfloat16)
+    slot = torch.arange(8, dtype=torch.int32)
+    kc = torch.zeros((nl, 16, hk, hd), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tee.river_kv_fold(w, w, hk, hd, F[:, :n_out])                       # F rows != 2 n_out
+    with pytest.raises(ValueError):
+        tee.river_kv_fold(w, w, hk, hd, F.float())                          # F not bf16
+    with pytest.raises(ValueError):
+        tee.river_kv_fold(w, w, hk, hd, F, maps=torch.zeros((nl, d, d - 8), dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        tee.river_kv_fill_folded(h, slot, F, hk, hd, kc[:2], kc)            # cache layers != F layers
+    with pytest.raises(ValueError):
+        tee.river_kv_fill_folded(h.float(), slot, F, hk, hd, kc, kc)        # states not bf16
+    with pytest.raises(ValueError):
+        tee.river_kv_fill_folded(h, slot[:4], F, hk, hd, kc, kc)            # slot shorter than h
+
+
 def test_binding_rejects_mismatched_decode_and_ridge_shapes():
     import torch
     h, slot, w, kc = _fill_args(nl=4)

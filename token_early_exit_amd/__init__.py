@@ -368,6 +368,8 @@ def river_kv_fill_folded(h, slot, F, n_kv_heads, head_dim, k_cache, v_cache, *, 
         m_max = row_idx.shape[0] if row_idx is not None else n_rows
     _need(tuple(F.shape) == (n_layers, 2 * n_out, d) and F.is_contiguous() and _dt(F) == RIVER_BF16,
           f"F must be contiguous bf16 [{n_layers}][{2 * n_out}][{d}], got {tuple(F.shape)}")
+    _need(_dt(h) == RIVER_BF16 and _dt(k_cache) == RIVER_BF16 and _dt(v_cache) == RIVER_BF16,
+          "the folded fill takes bf16 states and caches")
     for c, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
         _need(c.dim() == 4 and c.shape[0] == n_layers and tuple(c.shape[2:]) == (n_kv_heads, head_dim),
               f"{nm} must be [{n_layers}][n_slots][{n_kv_heads}][{head_dim}], got {tuple(c.shape)}")
