@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import bench as B
 import oracle as O
 import token_early_exit_amd as tee
 from synth import get_config
@@ -152,6 +153,25 @@ def test_static_decode_8b_routers_maps_two_calls():
     e = a[0].cpu().numpy()
     assert (e == 11).sum() >= 10 and (e == 31).sum() + (e == 11).sum() == 256
     cfg2, cks2 = llama8b(100, tag="second")
+    slot2 = G.slots(cfg2, n=100, device=DEV)
+    (a2, b2), _ = both(cks2, cfg2, wk, wv, slot2)
+    assert_same(a2, b2)
+
+
+def test_static_decode_8b_folded_two_calls():
+    """The same step with the maps folded into the K/V weights beforehand
+    (river_kv_fold: those checkpoints fill without workspace), then 100
+    tokens."""
+    cfg, cks = llama8b(256)
+    slot = G.slots(cfg, device=DEV)
+    wk, wv = _kv(cfg, list(range(1, cfg.L + 1)))
+    B.fold_checkpoints(cfg, cks, wk, wv, DEV)
+    (a, b), _ = both(cks, cfg, wk, wv, slot)
+    assert_same(a, b)
+    e = a[0].cpu().numpy()
+    assert (e == 11).sum() >= 10 and (e == 31).sum() + (e == 11).sum() == 256
+    cfg2, cks2 = llama8b(100, tag="second")
+    B.fold_checkpoints(cfg2, cks2, wk, wv, DEV)
     slot2 = G.slots(cfg2, n=100, device=DEV)
     (a2, b2), _ = both(cks2, cfg2, wk, wv, slot2)
     assert_same(a2, b2)
