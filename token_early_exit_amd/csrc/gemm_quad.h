@@ -247,8 +247,10 @@ struct QuadTile {
         const int slot = S[r];
         if (slot < 0 || slot >= g.n_slots) continue;
         const bool isv = col >= g.nh;
-        *(u32x4*)((uint16_t*)(isv ? g.vc : g.kc) + (int64_t)z * g.cache_bstride + (int64_t)slot * g.nh +
-                  (isv ? col - g.nh : col)) = v;
+        // non-temporal: the cache rows are not read again here, so they
+        // should not push the operand rows out of L2
+        __builtin_nontemporal_store(v, (u32x4*)((uint16_t*)(isv ? g.vc : g.kc) + (int64_t)z * g.cache_bstride +
+                                                (int64_t)slot * g.nh + (isv ? col - g.nh : col)));
       } else {
         *(u32x4*)(C + (int64_t)row * g.ldc + col) = v;
       }
